@@ -1,0 +1,159 @@
+"""Seeded synthetic inputs for the packed-int4 weight GEMM.
+
+Shared by the tests, the benchmark and the smoke check; used by both the HIP
+path and the CPU oracle.  It holds no arithmetic of the method itself: it only
+draws random tensors (and, for the W4A8 variant, turns fp16 activations into
+per-row int8 codes, which is how those inputs are produced before they reach
+the GEMM).
+
+Seeds: ``np.random.SeedSequence([20261202, config_id, case_id])``; tensors are
+drawn in the fixed order A, q, |s|, sign, zero-noise.
+
+Value distributions (the workloads named by the benchmark configurations):
+  * A ~ N(0, 1) rounded to fp16;
+  * q ~ uniform integers in [0, 15];
+  * |scale| ~ U[1e-3, 2e-2] rounded to fp16;
+  * asymmetric zero = fp16(-8 * scale + N(0, 1e-3)), rounded once from fp64;
+  * symmetric prefill case: scale sign negative with probability 1/2.
+"""
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+SEED_ROOT = 20261202
+
+
+def rng_for(config_id: int, case_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, config_id, case_id])))
+
+
+@dataclass
+class W4A16Case:
+    A: np.ndarray            # fp16 [M, K]
+    q: np.ndarray            # uint8 [K, N], codes 0..15
+    s: np.ndarray            # fp16 [G, N]
+    z: Optional[np.ndarray]  # fp16 [G, N] or None (symmetric)
+    g: int
+    name: str = ""
+
+    @property
+    def M(self):
+        return self.A.shape[0]
+
+    @property
+    def K(self):
+        return self.A.shape[1]
+
+    @property
+    def N(self):
+        return self.q.shape[1]
+
+    @property
+    def G(self):
+        return self.K // self.g
+
+
+def w4a16_case(M, K, N, g, asym=True, signed_scales=False, config_id=0, case_id=0,
+               name="") -> W4A16Case:
+    if g == -1:
+        g = K
+    assert K % g == 0
+    G = K // g
+    r = rng_for(config_id, case_id)
+    A = r.standard_normal((M, K)).astype(np.float16)
+    q = r.integers(0, 16, size=(K, N), dtype=np.uint8)
+    s_abs = r.uniform(1e-3, 2e-2, size=(G, N))
+    s = s_abs.astype(np.float16)
+    if signed_scales:
+        neg = r.random((G, N)) < 0.5
+        s = np.where(neg, -s, s).astype(np.float16)
+    z = None
+    if asym:
+        noise = r.standard_normal((G, N)) * 1e-3
+        z = (-8.0 * s.astype(np.float64) + noise).astype(np.float16)
+    return W4A16Case(A=A, q=q, s=s, z=z, g=g, name=name)
+
+
+def quantize_rows_int8(A16: np.ndarray):
+    """Per-row symmetric int8 codes of fp16 activations (input preparation for
+    the W4A8 variant): a_scale = max|row| / 127 in fp32, codes = clamp(
+    round-half-even(A / a_scale), -127, 127).  An all-zero row gets scale 0 and
+    codes 0."""
+    A32 = A16.astype(np.float32)
+    amax = np.max(np.abs(A32), axis=1)
+    a_scale = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(a_scale > 0, a_scale, np.float32(1.0)).astype(np.float32)
+    codes = np.rint(A32 / safe[:, None])
+    codes = np.clip(codes, -127, 127).astype(np.int8)
+    codes[a_scale == 0] = 0
+    return codes, a_scale
+
+
+@dataclass
+class W4A8Case:
+    A16: np.ndarray          # fp16 [M_total, K] (unquantized, for reporting)
+    Aq: np.ndarray           # int8 [M_total, K]
+    a_scale: np.ndarray      # fp32 [M_total]
+    q: np.ndarray            # uint8 [E, K, N]
+    s: np.ndarray            # fp16 [E, G, N]
+    offsets: np.ndarray      # int32 [E + 1]
+    g: int
+    name: str = ""
+
+    @property
+    def E(self):
+        return self.q.shape[0]
+
+    @property
+    def K(self):
+        return self.q.shape[1]
+
+    @property
+    def N(self):
+        return self.q.shape[2]
+
+    @property
+    def M_total(self):
+        return self.Aq.shape[0]
+
+
+def w4a8_case(E, rows_per_expert, K, N, g, signed_scales=False, config_id=4, case_id=0,
+              rows=None, name="") -> W4A8Case:
+    """rows: optional explicit per-expert row counts (ragged groups)."""
+    if rows is None:
+        rows = [rows_per_expert] * E
+    assert len(rows) == E
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(rows)
+    M_total = int(offsets[-1])
+    G = K // g
+    r = rng_for(config_id, case_id)
+    A16 = r.standard_normal((M_total, K)).astype(np.float16)
+    q = r.integers(0, 16, size=(E, K, N), dtype=np.uint8)
+    s = r.uniform(1e-3, 2e-2, size=(E, G, N)).astype(np.float16)
+    if signed_scales:
+        neg = r.random((E, G, N)) < 0.5
+        s = np.where(neg, -s, s).astype(np.float16)
+    Aq, a_scale = quantize_rows_int8(A16)
+    return W4A8Case(A16=A16, Aq=Aq, a_scale=a_scale, q=q, s=s, offsets=offsets, g=g, name=name)
+
+
+# The benchmark workloads (shapes and value recipes), by configuration id.
+CONFIGS = {
+    0: dict(kind="w4a16", cases=[dict(M=16, K=1024, N=1024, g=128, asym=True)]),
+    1: dict(kind="w4a16", cases=[dict(M=m, K=k, N=n, g=128, asym=True)
+                                 for (k, n) in ((5120, 17408), (17408, 5120)) for m in (1, 4, 16)]),
+    2: dict(kind="w4a16", cases=[dict(M=256, K=4096, N=8192, g=256, asym=True),
+                                 dict(M=256, K=4096, N=8192, g=4096, asym=True)]),
+    3: dict(kind="w4a16", cases=[dict(M=4096, K=5120, N=17408, g=128, asym=False,
+                                      signed_scales=True)]),
+    4: dict(kind="w4a8", cases=[dict(E=8, rows_per_expert=64, K=2048, N=7168, g=128)]),
+}
+
+
+def config_case(config_id: int, case_id: int):
+    spec = dict(CONFIGS[config_id]["cases"][case_id])
+    if CONFIGS[config_id]["kind"] == "w4a16":
+        return w4a16_case(config_id=config_id, case_id=case_id, **spec)
+    return w4a8_case(config_id=config_id, case_id=case_id, **spec)
