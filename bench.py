@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed-int4 weight GEMM library on one MI355X.
+
+One step = one call of the hot path on the primary workload: qgemm_w4a16 with
+the asymmetric delta term fused (a single kernel launch), decode shape M=16,
+K=5120, N=17408, group 128, inputs already resident in HBM.  The packed
+weights are rotated over enough copies (>= 512 MB in total) that they cannot
+stay in the 256 MB last-level cache between calls, so the weight reads are HBM
+reads.
+
+Prints ONE JSON line on stdout:
+  value      TFLOP/s (2*M*N*K per call) of the primary workload
+  roofline   the primary kernel against the HBM roofline: algorithmic weight
+             bytes (0.5 B per code + 2 B scale + 2 B delta per group and
+             column) per launch / average launch duration (HIP events on the
+             launch stream over the timed region)
+  cpu_baseline  the CPU oracle timed on this host on the same workload
+  cases      every other configuration measured the same way (decode shapes,
+             mid-batch, prefill M=4096, grouped W4A8, the load-time pack)
+Logs go to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+FP16_PEAK_TFLOPS = 2516.6       # dense fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+INT8_PEAK_TOPS = 5033.2         # dense int8 MFMA
+ROTATE_BYTES = 512 * 1024 * 1024
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--only-primary", action="store_true", help="skip the secondary cases")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cases", default="all", help="comma list of case names, or 'all'")
+    return p.parse_args()
+
+
+def weight_bytes(K, N, g, asym):
+    G = K // g
+    return K * N // 2 + G * N * 2 * (2 if asym else 1)
+
+
+def time_calls(fn, n_copies, steps, warmup):
+    """Average ms per call of fn(i) over `steps` calls, rotating i over copies.
+    HIP events recorded on the current stream, which is the stream every
+    library call is launched on."""
+    import torch
+    for i in range(warmup):
+        fn(i % n_copies)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(steps):
+        fn(i % n_copies)
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_w4a16(name, M, K, N, g, asym, signed, config_id, case_id, steps, warmup, flags=0):
+    import numpy as np
+    import torch
+
+    import int4_weight_only_uint32_amd as qg
+    import synth
+
+    c = synth.w4a16_case(M, K, N, g, asym=asym, signed_scales=signed, config_id=config_id,
+                         case_id=case_id)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q, s = dev(c.q), dev(c.s)
+    z = dev(c.z) if asym else None
+    wb = weight_bytes(K, N, g, asym)
+    # load-time pack, timed once per case (not part of the step)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    pw = qg.pack(q, s, z, g, fold=True)
+    torch.cuda.synchronize()
+    pack_ms = (time.perf_counter() - t0) * 1e3
+    R = max(1, math.ceil(ROTATE_BYTES / wb))
+    copies = [pw] + [qg.PackedWeight(w=pw.w.clone(), scale=pw.scale.clone(),
+                                     delta=None if pw.delta is None else pw.delta.clone(),
+                                     K=K, N=N, group_size=g) for _ in range(R - 1)]
+    del q, s, z
+    A = dev(c.A)
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ws = None
+    if flags & qg.QG_CORR_SEPARATE:
+        ws = torch.empty(max(4, qg.qg_workspace_bytes(qg.QG_OP_W4A16, M, N, K, g, 1, flags)),
+                         dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        p = copies[i]
+        qg.qgemm_w4a16(A, p.w, p.scale, p.delta, C, M, N, K, g, flags, ws)
+
+    ms = time_calls(call, R, steps, warmup)
+    flops = 2.0 * M * N * K
+    alg = wb + M * K * 2 + M * N * 2
+    res = dict(name=name, M=M, K=K, N=N, group=g, mode="asym" if asym else "sym-fold",
+               flags=flags, us_per_call=ms * 1e3, tflops=flops / (ms * 1e-3) / 1e12,
+               weight_gbps=wb / (ms * 1e-3) / 1e9, total_alg_gbps=alg / (ms * 1e-3) / 1e9,
+               weight_bytes=wb, rotated_copies=R, pack_ms_first_call=pack_ms)
+    res["pct_hbm_weight"] = 100.0 * res["weight_gbps"] / HBM_PEAK_GBPS
+    res["pct_fp16_mfma"] = 100.0 * res["tflops"] / FP16_PEAK_TFLOPS
+    del copies, A, C
+    torch.cuda.empty_cache()
+    return res, c
+
+
+def bench_w4a8(name, steps, warmup):
+    import numpy as np
+    import torch
+
+    import int4_weight_only_uint32_amd as qg
+    import synth
+
+    c = synth.config_case(4, 0)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    packs = [qg.pack(dev(c.q[e]), dev(c.s[e]), None, c.g, fold=True) for e in range(c.E)]
+    W = torch.stack([p.w for p in packs]).contiguous()
+    S = torch.stack([p.scale for p in packs]).contiguous()
+    wb = c.E * weight_bytes(c.K, c.N, c.g, False)
+    R = max(1, math.ceil(ROTATE_BYTES / wb))
+    Ws = [W] + [W.clone() for _ in range(R - 1)]
+    Ss = [S] + [S.clone() for _ in range(R - 1)]
+    Aq, asc, off = dev(c.Aq), dev(c.a_scale), dev(c.offsets)
+    C = torch.empty((c.M_total, c.N), dtype=torch.float16, device="cuda")
+    mr = int(np.max(np.diff(c.offsets)))
+
+    def call(i):
+        qg.qgemm_w4a8(Aq, asc, Ws[i], Ss[i], off, c.E, c.M_total, mr, c.N, c.K, c.g, C)
+
+    ms = time_calls(call, R, steps, warmup)
+    ops = 2.0 * c.M_total * c.N * c.K
+    alg = wb + c.M_total * c.K + c.M_total * 4 + c.M_total * c.N * 2
+    res = dict(name=name, E=c.E, rows_per_expert=mr, K=c.K, N=c.N, group=c.g,
+               us_per_call=ms * 1e3, tops=ops / (ms * 1e-3) / 1e12,
+               weight_gbps=wb / (ms * 1e-3) / 1e9, total_alg_gbps=alg / (ms * 1e-3) / 1e9,
+               weight_bytes=wb, rotated_copies=R)
+    res["pct_hbm_weight"] = 100.0 * res["weight_gbps"] / HBM_PEAK_GBPS
+    res["pct_int8_mfma"] = 100.0 * res["tops"] / INT8_PEAK_TOPS
+    del Ws, Ss, W, S
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(case):
+    """The oracle (fp64 dequant + naive loop, OpenMP) on the primary workload,
+    run whole; returns TFLOP/s and the thread count it used."""
+    import oracle
+    oracle.build(force=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.w4a16(case.A, case.q, case.s, case.z, case.g, fold=True)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * case.M * case.N * case.K
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"one whole oracle call on M={case.M} K={case.K} N={case.N} g={case.g} "
+                       f"asym ({dt:.2f} s wall, fp64 dequant + naive m-k-n loop)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import int4_weight_only_uint32_amd as qg
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if not qg.qg_device_supported(0):
+        print("bench.py: cuda:0 is not gfx950", file=sys.stderr)
+        sys.exit(1)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+
+    steps, warmup = args.steps, args.warmup
+    primary, pcase = bench_w4a16("c1a-M16", 16, 5120, 17408, 128, True, False, 1, 2, steps, warmup)
+    log(json.dumps(primary))
+
+    cases = []
+    want = None if args.cases == "all" else set(args.cases.split(","))
+    if not args.only_primary:
+        plan = [
+            ("c0-M16", 16, 1024, 1024, 128, True, False, 0, 0),
+            ("c1a-M1", 1, 5120, 17408, 128, True, False, 1, 0),
+            ("c1a-M4", 4, 5120, 17408, 128, True, False, 1, 1),
+            ("c1b-M1", 1, 17408, 5120, 128, True, False, 1, 3),
+            ("c1b-M4", 4, 17408, 5120, 128, True, False, 1, 4),
+            ("c1b-M16", 16, 17408, 5120, 128, True, False, 1, 5),
+            ("c2-g256", 256, 4096, 8192, 256, True, False, 2, 0),
+            ("c2-percol", 256, 4096, 8192, 4096, True, False, 2, 1),
+            ("c3-M4096", 4096, 5120, 17408, 128, False, True, 3, 0),
+        ]
+        for (nm, M, K, N, g, asym, signed, cid, kid) in plan:
+            if want and nm not in want:
+                continue
+            st = steps if M <= 256 else max(10, steps // 10)
+            r, _ = bench_w4a16(nm, M, K, N, g, asym, signed, cid, kid, st, min(warmup, st))
+            log(json.dumps(r))
+            cases.append(r)
+        if not want or "c1a-M16-separate" in want:
+            r, _ = bench_w4a16("c1a-M16-separate", 16, 5120, 17408, 128, True, False, 1, 2,
+                               steps, warmup, flags=qg.QG_CORR_SEPARATE)
+            log(json.dumps(r))
+            cases.append(r)
+        if not want or "c4-w4a8" in want:
+            r = bench_w4a8("c4-w4a8", steps, warmup)
+            log(json.dumps(r))
+            cases.append(r)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(pcase)
+        log(json.dumps(cpu))
+
+    launch_us = primary["us_per_call"]
+    achieved = primary["weight_bytes"] / (launch_us * 1e-6) / 1e9
+    out = {
+        "metric": "W4A16 g128 GEMM TFLOPS + weight GB/s (%roofline) at M=16 and M=4096",
+        "value": primary["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": primary["us_per_call"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic (seeded; A~N(0,1) fp16, q~U{0..15}, |s|~U[1e-3,2e-2], "
+                "z=-8s+N(0,1e-3)); weights rotated over >=512 MB of copies",
+        "config": {"workload": "w4a16-decode M=16 K=5120 N=17408 group=128 asymmetric, "
+                               "delta fused (one launch per step)",
+                   "M": 16, "K": 5120, "N": 17408, "group": 128},
+        "weight_gbps": primary["weight_gbps"],
+        "pct_hbm_roofline_weight": primary["pct_hbm_weight"],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "w4a16_skinny_kernel<1,2,16,true>",
+                     "algorithmic_bytes_per_launch": primary["weight_bytes"]},
+        "cpu_baseline": cpu,
+        "cases": cases,
+    }
+    prefill = [c for c in cases if c["name"] == "c3-M4096"]
+    if prefill:
+        out["prefill_M4096"] = {"tflops": prefill[0]["tflops"],
+                                "pct_fp16_mfma": prefill[0]["pct_fp16_mfma"],
+                                "us_per_call": prefill[0]["us_per_call"]}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * qgemm.h -- C ABI of the packed-int4 weight GEMM library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * It computes C[M,N] = A[M,K] . W[K,N] where W is held as 4-bit codes q in
+ * [0,15], eight to a uint32, with one fp16 scale (and, asymmetric, one fp16
+ * zero) per group of `group_size` consecutive k and per column n:
+ *
+ *   symmetric offset-binary  W[k,n] = (q[k,n] - 8) * scale[k/g, n]
+ *   asymmetric               W[k,n] =  q[k,n] * scale[k/g, n] + zero[k/g, n]
+ *
+ * Sources (web pages, cited by title and section):
+ *   [Marlin-Ada]  "Marlin INT4 on Ada - how it works" (TinyLoop docs):
+ *                 "The core mismatch: symmetric vs asymmetric" (both formats,
+ *                 delta = zero + 8*scale, C = C_sym + A_group_sum @ delta),
+ *                 "The pipeline, end to end" (pack, group-sum and correction
+ *                 stages), "How the dispatcher chooses" (K, N multiples of
+ *                 128; group_size == K written as -1 for per-column scales).
+ *   [HyperQwen]   "HyperQwen int8 tensor-core fix of the Marlin W4A8 negative
+ *                 scale bug and per-layer activation quantization": the W4A8
+ *                 path (int4 weights, per-token int8 activations, integer
+ *                 accumulation) and the load-time sign fold of negative group
+ *                 scales (scale -> -scale, code v -> 16 - v, clamped at 15).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous, owned
+ *     by the caller.  The library allocates no device memory and keeps no
+ *     device state; scratch memory is a caller-provided workspace whose size
+ *     qg_workspace_bytes() reports (0 for every path that needs none).
+ *   - fp16 tensors are passed as uint16_t (IEEE binary16 bit patterns).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued asynchronously; nothing is synchronised or read back.
+ *   - Every argument is validated on the host BEFORE anything is launched; on
+ *     error nothing is written and nothing is launched.  The return value is a
+ *     QG_* status; qg_last_error() gives a per-thread description.  There is no
+ *     internal fallback to another path: the caller decides what to do.
+ *   - Shapes: K % 128 == 0 and N % 128 == 0 (the tile multiples the pages'
+ *     dispatcher requires), M >= 1.  group_size must divide K and be a multiple
+ *     of 128, or equal K; -1 is accepted as an alias of K (per-column scales).
+ *   - A, C, scale, zero and delta must be 2-byte aligned; w_packed 16-byte
+ *     aligned; A 16-byte aligned for the W4A16 GEMM, A_q 8-byte aligned for
+ *     W4A8.
+ *   - Calls on the same stream are ordered; concurrent calls on different
+ *     streams that write the same output race (as any two kernels would).
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define QG_OK               0
+#define QG_ERR_INVALID_ARG  1  /* NULL pointer, bad alignment, M < 1, ...        */
+#define QG_ERR_UNSUPPORTED  2  /* shape or group size this library has no kernel for */
+#define QG_ERR_WORKSPACE    3  /* workspace missing or smaller than required      */
+#define QG_ERR_DEVICE       4  /* current device is not gfx950 / no device        */
+#define QG_ERR_LAUNCH       5  /* the HIP runtime rejected a launch               */
+
+/* ---- flags ---- */
+/* pack_int4_weights: fold negative group scales into the codes (symmetric
+ * packs only; ignored when zero != NULL).                                   */
+#define QG_PACK_FOLD_NEG_SCALES 0x1u
+/* qgemm_w4a16: add the asymmetric term with the two-stage
+ * group_sum_correction (after an fp16 store of the symmetric product)
+ * instead of fusing it into the GEMM epilogue.                              */
+#define QG_CORR_SEPARATE        0x1u
+
+/* ---- operations, for qg_workspace_bytes ---- */
+#define QG_OP_W4A16                 1
+#define QG_OP_W4A8                  2
+#define QG_OP_GROUP_SUM_CORRECTION  3
+#define QG_OP_PACK                  4
+
+/* 1 if HIP device `device` is a gfx950 GPU this library has kernels for,
+ * else 0 (also 0 when the device does not exist).  The analogue of the pages'
+ * runtime architecture gate ([Marlin-Ada], "How the dispatcher chooses").   */
+int qg_device_supported(int device);
+
+/* Static text for a QG_* status. Never NULL.                                */
+const char *qg_status_string(int status);
+
+/* Description of the last error on the calling thread ("" if none). The
+ * pointer stays valid until the next library call on that thread.          */
+const char *qg_last_error(void);
+
+/* Bytes of workspace `op` needs for this shape (0 when none). Returns
+ * (size_t)-1 when the arguments are invalid.                                */
+size_t qg_workspace_bytes(int op, int M, int N, int K, int group_size,
+                          int num_experts, unsigned flags);
+
+/* ---- load-time repack ([Marlin-Ada] "The pipeline, end to end";
+ *      [HyperQwen] negative group-scale section) ----
+ * q         [K,N] uint8, one code (0..15) per byte; larger values are an
+ *           error the kernel cannot report and give unspecified codes.
+ * scale     [G,N] fp16, G = K / group_size.
+ * zero      [G,N] fp16, or NULL for a symmetric weight.
+ * flags     QG_PACK_FOLD_NEG_SCALES: for a symmetric weight, every (g,n) with
+ *           scale < 0 (strictly; -0.0 is left alone) gets scale -> -scale and
+ *           codes v -> min(16 - v, 15) over that group.
+ * w_packed  [K*N/8] uint32 out, in this library's MFMA-operand tile order
+ *           (private layout; the only consumers are qgemm_w4a16/qgemm_w4a8).
+ * scale_out [G,N] fp16 out: the (folded) scale.  May alias `scale`.
+ * delta_out [G,N] fp16 out, required iff zero != NULL:
+ *           delta = round_to_nearest_even_fp16(zero + 8*scale), with the
+ *           pre-fold scale and the sum formed exactly.
+ * Runs one or two kernels on `stream`. No workspace.                        */
+int pack_int4_weights(const uint8_t *q, const uint16_t *scale, const uint16_t *zero,
+                      int K, int N, int group_size, unsigned flags,
+                      uint32_t *w_packed, uint16_t *scale_out, uint16_t *delta_out,
+                      void *stream);
+
+/* ---- W4A16 GEMM ([Marlin-Ada] "The core mismatch") ----
+ * A        [M,K] fp16 activations.
+ * w_packed, scale: from pack_int4_weights.
+ * delta    [G,N] fp16 from pack_int4_weights for an asymmetric weight, or NULL
+ *          for a symmetric one.
+ * C        [M,N] fp16 out, OVERWRITTEN with A . W (fp32 accumulation, one
+ *          rounding to fp16 at the end).
+ * flags    0: the delta term sum_g a_sum[m,g]*delta[g,n] is added in fp32 in
+ *          the GEMM epilogue (one launch).
+ *          QG_CORR_SEPARATE: C is first stored as the symmetric product and
+ *          then corrected in place by group_sum_correction (needs workspace).
+ * workspace/workspace_bytes: see qg_workspace_bytes(QG_OP_W4A16, ...).      */
+int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,
+                const uint16_t *delta, uint16_t *C, int M, int N, int K,
+                int group_size, unsigned flags, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/* ---- asymmetric correction as its own two stages ([Marlin-Ada] "The
+ *      pipeline, end to end", a_group_sum and correction_accum) ----
+ * C[m,n] += sum_g a_sum[m,g] * delta[g,n],  a_sum[m,g] = sum_{k in g} A[m,k]
+ * a_sum is formed in fp32 in the workspace; C is read, updated in fp32 and
+ * rounded back to fp16 (ACCUMULATES into C, unlike the GEMMs).
+ * workspace: qg_workspace_bytes(QG_OP_GROUP_SUM_CORRECTION, ...) bytes.     */
+int group_sum_correction(const uint16_t *A, const uint16_t *delta, uint16_t *C,
+                         int M, int N, int K, int group_size, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* ---- grouped W4A8 GEMM ([HyperQwen] "why int8 activation quantization
+ *      (W4A8) is worth doing") ----
+ * A_q          [M_total,K] int8 per-token codes; a_scale [M_total] fp32.
+ * w_packed     E stacked packs (each K*N/8 uint32, symmetric weights).
+ * w_scale      E stacked [G,N] fp16 scales (the packs' scale_out).
+ * expert_offsets  DEVICE int32[E+1], non-decreasing, offsets[0] = 0,
+ *              offsets[E] = M_total: expert e owns rows offsets[e] ..
+ *              offsets[e+1]-1.  NULL means one expert owning all rows (E must
+ *              be 1).  Rows are clipped to [0, M_total) in the kernel.
+ * max_rows_per_expert  an upper bound of offsets[e+1]-offsets[e] over e; rows
+ *              of an expert beyond this bound are NOT computed.
+ * C            [M_total,N] fp16 out, overwritten:
+ *              C[m,n] = a_scale[m] * sum_g scale_e[g,n] * acc[m,g,n]
+ *              acc[m,g,n] = sum_{k in g} A_q[m,k] * (v_e[k,n] - 8)  (int32, exact)
+ * acc_debug    NULL, or [M_total,G,N] int32 out receiving acc exactly.
+ * No workspace (pass NULL, 0).                                              */
+int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed,
+               const uint16_t *w_scale, const int32_t *expert_offsets, int num_experts,
+               int M_total, int max_rows_per_expert, int N, int K, int group_size,
+               uint16_t *C, int32_t *acc_debug, void *workspace, size_t workspace_bytes,
+               unsigned flags, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

@@ -1,0 +1,222 @@
+"""Python binding of the packed-int4 weight GEMM library (libqgemm.so, gfx950).
+
+Argument marshalling only: each function checks that it was given device
+tensors of the right dtype, passes their pointers and the current HIP stream to
+the C ABI declared in include/qgemm.h, and raises QGemmError on a non-zero
+status.  Every step of the computation runs in the library's HIP kernels; there
+is no fallback of any kind -- if libqgemm.so is missing, importing works but
+every call raises.
+
+Names follow the C ABI: pack_int4_weights, qgemm_w4a16, group_sum_correction,
+qgemm_w4a8 (plus qg_device_supported, qg_workspace_bytes).
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+
+QG_OK = 0
+QG_ERR_INVALID_ARG = 1
+QG_ERR_UNSUPPORTED = 2
+QG_ERR_WORKSPACE = 3
+QG_ERR_DEVICE = 4
+QG_ERR_LAUNCH = 5
+
+QG_PACK_FOLD_NEG_SCALES = 0x1
+QG_CORR_SEPARATE = 0x1
+
+QG_OP_W4A16 = 1
+QG_OP_W4A8 = 2
+QG_OP_GROUP_SUM_CORRECTION = 3
+QG_OP_PACK = 4
+
+EXPORTED = ("qg_device_supported", "qg_status_string", "qg_last_error", "qg_workspace_bytes",
+            "pack_int4_weights", "qgemm_w4a16", "group_sum_correction", "qgemm_w4a8")
+
+
+class QGemmError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"qgemm status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libqgemm.so (built by __graft_entry__.build() or build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python int4_weight_only_uint32_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, U, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+        L.qg_device_supported.restype = I
+        L.qg_device_supported.argtypes = [I]
+        L.qg_status_string.restype = ctypes.c_char_p
+        L.qg_status_string.argtypes = [I]
+        L.qg_last_error.restype = ctypes.c_char_p
+        L.qg_last_error.argtypes = []
+        L.qg_workspace_bytes.restype = Z
+        L.qg_workspace_bytes.argtypes = [I, I, I, I, I, I, U]
+        L.pack_int4_weights.restype = I
+        L.pack_int4_weights.argtypes = [P, P, P, I, I, I, U, P, P, P, P]
+        L.qgemm_w4a16.restype = I
+        L.qgemm_w4a16.argtypes = [P, P, P, P, P, I, I, I, I, U, P, Z, P]
+        L.group_sum_correction.restype = I
+        L.group_sum_correction.argtypes = [P, P, P, I, I, I, I, P, Z, P]
+        L.qgemm_w4a8.restype = I
+        L.qgemm_w4a8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, Z, U, P]
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != QG_OK:
+        raise QGemmError(rc, lib().qg_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def qg_device_supported(device: int = 0) -> bool:
+    return bool(lib().qg_device_supported(int(device)))
+
+
+def qg_workspace_bytes(op, M, N, K, group_size, num_experts=1, flags=0) -> int:
+    n = lib().qg_workspace_bytes(op, M, N, K, group_size, num_experts, flags)
+    if n == ctypes.c_size_t(-1).value:
+        raise QGemmError(QG_ERR_INVALID_ARG, lib().qg_last_error().decode())
+    return int(n)
+
+
+@dataclass
+class PackedWeight:
+    w: torch.Tensor                 # int32 [K*N/8] (uint32 bit patterns)
+    scale: torch.Tensor             # fp16 [G, N] (folded)
+    delta: Optional[torch.Tensor]   # fp16 [G, N] or None (symmetric)
+    K: int
+    N: int
+    group_size: int
+
+
+def pack_int4_weights(q, scale, zero, K, N, group_size, flags, w_packed, scale_out, delta_out):
+    """Same arguments as the C entry point, as device tensors (zero/delta_out may be None)."""
+    _check(lib().pack_int4_weights(_ptr(q, torch.uint8, "q"), _ptr(scale, torch.float16, "scale"),
+                                   _ptr(zero, torch.float16, "zero"), K, N, group_size, flags,
+                                   _ptr(w_packed, torch.int32, "w_packed"),
+                                   _ptr(scale_out, torch.float16, "scale_out"),
+                                   _ptr(delta_out, torch.float16, "delta_out"), _stream(q)))
+
+
+def pack(q: torch.Tensor, scale: torch.Tensor, zero: Optional[torch.Tensor] = None,
+         group_size: int = 128, fold: bool = True) -> PackedWeight:
+    """Allocate outputs (torch) and run pack_int4_weights."""
+    K, N = q.shape
+    g = K if group_size == -1 else group_size
+    w = torch.empty(K * N // 8, dtype=torch.int32, device=q.device)
+    s_out = torch.empty_like(scale)
+    d_out = torch.empty_like(scale) if zero is not None else None
+    pack_int4_weights(q, scale, zero, K, N, group_size,
+                      QG_PACK_FOLD_NEG_SCALES if fold else 0, w, s_out, d_out)
+    return PackedWeight(w=w, scale=s_out, delta=d_out, K=K, N=N, group_size=g)
+
+
+def qgemm_w4a16(A, w_packed, scale, delta, C, M, N, K, group_size, flags=0, workspace=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().qgemm_w4a16(_ptr(A, torch.float16, "A"), _ptr(w_packed, torch.int32, "w_packed"),
+                             _ptr(scale, torch.float16, "scale"),
+                             _ptr(delta, torch.float16, "delta"), _ptr(C, torch.float16, "C"),
+                             M, N, K, group_size, flags, _ptr(workspace, None, "workspace"),
+                             ws_bytes, _stream(A)))
+
+
+_workspaces = {}
+
+
+def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A zero-initialised workspace of at least `nbytes`, cached per (device,
+    current stream).  The library leaves the counter area of a W4A16 workspace
+    zeroed after every call, so the buffer can be reused as is; calls that
+    share it must be ordered (one stream)."""
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def w4a16(A: torch.Tensor, pw: PackedWeight, C: Optional[torch.Tensor] = None, flags: int = 0,
+          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    M, K = A.shape
+    if C is None:
+        C = torch.empty((M, pw.N), dtype=torch.float16, device=A.device)
+    if workspace is None:
+        n = qg_workspace_bytes(QG_OP_W4A16, M, pw.N, K, pw.group_size, 1,
+                               flags if pw.delta is not None else 0)
+        if n > 0:
+            workspace = workspace_for(A.device, n)
+    qgemm_w4a16(A, pw.w, pw.scale, pw.delta, C, M, pw.N, K, pw.group_size, flags, workspace)
+    return C
+
+
+def group_sum_correction(A, delta, C, M, N, K, group_size, workspace):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().group_sum_correction(_ptr(A, torch.float16, "A"), _ptr(delta, torch.float16, "delta"),
+                                      _ptr(C, torch.float16, "C"), M, N, K, group_size,
+                                      _ptr(workspace, None, "workspace"), ws_bytes, _stream(A)))
+
+
+def correct(A: torch.Tensor, delta: torch.Tensor, C: torch.Tensor, group_size: int) -> torch.Tensor:
+    """C += a_sum @ delta in place (allocates its fp32 workspace with torch)."""
+    M, K = A.shape
+    N = C.shape[1]
+    n = qg_workspace_bytes(QG_OP_GROUP_SUM_CORRECTION, M, N, K, group_size)
+    ws = torch.empty(max(n, 4), dtype=torch.uint8, device=A.device)
+    group_sum_correction(A, delta, C, M, N, K, group_size, ws)
+    return C
+
+
+def qgemm_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts, M_total,
+               max_rows_per_expert, N, K, group_size, C, acc_debug=None, flags=0):
+    _check(lib().qgemm_w4a8(_ptr(A_q, torch.int8, "A_q"), _ptr(a_scale, torch.float32, "a_scale"),
+                            _ptr(w_packed, torch.int32, "w_packed"),
+                            _ptr(w_scale, torch.float16, "w_scale"),
+                            _ptr(expert_offsets, torch.int32, "expert_offsets"), num_experts,
+                            M_total, max_rows_per_expert, N, K, group_size,
+                            _ptr(C, torch.float16, "C"), _ptr(acc_debug, torch.int32, "acc_debug"),
+                            None, 0, flags, _stream(A_q)))
+
+
+def w4a8(A_q: torch.Tensor, a_scale: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor,
+         expert_offsets: Optional[torch.Tensor], num_experts: int, max_rows_per_expert: int,
+         N: int, group_size: int, C: Optional[torch.Tensor] = None,
+         acc_debug: Optional[torch.Tensor] = None) -> torch.Tensor:
+    M_total, K = A_q.shape
+    if C is None:
+        C = torch.empty((M_total, N), dtype=torch.float16, device=A_q.device)
+    qgemm_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts, M_total,
+               max_rows_per_expert, N, K, group_size, C, acc_debug)
+    return C

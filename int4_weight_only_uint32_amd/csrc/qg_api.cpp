@@ -1,0 +1,263 @@
+// C ABI of the packed-int4 GEMM library: host-side validation, then launches.
+// Nothing is launched and nothing is written unless every check passes.
+#include "../../include/qgemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "qg_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return QG_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// gfx950 check of the current device; cached per device id.
+int check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(QG_ERR_DEVICE, "no HIP device is current");
+    if (!qg_device_supported(dev))
+        return fail(QG_ERR_DEVICE, "device %d is not a gfx950 GPU", dev);
+    return QG_OK;
+}
+
+int launch_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(QG_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Shape rules shared by every GEMM-like entry point.  Normalises the per-column
+// sentinel -1 to K.
+int check_shape(const char *what, int M, int N, int K, int *g)
+{
+    if (M < 1 || N < 1 || K < 1)
+        return fail(QG_ERR_INVALID_ARG, "%s: M, N, K must be >= 1 (got %d, %d, %d)", what, M, N, K);
+    if (K % 128 != 0 || N % 128 != 0)
+        return fail(QG_ERR_UNSUPPORTED, "%s: K and N must be multiples of 128 (got K=%d N=%d)",
+                    what, K, N);
+    if (*g == -1) *g = K;
+    if (*g < 1 || K % *g != 0)
+        return fail(QG_ERR_INVALID_ARG, "%s: group_size %d does not divide K=%d", what, *g, K);
+    if (*g != K && *g % 128 != 0)
+        return fail(QG_ERR_UNSUPPORTED,
+                    "%s: group_size %d unsupported (must be a multiple of 128, K, or -1)", what, *g);
+    if ((long long)M * K > (1ll << 40) || (long long)K * N > (1ll << 40))
+        return fail(QG_ERR_UNSUPPORTED, "%s: shape too large", what);
+    return QG_OK;
+}
+
+size_t corr_ws_bytes(int M, int K, int g) { return (size_t)M * (size_t)(K / g) * sizeof(float); }
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// W4A16 workspace: [GEMM split-K area][correction a_sum area when separate]
+size_t w4a16_ws_bytes(int M, int N, int K, int g, bool separate)
+{
+    size_t gemm = qg::w4a16_workspace_bytes(M, N, K);
+    if (!separate) return gemm;
+    return align256(gemm) + corr_ws_bytes(M, K, g);
+}
+
+} // namespace
+
+extern "C" {
+
+int qg_device_supported(int device)
+{
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return 0;
+    static std::mutex mu;
+    static int cache[64];
+    static bool cached[64];
+    if (device < 64) {
+        std::lock_guard<std::mutex> lk(mu);
+        if (cached[device]) return cache[device];
+    }
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, device) != hipSuccess) return 0;
+    int yes = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    if (device < 64) {
+        std::lock_guard<std::mutex> lk(mu);
+        cache[device] = yes;
+        cached[device] = true;
+    }
+    return yes;
+}
+
+const char *qg_status_string(int status)
+{
+    switch (status) {
+    case QG_OK: return "ok";
+    case QG_ERR_INVALID_ARG: return "invalid argument";
+    case QG_ERR_UNSUPPORTED: return "unsupported shape or group size";
+    case QG_ERR_WORKSPACE: return "workspace missing or too small";
+    case QG_ERR_DEVICE: return "no supported (gfx950) device";
+    case QG_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char *qg_last_error(void) { return g_err; }
+
+size_t qg_workspace_bytes(int op, int M, int N, int K, int group_size, int num_experts,
+                          unsigned flags)
+{
+    (void)num_experts;
+    int g = group_size;
+    switch (op) {
+    case QG_OP_W4A16:
+        if (check_shape("qg_workspace_bytes", M, N, K, &g) != QG_OK) return (size_t)-1;
+        return w4a16_ws_bytes(M, N, K, g, (flags & QG_CORR_SEPARATE) != 0);
+    case QG_OP_GROUP_SUM_CORRECTION:
+        if (check_shape("qg_workspace_bytes", M, N, K, &g) != QG_OK) return (size_t)-1;
+        return corr_ws_bytes(M, K, g);
+    case QG_OP_W4A8:
+    case QG_OP_PACK:
+        if (check_shape("qg_workspace_bytes", M < 1 ? 1 : M, N, K, &g) != QG_OK) return (size_t)-1;
+        return 0;
+    default:
+        fail(QG_ERR_INVALID_ARG, "qg_workspace_bytes: unknown op %d", op);
+        return (size_t)-1;
+    }
+}
+
+int pack_int4_weights(const uint8_t *q, const uint16_t *scale, const uint16_t *zero, int K,
+                      int N, int group_size, unsigned flags, uint32_t *w_packed,
+                      uint16_t *scale_out, uint16_t *delta_out, void *stream)
+{
+    int g = group_size;
+    int rc = check_shape("pack_int4_weights", 1, N, K, &g);
+    if (rc) return rc;
+    if (!q || !scale || !w_packed || !scale_out)
+        return fail(QG_ERR_INVALID_ARG, "pack_int4_weights: NULL q/scale/w_packed/scale_out");
+    if (zero && !delta_out)
+        return fail(QG_ERR_INVALID_ARG, "pack_int4_weights: delta_out is required with zero");
+    if (!aligned(w_packed, 16) || !aligned(scale, 2) || !aligned(scale_out, 2) ||
+        (zero && !aligned(zero, 2)) || (delta_out && !aligned(delta_out, 2)))
+        return fail(QG_ERR_INVALID_ARG, "pack_int4_weights: misaligned pointer");
+    if (flags & ~QG_PACK_FOLD_NEG_SCALES)
+        return fail(QG_ERR_INVALID_ARG, "pack_int4_weights: unknown flags 0x%x", flags);
+    if ((rc = check_device())) return rc;
+    hipError_t e = qg::launch_pack(q, scale, zero, K, N, g, (flags & QG_PACK_FOLD_NEG_SCALES) != 0,
+                                   w_packed, scale_out, zero ? delta_out : nullptr,
+                                   (hipStream_t)stream);
+    return launch_status(e, "pack_int4_weights");
+}
+
+int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,
+                const uint16_t *delta, uint16_t *C, int M, int N, int K, int group_size,
+                unsigned flags, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int g = group_size;
+    int rc = check_shape("qgemm_w4a16", M, N, K, &g);
+    if (rc) return rc;
+    if (!A || !w_packed || !scale || !C)
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16: NULL A/w_packed/scale/C");
+    if (!aligned(A, 16) || !aligned(w_packed, 16) || !aligned(scale, 2) || !aligned(C, 2) ||
+        (delta && !aligned(delta, 2)))
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16: misaligned pointer");
+    if (flags & ~QG_CORR_SEPARATE)
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16: unknown flags 0x%x", flags);
+    const bool separate = (flags & QG_CORR_SEPARATE) && delta;
+    const size_t need = w4a16_ws_bytes(M, N, K, g, separate);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(QG_ERR_WORKSPACE, "qgemm_w4a16: workspace of %zu bytes needed, got %zu",
+                        need, workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 256))
+            return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16: workspace must be 256-byte aligned");
+    }
+    if ((rc = check_device())) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t gemm_ws = qg::w4a16_workspace_bytes(M, N, K);
+    hipError_t e = qg::launch_w4a16(A, w_packed, scale, delta, C, M, N, K, g, !separate,
+                                    gemm_ws ? workspace : nullptr, st);
+    if (e == hipSuccess && separate)
+        e = qg::launch_group_sum_correction(A, delta, C, M, N, K, g,
+                                            (float *)((char *)workspace + align256(gemm_ws)), st);
+    return launch_status(e, "qgemm_w4a16");
+}
+
+int group_sum_correction(const uint16_t *A, const uint16_t *delta, uint16_t *C, int M, int N,
+                         int K, int group_size, void *workspace, size_t workspace_bytes,
+                         void *stream)
+{
+    int g = group_size;
+    int rc = check_shape("group_sum_correction", M, N, K, &g);
+    if (rc) return rc;
+    if (!A || !delta || !C)
+        return fail(QG_ERR_INVALID_ARG, "group_sum_correction: NULL A/delta/C");
+    if (!aligned(A, 2) || !aligned(delta, 2) || !aligned(C, 2))
+        return fail(QG_ERR_INVALID_ARG, "group_sum_correction: misaligned pointer");
+    size_t need = corr_ws_bytes(M, K, g);
+    if (!workspace || workspace_bytes < need)
+        return fail(QG_ERR_WORKSPACE, "group_sum_correction: workspace of %zu bytes needed, got %zu",
+                    need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 4))
+        return fail(QG_ERR_INVALID_ARG, "group_sum_correction: misaligned workspace");
+    if ((rc = check_device())) return rc;
+    hipError_t e = qg::launch_group_sum_correction(A, delta, C, M, N, K, g, (float *)workspace,
+                                                   (hipStream_t)stream);
+    return launch_status(e, "group_sum_correction");
+}
+
+int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed,
+               const uint16_t *w_scale, const int32_t *expert_offsets, int num_experts,
+               int M_total, int max_rows_per_expert, int N, int K, int group_size, uint16_t *C,
+               int32_t *acc_debug, void *workspace, size_t workspace_bytes, unsigned flags,
+               void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    int g = group_size;
+    int rc = check_shape("qgemm_w4a8", M_total, N, K, &g);
+    if (rc) return rc;
+    if (!A_q || !a_scale || !w_packed || !w_scale || !C)
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: NULL A_q/a_scale/w_packed/w_scale/C");
+    if (num_experts < 1 || num_experts > 65535)
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: num_experts %d out of range", num_experts);
+    if (!expert_offsets && num_experts != 1)
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: expert_offsets is required when E > 1");
+    if (max_rows_per_expert < 1)
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: max_rows_per_expert must be >= 1");
+    if (!expert_offsets && max_rows_per_expert < M_total)
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: max_rows_per_expert < M_total with one expert");
+    if (K > 131072)
+        return fail(QG_ERR_UNSUPPORTED, "qgemm_w4a8: K > 131072 would overflow int32 accumulators");
+    if (!aligned(A_q, 8) || !aligned(a_scale, 4) || !aligned(w_packed, 16) ||
+        !aligned(w_scale, 2) || !aligned(C, 2) || (acc_debug && !aligned(acc_debug, 4)) ||
+        (expert_offsets && !aligned(expert_offsets, 4)))
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: misaligned pointer");
+    if (flags != 0) return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: unknown flags 0x%x", flags);
+    if ((rc = check_device())) return rc;
+    int max_rows = max_rows_per_expert > M_total ? M_total : max_rows_per_expert;
+    hipError_t e = qg::launch_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts,
+                                   M_total, max_rows, N, K, g, C, acc_debug, (hipStream_t)stream);
+    return launch_status(e, "qgemm_w4a8");
+}
+
+} // extern "C"

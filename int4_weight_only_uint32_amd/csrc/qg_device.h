@@ -1,0 +1,117 @@
+// Internal device helpers of the packed-int4 GEMM library (gfx950 only).
+//
+// Packed weight layout (this library's own; produced by pack_int4_weights):
+//   The K x N code matrix is cut into tiles of 128 k x 16 n.  Tile (nt, kt)
+//   occupies 256 consecutive uint32 starting at (nt * (K/128) + kt) * 256, so
+//   the tiles of one 16-column strip are contiguous along K.  Inside a tile,
+//   "lane" l = 0..63 owns the 16 bytes (4 uint32) at l*4 .. l*4+3: column
+//   c = l % 16 of the strip and the k-quarter kq = l / 16.  uint32 j of lane
+//   l holds 8 codes; nibble p (bits 4p .. 4p+3) holds k = tile_k(kq, j, p):
+//       half = p >> 2, hi = p & 1, sh = (p >> 1) & 1
+//       slot = 4 * (j & 1) + 2 * sh + half          (0..7)
+//       step = (j >> 1) + 2 * hi                    (0..3)
+//       k    = 32 * step + 8 * kq + slot
+//   so that one 128-bit load per lane gives a wave the B operands of the four
+//   16x16x32 fp16 MFMA k-steps of a 128-k tile, and the nibbles of each
+//   operand are reachable with one AND (see split_codes below).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
+typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
+
+constexpr int KTILE = 128;    // k extent of one packed tile
+constexpr int NTILE = 16;     // n extent of one packed tile
+constexpr int TILE_U32 = 256; // uint32 per tile
+
+__host__ __device__ inline int tile_k(int kq, int j, int p)
+{
+    int half = p >> 2, hi = p & 1, sh = (p >> 1) & 1;
+    int slot = 4 * (j & 1) + 2 * sh + half;
+    int step = (j >> 1) + 2 * hi;
+    return 32 * step + 8 * kq + slot;
+}
+
+__device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ inline uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Strictly negative binary16 (not -0.0, not NaN).
+__host__ __device__ inline bool f16_is_negative(uint16_t b)
+{
+    bool nan = (b & 0x7c00) == 0x7c00 && (b & 0x03ff) != 0;
+    return (b & 0x8000) && (b & 0x7fff) && !nan;
+}
+
+// ---- fp16 B operands from one 128-bit group of codes (subnormal form) ----
+// A binary16 bit pattern 0x000v (v < 16) is the subnormal v * 2^-24 and a
+// pattern 0x00v0 is 16 v * 2^-24; both are exact MFMA inputs.  The four words
+// x0..x3 of a lane give four operands:
+//   lo[0] (k-step 0), lo[1] (k-step 1): values v * 2^-24
+//   hi[0] (k-step 2), hi[1] (k-step 3): values 16 v * 2^-24
+struct CodeOps {
+    half8 lo[2];
+    half8 hi[2];
+};
+
+__device__ inline CodeOps split_codes(uint4v w)
+{
+    CodeOps r;
+    uint4v l0, l1, h0, h1;
+    unsigned x0 = w.x, x1 = w.y, x2 = w.z, x3 = w.w;
+    unsigned y0 = x0 >> 8, y1 = x1 >> 8, y2 = x2 >> 8, y3 = x3 >> 8;
+    l0 = uint4v{x0 & 0x000F000Fu, y0 & 0x000F000Fu, x1 & 0x000F000Fu, y1 & 0x000F000Fu};
+    l1 = uint4v{x2 & 0x000F000Fu, y2 & 0x000F000Fu, x3 & 0x000F000Fu, y3 & 0x000F000Fu};
+    h0 = uint4v{x0 & 0x00F000F0u, y0 & 0x00F000F0u, x1 & 0x00F000F0u, y1 & 0x00F000F0u};
+    h1 = uint4v{x2 & 0x00F000F0u, y2 & 0x00F000F0u, x3 & 0x00F000F0u, y3 & 0x00F000F0u};
+    r.lo[0] = __builtin_bit_cast(half8, l0);
+    r.lo[1] = __builtin_bit_cast(half8, l1);
+    r.hi[0] = __builtin_bit_cast(half8, h0);
+    r.hi[1] = __builtin_bit_cast(half8, h1);
+    return r;
+}
+
+// ---- int8 B operands from one 128-bit group of codes ----
+// Byte b of ((x << 4) & 0xF0F0F0F0) is 16 * (nibble 2b); XOR 0x80 turns the
+// unsigned byte 16 v into the signed byte 16 (v - 8).  Likewise for the odd
+// nibbles with (x & 0xF0F0F0F0).  Returns the two 16x16x64 int8 operands of
+// the tile: [0] covers k-steps 0,1 of the fp16 numbering, [1] k-steps 2,3.
+struct CodeOpsI8 {
+    int4v op[2];
+};
+
+__device__ inline CodeOpsI8 split_codes_i8(uint4v w)
+{
+    CodeOpsI8 r;
+    const unsigned m = 0xF0F0F0F0u, f = 0x80808080u;
+    r.op[0] = int4v{(int)(((w.x << 4) & m) ^ f), (int)(((w.y << 4) & m) ^ f),
+                    (int)(((w.z << 4) & m) ^ f), (int)(((w.w << 4) & m) ^ f)};
+    r.op[1] = int4v{(int)((w.x & m) ^ f), (int)((w.y & m) ^ f),
+                    (int)((w.z & m) ^ f), (int)((w.w & m) ^ f)};
+    return r;
+}
+
+// Bytes [b0 b1 b2 b3] -> [b0 b2 b1 b3]: the int8 operand byte order of a
+// lane's four consecutive k (the even nibbles of a code word come first).
+__device__ inline unsigned swap_mid_bytes(unsigned x)
+{
+    return (x & 0xFF0000FFu) | ((x >> 8) & 0x0000FF00u) | ((x << 8) & 0x00FF0000u);
+}
+
+__device__ inline float4v mfma_f16(half8 a, half8 b, float4v c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline int4v mfma_i8(int4v a, int4v b, int4v c)
+{
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+} // namespace qg

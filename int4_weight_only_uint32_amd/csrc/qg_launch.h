@@ -1,0 +1,51 @@
+// Internal launchers between the validated C ABI (qg_api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+hipError_t launch_pack(const uint8_t *q, const uint16_t *s, const uint16_t *z, int K, int N,
+                       int g, bool fold, uint32_t *w, uint16_t *s_out, uint16_t *d_out,
+                       hipStream_t st);
+
+// Configuration of one skinny (small-M) W4A16 launch:
+//   MT  16-row m-tiles per wave        NT  16-column n-tiles per wave
+//   P   k-tiles kept in flight per wave (register ring)
+//   nw  waves per workgroup, splitting the workgroup's k-range
+//   S   k-splits across workgroups (only 1 is built)
+struct SkinnyCfg {
+    int MT, NT, P, nw, S;
+};
+SkinnyCfg skinny_config(int M, int N, int K);
+hipError_t launch_w4a16_skinny_cfg(const SkinnyCfg &c, const uint16_t *A, const uint32_t *W,
+                                   const uint16_t *S, const uint16_t *D, uint16_t *C, int M,
+                                   int N, int K, int g, bool fuse_delta, void *ws,
+                                   hipStream_t st);
+hipError_t launch_w4a16_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                              const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                              bool fuse_delta, hipStream_t st);
+
+// Bytes of workspace the W4A16 GEMM kernels need for this shape (0 = none).
+size_t w4a16_workspace_bytes(int M, int N, int K);
+
+// C = A . W; when D != nullptr and fuse_delta, the delta term is added in the
+// epilogue; when D == nullptr or !fuse_delta, C is the symmetric product.
+// `ws` must hold w4a16_workspace_bytes(M, N, K) bytes (may be null when 0).
+hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                        const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                        bool fuse_delta, void *ws, hipStream_t st);
+
+// a_sum[M, K/g] (fp32) into `a_sum`, then C += a_sum @ delta.
+hipError_t launch_group_sum_correction(const uint16_t *A, const uint16_t *D, uint16_t *C,
+                                       int M, int N, int K, int g, float *a_sum,
+                                       hipStream_t st);
+
+hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
+                       const uint16_t *S, const int32_t *offsets, int E, int M_total,
+                       int max_rows, int N, int K, int g, uint16_t *C, int32_t *acc_debug,
+                       hipStream_t st);
+
+} // namespace qg

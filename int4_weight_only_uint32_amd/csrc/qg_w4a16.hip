@@ -1,0 +1,533 @@
+// W4A16 GEMM kernels and the two-stage asymmetric correction.
+//
+// Method ("Marlin INT4 on Ada - how it works", section "The core mismatch:
+// symmetric vs asymmetric"): with delta[g,n] = zero[g,n] + 8*scale[g,n],
+//     C = A . W_sym + A_group_sum @ delta,  W_sym[k,n] = (q[k,n] - 8) scale[g,n]
+// which is exact because delta does not depend on k.
+//
+// Skinny kernel (small M).  A wave owns MT 16-row m-tiles x NT 16-column
+// n-tiles and a contiguous range of 128-k tiles, with P tiles of codes and
+// activations in flight in a register ring; the waves of a workgroup split K
+// and are summed through LDS at the end (one launch, no workspace).
+// Per 128-k tile and n-tile, a lane loads one 128-bit word of codes, turns it
+// into four fp16 MFMA operands by masking alone (codes as exact fp16
+// subnormals), and runs four 16x16x32 fp16 MFMAs that accumulate
+//     X = sum_k A[m,k] * q[k,n]            (unsigned codes, up to 2^-20)
+// The group scale is applied once per tile on the fp32 accumulator:
+//     acc += scale * X + (delta - 8 scale) * a_sum        (asymmetric)
+//     acc += scale * X - 8 scale * a_sum                   (symmetric)
+// where a_sum = sum_k A[m,k] over the tile comes from four MFMAs against an
+// all-ones operand (it lands in the accumulator layout, no shuffles).
+#include "qg_device.h"
+#include "qg_launch.h"
+
+namespace qg {
+
+template <int MT, int NT, int P, int NWMAX, bool DELTA>
+__global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
+    const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
+    const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g, int nw)
+{
+    extern __shared__ float red[];
+    const int lane = threadIdx.x & 63;
+    // the wave index is uniform across a wave: keep it (and everything derived
+    // from it) in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, kq = lane >> 4;
+    const int KT = K / KTILE;
+    const int nt0 = blockIdx.x * NT;
+    const int m0 = blockIdx.y * 16 * MT;
+    const int kt_beg = (wave * KT) / nw, kt_end = ((wave + 1) * KT) / nw;
+    const int n = kt_end - kt_beg;
+
+    // Rows past M read row M-1: those lanes only feed output rows >= M, which
+    // are never stored, so no load is predicated.
+    const uint16_t *arow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        int r = m0 + 16 * mt + c;
+        r = r < M ? r : M - 1;
+        arow[mt] = A + (size_t)r * K + 8 * kq;
+    }
+    const uint4v *wbase = W + (size_t)nt0 * KT * 64 + lane;
+    const int col0 = nt0 * NTILE + c;
+
+    float4v acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    const float4v fzero = {0.f, 0.f, 0.f, 0.f};
+
+    // P-deep register ring; every slot is refilled unconditionally (indices
+    // clamped to the wave's last tile) so the number of loads in flight is the
+    // same on every path and each wait only covers the slot being consumed.
+    uint4v rw[P][NT];
+    half8 ra[P][MT][4];
+    uint16_t rs[P][NT], rd[P][NT];
+    auto load = [&](int kt, uint4v (&w)[NT], half8 (&a)[MT][4], uint16_t (&sv)[NT],
+                    uint16_t (&dv)[NT]) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) w[t] = wbase[((size_t)t * KT + kt) * 64];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int o = 0; o < 4; ++o)
+                a[mt][o] = *reinterpret_cast<const half8 *>(arow[mt] + kt * KTILE + 32 * o);
+        const int gi = (kt * KTILE) / g;
+        const uint16_t *srow = S + (size_t)gi * N + col0;
+        const uint16_t *drow = DELTA ? D + (size_t)gi * N + col0 : nullptr;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            sv[t] = srow[16 * t];
+            dv[t] = DELTA ? drow[16 * t] : (uint16_t)0;
+        }
+    };
+    auto compute = [&](const uint4v (&w)[NT], const half8 (&a)[MT][4], const uint16_t (&sv)[NT],
+                       const uint16_t (&dv)[NT]) {
+        float4v as[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            float4v y = mfma_f16(a[mt][0], ones, fzero);
+            y = mfma_f16(a[mt][1], ones, y);
+            y = mfma_f16(a[mt][2], ones, y);
+            as[mt] = mfma_f16(a[mt][3], ones, y);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            CodeOps ops = split_codes(w[t]);
+            const float s = h2f(sv[t]);
+            const float c1 = s * 0x1p20f;
+            const float c2 = DELTA ? (h2f(dv[t]) - 8.0f * s) : (-8.0f * s);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                float4v x = mfma_f16(a[mt][0], ops.lo[0], fzero);
+                x = mfma_f16(a[mt][1], ops.lo[1], x);
+                x = x * 16.0f;
+                x = mfma_f16(a[mt][2], ops.hi[0], x);
+                x = mfma_f16(a[mt][3], ops.hi[1], x);
+                acc[mt][t] += c1 * x + c2 * as[mt];
+            }
+        }
+    };
+
+    if (n > 0) {
+        const int last = kt_end - 1;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int kt = kt_beg + i;
+            load(kt < last ? kt : last, rw[i], ra[i], rs[i], rd[i]);
+        }
+        // full rounds: the same load/compute sequence every time, so each
+        // slot's wait leaves the other P-1 slots in flight
+        int j = 0;
+        for (; j + P <= n; j += P) {
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                compute(rw[i], ra[i], rs[i], rd[i]);
+                const int kt = kt_beg + j + i + P;
+                load(kt < last ? kt : last, rw[i], ra[i], rs[i], rd[i]);
+            }
+        }
+        // remainder: fewer than P tiles, already in their slots
+#pragma unroll
+        for (int i = 0; i < P - 1; ++i)
+            if (j + i < n) compute(rw[i], ra[i], rs[i], rd[i]);
+    }
+
+    // sum the waves' partial products through LDS
+    constexpr int E4 = MT * NT * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[((size_t)wave * E4 + (mt * NT + t) * 4 + r) * 64 + lane] = acc[mt][t][r];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < E4 * 64; idx += blockDim.x) {
+        float v = 0.f;
+        for (int w = 0; w < nw; ++w) v += red[(size_t)w * E4 * 64 + idx];
+        const int e = idx >> 6, l = idx & 63;
+        const int r = e & 3, t = (e >> 2) % NT, mt = (e >> 2) / NT;
+        const int row = m0 + 16 * mt + 4 * (l >> 4) + r;
+        const int cc = (nt0 + t) * NTILE + (l & 15);
+        if (row < M) C[(size_t)row * N + cc] = f2h(v);
+    }
+}
+
+template <int MT, int NT, int P, int NWMAX, bool DELTA>
+static hipError_t run_skinny(const SkinnyCfg &cf, const uint16_t *A, const uint32_t *W,
+                             const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
+                             int K, int g, hipStream_t st)
+{
+    dim3 grid((unsigned)(N / (NTILE * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
+    size_t lds = (size_t)cf.nw * MT * NT * 4 * 64 * sizeof(float);
+    if (cf.nw < 1 || cf.nw > NWMAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((w4a16_skinny_kernel<MT, NT, P, NWMAX, DELTA>), grid, dim3(64 * cf.nw), lds,
+                       st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g, cf.nw);
+    return hipGetLastError();
+}
+
+// ---- tiled kernel (large M) ----
+// Workgroup tile 128 rows x 256 columns, 4 waves; wave w owns columns
+// [64w, 64w+64) (4 n-tiles) and all 128 rows (8 m-tiles).  A is staged
+// through LDS (two buffers of 128 x 128 fp16) with gfx950's direct
+// global->LDS 16-byte loads, no registers in between.  Within a 256-byte row
+// the 16-byte chunk ch is stored at position ch ^ (row % 16), so the 16 rows
+// an MFMA operand reads fall in distinct LDS banks; packed codes go
+// straight from global memory to registers, each wave reading only its own
+// columns.  Codes are dequantized per element to fp16 ((v - 8) * scale,
+// exact up to the one fp16 rounding of the product) and fed to 16x16x32 fp16
+// MFMAs.  Asymmetric weights: the per-group sums of A are accumulated by
+// MFMAs against an all-ones operand (wave w sums m-tiles 2w and 2w+1), parked
+// in LDS, and every 16 groups applied as one extra MFMA k-step whose A side is
+// the group sums (split into a high and a low fp16 part) and whose B side is
+// delta -- the "A_group_sum @ delta" term of the method, fused.
+// Rows from which the LDS-tiled kernel takes over from the skinny one.
+constexpr int TILED_MIN_M = 128;
+
+namespace tiled {
+constexpr int BM = 128, BN = 256;
+constexpr int WIN = 16;                         // groups per correction k-step
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// fp16 operand of k-step STEP (0..3) of a 128-k tile, scaled per element.
+template <int STEP>
+__device__ inline half8 dequant_scaled(uint4v w, half2v s2)
+{
+    const unsigned xa = (STEP & 1) ? w.z : w.x;
+    const unsigned xb = (STEP & 1) ? w.w : w.y;
+    const unsigned m = (STEP >= 2) ? 0x00F000F0u : 0x000F000Fu;
+    const unsigned magic = 0x64006400u;       // fp16 1024.0 in both halves
+    unsigned p[4] = {(xa & m) | magic, ((xa >> 8) & m) | magic, (xb & m) | magic,
+                     ((xb >> 8) & m) | magic};
+    unsigned out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        half2v h = __builtin_bit_cast(half2v, p[i]);
+        half2v v;
+        if (STEP >= 2) {
+            // 1024 + 16 v  ->  (1024 + 16 v) / 16 - 72 = v - 8   (exact)
+            v = h * half2v{(_Float16)0.0625f, (_Float16)0.0625f} - half2v{(_Float16)72.f, (_Float16)72.f};
+        } else {
+            // 1024 + v  ->  v - 8   (exact)
+            v = h - half2v{(_Float16)1032.f, (_Float16)1032.f};
+        }
+        v = v * s2;
+        out[i] = __builtin_bit_cast(unsigned, v);
+    }
+    return __builtin_bit_cast(half8, uint4v{out[0], out[1], out[2], out[3]});
+}
+
+template <bool DELTA>
+__global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
+    const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
+    const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g)
+{
+    using namespace tiled;
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * 128];
+    __shared__ __attribute__((aligned(16))) float asum_win[DELTA ? BM * WIN : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, kq = lane >> 4;
+    const int KT = K / KTILE, G = K / g;
+    const int m0 = blockIdx.y * BM;
+    const int n0 = blockIdx.x * BN + wave * 64;        // this wave's first column
+    const bool active = n0 < N;
+    const int ntile0 = n0 / NTILE;
+
+    // ---- A: global -> LDS directly.  One wave instruction fills 1 KB = 4
+    // rows; lane i lands at position i of that block, i.e. row 4b + i/16,
+    // physical chunk i%16, which holds logical chunk (i%16) ^ (row%16).
+    // Rows past M read row M-1 (their results are never stored).
+    auto load_a = [&](int kt, int st) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int blk = wave * 8 + i;             // 32 blocks of 4 rows
+            const int r = blk * 4 + (lane >> 4);
+            const int ch = (lane & 15) ^ (r & 15);
+            int row = m0 + r;
+            row = row < M ? row : M - 1;
+            const uint16_t *src = A + (size_t)row * K + kt * KTILE + ch * 8;
+            __builtin_amdgcn_global_load_lds(
+                (const void *)src,
+                (__attribute__((address_space(3))) void *)(&As[st][blk * 4 * 128]), 16, 0, 0);
+        }
+    };
+    auto a_frag = [&](const _Float16 *as, int mt, int o) {
+        const int r = 16 * mt + c;
+        const int pch = (4 * o + kq) ^ c;
+        return *reinterpret_cast<const half8 *>(as + r * 128 + pch * 8);
+    };
+    // ---- codes and scales of this wave's 4 n-tiles
+    uint4v wreg[4];
+    uint16_t sreg[4];
+    auto load_w = [&](int kt) {
+        if (!active) return;
+        const int gi = (kt * KTILE) / g;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            wreg[t] = W[((size_t)(ntile0 + t) * KT + kt) * 64 + lane];
+            sreg[t] = S[(size_t)gi * N + n0 + 16 * t + c];
+        }
+    };
+
+    float4v acc[8][4];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
+    float4v gsum[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
+    const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    if (DELTA)
+        for (int i = tid; i < BM * WIN; i += 256) asum_win[i] = 0.f;
+
+    // the delta k-step for the window of groups [gw0, gw0 + WIN)
+    auto delta_step = [&](int gw0) {
+        if (!active) return;
+        half8 be[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int colx = n0 + 16 * t + c;
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) {
+                const int gg = gw0 + 8 * (kq & 1) + s8;
+                be[t][s8] = gg < G ? __builtin_bit_cast(_Float16, D[(size_t)gg * N + colx])
+                                   : (_Float16)0.f;
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const float *src = &asum_win[(16 * mt + c) * WIN + 8 * (kq & 1)];
+            half8 ae;
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) {
+                const float a = src[s8];
+                const _Float16 hi = (_Float16)a;
+                ae[s8] = (kq < 2) ? hi : (_Float16)(a - (float)hi);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_f16(ae, be[t], acc[mt][t]);
+        }
+    };
+
+    load_a(0, 0);
+    load_w(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int st = kt & 1;
+        uint4v wc[4];
+        half2v s2[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            wc[t] = wreg[t];
+            const _Float16 sh = __builtin_bit_cast(_Float16, sreg[t]);
+            s2[t] = half2v{sh, sh};
+        }
+        if (kt + 1 < KT) {
+            load_a(kt + 1, st ^ 1);
+            load_w(kt + 1);
+        }
+        const _Float16 *as = As[st];
+        if (active) {
+#define QG_TILED_STEP(O)                                                                     \
+    {                                                                                        \
+        half8 b[4];                                                                          \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) b[t] = dequant_scaled<O>(wc[t], s2[t]); \
+        _Pragma("unroll") for (int mt = 0; mt < 8; ++mt)                                     \
+        {                                                                                    \
+            const half8 a = a_frag(as, mt, O);                                               \
+            _Pragma("unroll") for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_f16(a, b[t], acc[mt][t]); \
+        }                                                                                    \
+    }
+            QG_TILED_STEP(0)
+            QG_TILED_STEP(1)
+            QG_TILED_STEP(2)
+            QG_TILED_STEP(3)
+#undef QG_TILED_STEP
+        }
+        if (DELTA) {
+            // group sums of this wave's two m-tiles
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int mt = 2 * wave + j;
+#pragma unroll
+                for (int o = 0; o < 4; ++o) {
+                    const half8 a = a_frag(as, mt, o);
+                    gsum[j] = mfma_f16(a, ones, gsum[j]);
+                }
+            }
+            const int gi = (kt * KTILE) / g;
+            const bool gend = ((kt + 1) * KTILE) % g == 0;
+            if (gend) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        asum_win[(16 * (2 * wave + j) + 4 * kq + r) * WIN + (gi % WIN)] = gsum[j][r];
+                    gsum[j] = float4v{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+        // the direct loads of the next A tile (and the next codes) must have
+        // landed before any wave reads them
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (DELTA) {
+            const int gi = (kt * KTILE) / g;
+            const bool gend = ((kt + 1) * KTILE) % g == 0;
+            if (gend && (gi % WIN == WIN - 1 || gi == G - 1)) {
+                delta_step(gi - gi % WIN);
+                // later groups of the next window overwrite these slots only
+                // after the next barrier, when every wave has read them
+            }
+        }
+    }
+
+    if (!active) return;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + 16 * mt + 4 * kq + r;
+                if (row < M) C[(size_t)row * N + n0 + 16 * t + c] = f2h(acc[mt][t][r]);
+            }
+}
+
+template <bool DELTA>
+static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                            const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                            hipStream_t st)
+{
+    dim3 grid((unsigned)((N + tiled::BN - 1) / tiled::BN), (unsigned)((M + tiled::BM - 1) / tiled::BM));
+    hipLaunchKernelGGL((w4a16_tiled_kernel<DELTA>), grid, dim3(256), 0, st, A,
+                       reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a16_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                              const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                              bool fuse_delta, hipStream_t st)
+{
+    if (D && fuse_delta) return run_tiled<true>(A, W, S, D, C, M, N, K, g, st);
+    return run_tiled<false>(A, W, S, nullptr, C, M, N, K, g, st);
+}
+
+// Heuristic choice of the skinny configuration (also sizes the workspace).
+SkinnyCfg skinny_config(int M, int N, int K)
+{
+    SkinnyCfg c;
+    const int KT = K / KTILE, NT16 = N / NTILE;
+    if (M <= 16) {
+        c.MT = 1; c.NT = 2; c.P = 2;
+    } else if (M <= 32) {
+        c.MT = 2; c.NT = 4; c.P = 2;
+    } else {
+        c.MT = 4; c.NT = 2; c.P = 2;
+    }
+    const int nwmax = (c.MT == 1) ? 16 : 4;
+    c.S = 1;
+    const long blocks = (long)(NT16 / c.NT) * ((M + 16 * c.MT - 1) / (16 * c.MT));
+    // about 2000-3000 waves, each with at least 2 k-tiles
+    c.nw = 1;
+    while (c.nw < nwmax && blocks * c.nw * 2 <= 3072 && KT / (c.nw * 2) >= 2) c.nw *= 2;
+    return c;
+}
+
+size_t w4a16_workspace_bytes(int M, int N, int K)
+{
+    (void)M; (void)N; (void)K;
+    return 0;   // neither the skinny nor the tiled kernel needs scratch memory
+}
+
+template <bool DELTA>
+static hipError_t dispatch_skinny(const SkinnyCfg &c, const uint16_t *A, const uint32_t *W,
+                                  const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
+                                  int K, int g, hipStream_t st)
+{
+    if (c.S != 1) return hipErrorInvalidConfiguration;
+#define QG_SK(MT_, NT_, P_, NWMAX_)                                                             \
+    if (c.MT == MT_ && c.NT == NT_ && c.P == P_ && c.nw <= NWMAX_)                              \
+        return run_skinny<MT_, NT_, P_, NWMAX_, DELTA>(c, A, W, S, D, C, M, N, K, g, st);
+    QG_SK(1, 1, 4, 16) QG_SK(1, 1, 8, 8) QG_SK(1, 2, 2, 16) QG_SK(1, 2, 3, 8) QG_SK(1, 2, 4, 8)
+    QG_SK(1, 4, 2, 8) QG_SK(1, 4, 3, 4) QG_SK(1, 8, 2, 4)
+    QG_SK(2, 4, 2, 4) QG_SK(4, 2, 2, 4)
+#undef QG_SK
+    return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_w4a16_skinny_cfg(const SkinnyCfg &c, const uint16_t *A, const uint32_t *W,
+                                   const uint16_t *S, const uint16_t *D, uint16_t *C, int M,
+                                   int N, int K, int g, bool fuse_delta, void *ws,
+                                   hipStream_t st)
+{
+    (void)ws;
+    if (D && fuse_delta) return dispatch_skinny<true>(c, A, W, S, D, C, M, N, K, g, st);
+    return dispatch_skinny<false>(c, A, W, S, nullptr, C, M, N, K, g, st);
+}
+
+hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                        const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                        bool fuse_delta, void *ws, hipStream_t st)
+{
+    if (M >= TILED_MIN_M) return launch_w4a16_tiled(A, W, S, D, C, M, N, K, g, fuse_delta, st);
+    return launch_w4a16_skinny_cfg(skinny_config(M, N, K), A, W, S, D, C, M, N, K, g,
+                                   fuse_delta, ws, st);
+}
+
+// ---- two-stage correction ("The pipeline, end to end": a_group_sum then
+//      correction_accum) ----
+// Stage 1: one wave per (row, group); lanes sum a strided slice in fp32 and
+// the wave combines them with butterfly shuffles.
+__global__ __launch_bounds__(64) void group_sum_kernel(const uint16_t *__restrict__ A, int K,
+                                                       int g, int G, float *__restrict__ a_sum)
+{
+    const int cell = blockIdx.x;          // m * G + gi
+    const int m = cell / G, gi = cell % G;
+    const uint16_t *p = A + (size_t)m * K + (size_t)gi * g;
+    float v = 0.f;
+    for (int k = threadIdx.x; k < g; k += 64) v += h2f(p[k]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (threadIdx.x == 0) a_sum[cell] = v;
+}
+
+// Stage 2: one thread per output cell: C += sum_g a_sum[m,g] * delta[g,n].
+__global__ __launch_bounds__(256) void correction_accum_kernel(const float *__restrict__ a_sum,
+                                                               const uint16_t *__restrict__ D,
+                                                               uint16_t *__restrict__ C, int N,
+                                                               int G, size_t total)
+{
+    size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const size_t m = idx / N, n = idx % N;
+    float corr = 0.f;
+    for (int gi = 0; gi < G; ++gi) corr += a_sum[m * G + gi] * h2f(D[(size_t)gi * N + n]);
+    C[idx] = f2h(h2f(C[idx]) + corr);
+}
+
+hipError_t launch_group_sum_correction(const uint16_t *A, const uint16_t *D, uint16_t *C,
+                                       int M, int N, int K, int g, float *a_sum,
+                                       hipStream_t st)
+{
+    const int G = K / g;
+    hipLaunchKernelGGL(group_sum_kernel, dim3((unsigned)((size_t)M * G)), dim3(64), 0, st, A, K,
+                       g, G, a_sum);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    size_t total = (size_t)M * N;
+    hipLaunchKernelGGL(correction_accum_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                       0, st, a_sum, D, C, N, G, total);
+    return hipGetLastError();
+}
+
+} // namespace qg

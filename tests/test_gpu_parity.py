@@ -1,0 +1,269 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU
+oracle on the same seeded inputs.
+
+Bars: packing is bit-exact (codes, folded scales, delta); W4A16 relative
+Frobenius error <= 2e-3 plus an elementwise guard; W4A8 int32 accumulators
+bit-exact and output relative error <= 1e-2 plus the guard; integer-valued
+cases bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_uint32_amd as qg
+import oracle
+import synth
+from tests.gpu_util import dev, elementwise_guard, host, note, pack_case, rel_fro, run_w4a16
+from tests.layout_unpack import unpack_codes
+
+pytestmark = pytest.mark.gpu
+
+W4A16_TOL = 2e-3
+W4A8_TOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available()
+    assert qg.qg_device_supported(0), "GPU visible but not gfx950"
+    oracle.build(force=False)
+
+
+# ------------------------------------------------------------------ pack --
+@pytest.mark.parametrize("K,N,g,asym,signed", [
+    (256, 384, 128, False, True),
+    (512, 256, 256, False, True),
+    (1024, 128, -1, False, True),
+    (256, 384, 128, True, False),
+    (384, 256, 128, True, True),
+    (128, 128, 128, False, False),
+])
+def test_pack_bit_exact(K, N, g, asym, signed):
+    note(f"pack K={K} N={N} g={g} asym={asym}")
+    gg = K if g == -1 else g
+    c = synth.w4a16_case(1, K, N, gg, asym=asym, signed_scales=signed, config_id=80, case_id=K + N)
+    s = c.s.copy()
+    if signed:
+        s[0, :4] = np.float16(-0.0)          # negative zero: not folded
+    q = c.q.copy()
+    q[:gg, 0] = 0                            # a fully negative-scale group with code 0 -> clamp
+    s[0, 0] = np.float16(-0.5) if signed else s[0, 0]
+    pw = qg.pack(dev(q), dev(s), dev(c.z) if asym else None, g, fold=True)
+    torch.cuda.synchronize()
+    got_q = unpack_codes(host(pw.w), K, N)
+    got_s = host(pw.scale).view(np.uint16)
+    if asym:
+        assert np.array_equal(got_q, q)
+        assert np.array_equal(got_s, s.view(np.uint16))
+        _, dh = oracle.delta(s, c.z)
+        assert np.array_equal(host(pw.delta).view(np.uint16), dh)
+    else:
+        qf, sf, n = oracle.fold_negative_scales(q, s, gg)
+        assert np.array_equal(got_q, qf)
+        assert np.array_equal(got_s, sf)
+        if signed:
+            assert n > 0
+    # no fold requested: codes and scales pass through unchanged
+    pw2 = qg.pack(dev(q), dev(s), None, g, fold=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(unpack_codes(host(pw2.w), K, N), q)
+    assert np.array_equal(host(pw2.scale).view(np.uint16), s.view(np.uint16))
+
+
+def test_pack_structured_codes():
+    K, N = 512, 256
+    k = np.arange(K)[:, None]
+    n = np.arange(N)[None, :]
+    q = ((k + 3 * n) % 16).astype(np.uint8)
+    s = np.full((K // 128, N), 0.01, np.float16)
+    pw = qg.pack(dev(q), dev(s), None, 128, fold=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(unpack_codes(host(pw.w), K, N), q)
+
+
+# ----------------------------------------------------------------- W4A16 --
+def _check_w4a16(case, flags=0, fold=True, tol=W4A16_TOL):
+    note(f"w4a16 {case.name} M={case.M} K={case.K} N={case.N} g={case.g} "
+         f"asym={case.z is not None} flags={flags}")
+    got, _ = run_w4a16(case, flags=flags, fold=fold)
+    ref = oracle.w4a16(case.A, case.q, case.s, case.z, case.g, fold=fold)
+    err = rel_fro(got, ref)
+    assert np.all(np.isfinite(got))
+    assert err <= tol, err
+    assert elementwise_guard(got, ref) <= 0
+    return err
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 33, 64, 100, 130])
+@pytest.mark.parametrize("K,N,g,asym", [
+    (1024, 1024, 128, True),
+    (2048, 256, 256, True),
+    (512, 384, -1, True),
+    (1024, 512, 128, False),
+])
+def test_w4a16_ragged_shapes(M, K, N, g, asym):
+    gg = K if g == -1 else g
+    c = synth.w4a16_case(M, K, N, gg, asym=asym, signed_scales=not asym, config_id=81,
+                         case_id=M * 7 + K + N, name="ragged")
+    _check_w4a16(c)
+
+
+@pytest.mark.parametrize("case_id", [0])
+def test_w4a16_config0(case_id):
+    c = synth.config_case(0, case_id)
+    _check_w4a16(c)
+    _check_w4a16(c, flags=qg.QG_CORR_SEPARATE)
+
+
+@pytest.mark.parametrize("case_id", range(6))
+def test_w4a16_config1_decode(case_id):
+    _check_w4a16(synth.config_case(1, case_id))
+
+
+@pytest.mark.parametrize("case_id", range(2))
+def test_w4a16_config2_midbatch(case_id):
+    c = synth.config_case(2, case_id)
+    _check_w4a16(c)
+    _check_w4a16(c, flags=qg.QG_CORR_SEPARATE)
+
+
+def test_w4a16_config3_prefill_sampled():
+    """Full prefill shape (M=4096, K=5120, N=17408, random-sign scales, fold on)
+    in the benchmark's launch configuration; the oracle evaluates sampled cells
+    one by one (every row and column band is hit)."""
+    c = synth.config_case(3, 0)
+    note(f"w4a16 config3 M={c.M} K={c.K} N={c.N}")
+    got, _ = run_w4a16(c)
+    r = np.random.default_rng(5)
+    rows = np.concatenate([r.integers(0, c.M, 3000), [0, c.M - 1, 0, c.M - 1]])
+    cols = np.concatenate([r.integers(0, c.N, 3000), [0, 0, c.N - 1, c.N - 1]])
+    ref = oracle.w4a16_cells(c.A, c.q, c.s, None, c.g, rows, cols, fold=True)
+    g = got[rows, cols]
+    assert rel_fro(g, ref) <= W4A16_TOL
+    assert elementwise_guard(g, ref) <= 0
+    assert np.all(np.isfinite(got))
+    # the fold matters at this distribution: the unfolded product is far off
+    ref_nofold = oracle.w4a16_cells(c.A, c.q, c.s, None, c.g, rows, cols, fold=False)
+    assert rel_fro(ref_nofold, ref) > 10 * W4A16_TOL
+
+
+def test_w4a16_config3_dense_slice():
+    """A 256-row slice of the prefill case checked densely."""
+    c = synth.config_case(3, 0)
+    sl = synth.W4A16Case(A=c.A[:256], q=c.q[:, :2048], s=c.s[:, :2048], z=None, g=c.g,
+                         name="c3-slice")
+    _check_w4a16(sl)
+
+
+def test_w4a16_integer_exact():
+    """Integer data: every product and sum is exact, so the fp16 output must be
+    bit-identical to the exact result."""
+    r = np.random.default_rng(11)
+    M, K, N = 37, 256, 384
+    A = r.integers(-1, 2, (M, K)).astype(np.float16)
+    q = r.integers(0, 16, (K, N), dtype=np.uint8)
+    s = np.ones((2, N), np.float16)
+    z = np.full((2, N), -8.0, np.float16)
+    z[1] = -3.0
+    for zz in (None, z):
+        case = synth.W4A16Case(A=A, q=q, s=s, z=zz, g=128, name="int-exact")
+        got, _ = run_w4a16(case)
+        ref = oracle.w4a16(A, q, s, zz, 128, fold=False)
+        assert np.abs(ref).max() <= 2048
+        assert np.array_equal(got, ref)
+
+
+def test_w4a16_degenerate_values():
+    r = np.random.default_rng(12)
+    M, K, N = 16, 256, 128
+    A = r.standard_normal((M, K)).astype(np.float16)
+    q = np.full((K, N), 8, np.uint8)
+    s = r.uniform(1e-3, 2e-2, (2, N)).astype(np.float16)
+    got, _ = run_w4a16(synth.W4A16Case(A=A, q=q, s=s, z=None, g=128))
+    # the kernel forms s*sum(A*q) - 8s*sum(A): with q == 8 the two fp32 terms
+    # cancel up to their rounding, a few ulp of |8 s a_sum| (<= 8 here)
+    a_sum = np.abs(A.astype(np.float64).reshape(M, 2, 128).sum(axis=2)).max()
+    assert np.max(np.abs(got)) <= 8 * 2.0 ** -23 * 8 * 0.02 * a_sum * 2
+    A0 = np.zeros((M, K), np.float16)
+    c = synth.w4a16_case(M, K, N, 128, asym=True, config_id=82, case_id=1)
+    got, _ = run_w4a16(synth.W4A16Case(A=A0, q=c.q, s=c.s, z=c.z, g=128))
+    assert np.all(got == 0.0)
+
+
+def test_w4a16_fold_off_matches_unfolded():
+    c = synth.w4a16_case(16, 1024, 512, 128, asym=False, signed_scales=True, config_id=83,
+                         case_id=0)
+    _check_w4a16(c, fold=False)
+
+
+def test_w4a16_deterministic():
+    c = synth.config_case(1, 2)
+    a, _ = run_w4a16(c)
+    b, _ = run_w4a16(c)
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------ correction stage --
+@pytest.mark.parametrize("M,K,N,g", [(5, 1024, 256, 128), (64, 4096, 384, 4096), (130, 512, 128, 256)])
+def test_group_sum_correction(M, K, N, g):
+    note(f"group_sum_correction M={M} K={K} N={N} g={g}")
+    c = synth.w4a16_case(M, K, N, g, asym=True, config_id=84, case_id=M)
+    _, dh = oracle.delta(c.s, c.z)
+    r = np.random.default_rng(M)
+    Cin = r.standard_normal((M, N)).astype(np.float16)
+    Ct = dev(Cin)
+    qg.correct(dev(c.A), dev(dh.view(np.float16)), Ct, g)
+    torch.cuda.synchronize()
+    got = host(Ct).astype(np.float64)
+    ref = oracle.group_sum_correction(c.A, dh, Cin, g)
+    # fp32 accumulation then one fp16 rounding: within 2 fp16 ulps of the exact value
+    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 2 * np.maximum(ulp, 2.0 ** -24) + 1e-6 * np.abs(ref) + 1e-7)
+
+
+# ------------------------------------------------------------------ W4A8 --
+def _run_w4a8(case, max_rows=None, offsets=True, fold=True):
+    E, K, N, g = case.E, case.K, case.N, case.g
+    ws, ss = [], []
+    for e in range(E):
+        pw = qg.pack(dev(case.q[e]), dev(case.s[e]), None, g, fold=fold)
+        ws.append(pw.w)
+        ss.append(pw.scale)
+    W = torch.stack(ws).contiguous()
+    S = torch.stack(ss).contiguous()
+    G = K // g
+    acc = torch.full((case.M_total, G, N), -7, dtype=torch.int32, device="cuda")
+    off = dev(case.offsets) if offsets else None
+    mr = max_rows if max_rows is not None else int(np.max(np.diff(case.offsets)))
+    C = qg.w4a8(dev(case.Aq), dev(case.a_scale), W, S, off, E, max(mr, 1), N, g, acc_debug=acc)
+    torch.cuda.synchronize()
+    return host(C).astype(np.float64), host(acc)
+
+
+def _check_w4a8(case, **kw):
+    note(f"w4a8 {case.name} E={case.E} rows={np.diff(case.offsets).tolist()} K={case.K} N={case.N}")
+    got, acc = _run_w4a8(case, **kw)
+    ref, ref_acc = oracle.w4a8(case.Aq, case.a_scale, case.q, case.s, case.offsets, case.g, fold=True)
+    assert np.array_equal(acc.astype(np.int64), ref_acc)
+    err = rel_fro(got, ref)
+    assert err <= W4A8_TOL, err
+    assert elementwise_guard(got, ref) <= 0
+    return err
+
+
+def test_w4a8_config4():
+    c = synth.config_case(4, 0)
+    err = _check_w4a8(c)
+    note(f"w4a8 config4 rel_fro vs same-int8 oracle = {err:.3e}")
+
+
+def test_w4a8_ragged_experts_and_fold():
+    c = synth.w4a8_case(5, 0, 512, 256, 128, signed_scales=True, config_id=85, case_id=0,
+                        rows=[0, 17, 64, 3, 100])
+    _check_w4a8(c)
+
+
+def test_w4a8_single_expert_no_offsets():
+    c = synth.w4a8_case(1, 40, 1024, 384, 256, config_id=85, case_id=1)
+    _check_w4a8(c, offsets=False)
+    c2 = synth.w4a8_case(1, 7, 768, 128, 768, config_id=85, case_id=2)
+    _check_w4a8(c2, offsets=False)
