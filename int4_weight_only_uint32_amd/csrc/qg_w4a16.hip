@@ -28,7 +28,10 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g, int nw)
 {
-    extern __shared__ float red[];
+    // LDS: per wave, one k-tile of activations (16*MT rows x 128 k fp16,
+    // 16-byte chunks swizzled by row); reused for the cross-wave sum.
+    extern __shared__ __attribute__((aligned(16))) float red[];
+    constexpr int SLOT_HALVES = MT * 16 * KTILE;
     const int lane = threadIdx.x & 63;
     // the wave index is uniform across a wave: keep it (and everything derived
     // from it) in scalar registers
@@ -39,15 +42,22 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
     const int m0 = blockIdx.y * 16 * MT;
     const int kt_beg = (wave * KT) / nw, kt_end = ((wave + 1) * KT) / nw;
     const int n = kt_end - kt_beg;
+    _Float16 *scratch = reinterpret_cast<_Float16 *>(red) + (size_t)wave * SLOT_HALVES;
 
-    // Rows past M read row M-1: those lanes only feed output rows >= M, which
-    // are never stored, so no load is predicated.
-    const uint16_t *arow[MT];
+    // Activations are fetched row-contiguously (load j covers rows 4j..4j+3,
+    // 256 bytes each: lane i reads chunk i%16 of row 4j + i/16), which keeps a
+    // wave's request to 8 whole cache lines, then rearranged through LDS into
+    // the MFMA operand layout.  Rows past M read row M-1 (they only feed output
+    // rows that are never stored).
+    const uint4v *asrc[MT * 4];
+    int adst[MT * 4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        int r = m0 + 16 * mt + c;
-        r = r < M ? r : M - 1;
-        arow[mt] = A + (size_t)r * K + 8 * kq;
+    for (int j = 0; j < MT * 4; ++j) {
+        const int r = 4 * j + (lane >> 4);
+        int row = m0 + r;
+        row = row < M ? row : M - 1;
+        asrc[j] = reinterpret_cast<const uint4v *>(A + (size_t)row * K) + (lane & 15);
+        adst[j] = r * KTILE + 8 * ((lane & 15) ^ (r & 15));
     }
     const uint4v *wbase = W + (size_t)nt0 * KT * 64 + lane;
     const int col0 = nt0 * NTILE + c;
@@ -61,32 +71,57 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     const float4v fzero = {0.f, 0.f, 0.f, 0.f};
 
-    // P-deep register ring; every slot is refilled unconditionally (indices
-    // clamped to the wave's last tile) so the number of loads in flight is the
+    // P-deep register ring.  Every slot is refilled unconditionally (tile
+    // index clamped to the wave's last tile) so the loads in flight are the
     // same on every path and each wait only covers the slot being consumed.
+    uint4v ra[P][MT * 4];
     uint4v rw[P][NT];
-    half8 ra[P][MT][4];
     uint16_t rs[P][NT], rd[P][NT];
-    auto load = [&](int kt, uint4v (&w)[NT], half8 (&a)[MT][4], uint16_t (&sv)[NT],
+    auto load = [&](int kt, uint4v (&a)[MT * 4], uint4v (&w)[NT], uint16_t (&sv)[NT],
                     uint16_t (&dv)[NT]) {
 #pragma unroll
+        for (int j = 0; j < MT * 4; ++j) a[j] = asrc[j][kt * (KTILE / 8)];
+#pragma unroll
         for (int t = 0; t < NT; ++t) w[t] = wbase[((size_t)t * KT + kt) * 64];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int o = 0; o < 4; ++o)
-                a[mt][o] = *reinterpret_cast<const half8 *>(arow[mt] + kt * KTILE + 32 * o);
         const int gi = (kt * KTILE) / g;
         const uint16_t *srow = S + (size_t)gi * N + col0;
-        const uint16_t *drow = DELTA ? D + (size_t)gi * N + col0 : nullptr;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            sv[t] = srow[16 * t];
-            dv[t] = DELTA ? drow[16 * t] : (uint16_t)0;
+        for (int t = 0; t < NT; ++t) sv[t] = srow[16 * t];
+        if (DELTA) {
+            const uint16_t *drow = D + (size_t)gi * N + col0;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) dv[t] = drow[16 * t];
         }
     };
-    auto compute = [&](const uint4v (&w)[NT], const half8 (&a)[MT][4], const uint16_t (&sv)[NT],
-                       const uint16_t (&dv)[NT]) {
+    // Consuming a slot happens in two halves: `stage` moves the slot's
+    // activations into LDS and splits its codes into MFMA operands, after which
+    // the slot's registers are free and the refill can be issued; `finish`
+    // then does the MFMAs and the per-group scaling while the refill is in
+    // flight.
+    struct Staged {
+        CodeOps ops[NT];
+        float s[NT], d[NT];
+    };
+    auto stage = [&](const uint4v (&ar)[MT * 4], const uint4v (&w)[NT], const uint16_t (&sv)[NT],
+                     const uint16_t (&dv)[NT], Staged &st) {
+#pragma unroll
+        for (int j = 0; j < MT * 4; ++j) *reinterpret_cast<uint4v *>(scratch + adst[j]) = ar[j];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            st.ops[t] = split_codes(w[t]);
+            st.s[t] = h2f(sv[t]);
+            st.d[t] = DELTA ? h2f(dv[t]) : 0.f;
+        }
+    };
+    auto finish = [&](const Staged &st) {
+        half8 a[MT][4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int r = 16 * mt + c;
+#pragma unroll
+            for (int o = 0; o < 4; ++o)
+                a[mt][o] = *reinterpret_cast<const half8 *>(scratch + r * KTILE + 8 * ((4 * o + kq) ^ c));
+        }
         float4v as[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -97,18 +132,22 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            CodeOps ops = split_codes(w[t]);
-            const float s = h2f(sv[t]);
-            const float c1 = s * 0x1p20f;
-            const float c2 = DELTA ? (h2f(dv[t]) - 8.0f * s) : (-8.0f * s);
+            const float s = st.s[t];
+            const float c1 = s * 0x1p20f, c16 = s * 0x1p24f;
+            const float c2 = DELTA ? (st.d[t] - 8.0f * s) : (-8.0f * s);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                float4v x = mfma_f16(a[mt][0], ops.lo[0], fzero);
-                x = mfma_f16(a[mt][1], ops.lo[1], x);
-                x = x * 16.0f;
-                x = mfma_f16(a[mt][2], ops.hi[0], x);
-                x = mfma_f16(a[mt][3], ops.hi[1], x);
-                acc[mt][t] += c1 * x + c2 * as[mt];
+                float4v xl = mfma_f16(a[mt][0], st.ops[t].lo[0], fzero);
+                xl = mfma_f16(a[mt][1], st.ops[t].lo[1], xl);
+                float4v xh = mfma_f16(a[mt][2], st.ops[t].hi[0], fzero);
+                xh = mfma_f16(a[mt][3], st.ops[t].hi[1], xh);
+                // sum_k A q = 2^24 xl + 2^20 xh (exact powers of two)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = __builtin_fmaf(c16, xl[r], acc[mt][t][r]);
+                    v = __builtin_fmaf(c1, xh[r], v);
+                    acc[mt][t][r] = __builtin_fmaf(c2, as[mt][r], v);
+                }
             }
         }
     };
@@ -118,26 +157,30 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const int kt = kt_beg + i;
-            load(kt < last ? kt : last, rw[i], ra[i], rs[i], rd[i]);
+            load(kt < last ? kt : last, ra[i], rw[i], rs[i], rd[i]);
         }
-        // full rounds: the same load/compute sequence every time, so each
-        // slot's wait leaves the other P-1 slots in flight
         int j = 0;
         for (; j + P <= n; j += P) {
 #pragma unroll
             for (int i = 0; i < P; ++i) {
-                compute(rw[i], ra[i], rs[i], rd[i]);
+                Staged st;
+                stage(ra[i], rw[i], rs[i], rd[i], st);
                 const int kt = kt_beg + j + i + P;
-                load(kt < last ? kt : last, rw[i], ra[i], rs[i], rd[i]);
+                load(kt < last ? kt : last, ra[i], rw[i], rs[i], rd[i]);
+                finish(st);
             }
         }
-        // remainder: fewer than P tiles, already in their slots
 #pragma unroll
         for (int i = 0; i < P - 1; ++i)
-            if (j + i < n) compute(rw[i], ra[i], rs[i], rd[i]);
+            if (j + i < n) {
+                Staged st;
+                stage(ra[i], rw[i], rs[i], rd[i], st);
+                finish(st);
+            }
     }
 
-    // sum the waves' partial products through LDS
+    // sum the waves' partial products through LDS (the scratch is dead now)
+    __syncthreads();
     constexpr int E4 = MT * NT * 4;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -164,7 +207,10 @@ static hipError_t run_skinny(const SkinnyCfg &cf, const uint16_t *A, const uint3
                              int K, int g, hipStream_t st)
 {
     dim3 grid((unsigned)(N / (NTILE * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
-    size_t lds = (size_t)cf.nw * MT * NT * 4 * 64 * sizeof(float);
+    const size_t ring = (size_t)cf.nw * MT * 16 * KTILE * sizeof(uint16_t);
+    const size_t sum = (size_t)cf.nw * MT * NT * 4 * 64 * sizeof(float);
+    const size_t lds = ring > sum ? ring : sum;
+    if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
     if (cf.nw < 1 || cf.nw > NWMAX) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((w4a16_skinny_kernel<MT, NT, P, NWMAX, DELTA>), grid, dim3(64 * cf.nw), lds,
                        st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g, cf.nw);
@@ -437,9 +483,10 @@ SkinnyCfg skinny_config(int M, int N, int K)
     const int nwmax = (c.MT == 1) ? 16 : 4;
     c.S = 1;
     const long blocks = (long)(NT16 / c.NT) * ((M + 16 * c.MT - 1) / (16 * c.MT));
-    // about 2000-3000 waves, each with at least 2 k-tiles
+    // about 2500-4500 waves (measured best on MI355X for the decode shapes),
+    // each with at least 2 k-tiles
     c.nw = 1;
-    while (c.nw < nwmax && blocks * c.nw * 2 <= 3072 && KT / (c.nw * 2) >= 2) c.nw *= 2;
+    while (c.nw < nwmax && blocks * c.nw * 2 <= 4608 && KT / (c.nw * 2) >= 2) c.nw *= 2;
     return c;
 }
 
