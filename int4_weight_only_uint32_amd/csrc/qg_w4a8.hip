@@ -11,27 +11,35 @@
 // MFMA results are plain register values, and the compiler's dependency
 // tracking orders every read of an accumulator after the MFMA that wrote it.
 //
-// Kernel.  A wave owns MT 16-row m-tiles x NT 16-column n-tiles of one expert
-// and a range of whole weight groups.  Per 128-k tile and n-tile, one 128-bit
-// word of codes per lane becomes two 16x16x64 int8 operands of 16*(v-8) by
-// masking and an XOR; A's bytes are loaded in the same k order.  At the end of
-// each group the int32 accumulator (exactly 16x the group's integer product)
-// is shifted right by 4, optionally stored to acc_debug, and folded into the
-// fp32 accumulator with the group scale.  The waves of a workgroup split the
-// groups and are summed through LDS; the per-token scale is applied last.
+// Kernel.  Per 128-k tile and n-tile, one 128-bit word of codes per lane
+// becomes two 16x16x64 int8 operands of 16*(v-8) by masking and an XOR; A's
+// bytes are staged in the same k order.  At the end of each group the int32
+// accumulator (exactly 16x the group's integer product) is shifted right by 4,
+// optionally stored to acc_debug, and folded into the fp32 accumulator with
+// the group scale; the per-token scale is applied last.
 #include "qg_device.h"
 #include "qg_launch.h"
 
 namespace qg {
 
-template <int MT, int NT, int NWMAX>
-__global__ __launch_bounds__(NWMAX * 64) void w4a8_kernel(
+// Workgroup: 4 waves over the same 64 rows of one expert; wave w owns NT
+// n-tiles.  Each 128-k tile of A (64 rows x 128 int8) is fetched
+// row-contiguously by the whole workgroup and stored to LDS in MFMA operand
+// order (for lane (row, kq): the 16 bytes k = 8kq..8kq+7 and 32+8kq..39+8kq,
+// bytes reordered to match the codes' nibble order; then the same for the
+// upper 64 k), double-buffered, one barrier per tile.  Codes stream through a
+// P-deep register ring per wave.
+template <int NT, int P>
+__global__ __launch_bounds__(256) void w4a8_kernel(
     const int8_t *__restrict__ Aq, const float *__restrict__ a_scale,
     const uint4v *__restrict__ Wall, const uint16_t *__restrict__ Sall,
     const int32_t *__restrict__ offsets, int M_total, int N, int K, int g,
-    uint16_t *__restrict__ C, int32_t *__restrict__ acc_debug, int nw)
+    uint16_t *__restrict__ C, int32_t *__restrict__ acc_debug)
 {
-    extern __shared__ float red[];
+    constexpr int MT = 4;                                  // 64 rows
+    // [stage][row][op][kq] x 16 bytes; kq position swizzled with row bits
+    __shared__ __attribute__((aligned(16))) uint4v As[2][64 * 8];
+
     const int e = blockIdx.z;
     int r0 = 0, r1 = M_total;
     if (offsets) {
@@ -43,127 +51,147 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a8_kernel(
     const int m0 = r0 + blockIdx.y * 16 * MT;
     if (m0 >= r1) return;   // uniform over the workgroup, before any barrier
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, kq = lane >> 4;
-    const int KT = K / KTILE, G = K / g, kpg = g / KTILE;
-    const int nt0 = blockIdx.x * NT;
+    const int KT = K / KTILE, G = K / g;
+    const int nt0 = (blockIdx.x * 4 + wave) * NT;
+    const bool active = nt0 * NTILE < N;
     const uint4v *W = Wall + (size_t)e * KT * (N / NTILE) * 64;
     const uint16_t *S = Sall + (size_t)e * G * N;
-    const int g_beg = (wave * G) / nw, g_end = ((wave + 1) * G) / nw;
 
-    const int8_t *arow[MT];
-    bool aok[MT];
+    // ---- A staging: thread t copies 2 x 16 bytes: row t/4 (of 64), bytes
+    // 32 (t%4) .. 32 (t%4) + 31 of the 128-k tile.  Rows past the expert's
+    // last row read that last row (never stored).
+    int arow = m0 + (tid >> 2);
+    arow = arow < r1 ? arow : r1 - 1;
+    const int8_t *asrc = Aq + (size_t)arow * K + 32 * (tid & 3);
+    uint4v areg[2];
+    auto load_a = [&](int kt) {
+        areg[0] = *reinterpret_cast<const uint4v *>(asrc + kt * KTILE);
+        areg[1] = *reinterpret_cast<const uint4v *>(asrc + kt * KTILE + 16);
+    };
+    // the 32 bytes k0 .. k0+31 (k0 = 32 (t%4)) split into four 8-byte pieces:
+    // piece j holds k = k0 + 8j .. k0 + 8j + 7 -> operand op = k0 / 64, slot
+    // kq = j, half = (k0 / 32) % 2
+    auto slot = [&](int row, int op, int q) { return row * 8 + op * 4 + (q ^ ((row >> 1) & 3)); };
+    auto store_a = [&](int st) {
+        const int row = tid >> 2, k0 = 32 * (tid & 3);
+        const int op = k0 / 64, half = (k0 / 32) & 1;
+        unsigned d[8] = {areg[0].x, areg[0].y, areg[0].z, areg[0].w,
+                         areg[1].x, areg[1].y, areg[1].z, areg[1].w};
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        int r = m0 + 16 * mt + c;
-        aok[mt] = r < r1;
-        arow[mt] = Aq + (size_t)(aok[mt] ? r : 0) * K + 8 * kq;
-    }
-    const uint4v *wp[NT];
-    int col[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        wp[t] = W + (size_t)(nt0 + t) * KT * 64 + lane;
-        col[t] = (nt0 + t) * NTILE + c;
-    }
+        for (int j = 0; j < 4; ++j) {
+            uint2v piece = {swap_mid_bytes(d[2 * j]), swap_mid_bytes(d[2 * j + 1])};
+            *reinterpret_cast<uint2v *>(reinterpret_cast<char *>(&As[st][slot(row, op, j)]) + 8 * half) = piece;
+        }
+    };
+
+    const uint4v *wp = W + (size_t)nt0 * KT * 64 + lane;
+    const int col0 = nt0 * NTILE + c;
 
     float4v accf[MT][NT];
+    int4v acci[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) accf[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
-    const int4v izero = {0, 0, 0, 0};
+        for (int t = 0; t < NT; ++t) {
+            accf[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
+            acci[mt][t] = int4v{0, 0, 0, 0};
+        }
 
-    for (int gi = g_beg; gi < g_end; ++gi) {
-        int4v acci[MT][NT];
+    // P-deep register ring of codes; refilled unconditionally (clamped)
+    uint4v rw[P][NT];
+    auto load_w = [&](int kt, uint4v (&w)[NT]) {
+        const int k = kt < KT ? kt : KT - 1;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int t = 0; t < NT; ++t) w[t] = active ? wp[((size_t)t * KT + k) * 64] : uint4v{0u, 0u, 0u, 0u};
+    };
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acci[mt][t] = izero;
-        for (int kt = gi * kpg; kt < (gi + 1) * kpg; ++kt) {
+    for (int i = 0; i < P; ++i) load_w(i, rw[i]);
+    load_a(0);
+    store_a(0);
+    __syncthreads();
+
+    for (int kb = 0; kb < KT; kb += P) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int kt = kb + i;
+            if (kt >= KT) break;
+            const int st = kt & 1;
+            if (kt + 1 < KT) load_a(kt + 1);
             uint4v w[NT];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) w[t] = wp[t][(size_t)kt * 64];
-            int4v alo[MT], ahi[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int8_t *p = arow[mt] + kt * KTILE;
-                uint2v q0 = {0u, 0u}, q1 = {0u, 0u}, q2 = {0u, 0u}, q3 = {0u, 0u};
-                if (aok[mt]) {
-                    q0 = *reinterpret_cast<const uint2v *>(p);
-                    q1 = *reinterpret_cast<const uint2v *>(p + 32);
-                    q2 = *reinterpret_cast<const uint2v *>(p + 64);
-                    q3 = *reinterpret_cast<const uint2v *>(p + 96);
-                }
-                alo[mt] = int4v{(int)swap_mid_bytes(q0.x), (int)swap_mid_bytes(q0.y),
-                                (int)swap_mid_bytes(q1.x), (int)swap_mid_bytes(q1.y)};
-                ahi[mt] = int4v{(int)swap_mid_bytes(q2.x), (int)swap_mid_bytes(q2.y),
-                                (int)swap_mid_bytes(q3.x), (int)swap_mid_bytes(q3.y)};
-            }
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                CodeOpsI8 b = split_codes_i8(w[t]);
+            for (int t = 0; t < NT; ++t) w[t] = rw[i][t];
+            load_w(kt + P, rw[i]);
+            if (active) {
+                int4v alo[MT], ahi[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    acci[mt][t] = mfma_i8(alo[mt], b.op[0], acci[mt][t]);
-                    acci[mt][t] = mfma_i8(ahi[mt], b.op[1], acci[mt][t]);
+                    const int row = 16 * mt + c;
+                    alo[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 0, kq)]);
+                    ahi[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 1, kq)]);
                 }
-            }
-        }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const float s = h2f(S[(size_t)gi * N + col[t]]);
+                for (int t = 0; t < NT; ++t) {
+                    CodeOpsI8 b = split_codes_i8(w[t]);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                int4v qv = acci[mt][t] >> 4;   // exact: every term is a multiple of 16
-                accf[mt][t] += s * __builtin_convertvector(qv, float4v);
-                if (acc_debug) {
+                    for (int mt = 0; mt < MT; ++mt) {
+                        acci[mt][t] = mfma_i8(alo[mt], b.op[0], acci[mt][t]);
+                        acci[mt][t] = mfma_i8(ahi[mt], b.op[1], acci[mt][t]);
+                    }
+                }
+                if (((kt + 1) * KTILE) % g == 0) {        // end of a weight group
+                    const int gi = (kt * KTILE) / g;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        int row = m0 + 16 * mt + 4 * (lane >> 4) + r;
-                        if (row < r1) acc_debug[((size_t)row * G + gi) * N + col[t]] = qv[r];
+                    for (int t = 0; t < NT; ++t) {
+                        const float s = h2f(S[(size_t)gi * N + col0 + 16 * t]);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) {
+                            const int4v qv = acci[mt][t] >> 4;   // exact: terms are multiples of 16
+                            accf[mt][t] += s * __builtin_convertvector(qv, float4v);
+                            acci[mt][t] = int4v{0, 0, 0, 0};
+                            if (acc_debug) {
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const int row = m0 + 16 * mt + 4 * kq + r;
+                                    if (row < r1)
+                                        acc_debug[((size_t)row * G + gi) * N + col0 + 16 * t] = qv[r];
+                                }
+                            }
+                        }
                     }
                 }
             }
+            if (kt + 1 < KT) store_a(st ^ 1);
+            __syncthreads();
         }
     }
 
-    constexpr int E4 = MT * NT * 4;
+    if (!active) return;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + 16 * mt + 4 * kq + r;
+            if (row >= r1) continue;
+            const float as = a_scale[row];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                red[((size_t)wave * E4 + (mt * NT + t) * 4 + r) * 64 + lane] = accf[mt][t][r];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < E4 * 64; idx += blockDim.x) {
-        float v = 0.f;
-        for (int w = 0; w < nw; ++w) v += red[(size_t)w * E4 * 64 + idx];
-        const int ee = idx >> 6, l = idx & 63;
-        const int r = ee & 3, t = (ee >> 2) % NT, mt = (ee >> 2) / NT;
-        const int row = m0 + 16 * mt + 4 * (l >> 4) + r;
-        const int cc = (nt0 + t) * NTILE + (l & 15);
-        if (row < r1) C[(size_t)row * N + cc] = f2h(a_scale[row] * v);
-    }
+            for (int t = 0; t < NT; ++t) C[(size_t)row * N + col0 + 16 * t] = f2h(as * accf[mt][t][r]);
+        }
 }
 
-template <int MT, int NT, int NWMAX>
+template <int NT, int P>
 static hipError_t run_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
                            const uint16_t *S, const int32_t *offsets, int E, int M_total,
                            int max_rows, int N, int K, int g, uint16_t *C, int32_t *acc_debug,
                            hipStream_t st)
 {
-    const int G = K / g;
-    dim3 grid((unsigned)(N / NTILE / NT), (unsigned)((max_rows + 16 * MT - 1) / (16 * MT)),
-              (unsigned)E);
-    long blocks = (long)grid.x * grid.y * grid.z;
-    int nw = 1;
-    while (nw < NWMAX && blocks * nw * 2 <= 2560 && G / (nw * 2) >= 1) nw *= 2;
-    size_t lds = (size_t)nw * MT * NT * 4 * 64 * sizeof(float);
-    hipLaunchKernelGGL((w4a8_kernel<MT, NT, NWMAX>), grid, dim3(64 * nw), lds, st, Aq, a_scale,
+    const int NT16 = N / NTILE;
+    dim3 grid((unsigned)((NT16 + 4 * NT - 1) / (4 * NT)), (unsigned)((max_rows + 63) / 64), (unsigned)E);
+    hipLaunchKernelGGL((w4a8_kernel<NT, P>), grid, dim3(256), 0, st, Aq, a_scale,
                        reinterpret_cast<const uint4v *>(W), S, offsets, M_total, N, K, g, C,
-                       acc_debug, nw);
+                       acc_debug);
     return hipGetLastError();
 }
 
@@ -172,14 +200,10 @@ hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W
                        int max_rows, int N, int K, int g, uint16_t *C, int32_t *acc_debug,
                        hipStream_t st)
 {
-    if (max_rows <= 16)
-        return run_w4a8<1, 2, 16>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C,
-                                  acc_debug, st);
-    if (max_rows <= 32)
-        return run_w4a8<2, 2, 8>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C,
-                                 acc_debug, st);
-    return run_w4a8<4, 2, 4>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C,
-                             acc_debug, st);
+    // N % 128 == 0 -> the n-tile count is a multiple of 8: NT = 2 tiles the
+    // columns exactly (4 waves x 2 n-tiles = 128 columns per workgroup)
+    return run_w4a8<2, 4>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C,
+                          acc_debug, st);
 }
 
 } // namespace qg
