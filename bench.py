@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--only-primary", action="store_true", help="skip the secondary cases")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cases", default="all", help="comma list of case names, or 'all'")
+    p.add_argument("--eager", action="store_true", help="time plain launches instead of a graph replay")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a 256 MiB device-to-device copy 20 times (counter calibration)")
     return p.parse_args()
 
 
@@ -56,10 +59,12 @@ def weight_bytes(K, N, g, asym):
     return K * N // 2 + G * N * 2 * (2 if asym else 1)
 
 
-def time_calls(fn, n_copies, steps, warmup):
-    """Average ms per call of fn(i) over `steps` calls, rotating i over copies.
-    HIP events recorded on the current stream, which is the stream every
-    library call is launched on."""
+def time_calls(fn, n_copies, steps, warmup, graph=True):
+    """Average ms per call of fn(i) over `steps` calls, rotating i over the
+    copies.  With graph=True the `steps` calls are captured once into a HIP
+    graph and the timed region is one replay, so host-side launch overhead is
+    not measured; HIP events are recorded on the stream the calls are launched
+    on (torch's current stream, which the library uses)."""
     import torch
     for i in range(warmup):
         fn(i % n_copies)
@@ -67,23 +72,39 @@ def time_calls(fn, n_copies, steps, warmup):
     st = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    if not graph:
+        e0.record(st)
+        for i in range(steps):
+            fn(i % n_copies)
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i % n_copies)
+    g.replay()                      # warm replay
+    torch.cuda.synchronize()
     e0.record(st)
-    for i in range(steps):
-        fn(i % n_copies)
+    g.replay()
     e1.record(st)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
 
 
-def bench_w4a16(name, M, K, N, g, asym, signed, config_id, case_id, steps, warmup, flags=0):
+GRAPH = True
+
+
+def bench_w4a16(name, steps, warmup, flags=0, label=None):
     import numpy as np
     import torch
 
     import int4_weight_only_uint32_amd as qg
     import synth
 
-    c = synth.w4a16_case(M, K, N, g, asym=asym, signed_scales=signed, config_id=config_id,
-                         case_id=case_id)
+    c = synth.workload(name)
+    M, K, N, g = c.M, c.K, c.N, c.g
+    asym = c.z is not None
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q, s = dev(c.q), dev(c.s)
     z = dev(c.z) if asym else None
@@ -110,13 +131,15 @@ def bench_w4a16(name, M, K, N, g, asym, signed, config_id, case_id, steps, warmu
         p = copies[i]
         qg.qgemm_w4a16(A, p.w, p.scale, p.delta, C, M, N, K, g, flags, ws)
 
-    ms = time_calls(call, R, steps, warmup)
+    ms = time_calls(call, R, steps, warmup, GRAPH)
+    ms_eager = time_calls(call, R, min(steps, 50), 2, False)
     flops = 2.0 * M * N * K
     alg = wb + M * K * 2 + M * N * 2
-    res = dict(name=name, M=M, K=K, N=N, group=g, mode="asym" if asym else "sym-fold",
+    res = dict(name=label or name, M=M, K=K, N=N, group=g, mode="asym" if asym else "sym-fold",
                flags=flags, us_per_call=ms * 1e3, tflops=flops / (ms * 1e-3) / 1e12,
                weight_gbps=wb / (ms * 1e-3) / 1e9, total_alg_gbps=alg / (ms * 1e-3) / 1e9,
-               weight_bytes=wb, rotated_copies=R, pack_ms_first_call=pack_ms)
+               weight_bytes=wb, rotated_copies=R, pack_ms_first_call=pack_ms,
+               us_per_call_eager_launches=ms_eager * 1e3)
     res["pct_hbm_weight"] = 100.0 * res["weight_gbps"] / HBM_PEAK_GBPS
     res["pct_fp16_mfma"] = 100.0 * res["tflops"] / FP16_PEAK_TFLOPS
     del copies, A, C
@@ -131,7 +154,7 @@ def bench_w4a8(name, steps, warmup):
     import int4_weight_only_uint32_amd as qg
     import synth
 
-    c = synth.config_case(4, 0)
+    c = synth.workload(name)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     packs = [qg.pack(dev(c.q[e]), dev(c.s[e]), None, c.g, fold=True) for e in range(c.E)]
     W = torch.stack([p.w for p in packs]).contiguous()
@@ -147,7 +170,7 @@ def bench_w4a8(name, steps, warmup):
     def call(i):
         qg.qgemm_w4a8(Aq, asc, Ws[i], Ss[i], off, c.E, c.M_total, mr, c.N, c.K, c.g, C)
 
-    ms = time_calls(call, R, steps, warmup)
+    ms = time_calls(call, R, steps, warmup, GRAPH)
     ops = 2.0 * c.M_total * c.N * c.K
     alg = wb + c.M_total * c.K + c.M_total * 4 + c.M_total * c.N * 2
     res = dict(name=name, E=c.E, rows_per_expert=mr, K=c.K, N=c.N, group=c.g,
@@ -159,6 +182,21 @@ def bench_w4a8(name, steps, warmup):
     del Ws, Ss, W, S
     torch.cuda.empty_cache()
     return res
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3
+    counter summary, if the kernel source is unchanged since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "w4a16_decode_M16_K5120_N17408_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    except (OSError, ValueError, KeyError):
+        return None
+    return rec["traffic_bytes"] if sha == rec["source_sha256_16"] else None
 
 
 def cpu_baseline(case):
@@ -184,6 +222,9 @@ def main():
         sys.exit(2)
     import torch
     import int4_weight_only_uint32_amd as qg
+    import synth
+    global GRAPH
+    GRAPH = not args.eager
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
@@ -194,40 +235,43 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
 
+    if args.calibrate_copy:
+        n = 256 * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes x 20")
+        return
     steps, warmup = args.steps, args.warmup
-    primary, pcase = bench_w4a16("c1a-M16", 16, 5120, 17408, 128, True, False, 1, 2, steps, warmup)
+    primary_name = "w4a16-decode-M16-K5120-N17408-g128-asym"
+    primary, pcase = bench_w4a16(primary_name, steps, warmup)
     log(json.dumps(primary))
 
     cases = []
     want = None if args.cases == "all" else set(args.cases.split(","))
     if not args.only_primary:
-        plan = [
-            ("c0-M16", 16, 1024, 1024, 128, True, False, 0, 0),
-            ("c1a-M1", 1, 5120, 17408, 128, True, False, 1, 0),
-            ("c1a-M4", 4, 5120, 17408, 128, True, False, 1, 1),
-            ("c1b-M1", 1, 17408, 5120, 128, True, False, 1, 3),
-            ("c1b-M4", 4, 17408, 5120, 128, True, False, 1, 4),
-            ("c1b-M16", 16, 17408, 5120, 128, True, False, 1, 5),
-            ("c2-g256", 256, 4096, 8192, 256, True, False, 2, 0),
-            ("c2-percol", 256, 4096, 8192, 4096, True, False, 2, 1),
-            ("c3-M4096", 4096, 5120, 17408, 128, False, True, 3, 0),
-        ]
-        for (nm, M, K, N, g, asym, signed, cid, kid) in plan:
-            if want and nm not in want:
+        plan = (synth.names("w4a16-small") + synth.names("w4a16-decode") +
+                synth.names("w4a16-midbatch") + synth.names("w4a16-prefill"))
+        for nm in plan:
+            if nm == primary_name or (want and nm not in want):
                 continue
+            M = synth.WORKLOADS[nm]["spec"]["M"]
             st = steps if M <= 256 else max(10, steps // 10)
-            r, _ = bench_w4a16(nm, M, K, N, g, asym, signed, cid, kid, st, min(warmup, st))
+            r, _ = bench_w4a16(nm, st, min(warmup, st))
             log(json.dumps(r))
             cases.append(r)
-        if not want or "c1a-M16-separate" in want:
-            r, _ = bench_w4a16("c1a-M16-separate", 16, 5120, 17408, 128, True, False, 1, 2,
-                               steps, warmup, flags=qg.QG_CORR_SEPARATE)
+        sep = primary_name + "+separate-correction"
+        if not want or sep in want:
+            r, _ = bench_w4a16(primary_name, steps, warmup, flags=qg.QG_CORR_SEPARATE, label=sep)
             log(json.dumps(r))
             cases.append(r)
-        if not want or "c4-w4a8" in want:
-            r = bench_w4a8("c4-w4a8", steps, warmup)
-            log(json.dumps(r))
-            cases.append(r)
+        for nm in synth.names("w4a8"):
+            if not want or nm in want:
+                r = bench_w4a8(nm, steps, warmup)
+                log(json.dumps(r))
+                cases.append(r)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -250,19 +294,22 @@ def main():
         "dtype": "fp16",
         "data": "synthetic (seeded; A~N(0,1) fp16, q~U{0..15}, |s|~U[1e-3,2e-2], "
                 "z=-8s+N(0,1e-3)); weights rotated over >=512 MB of copies",
+        "timing": "graph replay of the timed calls (HIP events on the launch stream)"
+                  if GRAPH else "eager launches (HIP events on the launch stream)",
         "config": {"workload": "w4a16-decode M=16 K=5120 N=17408 group=128 asymmetric, "
                                "delta fused (one launch per step)",
                    "M": 16, "K": 5120, "N": 17408, "group": 128},
         "weight_gbps": primary["weight_gbps"],
         "pct_hbm_roofline_weight": primary["pct_hbm_weight"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "w4a16_skinny_kernel<1,2,16,true>",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(),
+                     "kernel": "w4a16_skinny_kernel (decode, fused delta)",
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                      "algorithmic_bytes_per_launch": primary["weight_bytes"]},
         "cpu_baseline": cpu,
         "cases": cases,
     }
-    prefill = [c for c in cases if c["name"] == "c3-M4096"]
+    prefill = [c for c in cases if c["name"].startswith("w4a16-prefill")]
     if prefill:
         out["prefill_M4096"] = {"tflops": prefill[0]["tflops"],
                                 "pct_fp16_mfma": prefill[0]["pct_fp16_mfma"],

@@ -156,10 +156,8 @@ _workspaces = {}
 
 
 def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A zero-initialised workspace of at least `nbytes`, cached per (device,
-    current stream).  The library leaves the counter area of a W4A16 workspace
-    zeroed after every call, so the buffer can be reused as is; calls that
-    share it must be ordered (one stream)."""
+    """A workspace of at least `nbytes`, cached per (device, current stream).
+    Calls that share it must be ordered (one stream): each call overwrites it."""
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:

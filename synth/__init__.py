@@ -6,10 +6,10 @@ draws random tensors (and, for the W4A8 variant, turns fp16 activations into
 per-row int8 codes, which is how those inputs are produced before they reach
 the GEMM).
 
-Seeds: ``np.random.SeedSequence([20261202, config_id, case_id])``; tensors are
+Seeds: ``np.random.SeedSequence([20261202, stream, case_id])``; tensors are
 drawn in the fixed order A, q, |s|, sign, zero-noise.
 
-Value distributions (the workloads named by the benchmark configurations):
+Value distributions of the named workloads (see WORKLOADS below):
   * A ~ N(0, 1) rounded to fp16;
   * q ~ uniform integers in [0, 15];
   * |scale| ~ U[1e-3, 2e-2] rounded to fp16;
@@ -24,8 +24,8 @@ import numpy as np
 SEED_ROOT = 20261202
 
 
-def rng_for(config_id: int, case_id: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, config_id, case_id])))
+def rng_for(stream: int, case_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, stream, case_id])))
 
 
 @dataclass
@@ -54,13 +54,13 @@ class W4A16Case:
         return self.K // self.g
 
 
-def w4a16_case(M, K, N, g, asym=True, signed_scales=False, config_id=0, case_id=0,
+def w4a16_case(M, K, N, g, asym=True, signed_scales=False, stream=0, case_id=0,
                name="") -> W4A16Case:
     if g == -1:
         g = K
     assert K % g == 0
     G = K // g
-    r = rng_for(config_id, case_id)
+    r = rng_for(stream, case_id)
     A = r.standard_normal((M, K)).astype(np.float16)
     q = r.integers(0, 16, size=(K, N), dtype=np.uint8)
     s_abs = r.uniform(1e-3, 2e-2, size=(G, N))
@@ -118,7 +118,7 @@ class W4A8Case:
         return self.Aq.shape[0]
 
 
-def w4a8_case(E, rows_per_expert, K, N, g, signed_scales=False, config_id=4, case_id=0,
+def w4a8_case(E, rows_per_expert, K, N, g, signed_scales=False, stream=4, case_id=0,
               rows=None, name="") -> W4A8Case:
     """rows: optional explicit per-expert row counts (ragged groups)."""
     if rows is None:
@@ -128,7 +128,7 @@ def w4a8_case(E, rows_per_expert, K, N, g, signed_scales=False, config_id=4, cas
     offsets[1:] = np.cumsum(rows)
     M_total = int(offsets[-1])
     G = K // g
-    r = rng_for(config_id, case_id)
+    r = rng_for(stream, case_id)
     A16 = r.standard_normal((M_total, K)).astype(np.float16)
     q = r.integers(0, 16, size=(E, K, N), dtype=np.uint8)
     s = r.uniform(1e-3, 2e-2, size=(E, G, N)).astype(np.float16)
@@ -139,21 +139,41 @@ def w4a8_case(E, rows_per_expert, K, N, g, signed_scales=False, config_id=4, cas
     return W4A8Case(A16=A16, Aq=Aq, a_scale=a_scale, q=q, s=s, offsets=offsets, g=g, name=name)
 
 
-# The benchmark workloads (shapes and value recipes), by configuration id.
-CONFIGS = {
-    0: dict(kind="w4a16", cases=[dict(M=16, K=1024, N=1024, g=128, asym=True)]),
-    1: dict(kind="w4a16", cases=[dict(M=m, K=k, N=n, g=128, asym=True)
-                                 for (k, n) in ((5120, 17408), (17408, 5120)) for m in (1, 4, 16)]),
-    2: dict(kind="w4a16", cases=[dict(M=256, K=4096, N=8192, g=256, asym=True),
-                                 dict(M=256, K=4096, N=8192, g=4096, asym=True)]),
-    3: dict(kind="w4a16", cases=[dict(M=4096, K=5120, N=17408, g=128, asym=False,
-                                      signed_scales=True)]),
-    4: dict(kind="w4a8", cases=[dict(E=8, rows_per_expert=64, K=2048, N=7168, g=128)]),
-}
+# The named workloads: shapes, value recipe and seed stream of each.
+#   small-asym  16 x 1024 x 1024, group 128, asymmetric (parity and smoke size)
+#   decode      M in {1, 4, 16}; K5120/N17408 and K17408/N5120; group 128 asym
+#   midbatch    M=256, K=4096, N=8192; group 256 and per-column; asymmetric
+#   prefill     M=4096, K=5120, N=17408; group 128 symmetric, half the scales
+#               negative (the sign fold matters)
+#   w4a8-moe    8 experts x 64 tokens, K=2048, N=7168, group 128
+WORKLOADS = {}
 
 
-def config_case(config_id: int, case_id: int):
-    spec = dict(CONFIGS[config_id]["cases"][case_id])
-    if CONFIGS[config_id]["kind"] == "w4a16":
-        return w4a16_case(config_id=config_id, case_id=case_id, **spec)
-    return w4a8_case(config_id=config_id, case_id=case_id, **spec)
+def _add(name, kind, stream, case_id, **spec):
+    WORKLOADS[name] = dict(kind=kind, stream=stream, case_id=case_id, spec=spec)
+
+
+_add("w4a16-small-asym-M16-K1024-N1024-g128", "w4a16", 0, 0, M=16, K=1024, N=1024, g=128, asym=True)
+for _i, (_k, _n, _m) in enumerate([(k, n, m) for (k, n) in ((5120, 17408), (17408, 5120))
+                                   for m in (1, 4, 16)]):
+    _add(f"w4a16-decode-M{_m}-K{_k}-N{_n}-g128-asym", "w4a16", 1, _i, M=_m, K=_k, N=_n, g=128,
+         asym=True)
+_add("w4a16-midbatch-M256-K4096-N8192-g256-asym", "w4a16", 2, 0, M=256, K=4096, N=8192, g=256,
+     asym=True)
+_add("w4a16-midbatch-M256-K4096-N8192-percol-asym", "w4a16", 2, 1, M=256, K=4096, N=8192,
+     g=4096, asym=True)
+_add("w4a16-prefill-M4096-K5120-N17408-g128-sym-signed", "w4a16", 3, 0, M=4096, K=5120,
+     N=17408, g=128, asym=False, signed_scales=True)
+_add("w4a8-moe-E8x64-K2048-N7168-g128", "w4a8", 4, 0, E=8, rows_per_expert=64, K=2048, N=7168,
+     g=128)
+
+
+def workload(name: str):
+    w = WORKLOADS[name]
+    if w["kind"] == "w4a16":
+        return w4a16_case(stream=w["stream"], case_id=w["case_id"], name=name, **w["spec"])
+    return w4a8_case(stream=w["stream"], case_id=w["case_id"], name=name, **w["spec"])
+
+
+def names(prefix: str):
+    return [n for n in WORKLOADS if n.startswith(prefix)]

@@ -40,7 +40,7 @@ def _device():
 def test_pack_bit_exact(K, N, g, asym, signed):
     note(f"pack K={K} N={N} g={g} asym={asym}")
     gg = K if g == -1 else g
-    c = synth.w4a16_case(1, K, N, gg, asym=asym, signed_scales=signed, config_id=80, case_id=K + N)
+    c = synth.w4a16_case(1, K, N, gg, asym=asym, signed_scales=signed, stream=80, case_id=K + N)
     s = c.s.copy()
     if signed:
         s[0, :4] = np.float16(-0.0)          # negative zero: not folded
@@ -102,36 +102,35 @@ def _check_w4a16(case, flags=0, fold=True, tol=W4A16_TOL):
 ])
 def test_w4a16_ragged_shapes(M, K, N, g, asym):
     gg = K if g == -1 else g
-    c = synth.w4a16_case(M, K, N, gg, asym=asym, signed_scales=not asym, config_id=81,
+    c = synth.w4a16_case(M, K, N, gg, asym=asym, signed_scales=not asym, stream=81,
                          case_id=M * 7 + K + N, name="ragged")
     _check_w4a16(c)
 
 
-@pytest.mark.parametrize("case_id", [0])
-def test_w4a16_config0(case_id):
-    c = synth.config_case(0, case_id)
+def test_w4a16_small_asym():
+    c = synth.workload("w4a16-small-asym-M16-K1024-N1024-g128")
     _check_w4a16(c)
     _check_w4a16(c, flags=qg.QG_CORR_SEPARATE)
 
 
-@pytest.mark.parametrize("case_id", range(6))
-def test_w4a16_config1_decode(case_id):
-    _check_w4a16(synth.config_case(1, case_id))
+@pytest.mark.parametrize("name", synth.names("w4a16-decode"))
+def test_w4a16_decode(name):
+    _check_w4a16(synth.workload(name))
 
 
-@pytest.mark.parametrize("case_id", range(2))
-def test_w4a16_config2_midbatch(case_id):
-    c = synth.config_case(2, case_id)
+@pytest.mark.parametrize("name", synth.names("w4a16-midbatch"))
+def test_w4a16_midbatch(name):
+    c = synth.workload(name)
     _check_w4a16(c)
     _check_w4a16(c, flags=qg.QG_CORR_SEPARATE)
 
 
-def test_w4a16_config3_prefill_sampled():
+def test_w4a16_prefill_sampled():
     """Full prefill shape (M=4096, K=5120, N=17408, random-sign scales, fold on)
-    in the benchmark's launch configuration; the oracle evaluates sampled cells
+    in the benchmark's launch shape; the oracle evaluates sampled cells
     one by one (every row and column band is hit)."""
-    c = synth.config_case(3, 0)
-    note(f"w4a16 config3 M={c.M} K={c.K} N={c.N}")
+    c = synth.workload("w4a16-prefill-M4096-K5120-N17408-g128-sym-signed")
+    note(f"w4a16 prefill M={c.M} K={c.K} N={c.N}")
     got, _ = run_w4a16(c)
     r = np.random.default_rng(5)
     rows = np.concatenate([r.integers(0, c.M, 3000), [0, c.M - 1, 0, c.M - 1]])
@@ -146,11 +145,11 @@ def test_w4a16_config3_prefill_sampled():
     assert rel_fro(ref_nofold, ref) > 10 * W4A16_TOL
 
 
-def test_w4a16_config3_dense_slice():
+def test_w4a16_prefill_dense_slice():
     """A 256-row slice of the prefill case checked densely."""
-    c = synth.config_case(3, 0)
+    c = synth.workload("w4a16-prefill-M4096-K5120-N17408-g128-sym-signed")
     sl = synth.W4A16Case(A=c.A[:256], q=c.q[:, :2048], s=c.s[:, :2048], z=None, g=c.g,
-                         name="c3-slice")
+                         name="prefill-slice")
     _check_w4a16(sl)
 
 
@@ -184,19 +183,19 @@ def test_w4a16_degenerate_values():
     a_sum = np.abs(A.astype(np.float64).reshape(M, 2, 128).sum(axis=2)).max()
     assert np.max(np.abs(got)) <= 8 * 2.0 ** -23 * 8 * 0.02 * a_sum * 2
     A0 = np.zeros((M, K), np.float16)
-    c = synth.w4a16_case(M, K, N, 128, asym=True, config_id=82, case_id=1)
+    c = synth.w4a16_case(M, K, N, 128, asym=True, stream=82, case_id=1)
     got, _ = run_w4a16(synth.W4A16Case(A=A0, q=c.q, s=c.s, z=c.z, g=128))
     assert np.all(got == 0.0)
 
 
 def test_w4a16_fold_off_matches_unfolded():
-    c = synth.w4a16_case(16, 1024, 512, 128, asym=False, signed_scales=True, config_id=83,
+    c = synth.w4a16_case(16, 1024, 512, 128, asym=False, signed_scales=True, stream=83,
                          case_id=0)
     _check_w4a16(c, fold=False)
 
 
 def test_w4a16_deterministic():
-    c = synth.config_case(1, 2)
+    c = synth.workload("w4a16-decode-M16-K5120-N17408-g128-asym")
     a, _ = run_w4a16(c)
     b, _ = run_w4a16(c)
     assert np.array_equal(a, b)
@@ -206,7 +205,7 @@ def test_w4a16_deterministic():
 @pytest.mark.parametrize("M,K,N,g", [(5, 1024, 256, 128), (64, 4096, 384, 4096), (130, 512, 128, 256)])
 def test_group_sum_correction(M, K, N, g):
     note(f"group_sum_correction M={M} K={K} N={N} g={g}")
-    c = synth.w4a16_case(M, K, N, g, asym=True, config_id=84, case_id=M)
+    c = synth.w4a16_case(M, K, N, g, asym=True, stream=84, case_id=M)
     _, dh = oracle.delta(c.s, c.z)
     r = np.random.default_rng(M)
     Cin = r.standard_normal((M, N)).astype(np.float16)
@@ -250,20 +249,20 @@ def _check_w4a8(case, **kw):
     return err
 
 
-def test_w4a8_config4():
-    c = synth.config_case(4, 0)
+def test_w4a8_moe():
+    c = synth.workload("w4a8-moe-E8x64-K2048-N7168-g128")
     err = _check_w4a8(c)
-    note(f"w4a8 config4 rel_fro vs same-int8 oracle = {err:.3e}")
+    note(f"w4a8 moe rel_fro vs same-int8 oracle = {err:.3e}")
 
 
 def test_w4a8_ragged_experts_and_fold():
-    c = synth.w4a8_case(5, 0, 512, 256, 128, signed_scales=True, config_id=85, case_id=0,
+    c = synth.w4a8_case(5, 0, 512, 256, 128, signed_scales=True, stream=85, case_id=0,
                         rows=[0, 17, 64, 3, 100])
     _check_w4a8(c)
 
 
 def test_w4a8_single_expert_no_offsets():
-    c = synth.w4a8_case(1, 40, 1024, 384, 256, config_id=85, case_id=1)
+    c = synth.w4a8_case(1, 40, 1024, 384, 256, stream=85, case_id=1)
     _check_w4a8(c, offsets=False)
-    c2 = synth.w4a8_case(1, 7, 768, 128, 768, config_id=85, case_id=2)
+    c2 = synth.w4a8_case(1, 7, 768, 128, 768, stream=85, case_id=2)
     _check_w4a8(c2, offsets=False)

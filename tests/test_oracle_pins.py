@@ -88,7 +88,7 @@ def _exact_w4a16(A, q, s, z, g, fold):
     (1, 256, 16, 128, False, True),
 ])
 def test_w4a16_matches_exact_rationals(oracle_lib, M, K, N, g, asym, signed):
-    c = synth.w4a16_case(M, K, N, g, asym=asym, signed_scales=signed, config_id=90, case_id=K + N + M)
+    c = synth.w4a16_case(M, K, N, g, asym=asym, signed_scales=signed, stream=90, case_id=K + N + M)
     got = oracle_lib.w4a16(c.A, c.q, c.s, c.z, g, fold=True)
     exact = _exact_w4a16(c.A, c.q, c.s, c.z, g, fold=True)
     ref = np.array([[float(x) for x in row] for row in exact])
@@ -142,7 +142,7 @@ def test_golden_group_sum_correction(oracle_lib):
 @pytest.mark.parametrize("g", [128, 256, 1024])
 def test_delta_identity(oracle_lib, g):
     """C_asym = C_sym + a_sum @ delta (exact because delta does not depend on k)."""
-    c = synth.w4a16_case(16, 1024, 256, g, asym=True, config_id=91, case_id=g)
+    c = synth.w4a16_case(16, 1024, 256, g, asym=True, stream=91, case_id=g)
     C_asym = oracle_lib.w4a16(c.A, c.q, c.s, c.z, g)
     C_sym = oracle_lib.w4a16(c.A, c.q, c.s, None, g, fold=False)
     de, _ = oracle_lib.delta(c.s, c.z)
@@ -156,7 +156,7 @@ def test_delta_identity(oracle_lib, g):
 
 def test_fold_invariant(oracle_lib):
     """Folding changes a weight only where s<0 and v==0, and there by exactly s."""
-    c = synth.w4a16_case(1, 512, 384, 128, asym=False, signed_scales=True, config_id=92, case_id=0)
+    c = synth.w4a16_case(1, 512, 384, 128, asym=False, signed_scales=True, stream=92, case_id=0)
     s = c.s.copy()
     s[0, 0] = np.float16(-0.0)   # negative zero is not folded
     W0 = oracle_lib.dequant_sym(c.q, s, 128)
@@ -175,13 +175,13 @@ def test_fold_invariant(oracle_lib):
 
 
 def test_fold_identity_without_negative_scales(oracle_lib):
-    c = synth.w4a16_case(2, 256, 128, 128, asym=False, signed_scales=False, config_id=92, case_id=1)
+    c = synth.w4a16_case(2, 256, 128, 128, asym=False, signed_scales=False, stream=92, case_id=1)
     qf, sf, n = oracle_lib.fold_negative_scales(c.q, c.s, 128)
     assert n == 0 and np.array_equal(qf, c.q) and np.array_equal(sf, c.s.view(np.uint16))
 
 
 def test_special_cases(oracle_lib):
-    c = synth.w4a16_case(4, 256, 64, 128, asym=True, config_id=93, case_id=0)
+    c = synth.w4a16_case(4, 256, 64, 128, asym=True, stream=93, case_id=0)
     # all codes at the offset 8 -> the symmetric product is exactly zero
     q8 = np.full_like(c.q, 8)
     assert np.all(oracle_lib.w4a16(c.A, q8, c.s, None, 128, fold=False) == 0.0)
@@ -226,7 +226,7 @@ def test_group_sum_closed_forms(oracle_lib):
 
 
 def test_w4a8_unit_scales_equal_integer_matmul(oracle_lib):
-    c = synth.w4a8_case(2, 5, 256, 64, 128, config_id=94, case_id=0, rows=[5, 3])
+    c = synth.w4a8_case(2, 5, 256, 64, 128, stream=94, case_id=0, rows=[5, 3])
     ones = np.ones_like(c.s)
     unit = np.ones(c.M_total, np.float32)
     C, acc = oracle_lib.w4a8(c.Aq, unit, c.q, ones, c.offsets, 128, fold=False)
@@ -244,7 +244,7 @@ def test_w4a8_unit_scales_equal_integer_matmul(oracle_lib):
 
 
 def test_w4a8_scaling_and_fold(oracle_lib):
-    c = synth.w4a8_case(2, 4, 256, 32, 128, signed_scales=True, config_id=94, case_id=1)
+    c = synth.w4a8_case(2, 4, 256, 32, 128, signed_scales=True, stream=94, case_id=1)
     C, acc = oracle_lib.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, 128, fold=True)
     for e in range(c.E):
         qf, sf, _ = oracle_lib.fold_negative_scales(c.q[e], c.s[e], 128)
