@@ -27,6 +27,14 @@
  *     by the caller.  The library allocates no device memory and keeps no
  *     device state; scratch memory is a caller-provided workspace whose size
  *     qg_workspace_bytes() reports (0 for every path that needs none).
+ *   - A W4A16 workspace starts with QG_W4A16_WS_COUNTER_BYTES bytes of
+ *     split-K counters, then the fp32 partial sums (M <= 16) and the
+ *     correction's group sums (QG_CORR_SEPARATE).  It must be zero-filled
+ *     before its first use; every qgemm_w4a16 call leaves the counters at zero
+ *     again, so one zero-filled workspace serves any sequence of qgemm_w4a16
+ *     calls on one stream, whatever their shapes and flags.  Do not use it for
+ *     anything else in between (group_sum_correction included).  Calls that
+ *     may overlap in time (different streams or devices) must not share one.
  *   - fp16 tensors are passed as uint16_t (IEEE binary16 bit patterns).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued asynchronously; nothing is synchronised or read back.
@@ -69,6 +77,10 @@ extern "C" {
  * group_sum_correction (after an fp16 store of the symmetric product)
  * instead of fusing it into the GEMM epilogue.                              */
 #define QG_CORR_SEPARATE        0x1u
+
+/* Size of the counter region at the start of every non-empty W4A16
+ * workspace (see the conventions above).                                    */
+#define QG_W4A16_WS_COUNTER_BYTES 65536u
 
 /* ---- operations, for qg_workspace_bytes ---- */
 #define QG_OP_W4A16                 1
@@ -125,7 +137,11 @@ int pack_int4_weights(const uint8_t *q, const uint16_t *scale, const uint16_t *z
  *          the GEMM epilogue (one launch).
  *          QG_CORR_SEPARATE: C is first stored as the symmetric product and
  *          then corrected in place by group_sum_correction (needs workspace).
- * workspace/workspace_bytes: see qg_workspace_bytes(QG_OP_W4A16, ...).      */
+ * workspace/workspace_bytes: qg_workspace_bytes(QG_OP_W4A16, ...) bytes,
+ *          256-byte aligned (NULL when that is 0).  For M <= 16 the K range
+ *          is split over several workgroups whose fp32 partial sums meet in
+ *          the workspace; the last to finish adds them in a fixed order, so
+ *          results do not depend on timing.                                 */
 int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,
                 const uint16_t *delta, uint16_t *C, int M, int N, int K,
                 int group_size, unsigned flags, void *workspace,

@@ -30,6 +30,8 @@ QG_ERR_LAUNCH = 5
 QG_PACK_FOLD_NEG_SCALES = 0x1
 QG_CORR_SEPARATE = 0x1
 
+QG_W4A16_WS_COUNTER_BYTES = 65536
+
 QG_OP_W4A16 = 1
 QG_OP_W4A8 = 2
 QG_OP_GROUP_SUM_CORRECTION = 3

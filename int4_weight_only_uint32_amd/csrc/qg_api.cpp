@@ -74,10 +74,20 @@ size_t corr_ws_bytes(int M, int K, int g) { return (size_t)M * (size_t)(K / g) *
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-// W4A16 workspace: [GEMM split-K area][correction a_sum area when separate]
+// W4A16 workspace: [counters][decode partial sums][correction a_sum when
+// separate].  The counter region is always first, whatever the call, so a
+// workspace shared by different shapes never has group sums or partials
+// written over a counter.
+size_t w4a16_gemm_ws_bytes(int M, int N, int K, bool separate)
+{
+    const size_t gemm = qg::w4a16_workspace_bytes(M, N, K);
+    if (gemm) return gemm;
+    return separate ? qg::W4A16_WS_COUNTER_BYTES : 0;
+}
+
 size_t w4a16_ws_bytes(int M, int N, int K, int g, bool separate)
 {
-    size_t gemm = qg::w4a16_workspace_bytes(M, N, K);
+    const size_t gemm = w4a16_gemm_ws_bytes(M, N, K, separate);
     if (!separate) return gemm;
     return align256(gemm) + corr_ws_bytes(M, K, g);
 }
@@ -193,9 +203,9 @@ int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *sca
     }
     if ((rc = check_device())) return rc;
     hipStream_t st = (hipStream_t)stream;
-    const size_t gemm_ws = qg::w4a16_workspace_bytes(M, N, K);
+    const size_t gemm_ws = w4a16_gemm_ws_bytes(M, N, K, separate);
     hipError_t e = qg::launch_w4a16(A, w_packed, scale, delta, C, M, N, K, g, !separate,
-                                    gemm_ws ? workspace : nullptr, st);
+                                    qg::w4a16_workspace_bytes(M, N, K) ? workspace : nullptr, st);
     if (e == hipSuccess && separate)
         e = qg::launch_group_sum_correction(A, delta, C, M, N, K, g,
                                             (float *)((char *)workspace + align256(gemm_ws)), st);

@@ -28,6 +28,21 @@ hipError_t launch_w4a16_tiled(const uint16_t *A, const uint32_t *W, const uint16
                               const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                               bool fuse_delta, hipStream_t st);
 
+// Every non-empty W4A16 workspace starts with this many bytes of split-K
+// counters.  Only the decode kernel writes them and it leaves them at zero, so
+// a workspace shared by calls of different shapes and flags keeps them zero
+// (the partial sums and the correction's group sums come after).
+constexpr size_t W4A16_WS_COUNTER_BYTES = 65536;
+
+// Decode kernel (M <= 16): split count the heuristic picks, and a launch with
+// an explicit split count (nsplit > 1 needs `ws` of decode_workspace_bytes).
+int decode_splits(int N, int K);
+bool use_decode_kernel(int M, int N, int K);
+size_t decode_workspace_bytes(int M, int N, int K);
+hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                               const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                               bool fuse_delta, int nsplit, void *ws, hipStream_t st);
+
 // Bytes of workspace the W4A16 GEMM kernels need for this shape (0 = none).
 size_t w4a16_workspace_bytes(int M, int N, int K);
 

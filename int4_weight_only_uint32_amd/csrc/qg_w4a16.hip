@@ -5,7 +5,8 @@
 //     C = A . W_sym + A_group_sum @ delta,  W_sym[k,n] = (q[k,n] - 8) scale[g,n]
 // which is exact because delta does not depend on k.
 //
-// Skinny kernel (small M).  A wave owns MT 16-row m-tiles x NT 16-column
+// Skinny kernel (M < 128; for most M <= 16 shapes the decode kernel below,
+// which shares the activation tile between waves, is used instead).  A wave owns MT 16-row m-tiles x NT 16-column
 // n-tiles and a contiguous range of 128-k tiles, with P tiles of codes and
 // activations in flight in a register ring; the waves of a workgroup split K
 // and are summed through LDS at the end (one launch, no workspace).
@@ -76,21 +77,25 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
     // same on every path and each wait only covers the slot being consumed.
     uint4v ra[P][MT * 4];
     uint4v rw[P][NT];
-    uint16_t rs[P][NT], rd[P][NT];
-    auto load = [&](int kt, uint4v (&a)[MT * 4], uint4v (&w)[NT], uint16_t (&sv)[NT],
-                    uint16_t (&dv)[NT]) {
+    // Scales and deltas are fetched as the aligned 32-bit pair holding this
+    // lane's column (half c&1 of it): 16-bit ring registers get packed in
+    // pairs by the compiler, and the packing waits for loads just issued.
+    uint32_t rs[P][NT], rd[P][NT];
+    const int sh = 16 * (c & 1);
+    auto load = [&](int kt, uint4v (&a)[MT * 4], uint4v (&w)[NT], uint32_t (&sv)[NT],
+                    uint32_t (&dv)[NT]) {
 #pragma unroll
         for (int j = 0; j < MT * 4; ++j) a[j] = asrc[j][kt * (KTILE / 8)];
 #pragma unroll
         for (int t = 0; t < NT; ++t) w[t] = wbase[((size_t)t * KT + kt) * 64];
         const int gi = (kt * KTILE) / g;
-        const uint16_t *srow = S + (size_t)gi * N + col0;
+        const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
 #pragma unroll
-        for (int t = 0; t < NT; ++t) sv[t] = srow[16 * t];
+        for (int t = 0; t < NT; ++t) sv[t] = srow[8 * t];
         if (DELTA) {
-            const uint16_t *drow = D + (size_t)gi * N + col0;
+            const uint32_t *drow = reinterpret_cast<const uint32_t *>(D + (size_t)gi * N + (col0 & ~1));
 #pragma unroll
-            for (int t = 0; t < NT; ++t) dv[t] = drow[16 * t];
+            for (int t = 0; t < NT; ++t) dv[t] = drow[8 * t];
         }
     };
     // Consuming a slot happens in two halves: `stage` moves the slot's
@@ -102,15 +107,15 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
         CodeOps ops[NT];
         float s[NT], d[NT];
     };
-    auto stage = [&](const uint4v (&ar)[MT * 4], const uint4v (&w)[NT], const uint16_t (&sv)[NT],
-                     const uint16_t (&dv)[NT], Staged &st) {
+    auto stage = [&](const uint4v (&ar)[MT * 4], const uint4v (&w)[NT], const uint32_t (&sv)[NT],
+                     const uint32_t (&dv)[NT], Staged &st) {
 #pragma unroll
         for (int j = 0; j < MT * 4; ++j) *reinterpret_cast<uint4v *>(scratch + adst[j]) = ar[j];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             st.ops[t] = split_codes(w[t]);
-            st.s[t] = h2f(sv[t]);
-            st.d[t] = DELTA ? h2f(dv[t]) : 0.f;
+            st.s[t] = h2f((uint16_t)(sv[t] >> sh));
+            st.d[t] = DELTA ? h2f((uint16_t)(dv[t] >> sh)) : 0.f;
         }
     };
     auto finish = [&](const Staged &st) {
@@ -168,6 +173,14 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
                 const int kt = kt_beg + j + i + P;
                 load(kt < last ? kt : last, ra[i], rw[i], rs[i], rd[i]);
                 finish(st);
+                // A memory clobber between each refill and the loop's back
+                // edge: without one, the compiler folds "phi(prologue load,
+                // refill load)" of the last slot into a single load at the
+                // top of the loop, right before its use, and that slot loses
+                // its prefetch distance.  The scheduling barrier keeps the
+                // next slot's work (and so its wait) out of this step.
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
@@ -199,6 +212,275 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
         const int cc = (nt0 + t) * NTILE + (l & 15);
         if (row < M) C[(size_t)row * N + cc] = f2h(v);
     }
+}
+
+// ---- decode kernel (M <= 16) ----
+// A workgroup of 4 waves owns 4*NT consecutive 16-column strips (wave w the
+// strips 4*NT*cg + NT*w .. +NT-1) and one of `nsplit` contiguous ranges of
+// 128-k tiles.  Each k-tile of A (16 rows x 128 k, 4 KB) is fetched once per
+// workgroup -- one 16-byte load per thread, rows past M reading row M-1 --
+// and shared through LDS (double buffered, one barrier per k-tile), so the
+// activation traffic is one tile per workgroup instead of one per wave.
+// Each wave streams its codes, scales and deltas through a P-deep register
+// ring; the MFMA and scaling steps are those of the skinny kernel.
+//
+// nsplit > 1: the workgroups of a column group each hold fp32 partial sums
+// for the same outputs.  Each writes them to its slot of the workspace with
+// device-coherent stores, waits for them to complete, and increments the
+// column group's counter (device-scope atomic).  The one that sees
+// nsplit - 1 adds the slots in split order (deterministic), converts to
+// fp16, stores C and puts the counter back to zero.  Only device-coherent
+// accesses touch the shared slots, so no cache-wide fence is needed; the
+// workspace counters must be zero before the first call and stay zero
+// between calls.
+template <int NT, int P, bool DELTA>
+__global__ __launch_bounds__(256) void w4a16_decode_kernel(
+    const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
+    const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g,
+    int nsplit, unsigned *__restrict__ counters, float *__restrict__ partials)
+{
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][16 * KTILE];
+    __shared__ unsigned arrived;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, kq = lane >> 4;
+    const int KT = K / KTILE;
+    const int cg = blockIdx.x / nsplit, sp = blockIdx.x - cg * nsplit;
+    const int kt_beg = (sp * KT) / nsplit, kt_end = ((sp + 1) * KT) / nsplit;
+    const int n = kt_end - kt_beg;
+    const int nt0 = (cg * 4 + wave) * NT;
+    const int col0 = nt0 * NTILE + c;
+
+    // activation tile: thread t fetches row t/16, 16-byte chunk t%16; the
+    // chunk lands at position chunk ^ row within its 256-byte LDS row so the
+    // 16 rows an MFMA operand reads fall in distinct banks
+    const int arow_i = tid >> 4, ach = tid & 15;
+    const int arow = arow_i < M ? arow_i : M - 1;
+    const uint4v *asrc = reinterpret_cast<const uint4v *>(A + (size_t)arow * K) + ach;
+    const int adst = arow_i * KTILE + 8 * (ach ^ (arow_i & 15));
+    const uint4v *wbase = W + (size_t)nt0 * KT * 64 + lane;
+    // scales/deltas are read as the aligned 32-bit pair holding this lane's
+    // column (half c & 1): 16-bit ring registers get packed in pairs by the
+    // compiler, and the packing waits for loads just issued
+    const int sh = 16 * (c & 1);
+
+    float4v acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
+    const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    const float4v fzero = {0.f, 0.f, 0.f, 0.f};
+
+    uint4v ra[P];
+    uint4v rw[P][NT];
+    uint32_t rs[P][NT], rd[P][NT];
+    auto load = [&](int kt, uint4v &a, uint4v (&w)[NT], uint32_t (&sv)[NT], uint32_t (&dv)[NT]) {
+        a = asrc[kt * (KTILE / 8)];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) w[t] = wbase[((size_t)t * KT + kt) * 64];
+        const int gi = (kt * KTILE) / g;
+        const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sv[t] = srow[8 * t];
+        if (DELTA) {
+            const uint32_t *drow = reinterpret_cast<const uint32_t *>(D + (size_t)gi * N + (col0 & ~1));
+#pragma unroll
+            for (int t = 0; t < NT; ++t) dv[t] = drow[8 * t];
+        }
+    };
+    struct Staged {
+        CodeOps ops[NT];
+        float s[NT], d[NT];
+    };
+    auto stage = [&](int buf, const uint4v &ar, const uint4v (&w)[NT], const uint32_t (&sv)[NT],
+                     const uint32_t (&dv)[NT], Staged &st) {
+        *reinterpret_cast<uint4v *>(&As[buf][adst]) = ar;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            st.ops[t] = split_codes(w[t]);
+            st.s[t] = h2f((uint16_t)(sv[t] >> sh));
+            st.d[t] = DELTA ? h2f((uint16_t)(dv[t] >> sh)) : 0.f;
+        }
+    };
+    auto finish = [&](int buf, const Staged &st) {
+        half8 a[4];
+#pragma unroll
+        for (int o = 0; o < 4; ++o)
+            a[o] = *reinterpret_cast<const half8 *>(&As[buf][c * KTILE + 8 * ((4 * o + kq) ^ c)]);
+        float4v as = mfma_f16(a[0], ones, fzero);
+        as = mfma_f16(a[1], ones, as);
+        as = mfma_f16(a[2], ones, as);
+        as = mfma_f16(a[3], ones, as);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float s = st.s[t];
+            const float c1 = s * 0x1p20f, c16 = s * 0x1p24f;
+            const float c2 = DELTA ? (st.d[t] - 8.0f * s) : (-8.0f * s);
+            float4v xl = mfma_f16(a[0], st.ops[t].lo[0], fzero);
+            xl = mfma_f16(a[1], st.ops[t].lo[1], xl);
+            float4v xh = mfma_f16(a[2], st.ops[t].hi[0], fzero);
+            xh = mfma_f16(a[3], st.ops[t].hi[1], xh);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = __builtin_fmaf(c16, xl[r], acc[t][r]);
+                v = __builtin_fmaf(c1, xh[r], v);
+                acc[t][r] = __builtin_fmaf(c2, as[r], v);
+            }
+        }
+    };
+
+    if (n > 0) {
+        const int last = kt_end - 1;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int kt = kt_beg + i;
+            load(kt < last ? kt : last, ra[i], rw[i], rs[i], rd[i]);
+        }
+        int j = 0;
+        for (; j + P <= n; j += P) {
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                const int buf = (j + i) & 1;
+                Staged st;
+                stage(buf, ra[i], rw[i], rs[i], rd[i], st);
+                const int kt = kt_beg + j + i + P;
+                load(kt < last ? kt : last, ra[i], rw[i], rs[i], rd[i]);
+                __syncthreads();
+                finish(buf, st);
+                // keep each refill ahead of the loop's back edge (see the
+                // skinny kernel) and the next slot's work out of this step
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < P - 1; ++i)
+            if (j + i < n) {
+                const int buf = (j + i) & 1;
+                Staged st;
+                stage(buf, ra[i], rw[i], rs[i], rd[i], st);
+                __syncthreads();
+                finish(buf, st);
+            }
+    }
+
+    // C rows 4 kq + r, columns (nt0 + t) * 16 + c
+    if (nsplit == 1) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * kq + r;
+                if (row < M) C[(size_t)row * N + col0 + 16 * t] = f2h(acc[t][r]);
+            }
+        return;
+    }
+    // slot layout: [cg][split][wave][t][r][lane] fp32
+    constexpr int PER_WAVE = NT * 4 * 64;
+    float *mine = partials + ((size_t)cg * nsplit + sp) * 4 * PER_WAVE + wave * PER_WAVE + lane;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            __hip_atomic_store(mine + (t * 4 + r) * 64, acc[t][r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);          // this thread's slot stores are complete
+    __syncthreads();                        // ... and every thread's
+    if (tid == 0)
+        arrived = __hip_atomic_fetch_add(&counters[cg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived != (unsigned)(nsplit - 1)) return;
+    float4v tot[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) tot[t] = fzero;
+    const float *base = partials + (size_t)cg * nsplit * 4 * PER_WAVE + wave * PER_WAVE + lane;
+    for (int s2 = 0; s2 < nsplit; ++s2) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                tot[t][r] += (s2 == sp) ? acc[t][r]
+                                        : __hip_atomic_load(base + (size_t)s2 * 4 * PER_WAVE + (t * 4 + r) * 64,
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * kq + r;
+            if (row < M) C[(size_t)row * N + col0 + 16 * t] = f2h(tot[t][r]);
+        }
+    if (tid == 0) __hip_atomic_store(&counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+namespace decode {
+constexpr int NT = 1, P = 2;
+constexpr int COLS = 4 * NT * NTILE;     // columns per workgroup
+}
+
+// Split count of the decode kernel: the smallest power of two giving at least
+// 512 workgroups (two per CU), keeping >= 2 k-tiles per split and <= 16 splits.
+int decode_splits(int N, int K)
+{
+    const int KT = K / KTILE, ncg = N / decode::COLS;
+    int ns = 1;
+    if ((size_t)ncg * sizeof(unsigned) > W4A16_WS_COUNTER_BYTES) return 1;   // no counter for it
+    while (ns < 16 && (long)ncg * ns < 512 && KT / (2 * ns) >= 2) ns *= 2;
+    return ns;
+}
+
+// Decode workspace: the fixed counter region (W4A16_WS_COUNTER_BYTES, shared
+// by every W4A16 layout and written by nothing but the counters), then the
+// partial-sum slots.  0 when the shape is not split.
+// Whether M <= 16 runs the decode kernel rather than the skinny one.  Measured
+// on MI355X: the decode kernel wins whenever two splits give enough
+// workgroups (wide N) and for 8 < M <= 16 on large weights (sharing the
+// activation tile matters most there); the skinny kernel, which splits K
+// between the waves of a workgroup and needs no cross-workgroup step, wins
+// for small M on narrow weights and for small problems, where the split-K
+// epilogue is a larger share of the time.
+bool use_decode_kernel(int M, int N, int K)
+{
+    if (M > 16 || N % decode::COLS) return false;
+    const int ns = decode_splits(N, K);
+    if (ns <= 2) return true;
+    return M > 8 && (long long)K * N >= (1ll << 24);
+}
+
+size_t decode_workspace_bytes(int M, int N, int K)
+{
+    if (!use_decode_kernel(M, N, K)) return 0;
+    const int ns = decode_splits(N, K);
+    if (ns == 1) return 0;
+    const size_t ncg = (size_t)(N / decode::COLS);
+    return W4A16_WS_COUNTER_BYTES + ncg * ns * 16 * decode::COLS * sizeof(float);
+}
+
+template <bool DELTA>
+static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                             int nsplit, void *ws, hipStream_t st)
+{
+    const int ncg = N / decode::COLS;
+    unsigned *counters = nullptr;
+    float *partials = nullptr;
+    if (nsplit > 1) {
+        counters = static_cast<unsigned *>(ws);
+        partials = reinterpret_cast<float *>(static_cast<char *>(ws) + W4A16_WS_COUNTER_BYTES);
+    }
+    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, DELTA>), dim3(ncg * nsplit),
+                       dim3(256), 0, st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K,
+                       g, nsplit, counters, partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                               const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                               bool fuse_delta, int nsplit, void *ws, hipStream_t st)
+{
+    if (M > 16 || N % decode::COLS || nsplit < 1 || (nsplit > 1 && !ws))
+        return hipErrorInvalidValue;
+    if (D && fuse_delta) return run_decode<true>(A, W, S, D, C, M, N, K, g, nsplit, ws, st);
+    return run_decode<false>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st);
 }
 
 template <int MT, int NT, int P, int NWMAX, bool DELTA>
@@ -480,7 +762,7 @@ SkinnyCfg skinny_config(int M, int N, int K)
     } else {
         c.MT = 4; c.NT = 2; c.P = 2;
     }
-    const int nwmax = (c.MT == 1) ? 16 : 4;
+    const int nwmax = (c.MT == 1) ? 8 : 4;
     c.S = 1;
     const long blocks = (long)(NT16 / c.NT) * ((M + 16 * c.MT - 1) / (16 * c.MT));
     // about 2500-4500 waves (measured best on MI355X for the decode shapes),
@@ -492,8 +774,9 @@ SkinnyCfg skinny_config(int M, int N, int K)
 
 size_t w4a16_workspace_bytes(int M, int N, int K)
 {
-    (void)M; (void)N; (void)K;
-    return 0;   // neither the skinny nor the tiled kernel needs scratch memory
+    // the decode kernel's split-K counters and partial sums (M <= 16); the
+    // skinny and tiled kernels need none
+    return decode_workspace_bytes(M, N, K);
 }
 
 template <bool DELTA>
@@ -505,9 +788,7 @@ static hipError_t dispatch_skinny(const SkinnyCfg &c, const uint16_t *A, const u
 #define QG_SK(MT_, NT_, P_, NWMAX_)                                                             \
     if (c.MT == MT_ && c.NT == NT_ && c.P == P_ && c.nw <= NWMAX_)                              \
         return run_skinny<MT_, NT_, P_, NWMAX_, DELTA>(c, A, W, S, D, C, M, N, K, g, st);
-    QG_SK(1, 1, 4, 16) QG_SK(1, 1, 8, 8) QG_SK(1, 2, 2, 16) QG_SK(1, 2, 3, 8) QG_SK(1, 2, 4, 8)
-    QG_SK(1, 4, 2, 8) QG_SK(1, 4, 3, 4) QG_SK(1, 8, 2, 4)
-    QG_SK(2, 4, 2, 4) QG_SK(4, 2, 2, 4)
+    QG_SK(1, 2, 2, 8) QG_SK(2, 4, 2, 4) QG_SK(4, 2, 2, 4)
 #undef QG_SK
     return hipErrorInvalidConfiguration;
 }
@@ -527,6 +808,10 @@ hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                         bool fuse_delta, void *ws, hipStream_t st)
 {
     if (M >= TILED_MIN_M) return launch_w4a16_tiled(A, W, S, D, C, M, N, K, g, fuse_delta, st);
+    if (use_decode_kernel(M, N, K))
+        return launch_w4a16_decode(A, W, S, D, C, M, N, K, g, fuse_delta,
+                                   decode_workspace_bytes(M, N, K) ? decode_splits(N, K) : 1, ws,
+                                   st);
     return launch_w4a16_skinny_cfg(skinny_config(M, N, K), A, W, S, D, C, M, N, K, g,
                                    fuse_delta, ws, st);
 }

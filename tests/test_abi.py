@@ -113,9 +113,32 @@ def test_group_sum_correction_validation():
     assert L.group_sum_correction(None, FAKE, FAKE, 4, 1024, 1024, 128, FAKE, 4096, None) == qg.QG_ERR_INVALID_ARG
 
 
+CTR = 65536   # QG_W4A16_WS_COUNTER_BYTES
+
+
+def test_decode_workspace_size():
+    # M <= 16: the fixed counter region + fp32 partials (16 rows x 64 columns
+    # per split per 64-column group).  Splits: the smallest power of two giving
+    # >= 512 workgroups with >= 2 k-tiles per split.
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 17408, 5120, 128) == CTR + 272 * 2 * 4096
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 9, 5120, 17408, 128) == CTR + 80 * 8 * 4096
+    # small M on a narrow weight, and small problems, run the skinny kernel
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 8, 5120, 17408, 128) == 0
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1024, 128) == 0
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 17, 5120, 17408, 128) == 0     # skinny path
+    # a K range too short to split needs none
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 256, 128) == 0
+    # the correction's group sums always come after the counter region
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 256, 1024, 1024, 128, 1,
+                                 qg.QG_CORR_SEPARATE) == CTR + 256 * 8 * 4
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1024, 128, 1, qg.QG_CORR_SEPARATE) == \
+        CTR + 16 * 8 * 4
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 17408, 5120, 128, 1, qg.QG_CORR_SEPARATE) == \
+        CTR + 272 * 2 * 4096 + 16 * 40 * 4
+
+
 def test_workspace_bytes():
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 256, 1024, 1024, 128) == 0
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 256, 1024, 1024, 128, 1, qg.QG_CORR_SEPARATE) == 256 * 8 * 4
     base = qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1024, 128)
     sep = qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1024, 128, 1, qg.QG_CORR_SEPARATE)
     assert sep >= base + 16 * 8 * 4

@@ -194,6 +194,30 @@ def test_w4a16_fold_off_matches_unfolded():
     _check_w4a16(c, fold=False)
 
 
+def test_w4a16_decode_workspace_returns_to_zero():
+    # the split-K counters must be zero after every call, so one zero-filled
+    # workspace serves calls of different shapes in sequence
+    cases = [synth.workload("w4a16-decode-M16-K5120-N17408-g128-asym"),
+             synth.workload("w4a16-decode-M16-K17408-N5120-g128-asym"),
+             synth.workload("w4a16-decode-M4-K17408-N5120-g128-asym"),
+             synth.workload("w4a16-small-asym-M16-K1024-N1024-g128")]
+    nbytes = max(qg.qg_workspace_bytes(qg.QG_OP_W4A16, c.M, c.N, c.K, c.g) for c in cases)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for c in cases:
+            note(f"w4a16 shared workspace {c.name} rep {rep}")
+            pw = pack_case(c)
+            C = qg.w4a16(dev(c.A), pw, workspace=ws)
+            torch.cuda.synchronize()
+            ncounters = c.N // 64
+            assert int(torch.count_nonzero(ws[: 4 * ncounters])) == 0
+            got = host(C).astype(np.float64)
+            ref = oracle.w4a16(c.A, c.q, c.s, c.z, c.g)
+            assert rel_fro(got, ref) <= W4A16_TOL
+            assert elementwise_guard(got, ref) <= 0
+
+
 def test_w4a16_deterministic():
     c = synth.workload("w4a16-decode-M16-K5120-N17408-g128-asym")
     a, _ = run_w4a16(c)
