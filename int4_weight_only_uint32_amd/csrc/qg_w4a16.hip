@@ -499,26 +499,29 @@ static hipError_t run_skinny(const SkinnyCfg &cf, const uint16_t *A, const uint3
     return hipGetLastError();
 }
 
-// ---- tiled kernel (large M) ----
-// Workgroup tile 128 rows x 256 columns, 4 waves; wave w owns columns
-// [64w, 64w+64) (4 n-tiles) and all 128 rows (8 m-tiles).  A is staged
-// through LDS (two buffers of 128 x 128 fp16) with gfx950's direct
-// global->LDS 16-byte loads, no registers in between.  Within a 256-byte row
-// the 16-byte chunk ch is stored at position ch ^ (row % 16), so the 16 rows
-// an MFMA operand reads fall in distinct LDS banks; packed codes go
-// straight from global memory to registers, each wave reading only its own
-// columns.  Codes are dequantized per element to fp16 ((v - 8) * scale,
-// exact up to the one fp16 rounding of the product) and fed to 16x16x32 fp16
-// MFMAs.  Asymmetric weights: the per-group sums of A are accumulated by
-// MFMAs against an all-ones operand (wave w sums m-tiles 2w and 2w+1), parked
-// in LDS, and every 16 groups applied as one extra MFMA k-step whose A side is
-// the group sums (split into a high and a low fp16 part) and whose B side is
-// delta -- the "A_group_sum @ delta" term of the method, fused.
-// Rows from which the LDS-tiled kernel takes over from the skinny one.
-constexpr int TILED_MIN_M = 128;
+// ---- tiled kernel (M >= 128) ----
+// Workgroup tile BM = 16*WM rows x BN = 64*WN columns, 4 waves; wave w owns
+// columns [16*WN*w, 16*WN*(w+1)) (WN n-tiles) and all BM rows (WM m-tiles).
+// Two configurations: 128 x 256 (WM = 8, WN = 4) for large M x N, and
+// 64 x 128 (WM = 4, WN = 2) when the large tile would leave the GPU short of
+// workgroups (mid-size M).  A is staged through LDS (two buffers of BM x 128
+// fp16) with gfx950's direct global->LDS 16-byte loads, no registers in
+// between.  Within a 256-byte row the 16-byte chunk ch is stored at position
+// ch ^ (row % 16), so the 16 rows an MFMA operand reads fall in distinct LDS
+// banks; packed codes go straight from global memory to registers, each wave
+// reading only its own columns.  Codes are dequantized per element to fp16
+// ((v - 8) * scale, exact up to the one fp16 rounding of the product) and fed
+// to 16x16x32 fp16 MFMAs.  Asymmetric weights: the per-group sums of A are
+// accumulated by MFMAs against an all-ones operand (wave w sums m-tiles
+// w*WM/4 .. (w+1)*WM/4 - 1), parked in LDS, and every 16 groups applied as
+// one extra MFMA k-step whose A side is the group sums (split into a high and
+// a low fp16 part) and whose B side is delta -- the "A_group_sum @ delta"
+// term of the method, fused.
+// Rows from which the tiled/mid kernels take over from the skinny one (the mid
+// kernel measured faster from about M = 80 on).
+constexpr int TILED_MIN_M = 81;
 
 namespace tiled {
-constexpr int BM = 128, BN = 256;
 constexpr int WIN = 16;                         // groups per correction k-step
 }
 
@@ -552,12 +555,16 @@ __device__ inline half8 dequant_scaled(uint4v w, half2v s2)
     return __builtin_bit_cast(half8, uint4v{out[0], out[1], out[2], out[3]});
 }
 
-template <bool DELTA>
-__global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
+template <int WM, int WN, bool DELTA>
+__global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g)
 {
     using namespace tiled;
+    static_assert(WM % 4 == 0, "each wave sums WM/4 m-tiles of the group sums");
+    constexpr int BM = 16 * WM, BN = 64 * WN;
+    constexpr int ABLK = BM / 16;                     // 1 KB A blocks per wave and k-tile
+    constexpr int GM = WM / 4;                        // group-sum m-tiles per wave
     __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * 128];
     __shared__ __attribute__((aligned(16))) float asum_win[DELTA ? BM * WIN : 1];
 
@@ -566,7 +573,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
     const int c = lane & 15, kq = lane >> 4;
     const int KT = K / KTILE, G = K / g;
     const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN + wave * 64;        // this wave's first column
+    const int n0 = blockIdx.x * BN + wave * 16 * WN;   // this wave's first column
     const bool active = n0 < N;
     const int ntile0 = n0 / NTILE;
 
@@ -576,8 +583,8 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
     // Rows past M read row M-1 (their results are never stored).
     auto load_a = [&](int kt, int st) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int blk = wave * 8 + i;             // 32 blocks of 4 rows
+        for (int i = 0; i < ABLK; ++i) {
+            const int blk = wave * ABLK + i;            // BM/4 blocks of 4 rows
             const int r = blk * 4 + (lane >> 4);
             const int ch = (lane & 15) ^ (r & 15);
             int row = m0 + r;
@@ -593,25 +600,27 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
         const int pch = (4 * o + kq) ^ c;
         return *reinterpret_cast<const half8 *>(as + r * 128 + pch * 8);
     };
-    // ---- codes and scales of this wave's 4 n-tiles
-    uint4v wreg[4];
-    uint16_t sreg[4];
+    // ---- codes and scales of this wave's WN n-tiles
+    uint4v wreg[WN];
+    uint16_t sreg[WN];
     auto load_w = [&](int kt) {
         if (!active) return;
         const int gi = (kt * KTILE) / g;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < WN; ++t) {
             wreg[t] = W[((size_t)(ntile0 + t) * KT + kt) * 64 + lane];
             sreg[t] = S[(size_t)gi * N + n0 + 16 * t + c];
         }
     };
 
-    float4v acc[8][4];
+    float4v acc[WM][WN];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
-    float4v gsum[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
+        for (int t = 0; t < WN; ++t) acc[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
+    float4v gsum[GM];
+#pragma unroll
+    for (int j = 0; j < GM; ++j) gsum[j] = float4v{0.f, 0.f, 0.f, 0.f};
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     if (DELTA)
         for (int i = tid; i < BM * WIN; i += 256) asum_win[i] = 0.f;
@@ -619,9 +628,9 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
     // the delta k-step for the window of groups [gw0, gw0 + WIN)
     auto delta_step = [&](int gw0) {
         if (!active) return;
-        half8 be[4];
+        half8 be[WN];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < WN; ++t) {
             const int colx = n0 + 16 * t + c;
 #pragma unroll
             for (int s8 = 0; s8 < 8; ++s8) {
@@ -631,7 +640,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
             }
         }
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
+        for (int mt = 0; mt < WM; ++mt) {
             const float *src = &asum_win[(16 * mt + c) * WIN + 8 * (kq & 1)];
             half8 ae;
 #pragma unroll
@@ -641,7 +650,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
                 ae[s8] = (kq < 2) ? hi : (_Float16)(a - (float)hi);
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_f16(ae, be[t], acc[mt][t]);
+            for (int t = 0; t < WN; ++t) acc[mt][t] = mfma_f16(ae, be[t], acc[mt][t]);
         }
     };
 
@@ -651,10 +660,10 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         const int st = kt & 1;
-        uint4v wc[4];
-        half2v s2[4];
+        uint4v wc[WN];
+        half2v s2[WN];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < WN; ++t) {
             wc[t] = wreg[t];
             const _Float16 sh = __builtin_bit_cast(_Float16, sreg[t]);
             s2[t] = half2v{sh, sh};
@@ -665,15 +674,15 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
         }
         const _Float16 *as = As[st];
         if (active) {
-#define QG_TILED_STEP(O)                                                                     \
-    {                                                                                        \
-        half8 b[4];                                                                          \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t) b[t] = dequant_scaled<O>(wc[t], s2[t]); \
-        _Pragma("unroll") for (int mt = 0; mt < 8; ++mt)                                     \
-        {                                                                                    \
-            const half8 a = a_frag(as, mt, O);                                               \
-            _Pragma("unroll") for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_f16(a, b[t], acc[mt][t]); \
-        }                                                                                    \
+#define QG_TILED_STEP(O)                                                                      \
+    {                                                                                         \
+        half8 b[WN];                                                                          \
+        _Pragma("unroll") for (int t = 0; t < WN; ++t) b[t] = dequant_scaled<O>(wc[t], s2[t]); \
+        _Pragma("unroll") for (int mt = 0; mt < WM; ++mt)                                     \
+        {                                                                                     \
+            const half8 a = a_frag(as, mt, O);                                                \
+            _Pragma("unroll") for (int t = 0; t < WN; ++t) acc[mt][t] = mfma_f16(a, b[t], acc[mt][t]); \
+        }                                                                                     \
     }
             QG_TILED_STEP(0)
             QG_TILED_STEP(1)
@@ -682,10 +691,10 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
 #undef QG_TILED_STEP
         }
         if (DELTA) {
-            // group sums of this wave's two m-tiles
+            // group sums of this wave's GM m-tiles
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int mt = 2 * wave + j;
+            for (int j = 0; j < GM; ++j) {
+                const int mt = GM * wave + j;
 #pragma unroll
                 for (int o = 0; o < 4; ++o) {
                     const half8 a = a_frag(as, mt, o);
@@ -696,10 +705,10 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
             const bool gend = ((kt + 1) * KTILE) % g == 0;
             if (gend) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < GM; ++j) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        asum_win[(16 * (2 * wave + j) + 4 * kq + r) * WIN + (gi % WIN)] = gsum[j][r];
+                        asum_win[(16 * (GM * wave + j) + 4 * kq + r) * WIN + (gi % WIN)] = gsum[j][r];
                     gsum[j] = float4v{0.f, 0.f, 0.f, 0.f};
                 }
             }
@@ -721,9 +730,9 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
 
     if (!active) return;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < WN; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + 16 * mt + 4 * kq + r;
@@ -731,23 +740,215 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_kernel(
             }
 }
 
-template <bool DELTA>
+template <int WM, int WN, bool DELTA>
 static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                             hipStream_t st)
 {
-    dim3 grid((unsigned)((N + tiled::BN - 1) / tiled::BN), (unsigned)((M + tiled::BM - 1) / tiled::BM));
-    hipLaunchKernelGGL((w4a16_tiled_kernel<DELTA>), grid, dim3(256), 0, st, A,
+    constexpr int BM = 16 * WM, BN = 64 * WN;
+    dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
+    hipLaunchKernelGGL((w4a16_tiled_kernel<WM, WN, DELTA>), grid, dim3(256), 0, st, A,
                        reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g);
     return hipGetLastError();
+}
+
+// ---- mid kernel (mid-size M) ----
+// Workgroup tile 64 rows x 64 columns, 4 waves in a 2 x 2 arrangement: wave
+// (mw, nw) owns rows 32 mw .. 32 mw + 31 (2 m-tiles) and columns
+// 32 nw .. 32 nw + 31 (2 n-tiles).  Small tiles keep two or more waves per
+// SIMD at mid-size M, where one wave per SIMD left every LDS and memory
+// latency exposed.  The arithmetic is the decode kernel's: codes enter the
+// MFMAs as exact fp16 subnormals (no per-element dequantization, which would
+// otherwise cost more VALU than the MFMAs take), the group sums of A come from
+// MFMAs against an all-ones operand, and scale and delta are applied once per
+// k-tile on the fp32 accumulators.  A k-tile of A (64 rows, 16 KB; wave w
+// fetches rows 16w .. 16w + 15 row-contiguously) is shared through two LDS
+// buffers with one barrier per k-tile; A, codes, scales and deltas of the
+// next P k-tiles wait in a register ring.
+template <int P, bool DELTA>
+__global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
+    const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
+    const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g)
+{
+    constexpr int WM = 2, WN = 2, BM = 64, BN = 64;
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * KTILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int mw = wave >> 1, nw = wave & 1;
+    const int c = lane & 15, kq = lane >> 4;
+    const int KT = K / KTILE;
+    const int m0 = blockIdx.y * BM;
+    const int ntile0 = blockIdx.x * (BN / NTILE) + WN * nw;
+    const int col0 = ntile0 * NTILE + c;
+    const int sh = 16 * (c & 1);
+
+    // A rows 16w + 4i + lane/16 (i = 0..3), 16-byte chunk lane%16, stored at
+    // position chunk ^ (row % 16); rows past M read row M-1 (never stored)
+    const uint4v *asrc[4];
+    int adst[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * i + (lane >> 4);
+        int row = m0 + r;
+        row = row < M ? row : M - 1;
+        asrc[i] = reinterpret_cast<const uint4v *>(A + (size_t)row * K) + (lane & 15);
+        adst[i] = r * KTILE + 8 * ((lane & 15) ^ (r & 15));
+    }
+    const uint4v *wbase = W + (size_t)ntile0 * KT * 64 + lane;
+
+    uint4v ra[P][4], rw[P][WN];
+    uint32_t rs[P][WN], rd[P][WN];
+    auto load = [&](int kt, int slot) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ra[slot][i] = asrc[i][kt * (KTILE / 8)];
+#pragma unroll
+        for (int t = 0; t < WN; ++t) rw[slot][t] = wbase[((size_t)t * KT + kt) * 64];
+        const int gi = (kt * KTILE) / g;
+        const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
+#pragma unroll
+        for (int t = 0; t < WN; ++t) rs[slot][t] = srow[8 * t];
+        if (DELTA) {
+            const uint32_t *drow = reinterpret_cast<const uint32_t *>(D + (size_t)gi * N + (col0 & ~1));
+#pragma unroll
+            for (int t = 0; t < WN; ++t) rd[slot][t] = drow[8 * t];
+        }
+    };
+
+    float4v acc[WM][WN];
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+        for (int t = 0; t < WN; ++t) acc[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
+    const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    const float4v fzero = {0.f, 0.f, 0.f, 0.f};
+
+    auto step = [&](int kt, int slot) {
+        const int buf = kt & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4v *>(&As[buf][adst[i]]) = ra[slot][i];
+        CodeOps ops[WN];
+        float s[WN], d[WN];
+#pragma unroll
+        for (int t = 0; t < WN; ++t) {
+            ops[t] = split_codes(rw[slot][t]);
+            s[t] = h2f((uint16_t)(rs[slot][t] >> sh));
+            d[t] = DELTA ? h2f((uint16_t)(rd[slot][t] >> sh)) : 0.f;
+        }
+        const int kn = kt + P < KT ? kt + P : KT - 1;
+        load(kn, slot);
+        __syncthreads();
+        const _Float16 *as = As[buf];
+#pragma unroll
+        for (int mt = 0; mt < WM; ++mt) {
+            const int r = 32 * mw + 16 * mt + c;
+            half8 a[4];
+#pragma unroll
+            for (int o = 0; o < 4; ++o)
+                a[o] = *reinterpret_cast<const half8 *>(as + r * KTILE + 8 * ((4 * o + kq) ^ c));
+            float4v asum = mfma_f16(a[0], ones, fzero);
+            asum = mfma_f16(a[1], ones, asum);
+            asum = mfma_f16(a[2], ones, asum);
+            asum = mfma_f16(a[3], ones, asum);
+#pragma unroll
+            for (int t = 0; t < WN; ++t) {
+                float4v xl = mfma_f16(a[0], ops[t].lo[0], fzero);
+                xl = mfma_f16(a[1], ops[t].lo[1], xl);
+                float4v xh = mfma_f16(a[2], ops[t].hi[0], fzero);
+                xh = mfma_f16(a[3], ops[t].hi[1], xh);
+                const float c16 = s[t] * 0x1p24f, c1 = s[t] * 0x1p20f;
+                const float c2 = DELTA ? (d[t] - 8.0f * s[t]) : (-8.0f * s[t]);
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    float v = __builtin_fmaf(c16, xl[r4], acc[mt][t][r4]);
+                    v = __builtin_fmaf(c1, xh[r4], v);
+                    acc[mt][t][r4] = __builtin_fmaf(c2, asum[r4], v);
+                }
+            }
+        }
+    };
+
+#pragma unroll
+    for (int i = 0; i < P; ++i) load(i < KT ? i : KT - 1, i);
+    int kt = 0;
+    for (; kt + P <= KT; kt += P) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            step(kt + i, i);
+            // keep each refill ahead of the loop's back edge (see the skinny
+            // kernel) and the next slot's work out of this step
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < P - 1; ++i)
+        if (kt + i < KT) step(kt + i, i);
+
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+        for (int t = 0; t < WN; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + 32 * mw + 16 * mt + 4 * kq + r;
+                if (row < M) C[(size_t)row * N + col0 + 16 * t] = f2h(acc[mt][t][r]);
+            }
+}
+
+template <bool DELTA>
+static hipError_t run_mid(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                          const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                          hipStream_t st)
+{
+    dim3 grid((unsigned)(N / 64), (unsigned)((M + 63) / 64));
+    hipLaunchKernelGGL((w4a16_mid_kernel<2, DELTA>), grid, dim3(256), 0, st, A,
+                       reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a16_mid(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                            const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                            bool fuse_delta, hipStream_t st)
+{
+    if (D && fuse_delta) return run_mid<true>(A, W, S, D, C, M, N, K, g, st);
+    return run_mid<false>(A, W, S, nullptr, C, M, N, K, g, st);
+}
+
+// Configuration for M >= MID_MIN_M: 0 = mid kernel (64 x 64 tiles),
+// 1 = tiled 64 x 128, 2 = tiled 128 x 256.  Measured on MI355X (K 4096-5120,
+// N 8192-17408): the big tile is the most efficient per tile and wins once it
+// fills whole rounds of two or more workgroups per CU; below that the
+// 64 x 128 tile wins while it has >= 512 workgroups; smaller problems need the
+// mid kernel's 64 x 64 tiles to keep two waves per SIMD busy.
+int tiled_config(int M, int N)
+{
+    const long big = (long)((M + 127) / 128) * ((N + 255) / 256);
+    const long small = (long)((M + 63) / 64) * ((N + 127) / 128);
+    if (big >= 512 && (big % 256 == 0 || big >= 1024)) return 2;
+    if (small >= 512) return 1;
+    return 0;
+}
+
+hipError_t launch_w4a16_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W,
+                                  const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
+                                  int K, int g, bool fuse_delta, hipStream_t st)
+{
+    const bool dl = D && fuse_delta;
+    if (cfg == 0) return launch_w4a16_mid(A, W, S, D, C, M, N, K, g, fuse_delta, st);
+    if (cfg == 1) {
+        if (dl) return run_tiled<4, 2, true>(A, W, S, D, C, M, N, K, g, st);
+        return run_tiled<4, 2, false>(A, W, S, nullptr, C, M, N, K, g, st);
+    }
+    if (dl) return run_tiled<8, 4, true>(A, W, S, D, C, M, N, K, g, st);
+    return run_tiled<8, 4, false>(A, W, S, nullptr, C, M, N, K, g, st);
 }
 
 hipError_t launch_w4a16_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                               const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                               bool fuse_delta, hipStream_t st)
 {
-    if (D && fuse_delta) return run_tiled<true>(A, W, S, D, C, M, N, K, g, st);
-    return run_tiled<false>(A, W, S, nullptr, C, M, N, K, g, st);
+    return launch_w4a16_tiled_cfg(tiled_config(M, N), A, W, S, D, C, M, N, K, g, fuse_delta, st);
 }
 
 // Heuristic choice of the skinny configuration (also sizes the workspace).
