@@ -104,6 +104,18 @@ __device__ inline unsigned swap_mid_bytes(unsigned x)
     return (x & 0xFF0000FFu) | ((x >> 8) & 0x0000FF00u) | ((x << 8) & 0x00FF0000u);
 }
 
+// Materialize a staged value here.  In a register ring the compiler may sink
+// pure arithmetic on a slot (code splitting, scale conversion) below the
+// refill load of that slot; the old registers then stay live across the
+// refill, the allocator rotates the ring's registers, and the copies at the
+// loop's back edge wait for the loads just issued.  An empty asm that reads
+// and writes the value keeps the arithmetic before the refill.
+template <class T>
+__device__ inline void pin(T &x)
+{
+    asm volatile("" : "+v"(x));
+}
+
 __device__ inline float4v mfma_f16(half8 a, half8 b, float4v c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);

@@ -27,10 +27,13 @@ namespace qg {
 // row-contiguously by the whole workgroup and stored to LDS in MFMA operand
 // order (for lane (row, kq): the 16 bytes k = 8kq..8kq+7 and 32+8kq..39+8kq,
 // bytes reordered to match the codes' nibble order; then the same for the
-// upper 64 k), double-buffered, one barrier per tile.  Codes stream through a
-// P-deep register ring per wave.
-template <int NT, int P>
-__global__ __launch_bounds__(256) void w4a8_kernel(
+// upper 64 k), double-buffered, one barrier per tile.  The activation
+// fragments, codes and group scales of the next P tiles wait in a register
+// ring whose loads are unconditional (indices clamped to the last tile), so
+// every wait covers only the slot being consumed -- a scale loaded just before
+// its use would wait for every load issued before it.
+template <int NT, int P, bool DEBUG>
+__global__ __launch_bounds__(256, 2) void w4a8_kernel(
     const int8_t *__restrict__ Aq, const float *__restrict__ a_scale,
     const uint4v *__restrict__ Wall, const uint16_t *__restrict__ Sall,
     const int32_t *__restrict__ offsets, int M_total, int N, int K, int g,
@@ -56,9 +59,9 @@ __global__ __launch_bounds__(256) void w4a8_kernel(
     const int c = lane & 15, kq = lane >> 4;
     const int KT = K / KTILE, G = K / g;
     const int nt0 = (blockIdx.x * 4 + wave) * NT;
-    const bool active = nt0 * NTILE < N;
     const uint4v *W = Wall + (size_t)e * KT * (N / NTILE) * 64;
     const uint16_t *S = Sall + (size_t)e * G * N;
+    const int sh = 16 * (c & 1);
 
     // ---- A staging: thread t copies 2 x 16 bytes: row t/4 (of 64), bytes
     // 32 (t%4) .. 32 (t%4) + 31 of the 128-k tile.  Rows past the expert's
@@ -66,16 +69,11 @@ __global__ __launch_bounds__(256) void w4a8_kernel(
     int arow = m0 + (tid >> 2);
     arow = arow < r1 ? arow : r1 - 1;
     const int8_t *asrc = Aq + (size_t)arow * K + 32 * (tid & 3);
-    uint4v areg[2];
-    auto load_a = [&](int kt) {
-        areg[0] = *reinterpret_cast<const uint4v *>(asrc + kt * KTILE);
-        areg[1] = *reinterpret_cast<const uint4v *>(asrc + kt * KTILE + 16);
-    };
     // the 32 bytes k0 .. k0+31 (k0 = 32 (t%4)) split into four 8-byte pieces:
     // piece j holds k = k0 + 8j .. k0 + 8j + 7 -> operand op = k0 / 64, slot
     // kq = j, half = (k0 / 32) % 2
     auto slot = [&](int row, int op, int q) { return row * 8 + op * 4 + (q ^ ((row >> 1) & 3)); };
-    auto store_a = [&](int st) {
+    auto store_a = [&](int st, const uint4v (&areg)[2]) {
         const int row = tid >> 2, k0 = 32 * (tid & 3);
         const int op = k0 / 64, half = (k0 / 32) & 1;
         unsigned d[8] = {areg[0].x, areg[0].y, areg[0].z, areg[0].w,
@@ -100,75 +98,90 @@ __global__ __launch_bounds__(256) void w4a8_kernel(
             acci[mt][t] = int4v{0, 0, 0, 0};
         }
 
-    // P-deep register ring of codes; refilled unconditionally (clamped)
-    uint4v rw[P][NT];
-    auto load_w = [&](int kt, uint4v (&w)[NT]) {
+    // register ring: activations, codes, group scales (32-bit pair holding
+    // this lane's column, half c & 1)
+    uint4v ra[P][2], rw[P][NT];
+    uint32_t rs[P][NT];
+    auto load = [&](int kt, int sl) {
         const int k = kt < KT ? kt : KT - 1;
+        ra[sl][0] = *reinterpret_cast<const uint4v *>(asrc + k * KTILE);
+        ra[sl][1] = *reinterpret_cast<const uint4v *>(asrc + k * KTILE + 16);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) w[t] = active ? wp[((size_t)t * KT + k) * 64] : uint4v{0u, 0u, 0u, 0u};
+        for (int t = 0; t < NT; ++t) rw[sl][t] = wp[((size_t)t * KT + k) * 64];
+        const int gi = (k * KTILE) / g;
+        const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) rs[sl][t] = srow[8 * t];
     };
-#pragma unroll
-    for (int i = 0; i < P; ++i) load_w(i, rw[i]);
-    load_a(0);
-    store_a(0);
-    __syncthreads();
 
-    for (int kb = 0; kb < KT; kb += P) {
+    auto step = [&](int kt, int sl) {
+        const int st = kt & 1;
+        store_a(st, ra[sl]);
+        CodeOpsI8 b[NT];
+        float sv[NT];
 #pragma unroll
-        for (int i = 0; i < P; ++i) {
-            const int kt = kb + i;
-            if (kt >= KT) break;
-            const int st = kt & 1;
-            if (kt + 1 < KT) load_a(kt + 1);
-            uint4v w[NT];
+        for (int t = 0; t < NT; ++t) {
+            b[t] = split_codes_i8(rw[sl][t]);
+            sv[t] = h2f((uint16_t)(rs[sl][t] >> sh));
+            pin(b[t].op[0]);
+            pin(b[t].op[1]);
+            pin(sv[t]);
+        }
+        load(kt + P, sl);
+        __syncthreads();
+        int4v alo[MT], ahi[MT];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) w[t] = rw[i][t];
-            load_w(kt + P, rw[i]);
-            if (active) {
-                int4v alo[MT], ahi[MT];
+        for (int mt = 0; mt < MT; ++mt) {
+            const int row = 16 * mt + c;
+            alo[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 0, kq)]);
+            ahi[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 1, kq)]);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                acci[mt][t] = mfma_i8(alo[mt], b[t].op[0], acci[mt][t]);
+                acci[mt][t] = mfma_i8(ahi[mt], b[t].op[1], acci[mt][t]);
+            }
+        if (((kt + 1) * KTILE) % g == 0) {        // end of a weight group
+            const int gi = (kt * KTILE) / g;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const int row = 16 * mt + c;
-                    alo[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 0, kq)]);
-                    ahi[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 1, kq)]);
-                }
+                    const int4v qv = acci[mt][t] >> 4;   // exact: terms are multiples of 16
+                    accf[mt][t] += sv[t] * __builtin_convertvector(qv, float4v);
+                    acci[mt][t] = int4v{0, 0, 0, 0};
+                    if (DEBUG) {
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    CodeOpsI8 b = split_codes_i8(w[t]);
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        acci[mt][t] = mfma_i8(alo[mt], b.op[0], acci[mt][t]);
-                        acci[mt][t] = mfma_i8(ahi[mt], b.op[1], acci[mt][t]);
-                    }
-                }
-                if (((kt + 1) * KTILE) % g == 0) {        // end of a weight group
-                    const int gi = (kt * KTILE) / g;
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) {
-                        const float s = h2f(S[(size_t)gi * N + col0 + 16 * t]);
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) {
-                            const int4v qv = acci[mt][t] >> 4;   // exact: terms are multiples of 16
-                            accf[mt][t] += s * __builtin_convertvector(qv, float4v);
-                            acci[mt][t] = int4v{0, 0, 0, 0};
-                            if (acc_debug) {
-#pragma unroll
-                                for (int r = 0; r < 4; ++r) {
-                                    const int row = m0 + 16 * mt + 4 * kq + r;
-                                    if (row < r1)
-                                        acc_debug[((size_t)row * G + gi) * N + col0 + 16 * t] = qv[r];
-                                }
-                            }
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = m0 + 16 * mt + 4 * kq + r;
+                            if (row < r1)
+                                acc_debug[((size_t)row * G + gi) * N + col0 + 16 * t] = qv[r];
                         }
                     }
                 }
-            }
-            if (kt + 1 < KT) store_a(st ^ 1);
-            __syncthreads();
+        }
+    };
+
+#pragma unroll
+    for (int i = 0; i < P; ++i) load(i, i);
+    int kt = 0;
+    for (; kt + P <= KT; kt += P) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            step(kt + i, i);
+            // keep each refill ahead of the loop's back edge and the next
+            // slot's work out of this step (the compiler would otherwise fold
+            // the last slot's loads into the top of the loop)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+#pragma unroll
+    for (int i = 0; i < P - 1; ++i)
+        if (kt + i < KT) step(kt + i, i);
 
-    if (!active) return;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -181,7 +194,7 @@ __global__ __launch_bounds__(256) void w4a8_kernel(
         }
 }
 
-template <int NT, int P>
+template <int NT, int P, bool DEBUG>
 static hipError_t run_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
                            const uint16_t *S, const int32_t *offsets, int E, int M_total,
                            int max_rows, int N, int K, int g, uint16_t *C, int32_t *acc_debug,
@@ -189,7 +202,7 @@ static hipError_t run_w4a8(const int8_t *Aq, const float *a_scale, const uint32_
 {
     const int NT16 = N / NTILE;
     dim3 grid((unsigned)((NT16 + 4 * NT - 1) / (4 * NT)), (unsigned)((max_rows + 63) / 64), (unsigned)E);
-    hipLaunchKernelGGL((w4a8_kernel<NT, P>), grid, dim3(256), 0, st, Aq, a_scale,
+    hipLaunchKernelGGL((w4a8_kernel<NT, P, DEBUG>), grid, dim3(256), 0, st, Aq, a_scale,
                        reinterpret_cast<const uint4v *>(W), S, offsets, M_total, N, K, g, C,
                        acc_debug);
     return hipGetLastError();
@@ -202,8 +215,11 @@ hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W
 {
     // N % 128 == 0 -> the n-tile count is a multiple of 8: NT = 2 tiles the
     // columns exactly (4 waves x 2 n-tiles = 128 columns per workgroup)
-    return run_w4a8<2, 4>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C,
-                          acc_debug, st);
+    if (acc_debug)
+        return run_w4a8<2, 3, true>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C,
+                                    acc_debug, st);
+    return run_w4a8<2, 3, false>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C,
+                                 nullptr, st);
 }
 
 } // namespace qg
