@@ -28,6 +28,7 @@ hipError_t launch_w4a16_mid(const uint16_t *A, const uint32_t *W, const uint16_t
                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                             bool fuse_delta, hipStream_t st);
 int tiled_config(int M, int N);
+int tiled_row_split(int M, int N);
 hipError_t launch_w4a16_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W,
                                   const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
                                   int K, int g, bool fuse_delta, hipStream_t st);

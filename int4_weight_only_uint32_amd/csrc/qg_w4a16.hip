@@ -22,6 +22,8 @@
 #include "qg_device.h"
 #include "qg_launch.h"
 
+#include <type_traits>
+
 namespace qg {
 
 template <int MT, int NT, int P, int NWMAX, bool DELTA>
@@ -233,14 +235,21 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
 // accesses touch the shared slots, so no cache-wide fence is needed; the
 // workspace counters must be zero before the first call and stay zero
 // between calls.
-template <int NT, int P, bool DELTA>
-__global__ __launch_bounds__(256) void w4a16_decode_kernel(
+template <int NT, int P, int WV, bool DELTA>
+__global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g,
     int nsplit, unsigned *__restrict__ counters, float *__restrict__ partials)
 {
+    static_assert(NT == 1, "the scale table holds one column per lane");
+    static_assert(WV == 4 || WV == 8, "4 or 8 waves per workgroup");
+    constexpr int COLS = 16 * WV;            // columns per workgroup
     __shared__ __attribute__((aligned(16))) _Float16 As[2][16 * KTILE];
     __shared__ unsigned arrived;
+    // (scale | delta << 16) of this workgroup's 64 columns for every group its
+    // k-range touches: filled once, read once per k-tile (an LDS read instead
+    // of two global loads per k-tile)
+    extern __shared__ uint32_t sdt[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, kq = lane >> 4;
@@ -248,21 +257,39 @@ __global__ __launch_bounds__(256) void w4a16_decode_kernel(
     const int cg = blockIdx.x / nsplit, sp = blockIdx.x - cg * nsplit;
     const int kt_beg = (sp * KT) / nsplit, kt_end = ((sp + 1) * KT) / nsplit;
     const int n = kt_end - kt_beg;
-    const int nt0 = (cg * 4 + wave) * NT;
+    const int last = kt_end - 1;
+    const int nt0 = (cg * WV + wave) * NT;
     const int col0 = nt0 * NTILE + c;
 
-    // activation tile: thread t fetches row t/16, 16-byte chunk t%16; the
-    // chunk lands at position chunk ^ row within its 256-byte LDS row so the
-    // 16 rows an MFMA operand reads fall in distinct banks
-    const int arow_i = tid >> 4, ach = tid & 15;
+    // scale table first: its loads are the oldest in flight, so the waits
+    // for them cover nothing else
+    if (n > 0) {
+        const int gi0 = (kt_beg * KTILE) / g, gi1 = ((kt_end - 1) * KTILE) / g;
+        const int ng = gi1 - gi0 + 1;
+        const uint32_t *s32 = reinterpret_cast<const uint32_t *>(S) + (size_t)gi0 * (N / 2) + cg * (COLS / 2);
+        const uint32_t *d32 = DELTA ? reinterpret_cast<const uint32_t *>(D) + (size_t)gi0 * (N / 2) + cg * (COLS / 2) : nullptr;
+        for (int idx = tid; idx < ng * (COLS / 2); idx += 64 * WV) {
+            const int gl = idx / (COLS / 2), pr = idx % (COLS / 2);
+            const uint32_t s2 = s32[(size_t)gl * (N / 2) + pr];
+            const uint32_t d2 = DELTA ? d32[(size_t)gl * (N / 2) + pr] : 0u;
+            sdt[gl * COLS + 2 * pr] = (s2 & 0xFFFFu) | (d2 << 16);
+            sdt[gl * COLS + 2 * pr + 1] = (s2 >> 16) | (d2 & 0xFFFF0000u);
+        }
+    }
+
+    // activation tile (16 rows x 256 bytes): with 4 waves thread t fetches
+    // row t/16, 16-byte chunk t%16; with 8 waves row t/32, 8-byte piece t%32.
+    // A 16-byte chunk lands at position chunk ^ row within its 256-byte LDS
+    // row so the 16 rows an MFMA operand reads fall in distinct banks.
+    using AVec = typename std::conditional<WV == 4, uint4v, uint2v>::type;
+    constexpr int APR = 256 / sizeof(AVec);      // pieces per row
+    const int arow_i = tid / APR, apc = tid % APR;
     const int arow = arow_i < M ? arow_i : M - 1;
-    const uint4v *asrc = reinterpret_cast<const uint4v *>(A + (size_t)arow * K) + ach;
-    const int adst = arow_i * KTILE + 8 * (ach ^ (arow_i & 15));
+    const AVec *asrc = reinterpret_cast<const AVec *>(A + (size_t)arow * K) + apc;
+    const int ach = apc * (int)sizeof(AVec) / 16, asub = (apc * (int)sizeof(AVec) % 16) / 2;
+    const int adst = arow_i * KTILE + 8 * (ach ^ (arow_i & 15)) + asub;
     const uint4v *wbase = W + (size_t)nt0 * KT * 64 + lane;
-    // scales/deltas are read as the aligned 32-bit pair holding this lane's
-    // column (half c & 1): 16-bit ring registers get packed in pairs by the
-    // compiler, and the packing waits for loads just issued
-    const int sh = 16 * (c & 1);
+    const int gbase = (kt_beg * KTILE) / g;
 
     float4v acc[NT];
 #pragma unroll
@@ -270,55 +297,33 @@ __global__ __launch_bounds__(256) void w4a16_decode_kernel(
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     const float4v fzero = {0.f, 0.f, 0.f, 0.f};
 
-    uint4v ra[P];
+    AVec ra[P];
     uint4v rw[P][NT];
-    uint32_t rs[P][NT], rd[P][NT];
-    auto load = [&](int kt, uint4v &a, uint4v (&w)[NT], uint32_t (&sv)[NT], uint32_t (&dv)[NT]) {
-        a = asrc[kt * (KTILE / 8)];
+    auto load = [&](int kt, AVec &a, uint4v (&w)[NT]) {
+        a = asrc[(size_t)kt * (KTILE * 2 / sizeof(AVec))];
 #pragma unroll
         for (int t = 0; t < NT; ++t) w[t] = wbase[((size_t)t * KT + kt) * 64];
-        const int gi = (kt * KTILE) / g;
-        const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) sv[t] = srow[8 * t];
-        if (DELTA) {
-            const uint32_t *drow = reinterpret_cast<const uint32_t *>(D + (size_t)gi * N + (col0 & ~1));
-#pragma unroll
-            for (int t = 0; t < NT; ++t) dv[t] = drow[8 * t];
-        }
     };
-    struct Staged {
-        CodeOps ops[NT];
-        float s[NT], d[NT];
-    };
-    auto stage = [&](int buf, const uint4v &ar, const uint4v (&w)[NT], const uint32_t (&sv)[NT],
-                     const uint32_t (&dv)[NT], Staged &st) {
-        *reinterpret_cast<uint4v *>(&As[buf][adst]) = ar;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            st.ops[t] = split_codes(w[t]);
-            st.s[t] = h2f((uint16_t)(sv[t] >> sh));
-            st.d[t] = DELTA ? h2f((uint16_t)(dv[t] >> sh)) : 0.f;
-        }
-    };
-    auto finish = [&](int buf, const Staged &st) {
+    auto finish = [&](int buf, int kt, const CodeOps (&ops)[NT]) {
         half8 a[4];
 #pragma unroll
         for (int o = 0; o < 4; ++o)
             a[o] = *reinterpret_cast<const half8 *>(&As[buf][c * KTILE + 8 * ((4 * o + kq) ^ c)]);
+        const uint32_t sd = sdt[((kt * KTILE) / g - gbase) * COLS + 16 * wave + c];
         float4v as = mfma_f16(a[0], ones, fzero);
         as = mfma_f16(a[1], ones, as);
         as = mfma_f16(a[2], ones, as);
         as = mfma_f16(a[3], ones, as);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float s = st.s[t];
+            const float s = h2f((uint16_t)(sd & 0xFFFFu));
+            const float d = DELTA ? h2f((uint16_t)(sd >> 16)) : 0.f;
             const float c1 = s * 0x1p20f, c16 = s * 0x1p24f;
-            const float c2 = DELTA ? (st.d[t] - 8.0f * s) : (-8.0f * s);
-            float4v xl = mfma_f16(a[0], st.ops[t].lo[0], fzero);
-            xl = mfma_f16(a[1], st.ops[t].lo[1], xl);
-            float4v xh = mfma_f16(a[2], st.ops[t].hi[0], fzero);
-            xh = mfma_f16(a[3], st.ops[t].hi[1], xh);
+            const float c2 = DELTA ? (d - 8.0f * s) : (-8.0f * s);
+            float4v xl = mfma_f16(a[0], ops[t].lo[0], fzero);
+            xl = mfma_f16(a[1], ops[t].lo[1], xl);
+            float4v xh = mfma_f16(a[2], ops[t].hi[0], fzero);
+            xh = mfma_f16(a[3], ops[t].hi[1], xh);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float v = __builtin_fmaf(c16, xl[r], acc[t][r]);
@@ -327,25 +332,34 @@ __global__ __launch_bounds__(256) void w4a16_decode_kernel(
             }
         }
     };
+    auto step = [&](int kt, int slot, int kt_next) {
+        const int buf = (kt - kt_beg) & 1;
+        *reinterpret_cast<AVec *>(&As[buf][adst]) = ra[slot];
+        CodeOps ops[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            ops[t] = split_codes(rw[slot][t]);
+            pin(ops[t].lo[0]); pin(ops[t].lo[1]); pin(ops[t].hi[0]); pin(ops[t].hi[1]);
+        }
+        // unconditional (clamped) refill: a conditional load would make every
+        // later wait assume it might be missing and wait for everything
+        load(kt_next, ra[slot], rw[slot]);
+        __syncthreads();
+        finish(buf, kt, ops);
+    };
 
     if (n > 0) {
-        const int last = kt_end - 1;
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const int kt = kt_beg + i;
-            load(kt < last ? kt : last, ra[i], rw[i], rs[i], rd[i]);
+            load(kt < last ? kt : last, ra[i], rw[i]);
         }
         int j = 0;
         for (; j + P <= n; j += P) {
 #pragma unroll
             for (int i = 0; i < P; ++i) {
-                const int buf = (j + i) & 1;
-                Staged st;
-                stage(buf, ra[i], rw[i], rs[i], rd[i], st);
                 const int kt = kt_beg + j + i + P;
-                load(kt < last ? kt : last, ra[i], rw[i], rs[i], rd[i]);
-                __syncthreads();
-                finish(buf, st);
+                step(kt_beg + j + i, i, kt < last ? kt : last);
                 // keep each refill ahead of the loop's back edge (see the
                 // skinny kernel) and the next slot's work out of this step
                 asm volatile("" ::: "memory");
@@ -354,13 +368,7 @@ __global__ __launch_bounds__(256) void w4a16_decode_kernel(
         }
 #pragma unroll
         for (int i = 0; i < P - 1; ++i)
-            if (j + i < n) {
-                const int buf = (j + i) & 1;
-                Staged st;
-                stage(buf, ra[i], rw[i], rs[i], rd[i], st);
-                __syncthreads();
-                finish(buf, st);
-            }
+            if (j + i < n) step(kt_beg + j + i, i, last);
     }
 
     // C rows 4 kq + r, columns (nt0 + t) * 16 + c
@@ -376,7 +384,7 @@ __global__ __launch_bounds__(256) void w4a16_decode_kernel(
     }
     // slot layout: [cg][split][wave][t][r][lane] fp32
     constexpr int PER_WAVE = NT * 4 * 64;
-    float *mine = partials + ((size_t)cg * nsplit + sp) * 4 * PER_WAVE + wave * PER_WAVE + lane;
+    float *mine = partials + ((size_t)cg * nsplit + sp) * WV * PER_WAVE + wave * PER_WAVE + lane;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -392,14 +400,14 @@ __global__ __launch_bounds__(256) void w4a16_decode_kernel(
     float4v tot[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) tot[t] = fzero;
-    const float *base = partials + (size_t)cg * nsplit * 4 * PER_WAVE + wave * PER_WAVE + lane;
+    const float *base = partials + (size_t)cg * nsplit * WV * PER_WAVE + wave * PER_WAVE + lane;
     for (int s2 = 0; s2 < nsplit; ++s2) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 tot[t][r] += (s2 == sp) ? acc[t][r]
-                                        : __hip_atomic_load(base + (size_t)s2 * 4 * PER_WAVE + (t * 4 + r) * 64,
+                                        : __hip_atomic_load(base + (size_t)s2 * WV * PER_WAVE + (t * 4 + r) * 64,
                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
@@ -413,18 +421,30 @@ __global__ __launch_bounds__(256) void w4a16_decode_kernel(
 }
 
 namespace decode {
-constexpr int NT = 1, P = 2;
-constexpr int COLS = 4 * NT * NTILE;     // columns per workgroup
+constexpr int NT = 1, P = 2, WV = 4;      // 8 waves measured slower
+constexpr int COLS = WV * NT * NTILE;    // columns per workgroup
+}
+
+// Groups the k-range of one split touches (at most): the size of the decode
+// kernel's scale table in 64-column rows.
+int decode_max_groups(int K, int g, int nsplit)
+{
+    const int KT = K / KTILE;
+    const int span = (KT + nsplit - 1) / nsplit;          // k-tiles per split, at most
+    const int per_group = g / KTILE > 0 ? g / KTILE : 1;  // k-tiles per group
+    return (span + per_group - 1) / per_group + 1;
 }
 
 // Split count of the decode kernel: the smallest power of two giving at least
-// 512 workgroups (two per CU), keeping >= 2 k-tiles per split and <= 16 splits.
+// 512 workgroups (two per CU), keeping >= 2 k-tiles per split and <= 16
+// splits; more splits while one split's scale table would exceed 32 KB of LDS.
 int decode_splits(int N, int K)
 {
     const int KT = K / KTILE, ncg = N / decode::COLS;
     int ns = 1;
     if ((size_t)ncg * sizeof(unsigned) > W4A16_WS_COUNTER_BYTES) return 1;   // no counter for it
     while (ns < 16 && (long)ncg * ns < 512 && KT / (2 * ns) >= 2) ns *= 2;
+    while (ns < 1024 && (size_t)decode_max_groups(K, KTILE, ns) * decode::COLS * 4 > 32768) ns *= 2;
     return ns;
 }
 
@@ -467,9 +487,10 @@ static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_
         counters = static_cast<unsigned *>(ws);
         partials = reinterpret_cast<float *>(static_cast<char *>(ws) + W4A16_WS_COUNTER_BYTES);
     }
-    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, DELTA>), dim3(ncg * nsplit),
-                       dim3(256), 0, st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K,
-                       g, nsplit, counters, partials);
+    const size_t table = (size_t)decode_max_groups(K, g, nsplit) * decode::COLS * sizeof(uint32_t);
+    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA>),
+                       dim3(ncg * nsplit), dim3(64 * decode::WV), table, st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M,
+                       N, K, g, nsplit, counters, partials);
     return hipGetLastError();
 }
 
@@ -944,11 +965,38 @@ hipError_t launch_w4a16_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W,
     return run_tiled<8, 4, false>(A, W, S, nullptr, C, M, N, K, g, st);
 }
 
+// Rows of the first launch when the 128 x 256 tiles would end in a partly
+// filled round (two workgroups per CU, 512 per round): that launch covers the
+// largest multiple of 128 rows whose tiles fill whole rounds and the rows left
+// over go to a second launch with its own configuration (smaller tiles), so
+// the last round is not run a quarter full.  M when no split pays.
+int tiled_row_split(int M, int N)
+{
+    constexpr long ROUND = 512;
+    const long nbn = (N + 255) / 256, nbm = (M + 127) / 128;
+    const long tiles = nbn * nbm;
+    const long rem = tiles % ROUND;
+    if (tiles < ROUND || rem == 0 || rem > ROUND / 2) return M;
+    const long m1 = ((tiles - rem) / nbn) * 128;
+    return m1 > 0 && m1 < M ? (int)m1 : M;
+}
+
 hipError_t launch_w4a16_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                               const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                               bool fuse_delta, hipStream_t st)
 {
-    return launch_w4a16_tiled_cfg(tiled_config(M, N), A, W, S, D, C, M, N, K, g, fuse_delta, st);
+    const int cfg = tiled_config(M, N);
+    if (cfg == 2) {
+        const int m1 = tiled_row_split(M, N);
+        if (m1 < M) {
+            hipError_t e = launch_w4a16_tiled_cfg(2, A, W, S, D, C, m1, N, K, g, fuse_delta, st);
+            if (e != hipSuccess) return e;
+            const int m2 = M - m1;
+            return launch_w4a16_tiled_cfg(tiled_config(m2, N), A + (size_t)m1 * K, W, S, D,
+                                          C + (size_t)m1 * N, m2, N, K, g, fuse_delta, st);
+        }
+    }
+    return launch_w4a16_tiled_cfg(cfg, A, W, S, D, C, M, N, K, g, fuse_delta, st);
 }
 
 // Heuristic choice of the skinny configuration (also sizes the workspace).
