@@ -107,6 +107,46 @@ def test_w4a16_ragged_shapes(M, K, N, g, asym):
     _check_w4a16(c)
 
 
+# Shapes chosen to reach each kernel path (the dispatch rules live in
+# csrc/qg_w4a16.hip): the decode kernel split 8 ways with every group size and
+# both weight kinds; the decode kernel unsplit (wide N: one split already gives
+# enough workgroups); the 64x128 tiled configuration with the fused delta; the
+# 128x256 tiles with the row split (two launches).
+@pytest.mark.parametrize("M", [9, 12, 16])
+@pytest.mark.parametrize("g,asym", [(128, True), (256, True), (-1, True), (128, False), (256, False)])
+def test_w4a16_decode_kernel_splits(M, g, asym):
+    K, N = 4096, 4096
+    gg = K if g == -1 else g
+    c = synth.w4a16_case(M, K, N, gg, asym=asym, signed_scales=not asym, stream=85,
+                         case_id=M * 31 + gg + asym, name="decode-split8")
+    _check_w4a16(c)
+
+
+@pytest.mark.parametrize("M,asym", [(1, False), (5, True), (16, True)])
+def test_w4a16_decode_kernel_unsplit(M, asym):
+    c = synth.w4a16_case(M, 1024, 32768, 128, asym=asym, signed_scales=not asym, stream=86,
+                         case_id=M, name="decode-unsplit")
+    _check_w4a16(c)
+
+
+def test_w4a16_tiled_64x128_fused_delta():
+    c = synth.w4a16_case(512, 1024, 8192, 128, asym=True, stream=87, case_id=0, name="tiled-64x128")
+    _check_w4a16(c)
+
+
+def test_w4a16_tiled_row_split():
+    # M = 2048, N = 17408: 128 x 256 tiles on the first 1920 rows, the rest in
+    # a second launch; checked on sampled rows across both parts
+    M, K, N, g = 2048, 512, 17408, 128
+    c = synth.w4a16_case(M, K, N, g, asym=True, stream=88, case_id=0, name="row-split")
+    note(f"w4a16 row split M={M} K={K} N={N}")
+    got, _ = run_w4a16(c)
+    rows = np.array([0, 1, 127, 128, 1000, 1919, 1920, 1921, 2000, 2047])
+    ref = oracle.w4a16(c.A[rows], c.q, c.s, c.z, c.g)
+    assert rel_fro(got[rows], ref) <= W4A16_TOL
+    assert elementwise_guard(got[rows], ref) <= 0
+
+
 def test_w4a16_small_asym():
     c = synth.workload("w4a16-small-asym-M16-K1024-N1024-g128")
     _check_w4a16(c)
