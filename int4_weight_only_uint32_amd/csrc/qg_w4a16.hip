@@ -761,6 +761,183 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
             }
 }
 
+// ---- tiled kernel, symmetric weights, 128 x 256 tile, ordered schedule ----
+// The same tile, operands and arithmetic as w4a16_tiled_kernel<8, 4, false>
+// (its output is bit-identical), with the k-tile body laid out by hand: each
+// 32-k step reads its eight activation fragments in pairs, one pair ahead of
+// the MFMAs that use them, and dequantizes the next step's codes between
+// those MFMAs, so that LDS latency and dequantization VALU both hide under
+// matrix work.  sched_barrier fences keep the compiler from regrouping the
+// pairs.  (x & mask) | 0x6400 is one v_and_or_b32 (the compiler emits an AND
+// and an OR when both constants are literals).  Codes and scales of the next
+// tile are issued after its activations, so the end-of-tile wait leaves them
+// in flight.
+__device__ inline unsigned and_or_b32(unsigned x, unsigned m, unsigned c)
+{
+    unsigned r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+    return r;
+}
+
+template <int STEP>
+__device__ inline half8 dequant_scaled_ao(uint4v w, half2v s2, unsigned magic)
+{
+    const unsigned xa = (STEP & 1) ? w.z : w.x;
+    const unsigned xb = (STEP & 1) ? w.w : w.y;
+    const unsigned m = (STEP >= 2) ? 0x00F000F0u : 0x000F000Fu;
+    const unsigned p[4] = {and_or_b32(xa, m, magic), and_or_b32(xa >> 8, m, magic),
+                           and_or_b32(xb, m, magic), and_or_b32(xb >> 8, m, magic)};
+    unsigned out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half2v h = __builtin_bit_cast(half2v, p[i]);
+        half2v v;
+        if (STEP >= 2)
+            v = h * half2v{(_Float16)0.0625f, (_Float16)0.0625f} - half2v{(_Float16)72.f, (_Float16)72.f};
+        else
+            v = h - half2v{(_Float16)1032.f, (_Float16)1032.f};
+        out[i] = __builtin_bit_cast(unsigned, v * s2);
+    }
+    return __builtin_bit_cast(half8, uint4v{out[0], out[1], out[2], out[3]});
+}
+
+__global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
+    const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
+    uint16_t *__restrict__ C, int M, int N, int K, int g)
+{
+    constexpr int WM = 8, WN = 4, BM = 16 * WM, BN = 64 * WN, ABLK = BM / 16;
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * 128];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, kq = lane >> 4;
+    const int KT = K / KTILE;
+    const int m0 = blockIdx.y * BM;
+    const int n0 = blockIdx.x * BN + wave * 16 * WN;
+    const bool active = n0 < N;
+    // waves past the last column load valid columns (their results are not
+    // stored) so that every wave issues the same loads
+    const int n0c = active ? n0 : N - 16 * WN;
+    const int ntile0 = n0c / NTILE;
+    const int sh = 16 * (c & 1);
+
+    auto load_a = [&](int kt, int st) {
+#pragma unroll
+        for (int i = 0; i < ABLK; ++i) {
+            const int blk = wave * ABLK + i;
+            const int r = blk * 4 + (lane >> 4);
+            const int ch = (lane & 15) ^ (r & 15);
+            int row = m0 + r;
+            row = row < M ? row : M - 1;
+            const uint16_t *src = A + (size_t)row * K + kt * KTILE + ch * 8;
+            __builtin_amdgcn_global_load_lds(
+                (const void *)src,
+                (__attribute__((address_space(3))) void *)(&As[st][blk * 4 * 128]), 16, 0, 0);
+        }
+    };
+    auto a_frag = [&](const _Float16 *as, int mt, int o) {
+        const int r = 16 * mt + c;
+        const int pch = (4 * o + kq) ^ c;
+        return *reinterpret_cast<const half8 *>(as + r * 128 + pch * 8);
+    };
+    uint4v wreg[WN];
+    uint32_t sreg[WN];   // aligned scale pair holding this lane's column (half c & 1)
+    auto load_w = [&](int kt) {
+        const int k = kt < KT ? kt : KT - 1;
+        const int gi = (k * KTILE) / g;
+#pragma unroll
+        for (int t = 0; t < WN; ++t) wreg[t] = W[((size_t)(ntile0 + t) * KT + k) * 64 + lane];
+        const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + ((n0c + c) & ~1));
+#pragma unroll
+        for (int t = 0; t < WN; ++t) sreg[t] = srow[8 * t];
+    };
+
+    float4v acc[WM][WN];
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+        for (int t = 0; t < WN; ++t) acc[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
+    unsigned magic;   // 0x6400 (fp16 1024) in both halves, in a register
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+    load_a(0, 0);
+    load_w(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int st = kt & 1;
+        uint4v wc[WN];
+        half2v s2[WN];
+#pragma unroll
+        for (int t = 0; t < WN; ++t) {
+            wc[t] = wreg[t];
+            const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(sreg[t] >> sh));
+            s2[t] = half2v{sv, sv};
+            pin(wc[t]);
+        }
+        // take this tile's codes before any new load is issued (the wait for
+        // them must not cover the loads below)
+        __builtin_amdgcn_sched_barrier(0);
+        // next tile: activations first, then codes (the last tile reloads its
+        // own activations into the idle buffer, keeping the load count fixed)
+        load_a(kt + 1 < KT ? kt + 1 : kt, st ^ 1);
+        load_w(kt + 1);
+        const _Float16 *as = As[st];
+        if (active) {
+            half8 bc[WN];
+#pragma unroll
+            for (int t = 0; t < WN; ++t) bc[t] = dequant_scaled_ao<0>(wc[t], s2[t], magic);
+#define QG_SYM_STEP(O)                                                                        \
+            {                                                                                 \
+                half8 bn[WN];                                                                 \
+                half8 af[2][2];                                                               \
+                af[0][0] = a_frag(as, 0, O);                                                  \
+                af[0][1] = a_frag(as, 1, O);                                                  \
+                _Pragma("unroll") for (int p = 0; p < WM / 2; ++p) {                          \
+                    if (p + 1 < WM / 2) {                                                     \
+                        af[(p + 1) & 1][0] = a_frag(as, 2 * p + 2, O);                        \
+                        af[(p + 1) & 1][1] = a_frag(as, 2 * p + 3, O);                        \
+                    }                                                                         \
+                    _Pragma("unroll") for (int t = 0; t < WN; ++t) {                          \
+                        acc[2 * p][t] = mfma_f16(af[p & 1][0], bc[t], acc[2 * p][t]);         \
+                        acc[2 * p + 1][t] = mfma_f16(af[p & 1][1], bc[t], acc[2 * p + 1][t]); \
+                    }                                                                         \
+                    if (O < 3) bn[p] = dequant_scaled_ao<(O + 1) & 3>(wc[p], s2[p], magic);   \
+                    __builtin_amdgcn_sched_barrier(0);                                        \
+                }                                                                             \
+                if (O < 3) {                                                                  \
+                    _Pragma("unroll") for (int t = 0; t < WN; ++t) bc[t] = bn[t];             \
+                }                                                                             \
+            }
+            QG_SYM_STEP(0)
+            QG_SYM_STEP(1)
+            QG_SYM_STEP(2)
+            QG_SYM_STEP(3)
+#undef QG_SYM_STEP
+        }
+        // this wave's activation loads of the next tile have landed (only its
+        // 2 WN code and scale loads may still be in flight); the barrier then
+        // makes every wave's part visible and frees this tile's buffer
+        __builtin_amdgcn_s_waitcnt((2 * WN) | (0x7 << 4) | (0xF << 8));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the last (unused) code loads
+
+    if (!active) return;
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+        for (int t = 0; t < WN; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + 16 * mt + 4 * kq + r;
+                if (row < M) C[(size_t)row * N + n0 + 16 * t + c] = f2h(acc[mt][t][r]);
+            }
+}
+
 template <int WM, int WN, bool DELTA>
 static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
@@ -962,7 +1139,10 @@ hipError_t launch_w4a16_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W,
         return run_tiled<4, 2, false>(A, W, S, nullptr, C, M, N, K, g, st);
     }
     if (dl) return run_tiled<8, 4, true>(A, W, S, D, C, M, N, K, g, st);
-    return run_tiled<8, 4, false>(A, W, S, nullptr, C, M, N, K, g, st);
+    dim3 grid((unsigned)((N + 255) / 256), (unsigned)((M + 127) / 128));
+    hipLaunchKernelGGL(w4a16_tiled_sym_kernel, grid, dim3(256), 0, st, A,
+                       reinterpret_cast<const uint4v *>(W), S, C, M, N, K, g);
+    return hipGetLastError();
 }
 
 // Rows of the first launch when the 128 x 256 tiles would end in a partly
