@@ -147,6 +147,19 @@ def test_w4a16_tiled_row_split():
     assert elementwise_guard(got[rows], ref) <= 0
 
 
+@pytest.mark.parametrize("g,asym,flags", [(128, False, 0), (-1, False, 0), (128, True, 1)])
+def test_w4a16_tiled_128x256_symmetric(g, asym, flags):
+    # M = 1000 (ragged last tile), N = 16256 (the last workgroup's upper two
+    # waves have no columns), K = 640 (an odd number of k-tiles): 8 x 64 =
+    # 512 tiles of 128 x 256, one launch.  Symmetric weights, or asymmetric
+    # ones with the two-kernel correction, take the hand-ordered kernel.
+    M, K, N = 1000, 640, 16256
+    gg = K if g == -1 else g
+    c = synth.w4a16_case(M, K, N, gg, asym=asym, signed_scales=not asym, stream=89,
+                         case_id=gg + 2 * asym, name="tiled-128x256-sym")
+    _check_w4a16(c, flags=qg.QG_CORR_SEPARATE if flags else 0)
+
+
 def test_w4a16_small_asym():
     c = synth.workload("w4a16-small-asym-M16-K1024-N1024-g128")
     _check_w4a16(c)
