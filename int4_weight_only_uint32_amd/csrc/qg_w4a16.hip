@@ -261,19 +261,37 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const int nt0 = (cg * WV + wave) * NT;
     const int col0 = nt0 * NTILE + c;
 
-    // scale table first: its loads are the oldest in flight, so the waits
-    // for them cover nothing else
+    // scale table: its loads are issued first (the oldest in flight), and,
+    // when it fits in TB words per thread, written to LDS only after the
+    // ring's first loads are out, so its latency overlaps theirs instead of
+    // preceding them
+    constexpr int TB = 4;
+    const int gi0 = (kt_beg * KTILE) / g;
+    const int ng = n > 0 ? ((kt_end - 1) * KTILE) / g - gi0 + 1 : 0;
+    const int total = ng * (COLS / 2);
+    const bool tfast = total <= TB * 64 * WV;
+    const uint32_t *s32 = reinterpret_cast<const uint32_t *>(S) + (size_t)gi0 * (N / 2) + cg * (COLS / 2);
+    const uint32_t *d32 = DELTA ? reinterpret_cast<const uint32_t *>(D) + (size_t)gi0 * (N / 2) + cg * (COLS / 2) : nullptr;
+    uint32_t tsv[TB], tdv[TB];
     if (n > 0) {
-        const int gi0 = (kt_beg * KTILE) / g, gi1 = ((kt_end - 1) * KTILE) / g;
-        const int ng = gi1 - gi0 + 1;
-        const uint32_t *s32 = reinterpret_cast<const uint32_t *>(S) + (size_t)gi0 * (N / 2) + cg * (COLS / 2);
-        const uint32_t *d32 = DELTA ? reinterpret_cast<const uint32_t *>(D) + (size_t)gi0 * (N / 2) + cg * (COLS / 2) : nullptr;
-        for (int idx = tid; idx < ng * (COLS / 2); idx += 64 * WV) {
-            const int gl = idx / (COLS / 2), pr = idx % (COLS / 2);
-            const uint32_t s2 = s32[(size_t)gl * (N / 2) + pr];
-            const uint32_t d2 = DELTA ? d32[(size_t)gl * (N / 2) + pr] : 0u;
-            sdt[gl * COLS + 2 * pr] = (s2 & 0xFFFFu) | (d2 << 16);
-            sdt[gl * COLS + 2 * pr + 1] = (s2 >> 16) | (d2 & 0xFFFF0000u);
+        if (tfast) {
+            // unconditional, clamped: the waits for these count exactly
+#pragma unroll
+            for (int i = 0; i < TB; ++i) {
+                int idx = tid + i * 64 * WV;
+                idx = idx < total ? idx : total - 1;
+                const int gl = idx / (COLS / 2), pr = idx % (COLS / 2);
+                tsv[i] = s32[(size_t)gl * (N / 2) + pr];
+                tdv[i] = DELTA ? d32[(size_t)gl * (N / 2) + pr] : 0u;
+            }
+        } else {
+            for (int idx = tid; idx < total; idx += 64 * WV) {
+                const int gl = idx / (COLS / 2), pr = idx % (COLS / 2);
+                const uint32_t s2 = s32[(size_t)gl * (N / 2) + pr];
+                const uint32_t d2 = DELTA ? d32[(size_t)gl * (N / 2) + pr] : 0u;
+                sdt[gl * COLS + 2 * pr] = (s2 & 0xFFFFu) | (d2 << 16);
+                sdt[gl * COLS + 2 * pr + 1] = (s2 >> 16) | (d2 & 0xFFFF0000u);
+            }
         }
     }
 
@@ -353,6 +371,20 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
         for (int i = 0; i < P; ++i) {
             const int kt = kt_beg + i;
             load(kt < last ? kt : last, ra[i], rw[i]);
+            // slot by slot, in the order the loop refills them (the waits in
+            // the loop are computed for both orders)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (tfast) {
+#pragma unroll
+            for (int i = 0; i < TB; ++i) {
+                const int idx = tid + i * 64 * WV;
+                if (idx < total) {
+                    const int gl = idx / (COLS / 2), pr = idx % (COLS / 2);
+                    sdt[gl * COLS + 2 * pr] = (tsv[i] & 0xFFFFu) | (tdv[i] << 16);
+                    sdt[gl * COLS + 2 * pr + 1] = (tsv[i] >> 16) | (tdv[i] & 0xFFFF0000u);
+                }
+            }
         }
         int j = 0;
         for (; j + P <= n; j += P) {
