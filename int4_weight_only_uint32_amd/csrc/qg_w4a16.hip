@@ -991,17 +991,30 @@ static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t
 // MFMAs as exact fp16 subnormals (no per-element dequantization, which would
 // otherwise cost more VALU than the MFMAs take), the group sums of A come from
 // MFMAs against an all-ones operand, and scale and delta are applied once per
-// k-tile on the fp32 accumulators.  A k-tile of A (64 rows, 16 KB; wave w
-// fetches rows 16w .. 16w + 15 row-contiguously) is shared through two LDS
-// buffers with one barrier per k-tile; A, codes, scales and deltas of the
-// next P k-tiles wait in a register ring.
-template <int P, bool DELTA>
+// k-tile on the fp32 accumulators.  Pipeline: MID_STAGES k-tiles in flight.
+// A k-tile of A (64 rows, 16 KB) goes straight from global memory to one of
+// MID_STAGES LDS buffers (wave w fills rows 16w .. 16w + 15; 16-byte chunk ch
+// of row r lands at position ch ^ (r % 16)); codes, scales and deltas of the
+// same k-tile go to the matching slot of a register ring.  Each k-tile starts
+// with a wait that leaves the later k-tiles' loads in flight and one barrier,
+// after which the slot used by the previous k-tile is refilled.
+constexpr int MID_STAGES = 4;
+
+constexpr unsigned waitcnt_vm(int n)
+{
+    // s_waitcnt immediate: vmcnt n (6 bits, split), expcnt and lgkmcnt not waited
+    return (unsigned)((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int SG, bool DELTA>
 __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g)
 {
     constexpr int WM = 2, WN = 2, BM = 64, BN = 64;
-    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * KTILE];
+    constexpr int L = 4 + WN + WN + (DELTA ? WN : 0);     // loads per thread and k-tile
+    static_assert((SG - 2) * L < 64, "vmcnt holds 6 bits");
+    extern __shared__ __attribute__((aligned(16))) _Float16 Asm[];   // [SG][BM * KTILE]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1013,28 +1026,33 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
     const int col0 = ntile0 * NTILE + c;
     const int sh = 16 * (c & 1);
 
-    // A rows 16w + 4i + lane/16 (i = 0..3), 16-byte chunk lane%16, stored at
-    // position chunk ^ (row % 16); rows past M read row M-1 (never stored)
-    const uint4v *asrc[4];
-    int adst[4];
+    // direct global -> LDS loads: one wave instruction fills 1 KB = 4 rows;
+    // rows past M read row M-1 (their results are never stored)
+    auto load_a = [&](int kt, int st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wave + 4 * i + (lane >> 4);
-        int row = m0 + r;
-        row = row < M ? row : M - 1;
-        asrc[i] = reinterpret_cast<const uint4v *>(A + (size_t)row * K) + (lane & 15);
-        adst[i] = r * KTILE + 8 * ((lane & 15) ^ (r & 15));
-    }
+        for (int i = 0; i < 4; ++i) {
+            const int blk = wave * 4 + i;
+            const int r = blk * 4 + (lane >> 4);
+            const int ch = (lane & 15) ^ (r & 15);
+            int row = m0 + r;
+            row = row < M ? row : M - 1;
+            const uint16_t *src = A + (size_t)row * K + kt * KTILE + ch * 8;
+            __builtin_amdgcn_global_load_lds(
+                (const void *)src,
+                (__attribute__((address_space(3))) void *)(Asm + st * BM * KTILE + blk * 4 * KTILE), 16, 0, 0);
+        }
+    };
     const uint4v *wbase = W + (size_t)ntile0 * KT * 64 + lane;
-
-    uint4v ra[P][4], rw[P][WN];
-    uint32_t rs[P][WN], rd[P][WN];
+    uint4v rw[SG][WN];
+    uint32_t rs[SG][WN], rd[SG][WN];   // aligned scale / delta pairs (half c & 1)
+    // every load of k-tile kt (clamped: the count per k-tile is fixed, which
+    // the waits rely on)
     auto load = [&](int kt, int slot) {
+        const int k = kt < KT ? kt : KT - 1;
+        load_a(k, slot);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ra[slot][i] = asrc[i][kt * (KTILE / 8)];
-#pragma unroll
-        for (int t = 0; t < WN; ++t) rw[slot][t] = wbase[((size_t)t * KT + kt) * 64];
-        const int gi = (kt * KTILE) / g;
+        for (int t = 0; t < WN; ++t) rw[slot][t] = wbase[((size_t)t * KT + k) * 64];
+        const int gi = (k * KTILE) / g;
         const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
 #pragma unroll
         for (int t = 0; t < WN; ++t) rs[slot][t] = srow[8 * t];
@@ -1054,21 +1072,16 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
     const float4v fzero = {0.f, 0.f, 0.f, 0.f};
 
     auto step = [&](int kt, int slot) {
-        const int buf = kt & 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4v *>(&As[buf][adst[i]]) = ra[slot][i];
-        CodeOps ops[WN];
-        float s[WN], d[WN];
-#pragma unroll
-        for (int t = 0; t < WN; ++t) {
-            ops[t] = split_codes(rw[slot][t]);
-            s[t] = h2f((uint16_t)(rs[slot][t] >> sh));
-            d[t] = DELTA ? h2f((uint16_t)(rd[slot][t] >> sh)) : 0.f;
-        }
-        const int kn = kt + P < KT ? kt + P : KT - 1;
-        load(kn, slot);
-        __syncthreads();
-        const _Float16 *as = As[buf];
+        // this thread's loads of k-tile kt have landed (the SG - 2 later
+        // k-tiles' may still be in flight); the barrier makes every wave's
+        // part visible and frees the slot of k-tile kt - 1
+        constexpr unsigned WAIT = waitcnt_vm((SG - 2) * L);
+        __builtin_amdgcn_s_waitcnt(WAIT);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        load(kt + SG - 1, (slot + SG - 1) % SG);
+        const _Float16 *as = Asm + slot * BM * KTILE;
 #pragma unroll
         for (int mt = 0; mt < WM; ++mt) {
             const int r = 32 * mw + 16 * mt + c;
@@ -1082,12 +1095,15 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
             asum = mfma_f16(a[3], ones, asum);
 #pragma unroll
             for (int t = 0; t < WN; ++t) {
-                float4v xl = mfma_f16(a[0], ops[t].lo[0], fzero);
-                xl = mfma_f16(a[1], ops[t].lo[1], xl);
-                float4v xh = mfma_f16(a[2], ops[t].hi[0], fzero);
-                xh = mfma_f16(a[3], ops[t].hi[1], xh);
-                const float c16 = s[t] * 0x1p24f, c1 = s[t] * 0x1p20f;
-                const float c2 = DELTA ? (d[t] - 8.0f * s[t]) : (-8.0f * s[t]);
+                const CodeOps ops = split_codes(rw[slot][t]);
+                const float s = h2f((uint16_t)(rs[slot][t] >> sh));
+                const float d = DELTA ? h2f((uint16_t)(rd[slot][t] >> sh)) : 0.f;
+                float4v xl = mfma_f16(a[0], ops.lo[0], fzero);
+                xl = mfma_f16(a[1], ops.lo[1], xl);
+                float4v xh = mfma_f16(a[2], ops.hi[0], fzero);
+                xh = mfma_f16(a[3], ops.hi[1], xh);
+                const float c16 = s * 0x1p24f, c1 = s * 0x1p20f;
+                const float c2 = DELTA ? (d - 8.0f * s) : (-8.0f * s);
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     float v = __builtin_fmaf(c16, xl[r4], acc[mt][t][r4]);
@@ -1099,21 +1115,23 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
     };
 
 #pragma unroll
-    for (int i = 0; i < P; ++i) load(i < KT ? i : KT - 1, i);
+    for (int i = 0; i < SG - 1; ++i) {
+        load(i, i);
+        __builtin_amdgcn_sched_barrier(0);   // k-tile by k-tile, as the loop refills
+    }
     int kt = 0;
-    for (; kt + P <= KT; kt += P) {
+    for (; kt + SG <= KT; kt += SG) {
 #pragma unroll
-        for (int i = 0; i < P; ++i) {
+        for (int i = 0; i < SG; ++i) {
             step(kt + i, i);
-            // keep each refill ahead of the loop's back edge (see the skinny
-            // kernel) and the next slot's work out of this step
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
-    for (int i = 0; i < P - 1; ++i)
+    for (int i = 0; i < SG - 1; ++i)
         if (kt + i < KT) step(kt + i, i);
+    __builtin_amdgcn_s_waitcnt(0);   // the last (unused) loads
 
 #pragma unroll
     for (int mt = 0; mt < WM; ++mt)
@@ -1132,7 +1150,8 @@ static hipError_t run_mid(const uint16_t *A, const uint32_t *W, const uint16_t *
                           hipStream_t st)
 {
     dim3 grid((unsigned)(N / 64), (unsigned)((M + 63) / 64));
-    hipLaunchKernelGGL((w4a16_mid_kernel<2, DELTA>), grid, dim3(256), 0, st, A,
+    const size_t lds = (size_t)MID_STAGES * 64 * KTILE * sizeof(_Float16);
+    hipLaunchKernelGGL((w4a16_mid_kernel<MID_STAGES, DELTA>), grid, dim3(256), lds, st, A,
                        reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g);
     return hipGetLastError();
 }
