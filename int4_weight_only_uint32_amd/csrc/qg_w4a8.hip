@@ -32,7 +32,7 @@ namespace qg {
 // ring whose loads are unconditional (indices clamped to the last tile), so
 // every wait covers only the slot being consumed -- a scale loaded just before
 // its use would wait for every load issued before it.
-template <int NT, int P, bool DEBUG>
+template <int NT, int P, bool DEBUG, bool G1>
 __global__ __launch_bounds__(256, 2) void w4a8_kernel(
     const int8_t *__restrict__ Aq, const float *__restrict__ a_scale,
     const uint4v *__restrict__ Wall, const uint16_t *__restrict__ Sall,
@@ -136,31 +136,41 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
             alo[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 0, kq)]);
             ahi[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 1, kq)]);
         }
+        // G1 (one k-tile per group): each tile's group sum starts from a zero
+        // MFMA operand, so nothing is reset and nothing stays live across tiles
+        const int4v zero4 = {0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                acci[mt][t] = mfma_i8(alo[mt], b[t].op[0], acci[mt][t]);
+                acci[mt][t] = mfma_i8(alo[mt], b[t].op[0], G1 ? zero4 : acci[mt][t]);
                 acci[mt][t] = mfma_i8(ahi[mt], b[t].op[1], acci[mt][t]);
             }
-        if (((kt + 1) * KTILE) % g == 0) {        // end of a weight group
+        if (G1 || ((kt + 1) * KTILE) % g == 0) {   // end of a weight group
             const int gi = (kt * KTILE) / g;
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT; ++t) {
+                // acci is exactly 16x the group's integer product (|acci| < 2^24,
+                // so its fp32 conversion is exact); scaling it by s/16 (exact)
+                // gives the same fma result as scaling acci >> 4 by s
+                const float sv16 = sv[t] * 0.0625f;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const int4v qv = acci[mt][t] >> 4;   // exact: terms are multiples of 16
-                    accf[mt][t] += sv[t] * __builtin_convertvector(qv, float4v);
-                    acci[mt][t] = int4v{0, 0, 0, 0};
                     if (DEBUG) {
+                        const int4v qv = acci[mt][t] >> 4;   // exact: terms are multiples of 16
+                        accf[mt][t] += sv[t] * __builtin_convertvector(qv, float4v);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int row = m0 + 16 * mt + 4 * kq + r;
                             if (row < r1)
                                 acc_debug[((size_t)row * G + gi) * N + col0 + 16 * t] = qv[r];
                         }
+                    } else {
+                        accf[mt][t] += sv16 * __builtin_convertvector(acci[mt][t], float4v);
                     }
+                    if (!G1) acci[mt][t] = int4v{0, 0, 0, 0};
                 }
+            }
         }
     };
 
@@ -194,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
         }
 }
 
-template <int NT, int P, bool DEBUG>
+template <int NT, int P, bool DEBUG, bool G1>
 static hipError_t run_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
                            const uint16_t *S, const int32_t *offsets, int E, int M_total,
                            int max_rows, int N, int K, int g, uint16_t *C, int32_t *acc_debug,
@@ -202,7 +212,7 @@ static hipError_t run_w4a8(const int8_t *Aq, const float *a_scale, const uint32_
 {
     const int NT16 = N / NTILE;
     dim3 grid((unsigned)((NT16 + 4 * NT - 1) / (4 * NT)), (unsigned)((max_rows + 63) / 64), (unsigned)E);
-    hipLaunchKernelGGL((w4a8_kernel<NT, P, DEBUG>), grid, dim3(256), 0, st, Aq, a_scale,
+    hipLaunchKernelGGL((w4a8_kernel<NT, P, DEBUG, G1>), grid, dim3(256), 0, st, Aq, a_scale,
                        reinterpret_cast<const uint4v *>(W), S, offsets, M_total, N, K, g, C,
                        acc_debug);
     return hipGetLastError();
@@ -215,11 +225,12 @@ hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W
 {
     // N % 128 == 0 -> the n-tile count is a multiple of 8: NT = 2 tiles the
     // columns exactly (4 waves x 2 n-tiles = 128 columns per workgroup)
+    const bool g1 = g == KTILE;
     if (acc_debug)
-        return run_w4a8<2, 3, true>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C,
-                                    acc_debug, st);
-    return run_w4a8<2, 3, false>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C,
-                                 nullptr, st);
+        return g1 ? run_w4a8<2, 3, true, true>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)
+                  : run_w4a8<2, 3, true, false>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
+    return g1 ? run_w4a8<2, 3, false, true>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st)
+              : run_w4a8<2, 3, false, false>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st);
 }
 
 } // namespace qg
