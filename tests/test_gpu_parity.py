@@ -160,6 +160,18 @@ def test_w4a16_tiled_128x256_symmetric(g, asym, flags):
     _check_w4a16(c, flags=qg.QG_CORR_SEPARATE if flags else 0)
 
 
+@pytest.mark.parametrize("K,g,asym", [(256, 128, True), (384, 128, False), (640, -1, True)])
+def test_w4a16_mid_kernel_short_k(K, g, asym):
+    # M = 200 on N = 1024 takes the 64 x 64 mid kernel, whose pipeline keeps
+    # several k-tiles in flight: fewer k-tiles (2, 3, 5) than its stages plus
+    # a ragged last row tile
+    M, N = 200, 1024
+    gg = K if g == -1 else g
+    c = synth.w4a16_case(M, K, N, gg, asym=asym, signed_scales=not asym, stream=90,
+                         case_id=K + gg + asym, name="mid-short-k")
+    _check_w4a16(c)
+
+
 def test_w4a16_small_asym():
     c = synth.workload("w4a16-small-asym-M16-K1024-N1024-g128")
     _check_w4a16(c)
