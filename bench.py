@@ -15,6 +15,10 @@ Prints ONE JSON line on stdout:
              column) per launch / average launch duration (HIP events on the
              launch stream over the timed region)
   cpu_baseline  the CPU oracle timed on this host on the same workload
+  achievable what this GPU sustains in the same run (an HBM streaming-read
+             probe at the primary weight size and at 1 GiB, fp16 and int8 MFMA
+             loop probes, best of a small launch-shape sweep each); every
+             fraction is given against it beside the published peak
   cases      every other configuration measured the same way (decode shapes,
              mid-batch, prefill M=4096, grouped W4A8, the load-time pack)
 Logs go to stderr.
@@ -49,6 +53,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cases", default="all", help="comma list of case names, or 'all'")
     p.add_argument("--eager", action="store_true", help="time plain launches instead of a graph replay")
+    p.add_argument("--no-probes", action="store_true", help="skip the achievable-peak probes")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a 256 MiB device-to-device copy 20 times (counter calibration)")
     return p.parse_args()
@@ -214,6 +219,56 @@ def measured_traffic():
     return rec["traffic_bytes"] if sha == rec["source_sha256_16"] else None
 
 
+def achievable(primary_bytes):
+    """Best sustained rates of the probe kernels (libqgprobe.so) over a small
+    sweep of launch shapes, HIP events on the launch stream."""
+    import torch
+    from int4_weight_only_uint32_amd import probe
+    res = {"sweeps": {}}
+
+    def sweep(key, fn, shapes):
+        vals = {}
+        for sh in shapes:
+            vals["/".join(map(str, sh))] = fn(*sh)
+        res["sweeps"][key] = vals
+        best = max(vals, key=vals.get)
+        return vals[best], best
+
+    # HBM reads, rotated over copies so nothing is served from the caches
+    for key, size in (("hbm_read_gbps_primary_size", primary_bytes), ("hbm_read_gbps_1GiB", 1 << 30)):
+        size = size // 1024 * 1024
+        n = max(2, math.ceil(ROTATE_BYTES / size))
+        bufs = [torch.ones(size, dtype=torch.uint8, device="cuda") for _ in range(n)]
+        best, at = sweep(key, lambda G, U: probe.hbm_read_gbps(bufs, G, U),
+                         [(G, U) for G in (1024, 2048, 4096) for U in (1, 2, 4)])
+        res[key] = best
+        res[key + "_at"] = "workgroups/unroll " + at
+        del bufs
+        torch.cuda.empty_cache()
+    # about 1 ms per launch at the published rates
+    for key, fn, shapes in (
+            ("mfma_f16_16x16x32_tflops", lambda G: probe.mfma_f16_tflops(16, G, 2048 * 1024 // G), [(512,), (1024,), (2048,)]),
+            ("mfma_f16_32x32x16_tflops", lambda G: probe.mfma_f16_tflops(32, G, 4096 * 1024 // G), [(512,), (1024,), (2048,)]),
+            ("mfma_i8_16x16x64_tops", lambda G: probe.mfma_i8_tops(G, 2048 * 1024 // G), [(512,), (1024,), (2048,)])):
+        best, at = sweep(key, fn, shapes)
+        res[key] = best
+        res[key + "_at"] = "workgroups " + at
+    res["hbm_read_gbps"] = max(res["hbm_read_gbps_primary_size"], res["hbm_read_gbps_1GiB"])
+    res["mfma_f16_tflops"] = max(res["mfma_f16_16x16x32_tflops"], res["mfma_f16_32x32x16_tflops"])
+    return res
+
+
+def add_fractions(r, ach):
+    """Fractions of one case against the measured achievable rates."""
+    if ach is None:
+        return
+    r["frac_achievable_hbm_weight"] = r["weight_gbps"] / ach["hbm_read_gbps"]
+    if "tflops" in r:
+        r["frac_achievable_fp16_mfma"] = r["tflops"] / ach["mfma_f16_tflops"]
+    if "tops" in r:
+        r["frac_achievable_int8_mfma"] = r["tops"] / ach["mfma_i8_16x16x64_tops"]
+
+
 def cpu_baseline(case):
     """The oracle (fp64 dequant + naive loop, OpenMP) on the primary workload,
     run whole; returns TFLOP/s and the thread count it used."""
@@ -288,6 +343,13 @@ def main():
                 log(json.dumps(r))
                 cases.append(r)
 
+    ach = None
+    if not args.no_probes:
+        ach = achievable(primary["weight_bytes"])
+        log(json.dumps(ach))
+        for r in [primary] + cases:
+            add_fractions(r, ach)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(pcase)
@@ -321,7 +383,10 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(),
                      "kernel": "w4a16_decode_kernel (split-K, fused delta)",
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-                     "algorithmic_bytes_per_launch": primary["weight_bytes"]},
+                     "algorithmic_bytes_per_launch": primary["weight_bytes"],
+                     "achievable": ach["hbm_read_gbps_primary_size"] if ach else None,
+                     "frac_of_achievable": achieved / ach["hbm_read_gbps_primary_size"] if ach else None},
+        "achievable": ach,
         "cpu_baseline": cpu,
         "cases": cases,
     }
@@ -329,6 +394,7 @@ def main():
     if prefill:
         out["prefill_M4096"] = {"tflops": prefill[0]["tflops"],
                                 "pct_fp16_mfma": prefill[0]["pct_fp16_mfma"],
+                                "frac_achievable_fp16_mfma": prefill[0].get("frac_achievable_fp16_mfma"),
                                 "us_per_call": prefill[0]["us_per_call"]}
     print(json.dumps(out), flush=True)
 

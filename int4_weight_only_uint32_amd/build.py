@@ -1,4 +1,5 @@
-"""Build the HIP library libqgemm.so in-tree for gfx950 with hipcc."""
+"""Build the HIP libraries in-tree for gfx950 with hipcc: libqgemm.so (the
+GEMM library) and libqgprobe.so (achievable-peak probes for the benchmark)."""
 import glob
 import os
 import subprocess
@@ -7,6 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqgemm.so")
+PROBE_LIB = os.path.join(HERE, "libqgprobe.so")
+PROBE_SRC = [os.path.join(HERE, "probe", "qg_probe.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -20,9 +23,9 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "qg_api.cpp")]
 
 
-def build(verbose=False):
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(HERE, "..", "include")] + sources() + ["-o", tmp]
+def _hipcc(srcs, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(HERE, "..", "include")] + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -31,11 +34,17 @@ def build(verbose=False):
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
     if res.returncode != 0:
         sys.stderr.write(err + "\n")
-        raise RuntimeError("hipcc failed building libqgemm.so")
+        raise RuntimeError("hipcc failed building " + os.path.basename(out))
     if verbose and err.strip():
         sys.stderr.write(err + "\n")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose=False):
+    """Build both libraries; returns the path of libqgemm.so."""
+    _hipcc(PROBE_SRC, PROBE_LIB, verbose)
+    return _hipcc(sources(), LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -16,8 +16,8 @@ P = ctypes.c_void_p
 FAKE = P(0x10000)     # never dereferenced: validation fails (or the device check does) first
 
 
-def _declared():
-    txt = open(HEADER).read()
+def _declared(header=HEADER):
+    txt = open(header).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", txt)) - {"defined"})
 
@@ -33,6 +33,25 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert sorted(qg.EXPORTED) == _declared()
+
+
+def test_probe_library_exports_every_declared_symbol():
+    from int4_weight_only_uint32_amd import probe
+    L = probe.lib()
+    names = _declared(os.path.join(ROOT, "include", "qgprobe.h"))
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(probe.EXPORTED) == names
+    # host-side argument checks: rejected before any launch
+    assert L.qgprobe_mfma_f16(8, FAKE, 1, 1, None) == 1
+    assert L.qgprobe_mfma_f16(16, FAKE, 0, 1, None) == 1
+    assert L.qgprobe_hbm_read(FAKE, 4096, FAKE, 1, 3, None) == 1
+    assert L.qgprobe_hbm_read(FAKE, 100, FAKE, 1, 2, None) == 1
+    assert L.qgprobe_mfma_flops(16, 2, 3) == 16 * 16 * 32 * 2 * 16 * 3 * 2 * 4
+    assert L.qgprobe_mfma_flops(32, 2, 3) == 32 * 32 * 16 * 2 * 4 * 3 * 2 * 4
+    assert L.qgprobe_mfma_flops(64, 2, 3) == 16 * 16 * 64 * 2 * 16 * 3 * 2 * 4
+    assert L.qgprobe_mfma_flops(7, 2, 3) == 0
+    assert L.qgprobe_mfma_i8(FAKE, 0, 1, None) == 1
 
 
 def test_status_strings():
