@@ -467,15 +467,24 @@ int decode_max_groups(int K, int g, int nsplit)
     return (span + per_group - 1) / per_group + 1;
 }
 
-// Split count of the decode kernel: the smallest power of two giving at least
-// 512 workgroups (two per CU), keeping >= 2 k-tiles per split and <= 16
-// splits; more splits while one split's scale table would exceed 32 KB of LDS.
+// Split count of the decode kernel.  All workgroups are resident at once, and
+// a CU holding one workgroup more than the others finishes last, so the count
+// that keeps every CU at <= 2 workgroups (512 slots on 256 CUs) is taken when
+// it still fills >= 7/8 of the slots (at K = 17408, N = 5120: 6 splits, 480
+// workgroups, 6-12 % faster than 8 splits and 640 workgroups).  Otherwise the
+// smallest power of two giving at least 512 workgroups.  Both keep >= 2
+// k-tiles per split and <= 16 splits; more splits while one split's scale
+// table would exceed 32 KB of LDS.
 int decode_splits(int N, int K)
 {
     const int KT = K / KTILE, ncg = N / decode::COLS;
     int ns = 1;
     if ((size_t)ncg * sizeof(unsigned) > W4A16_WS_COUNTER_BYTES) return 1;   // no counter for it
-    while (ns < 16 && (long)ncg * ns < 512 && KT / (2 * ns) >= 2) ns *= 2;
+    const int fit = 512 / ncg;
+    if (fit >= 2 && fit <= 16 && ncg * fit >= 448 && KT / fit >= 2)
+        ns = fit;
+    else
+        while (ns < 16 && (long)ncg * ns < 512 && KT / (2 * ns) >= 2) ns *= 2;
     while (ns < 1024 && (size_t)decode_max_groups(K, KTILE, ns) * decode::COLS * 4 > 32768) ns *= 2;
     return ns;
 }

@@ -122,6 +122,19 @@ def test_w4a16_decode_kernel_splits(M, g, asym):
     _check_w4a16(c)
 
 
+# N = 5120: 80 workgroup column groups, split 6 ways (480 workgroups, at most
+# two per CU) with uneven k-ranges (5 or 6 k-tiles at K = 4096, 4 or 5 at 3584)
+@pytest.mark.parametrize("M,K", [(16, 4096), (9, 3584)])
+@pytest.mark.parametrize("g,asym", [(128, True), (256, False), (-1, True)])
+def test_w4a16_decode_kernel_six_splits(M, K, g, asym):
+    N = 5120
+    gg = K if g == -1 else g
+    note(f"decode six splits M={M} K={K} N={N} g={gg} asym={asym}")
+    c = synth.w4a16_case(M, K, N, gg, asym=asym, signed_scales=not asym, stream=93,
+                         case_id=M * 7 + K + gg, name="decode-split6")
+    _check_w4a16(c)
+
+
 @pytest.mark.parametrize("M,asym", [(1, False), (5, True), (16, True)])
 def test_w4a16_decode_kernel_unsplit(M, asym):
     c = synth.w4a16_case(M, 1024, 32768, 128, asym=asym, signed_scales=not asym, stream=86,
