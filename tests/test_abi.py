@@ -137,10 +137,13 @@ CTR = 65536   # QG_W4A16_WS_COUNTER_BYTES
 
 def test_decode_workspace_size():
     # M <= 16: the fixed counter region + fp32 partials (16 rows x 64 columns
-    # per split per 64-column group).  Splits: the smallest power of two giving
-    # >= 512 workgroups with >= 2 k-tiles per split.
+    # per split per 64-column group).  Splits: the most that keep <= 512
+    # workgroups (two per CU) when that fills >= 448 of them, else the smallest
+    # power of two giving >= 512 workgroups; >= 2 k-tiles per split.
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 17408, 5120, 128) == CTR + 272 * 2 * 4096
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 9, 5120, 17408, 128) == CTR + 80 * 8 * 4096
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 9, 5120, 17408, 128) == CTR + 80 * 6 * 4096
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 4096, 4096, 128) == CTR + 64 * 8 * 4096
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 12288, 4096, 128) == CTR + 192 * 4 * 4096
     # small M on a narrow weight, and small problems, run the skinny kernel
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 8, 5120, 17408, 128) == 0
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1024, 128) == 0
