@@ -475,13 +475,20 @@ int decode_max_groups(int K, int g, int nsplit)
 // smallest power of two giving at least 512 workgroups.  Both keep >= 2
 // k-tiles per split and <= 16 splits; more splits while one split's scale
 // table would exceed 32 KB of LDS.
+// The two-per-CU split count when it applies (see decode_splits), else 0.
+static int decode_balanced_splits(int N, int K)
+{
+    const int KT = K / KTILE, ncg = N / decode::COLS;
+    const int fit = 512 / ncg;
+    return (fit >= 2 && fit <= 16 && ncg * fit >= 448 && KT / fit >= 2) ? fit : 0;
+}
+
 int decode_splits(int N, int K)
 {
     const int KT = K / KTILE, ncg = N / decode::COLS;
     int ns = 1;
     if ((size_t)ncg * sizeof(unsigned) > W4A16_WS_COUNTER_BYTES) return 1;   // no counter for it
-    const int fit = 512 / ncg;
-    if (fit >= 2 && fit <= 16 && ncg * fit >= 448 && KT / fit >= 2)
+    if (const int fit = decode_balanced_splits(N, K))
         ns = fit;
     else
         while (ns < 16 && (long)ncg * ns < 512 && KT / (2 * ns) >= 2) ns *= 2;
@@ -492,19 +499,27 @@ int decode_splits(int N, int K)
 // Decode workspace: the fixed counter region (W4A16_WS_COUNTER_BYTES, shared
 // by every W4A16 layout and written by nothing but the counters), then the
 // partial-sum slots.  0 when the shape is not split.
-// Whether M <= 16 runs the decode kernel rather than the skinny one.  Measured
-// on MI355X: the decode kernel wins whenever two splits give enough
-// workgroups (wide N) and for 8 < M <= 16 on large weights (sharing the
-// activation tile matters most there); the skinny kernel, which splits K
-// between the waves of a workgroup and needs no cross-workgroup step, wins
-// for small M on narrow weights and for small problems, where the split-K
-// epilogue is a larger share of the time.
+// Whether M <= 16 runs the decode kernel rather than the skinny one (which
+// splits K between the 8 waves of a workgroup of 32 columns and needs no
+// cross-workgroup step).  Measured on MI355X (M = 4-16, interleaved repeats):
+// * two or fewer decode splits (wide N): the decode kernel;
+// * more than 256 skinny workgroups (some CUs hold two, the rest one) on
+//   weights of >= 32 M elements: the decode kernel (K = 4096: N = 10240
+//   9.6 against 13.2 us, N = 12288 12.0 against 13.9);
+// * otherwise the decode kernel only when the skinny kernel leaves CUs idle
+//   (< 256 workgroups) and each decode split still streams >= 16 k-tiles
+//   (K = 16384, N = 4096: 14.8 against 17.4 us; K = 17408, N = 5120); with
+//   shorter splits its fixed costs (scale table, split-K epilogue) lose
+//   (K = 4096, N = 4096-8192: 9.2-10 against 7.2-8.5 us; K = N = 8192: 12.7
+//   against 11.7).
 bool use_decode_kernel(int M, int N, int K)
 {
     if (M > 16 || N % decode::COLS) return false;
     const int ns = decode_splits(N, K);
     if (ns <= 2) return true;
-    return M > 8 && (long long)K * N >= (1ll << 24);
+    const long skinny_wgs = N / 32;
+    if (skinny_wgs > 256) return (long long)K * N >= (1ll << 25);
+    return skinny_wgs < 256 && (K / KTILE) / ns >= 16;
 }
 
 size_t decode_workspace_bytes(int M, int N, int K)

@@ -142,10 +142,13 @@ def test_decode_workspace_size():
     # power of two giving >= 512 workgroups; >= 2 k-tiles per split.
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 17408, 5120, 128) == CTR + 272 * 2 * 4096
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 9, 5120, 17408, 128) == CTR + 80 * 6 * 4096
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 4096, 4096, 128) == CTR + 64 * 8 * 4096
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 4096, 16384, 128) == CTR + 64 * 8 * 4096
+    # short decode splits lose to the skinny kernel, which needs none
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 4096, 4096, 128) == 0
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 12288, 4096, 128) == CTR + 192 * 4 * 4096
-    # small M on a narrow weight, and small problems, run the skinny kernel
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 8, 5120, 17408, 128) == 0
+    # at K = 17408, N = 5120 the decode kernel runs at every M <= 16 (splits
+    # of 22-23 k-tiles); small problems run the skinny kernel
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 8, 5120, 17408, 128) == CTR + 80 * 6 * 4096
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1024, 128) == 0
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 17, 5120, 17408, 128) == 0     # skinny path
     # a K range too short to split needs none

@@ -108,14 +108,15 @@ def test_w4a16_ragged_shapes(M, K, N, g, asym):
 
 
 # Shapes chosen to reach each kernel path (the dispatch rules live in
-# csrc/qg_w4a16.hip): the decode kernel split 8 ways with every group size and
-# both weight kinds; the decode kernel unsplit (wide N: one split already gives
-# enough workgroups); the 64x128 tiled configuration with the fused delta; the
-# 128x256 tiles with the row split (two launches).
-@pytest.mark.parametrize("M", [9, 12, 16])
+# csrc/qg_w4a16.hip): the decode kernel split 8 ways (16 k-tiles per split)
+# with every group size and both weight kinds; the decode kernel unsplit (wide
+# N: one split already gives enough workgroups); the 64x128 tiled
+# configuration with the fused delta; the 128x256 tiles with the row split
+# (two launches).
+@pytest.mark.parametrize("M", [9, 16])
 @pytest.mark.parametrize("g,asym", [(128, True), (256, True), (-1, True), (128, False), (256, False)])
 def test_w4a16_decode_kernel_splits(M, g, asym):
-    K, N = 4096, 4096
+    K, N = 16384, 4096
     gg = K if g == -1 else g
     c = synth.w4a16_case(M, K, N, gg, asym=asym, signed_scales=not asym, stream=85,
                          case_id=M * 31 + gg + asym, name="decode-split8")
@@ -123,8 +124,9 @@ def test_w4a16_decode_kernel_splits(M, g, asym):
 
 
 # N = 5120: 80 workgroup column groups, split 6 ways (480 workgroups, at most
-# two per CU) with uneven k-ranges (5 or 6 k-tiles at K = 4096, 4 or 5 at 3584)
-@pytest.mark.parametrize("M,K", [(16, 4096), (9, 3584)])
+# two per CU) with uneven k-ranges (16 or 17 k-tiles at K = 12800, 17 or 18 at
+# 13312)
+@pytest.mark.parametrize("M,K", [(16, 12800), (9, 13312)])
 @pytest.mark.parametrize("g,asym", [(128, True), (256, False), (-1, True)])
 def test_w4a16_decode_kernel_six_splits(M, K, g, asym):
     N = 5120

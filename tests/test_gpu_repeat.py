@@ -32,7 +32,7 @@ def _device():
 # mid-size M, 64x128 tiles with the fused delta, 128x256 symmetric tiles with
 # the row split, and the separate correction launch
 CASES = [
-    (16, 4096, 4096, 128, True, 0),
+    (16, 16384, 4096, 128, True, 0),
     (4, 1024, 32768, 128, False, 0),
     (40, 2048, 1024, 128, True, 0),
     (256, 4096, 2048, 256, True, 0),
