@@ -1014,8 +1014,15 @@ static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t
 // latency exposed.  The arithmetic is the decode kernel's: codes enter the
 // MFMAs as exact fp16 subnormals (no per-element dequantization, which would
 // otherwise cost more VALU than the MFMAs take), the group sums of A come from
-// MFMAs against an all-ones operand, and scale and delta are applied once per
-// k-tile on the fp32 accumulators.  Pipeline: MID_STAGES k-tiles in flight.
+// MFMAs against an all-ones operand, and scale and delta are applied on the
+// fp32 accumulators -- once per weight group: the MFMAs accumulate a group's
+// raw sums (low-nibble, high-nibble and activation sums apart) across its
+// k-tiles, so a group of 2 k-tiles (g = 256) costs half the scaling FMAs of
+// per-k-tile scaling and one group over all of K (g = K) almost none (the
+// loop is issue-bound: 24 MFMAs against ~110 VALU instructions per k-tile and
+// wave with per-k-tile scaling).  GK selects the form: 1 = every k-tile is
+// scaled on its own (any g), 2 = groups of two k-tiles (g = 256), 0 = one
+// group (g = K).  Pipeline: MID_STAGES k-tiles in flight.
 // A k-tile of A (64 rows, 16 KB) goes straight from global memory to one of
 // MID_STAGES LDS buffers (wave w fills rows 16w .. 16w + 15; 16-byte chunk ch
 // of row r lands at position ch ^ (r % 16)); codes, scales and deltas of the
@@ -1030,7 +1037,7 @@ constexpr unsigned waitcnt_vm(int n)
     return (unsigned)((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int SG, bool DELTA>
+template <int SG, bool DELTA, int GK>
 __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g)
@@ -1087,24 +1094,37 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
         }
     };
 
-    float4v acc[WM][WN];
-#pragma unroll
-    for (int mt = 0; mt < WM; ++mt)
-#pragma unroll
-        for (int t = 0; t < WN; ++t) acc[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
+    // fp32 accumulators, and the raw sums of the current weight group (codes
+    // as subnormals, low and high nibbles apart, and the activation sums);
+    // the group's scale and delta are applied once, at its last k-tile
+    float4v acc[WM][WN], xl[WM][WN], xh[WM][WN], asum[WM];
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     const float4v fzero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt) {
+        asum[mt] = fzero;
+#pragma unroll
+        for (int t = 0; t < WN; ++t) acc[mt][t] = xl[mt][t] = xh[mt][t] = fzero;
+    }
+    int kt_ = 0;   // the k-tile being computed
 
-    auto step = [&](int kt, int slot) {
-        // this thread's loads of k-tile kt have landed (the SG - 2 later
-        // k-tiles' may still be in flight); the barrier makes every wave's
-        // part visible and frees the slot of k-tile kt - 1
-        constexpr unsigned WAIT = waitcnt_vm((SG - 2) * L);
-        __builtin_amdgcn_s_waitcnt(WAIT);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        load(kt + SG - 1, (slot + SG - 1) % SG);
+    // the group constants of the slot being computed (converted at every
+    // k-tile, used at a group's last: every slot's registers are then
+    // consumed at the same point of its step, which keeps the compiler's load
+    // tracking exact)
+    float k16[WN], k1[WN], k2[WN];
+    // first: this k-tile starts its weight group (the raw sums restart)
+    auto compute = [&](int slot, bool first) {
+#pragma unroll
+        for (int t = 0; t < WN; ++t) {
+            const float s = h2f((uint16_t)(rs[slot][t] >> sh));
+            const float d = DELTA ? h2f((uint16_t)(rd[slot][t] >> sh)) : 0.f;
+            k16[t] = s * 0x1p24f;
+            k1[t] = s * 0x1p20f;
+            k2[t] = DELTA ? (d - 8.0f * s) : (-8.0f * s);
+            pin(k16[t]); pin(k1[t]); pin(k2[t]);
+        }
+        load(kt_ + SG - 1, (slot + SG - 1) % SG);
         const _Float16 *as = Asm + slot * BM * KTILE;
 #pragma unroll
         for (int mt = 0; mt < WM; ++mt) {
@@ -1113,28 +1133,57 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
 #pragma unroll
             for (int o = 0; o < 4; ++o)
                 a[o] = *reinterpret_cast<const half8 *>(as + r * KTILE + 8 * ((4 * o + kq) ^ c));
-            float4v asum = mfma_f16(a[0], ones, fzero);
-            asum = mfma_f16(a[1], ones, asum);
-            asum = mfma_f16(a[2], ones, asum);
-            asum = mfma_f16(a[3], ones, asum);
+            asum[mt] = mfma_f16(a[0], ones, first ? fzero : asum[mt]);
+            asum[mt] = mfma_f16(a[1], ones, asum[mt]);
+            asum[mt] = mfma_f16(a[2], ones, asum[mt]);
+            asum[mt] = mfma_f16(a[3], ones, asum[mt]);
 #pragma unroll
             for (int t = 0; t < WN; ++t) {
                 const CodeOps ops = split_codes(rw[slot][t]);
-                const float s = h2f((uint16_t)(rs[slot][t] >> sh));
-                const float d = DELTA ? h2f((uint16_t)(rd[slot][t] >> sh)) : 0.f;
-                float4v xl = mfma_f16(a[0], ops.lo[0], fzero);
-                xl = mfma_f16(a[1], ops.lo[1], xl);
-                float4v xh = mfma_f16(a[2], ops.hi[0], fzero);
-                xh = mfma_f16(a[3], ops.hi[1], xh);
-                const float c16 = s * 0x1p24f, c1 = s * 0x1p20f;
-                const float c2 = DELTA ? (d - 8.0f * s) : (-8.0f * s);
+                xl[mt][t] = mfma_f16(a[0], ops.lo[0], first ? fzero : xl[mt][t]);
+                xl[mt][t] = mfma_f16(a[1], ops.lo[1], xl[mt][t]);
+                xh[mt][t] = mfma_f16(a[2], ops.hi[0], first ? fzero : xh[mt][t]);
+                xh[mt][t] = mfma_f16(a[3], ops.hi[1], xh[mt][t]);
+            }
+        }
+    };
+    // end of a weight group: scale and delta applied to its raw sums
+    auto apply = [&](bool clear) {
+#pragma unroll
+        for (int mt = 0; mt < WM; ++mt) {
+#pragma unroll
+            for (int t = 0; t < WN; ++t) {
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    float v = __builtin_fmaf(c16, xl[r4], acc[mt][t][r4]);
-                    v = __builtin_fmaf(c1, xh[r4], v);
-                    acc[mt][t][r4] = __builtin_fmaf(c2, asum[r4], v);
+                    float v = __builtin_fmaf(k16[t], xl[mt][t][r4], acc[mt][t][r4]);
+                    v = __builtin_fmaf(k1[t], xh[mt][t][r4], v);
+                    acc[mt][t][r4] = __builtin_fmaf(k2[t], asum[mt][r4], v);
                 }
+                if (clear) xl[mt][t] = xh[mt][t] = fzero;
             }
+            if (clear) asum[mt] = fzero;
+        }
+    };
+    auto step = [&](int kt, int slot) {
+        constexpr unsigned WAIT = waitcnt_vm((SG - 2) * L);
+        __builtin_amdgcn_s_waitcnt(WAIT);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // nothing that reads this slot's registers moves above the wait
+        __builtin_amdgcn_sched_barrier(0);
+        kt_ = kt;
+        if (GK == 1) {
+            compute(slot, true);
+            apply(false);
+        } else if (GK == 2) {
+            // k-tiles come in slot order from a multiple of SG (even)
+            compute(slot, (slot & 1) == 0);
+            if (slot & 1) apply(false);
+        } else {
+            // GK == 0, one group over all of K: the raw sums start at zero
+            // and are applied once, after the loop
+            compute(slot, false);
         }
     };
 
@@ -1155,6 +1204,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
 #pragma unroll
     for (int i = 0; i < SG - 1; ++i)
         if (kt + i < KT) step(kt + i, i);
+    if (GK == 0) apply(false);   // the single group (g = K) ends with the last k-tile
     __builtin_amdgcn_s_waitcnt(0);   // the last (unused) loads
 
 #pragma unroll
@@ -1168,24 +1218,37 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
             }
 }
 
-template <bool DELTA>
+template <bool DELTA, int GK>
 static hipError_t run_mid(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                           const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                           hipStream_t st)
 {
     dim3 grid((unsigned)(N / 64), (unsigned)((M + 63) / 64));
     const size_t lds = (size_t)MID_STAGES * 64 * KTILE * sizeof(_Float16);
-    hipLaunchKernelGGL((w4a16_mid_kernel<MID_STAGES, DELTA>), grid, dim3(256), lds, st, A,
+    hipLaunchKernelGGL((w4a16_mid_kernel<MID_STAGES, DELTA, GK>), grid, dim3(256), lds, st, A,
                        reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g);
     return hipGetLastError();
+}
+
+template <bool DELTA>
+static hipError_t run_mid_g(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                            const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                            hipStream_t st)
+{
+    // the two-k-tile form needs groups of exactly 2 k-tiles (MID_STAGES even:
+    // group parity follows the ring slot)
+    static_assert(MID_STAGES % 2 == 0, "k-tile parity must follow the ring slot");
+    if (g == K) return run_mid<DELTA, 0>(A, W, S, D, C, M, N, K, g, st);
+    if (g == 2 * KTILE) return run_mid<DELTA, 2>(A, W, S, D, C, M, N, K, g, st);
+    return run_mid<DELTA, 1>(A, W, S, D, C, M, N, K, g, st);
 }
 
 hipError_t launch_w4a16_mid(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                             bool fuse_delta, hipStream_t st)
 {
-    if (D && fuse_delta) return run_mid<true>(A, W, S, D, C, M, N, K, g, st);
-    return run_mid<false>(A, W, S, nullptr, C, M, N, K, g, st);
+    if (D && fuse_delta) return run_mid_g<true>(A, W, S, D, C, M, N, K, g, st);
+    return run_mid_g<false>(A, W, S, nullptr, C, M, N, K, g, st);
 }
 
 // Configuration for M >= MID_MIN_M: 0 = mid kernel (64 x 64 tiles),

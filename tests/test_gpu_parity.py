@@ -175,11 +175,16 @@ def test_w4a16_tiled_128x256_symmetric(g, asym, flags):
     _check_w4a16(c, flags=qg.QG_CORR_SEPARATE if flags else 0)
 
 
-@pytest.mark.parametrize("K,g,asym", [(256, 128, True), (384, 128, False), (640, -1, True)])
+@pytest.mark.parametrize("K,g,asym", [(256, 128, True), (384, 128, False), (640, -1, True),
+                                       (256, -1, False), (512, 256, True), (768, 256, False),
+                                       (1280, 256, True), (1024, 512, True)])
 def test_w4a16_mid_kernel_short_k(K, g, asym):
     # M = 200 on N = 1024 takes the 64 x 64 mid kernel, whose pipeline keeps
-    # several k-tiles in flight: fewer k-tiles (2, 3, 5) than its stages plus
-    # a ragged last row tile
+    # several k-tiles in flight: fewer k-tiles (2, 3, 5) than its stages, or a
+    # few more (6, 10), plus a ragged last row tile; per-k-tile scaling
+    # (g = 128, 512), two-k-tile groups (g = 256: one group, one full pipeline
+    # round, a round plus a one-group tail, two rounds plus a one-group tail)
+    # and one group over all of K
     M, N = 200, 1024
     gg = K if g == -1 else g
     c = synth.w4a16_case(M, K, N, gg, asym=asym, signed_scales=not asym, stream=90,
