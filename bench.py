@@ -206,17 +206,22 @@ def bench_w4a8(name, steps, warmup):
 
 def measured_traffic():
     """HBM bytes per launch of the decode kernel from the committed rocprofv3
-    counter summary, if the kernel source is unchanged since it was taken."""
+    counter summary, if neither the kernel source nor the build flags have
+    changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "w4a16_decode_M16_K5120_N17408_traffic.json")
+
+    def sha(rel):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()[:16]
     try:
         with open(path) as f:
             rec = json.load(f)
-        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+        same = (sha(rec["source"]) == rec["source_sha256_16"]
+                and sha(rec["build"]) == rec["build_sha256_16"])
     except (OSError, ValueError, KeyError):
         return None
-    return rec["traffic_bytes"] if sha == rec["source_sha256_16"] else None
+    return rec["traffic_bytes"] if same else None
 
 
 def achievable(primary_bytes):
