@@ -204,12 +204,11 @@ def bench_w4a8(name, steps, warmup):
     return res
 
 
-def measured_traffic():
-    """HBM bytes per launch of the decode kernel from the committed rocprofv3
-    counter summary, if neither the kernel source nor the build flags have
-    changed since it was taken."""
+def _committed(name):
+    """A committed rocprofv3 counter record under profiles/, if neither the
+    kernel source nor the build flags have changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "w4a16_decode_M16_K5120_N17408_traffic.json")
+    path = os.path.join(ROOT, "profiles", name)
 
     def sha(rel):
         with open(os.path.join(ROOT, rel), "rb") as f:
@@ -221,7 +220,29 @@ def measured_traffic():
                 and sha(rec["build"]) == rec["build_sha256_16"])
     except (OSError, ValueError, KeyError):
         return None
-    return rec["traffic_bytes"] if same else None
+    return rec if same else None
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode kernel (FETCH_SIZE + WRITE_SIZE,
+    copy-calibrated) from the committed counter summary, or None."""
+    rec = _committed("w4a16_decode_M16_K5120_N17408_traffic.json")
+    return rec["traffic_bytes"] if rec else None
+
+
+def prefill_counters():
+    """Clock, matrix-core busy and fabric traffic of the prefill kernels from
+    the committed counter summary, or None."""
+    rec = _committed("w4a16_prefill_M4096_K5120_N17408_counters.json")
+    if not rec:
+        return None
+    out = {}
+    for k, v in rec["kernels"].items():
+        if "w4a16" in k:
+            out[k] = {f: v[f] for f in ("duration_us", "clock_ghz", "mfma_busy", "traffic_bytes",
+                                        "algorithmic_bytes") if f in v}
+    out["source"] = "profiles/w4a16_prefill_M4096_K5120_N17408_clock.md (rocprofv3 --pmc)"
+    return out
 
 
 def achievable(primary_bytes):
@@ -400,7 +421,8 @@ def main():
         out["prefill_M4096"] = {"tflops": prefill[0]["tflops"],
                                 "pct_fp16_mfma": prefill[0]["pct_fp16_mfma"],
                                 "frac_achievable_fp16_mfma": prefill[0].get("frac_achievable_fp16_mfma"),
-                                "us_per_call": prefill[0]["us_per_call"]}
+                                "us_per_call": prefill[0]["us_per_call"],
+                                "counters": prefill_counters()}
     print(json.dumps(out), flush=True)
 
 
