@@ -1031,6 +1031,15 @@ static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t
 // after which the slot used by the previous k-tile is refilled.
 constexpr int MID_STAGES = 4;
 
+// Buffer resource over [p, p + bytes) for raw (unstructured) buffer loads:
+// base address, stride 0, range in bytes (clamped to 32 bits), and the fixed
+// third-word value of this GPU family for raw dword access.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, size_t bytes)
+{
+    const int range = bytes > 0xFFFFFFFFull ? (int)0xFFFFFFFF : (int)(unsigned)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, range, 0x00020000);
+}
+
 constexpr unsigned waitcnt_vm(int n)
 {
     // s_waitcnt immediate: vmcnt n (6 bits, split), expcnt and lgkmcnt not waited
@@ -1057,40 +1066,51 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
     const int col0 = ntile0 * NTILE + c;
     const int sh = 16 * (c & 1);
 
-    // direct global -> LDS loads: one wave instruction fills 1 KB = 4 rows;
+    // Every load below is a buffer load: a workgroup-uniform resource (base
+    // address), a fixed per-lane byte offset and the k-dependent byte offset
+    // in a scalar register, so the k-loop does no per-lane address arithmetic.
+    // The ranges cover the arrays from each base to their end.
+    // A: direct global -> LDS loads, one wave instruction fills 1 KB = 4 rows;
     // rows past M read row M-1 (their results are never stored)
+    const __amdgpu_buffer_rsrc_t a_rs = buffer_rsrc(A + (size_t)m0 * K, (size_t)(M - m0) * K * 2);
+    unsigned a_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = (wave * 4 + i) * 4 + (lane >> 4);
+        const int ch = (lane & 15) ^ (r & 15);
+        const int row = m0 + r < M ? r : M - 1 - m0;
+        a_off[i] = (unsigned)(row * K + ch * 8) * 2u;
+    }
     auto load_a = [&](int kt, int st) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int blk = wave * 4 + i;
-            const int r = blk * 4 + (lane >> 4);
-            const int ch = (lane & 15) ^ (r & 15);
-            int row = m0 + r;
-            row = row < M ? row : M - 1;
-            const uint16_t *src = A + (size_t)row * K + kt * KTILE + ch * 8;
-            __builtin_amdgcn_global_load_lds(
-                (const void *)src,
-                (__attribute__((address_space(3))) void *)(Asm + st * BM * KTILE + blk * 4 * KTILE), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                a_rs, (__attribute__((address_space(3))) void *)(Asm + st * BM * KTILE + blk * 4 * KTILE), 16,
+                a_off[i], kt * KTILE * 2, 0, 0);
         }
     };
-    const uint4v *wbase = W + (size_t)ntile0 * KT * 64 + lane;
+    const __amdgpu_buffer_rsrc_t w_rs = buffer_rsrc(W + (size_t)ntile0 * KT * 64, (size_t)(N / NTILE - ntile0) * KT * 1024);
+    const __amdgpu_buffer_rsrc_t s_rs = buffer_rsrc(S + ntile0 * NTILE, ((size_t)(K / g) * N - ntile0 * NTILE) * 2);
+    const __amdgpu_buffer_rsrc_t d_rs = buffer_rsrc(DELTA ? D + ntile0 * NTILE : S, DELTA ? ((size_t)(K / g) * N - ntile0 * NTILE) * 2 : 4);
     uint4v rw[SG][WN];
     uint32_t rs[SG][WN], rd[SG][WN];   // aligned scale / delta pairs (half c & 1)
+    const unsigned w_off = (unsigned)lane * 16u;      // this lane's 16 bytes of a code tile
+    const unsigned s_off = ((unsigned)c >> 1) * 4u;   // this lane's scale pair within 16 columns
     // every load of k-tile kt (clamped: the count per k-tile is fixed, which
     // the waits rely on)
     auto load = [&](int kt, int slot) {
         const int k = kt < KT ? kt : KT - 1;
         load_a(k, slot);
 #pragma unroll
-        for (int t = 0; t < WN; ++t) rw[slot][t] = wbase[((size_t)t * KT + k) * 64];
-        const int gi = (k * KTILE) / g;
-        const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
+        for (int t = 0; t < WN; ++t)
+            rw[slot][t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off, (t * KT + k) * 1024, 0));
+        const int gb = ((k * KTILE) / g) * N * 2;      // byte offset of this k-tile's group row
 #pragma unroll
-        for (int t = 0; t < WN; ++t) rs[slot][t] = srow[8 * t];
+        for (int t = 0; t < WN; ++t) rs[slot][t] = __builtin_amdgcn_raw_buffer_load_b32(s_rs, s_off, gb + 32 * t, 0);
         if (DELTA) {
-            const uint32_t *drow = reinterpret_cast<const uint32_t *>(D + (size_t)gi * N + (col0 & ~1));
 #pragma unroll
-            for (int t = 0; t < WN; ++t) rd[slot][t] = drow[8 * t];
+            for (int t = 0; t < WN; ++t) rd[slot][t] = __builtin_amdgcn_raw_buffer_load_b32(d_rs, s_off, gb + 32 * t, 0);
         }
     };
 
