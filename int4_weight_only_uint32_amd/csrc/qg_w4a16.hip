@@ -857,6 +857,15 @@ __device__ inline half8 dequant_scaled_ao(uint4v w, half2v s2, unsigned magic)
     return __builtin_bit_cast(half8, uint4v{out[0], out[1], out[2], out[3]});
 }
 
+// Buffer resource over [p, p + bytes) for raw (unstructured) buffer loads:
+// base address, stride 0, range in bytes (clamped to 32 bits), and the fixed
+// third-word value of this GPU family for raw dword access.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, size_t bytes)
+{
+    const int range = bytes > 0xFFFFFFFFull ? (int)0xFFFFFFFF : (int)(unsigned)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, range, 0x00020000);
+}
+
 __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     uint16_t *__restrict__ C, int M, int N, int K, int g)
@@ -877,18 +886,26 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
     const int ntile0 = n0c / NTILE;
     const int sh = 16 * (c & 1);
 
+    // Buffer loads: a workgroup-uniform resource, a fixed per-lane byte
+    // offset and the k-dependent byte offset in a scalar register (no
+    // per-lane address arithmetic in the k-loop).  A rows past M read row
+    // M-1 (their results are never stored).
+    const __amdgpu_buffer_rsrc_t a_rs = buffer_rsrc(A + (size_t)m0 * K, (size_t)(M - m0) * K * 2);
+    unsigned a_off[ABLK];
+#pragma unroll
+    for (int i = 0; i < ABLK; ++i) {
+        const int r = (wave * ABLK + i) * 4 + (lane >> 4);
+        const int ch = (lane & 15) ^ (r & 15);
+        const int row = m0 + r < M ? r : M - 1 - m0;
+        a_off[i] = (unsigned)(row * K + ch * 8) * 2u;
+    }
     auto load_a = [&](int kt, int st) {
 #pragma unroll
         for (int i = 0; i < ABLK; ++i) {
             const int blk = wave * ABLK + i;
-            const int r = blk * 4 + (lane >> 4);
-            const int ch = (lane & 15) ^ (r & 15);
-            int row = m0 + r;
-            row = row < M ? row : M - 1;
-            const uint16_t *src = A + (size_t)row * K + kt * KTILE + ch * 8;
-            __builtin_amdgcn_global_load_lds(
-                (const void *)src,
-                (__attribute__((address_space(3))) void *)(&As[st][blk * 4 * 128]), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                a_rs, (__attribute__((address_space(3))) void *)(&As[st][blk * 4 * 128]), 16, a_off[i],
+                kt * KTILE * 2, 0, 0);
         }
     };
     auto a_frag = [&](const _Float16 *as, int mt, int o) {
@@ -898,14 +915,18 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
     };
     uint4v wreg[WN];
     uint32_t sreg[WN];   // aligned scale pair holding this lane's column (half c & 1)
+    const __amdgpu_buffer_rsrc_t w_rs = buffer_rsrc(W + (size_t)ntile0 * KT * 64, (size_t)(N / NTILE - ntile0) * KT * 1024);
+    const __amdgpu_buffer_rsrc_t s_rs = buffer_rsrc(S + n0c, ((size_t)(K / g) * N - n0c) * 2);
+    const unsigned w_off = (unsigned)lane * 16u;      // this lane's 16 bytes of a code tile
+    const unsigned s_off = ((unsigned)c >> 1) * 4u;   // this lane's scale pair within 16 columns
     auto load_w = [&](int kt) {
         const int k = kt < KT ? kt : KT - 1;
-        const int gi = (k * KTILE) / g;
+        const int gb = ((k * KTILE) / g) * N * 2;      // byte offset of this k-tile's group row
 #pragma unroll
-        for (int t = 0; t < WN; ++t) wreg[t] = W[((size_t)(ntile0 + t) * KT + k) * 64 + lane];
-        const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + ((n0c + c) & ~1));
+        for (int t = 0; t < WN; ++t)
+            wreg[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off, (t * KT + k) * 1024, 0));
 #pragma unroll
-        for (int t = 0; t < WN; ++t) sreg[t] = srow[8 * t];
+        for (int t = 0; t < WN; ++t) sreg[t] = __builtin_amdgcn_raw_buffer_load_b32(s_rs, s_off, gb + 32 * t, 0);
     };
 
     float4v acc[WM][WN];
@@ -1030,15 +1051,6 @@ static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t
 // with a wait that leaves the later k-tiles' loads in flight and one barrier,
 // after which the slot used by the previous k-tile is refilled.
 constexpr int MID_STAGES = 4;
-
-// Buffer resource over [p, p + bytes) for raw (unstructured) buffer loads:
-// base address, stride 0, range in bytes (clamped to 32 bits), and the fixed
-// third-word value of this GPU family for raw dword access.
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, size_t bytes)
-{
-    const int range = bytes > 0xFFFFFFFFull ? (int)0xFFFFFFFF : (int)(unsigned)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, range, 0x00020000);
-}
 
 constexpr unsigned waitcnt_vm(int n)
 {
