@@ -632,6 +632,15 @@ __device__ inline half8 dequant_scaled(uint4v w, half2v s2)
     return __builtin_bit_cast(half8, uint4v{out[0], out[1], out[2], out[3]});
 }
 
+// Buffer resource over [p, p + bytes) for raw (unstructured) buffer loads:
+// base address, stride 0, range in bytes (clamped to 32 bits), and the fixed
+// third-word value of this GPU family for raw dword access.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, size_t bytes)
+{
+    const int range = bytes > 0xFFFFFFFFull ? (int)0xFFFFFFFF : (int)(unsigned)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, range, 0x00020000);
+}
+
 template <int WM, int WN, bool DELTA>
 __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
@@ -658,18 +667,31 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
     // rows; lane i lands at position i of that block, i.e. row 4b + i/16,
     // physical chunk i%16, which holds logical chunk (i%16) ^ (row%16).
     // Rows past M read row M-1 (their results are never stored).
+    // Buffer loads (uniform resource, fixed per-lane byte offset, k offset in
+    // a scalar register): no per-lane address arithmetic in the k-loop, and
+    // the compiler then does not drain the next tile's direct-to-LDS loads
+    // before this tile's LDS reads.
+    const __amdgpu_buffer_rsrc_t a_rs = buffer_rsrc(A + (size_t)m0 * K, (size_t)(M - m0) * K * 2);
+    unsigned a_off[ABLK];
+#pragma unroll
+    for (int i = 0; i < ABLK; ++i) {
+        const int r = (wave * ABLK + i) * 4 + (lane >> 4);   // BM/4 blocks of 4 rows
+        const int ch = (lane & 15) ^ (r & 15);
+        const int row = m0 + r < M ? r : M - 1 - m0;
+        a_off[i] = (unsigned)(row * K + ch * 8) * 2u;
+    }
     auto load_a = [&](int kt, int st) {
 #pragma unroll
         for (int i = 0; i < ABLK; ++i) {
-            const int blk = wave * ABLK + i;            // BM/4 blocks of 4 rows
-            const int r = blk * 4 + (lane >> 4);
-            const int ch = (lane & 15) ^ (r & 15);
-            int row = m0 + r;
-            row = row < M ? row : M - 1;
-            const uint16_t *src = A + (size_t)row * K + kt * KTILE + ch * 8;
-            __builtin_amdgcn_global_load_lds(
-                (const void *)src,
-                (__attribute__((address_space(3))) void *)(&As[st][blk * 4 * 128]), 16, 0, 0);
+            const int blk = wave * ABLK + i;
+            // (arguments in variables of non-dependent type: a target
+            // builtin called with template-dependent arguments is
+            // instantiated in the host pass too, where it does not exist,
+            // and the kernel would silently lose its host launch stub)
+            __attribute__((address_space(3))) void *dst =
+                (__attribute__((address_space(3))) void *)(&As[st][blk * 4 * 128]);
+            const unsigned off = a_off[i];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, dst, 16, off, kt * KTILE * 2, 0, 0);
         }
     };
     auto a_frag = [&](const _Float16 *as, int mt, int o) {
@@ -680,13 +702,17 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
     // ---- codes and scales of this wave's WN n-tiles
     uint4v wreg[WN];
     uint16_t sreg[WN];
+    const int ntw = active ? ntile0 : 0;   // (inactive waves load nothing)
+    const __amdgpu_buffer_rsrc_t w_rs = buffer_rsrc(W + (size_t)ntw * KT * 64, (size_t)(N / NTILE - ntw) * KT * 1024);
+    const __amdgpu_buffer_rsrc_t s_rs = buffer_rsrc(S + ntw * NTILE, ((size_t)G * N - ntw * NTILE) * 2);
+    const unsigned w_off = (unsigned)lane * 16u, s_off = (unsigned)c * 2u;
     auto load_w = [&](int kt) {
         if (!active) return;
-        const int gi = (kt * KTILE) / g;
+        const int gb = ((kt * KTILE) / g) * N * 2;
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
-            wreg[t] = W[((size_t)(ntile0 + t) * KT + kt) * 64 + lane];
-            sreg[t] = S[(size_t)gi * N + n0 + 16 * t + c];
+            wreg[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off, (t * KT + kt) * 1024, 0));
+            sreg[t] = __builtin_amdgcn_raw_buffer_load_b16(s_rs, s_off, gb + 32 * t, 0);
         }
     };
 
@@ -745,10 +771,11 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
             const _Float16 sh = __builtin_bit_cast(_Float16, sreg[t]);
             s2[t] = half2v{sh, sh};
         }
-        if (kt + 1 < KT) {
-            load_a(kt + 1, st ^ 1);
-            load_w(kt + 1);
-        }
+        // unconditional, clamped: the last k-tile reloads its own tile into
+        // the idle buffer (a conditional load would leave the compiler unsure
+        // which loads are in flight, and it would drain them all)
+        load_a(kt + 1 < KT ? kt + 1 : kt, st ^ 1);
+        load_w(kt + 1 < KT ? kt + 1 : kt);
         const _Float16 *as = As[st];
         if (active) {
 #define QG_TILED_STEP(O)                                                                      \
@@ -855,15 +882,6 @@ __device__ inline half8 dequant_scaled_ao(uint4v w, half2v s2, unsigned magic)
         out[i] = __builtin_bit_cast(unsigned, v * s2);
     }
     return __builtin_bit_cast(half8, uint4v{out[0], out[1], out[2], out[3]});
-}
-
-// Buffer resource over [p, p + bytes) for raw (unstructured) buffer loads:
-// base address, stride 0, range in bytes (clamped to 32 bits), and the fixed
-// third-word value of this GPU family for raw dword access.
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, size_t bytes)
-{
-    const int range = bytes > 0xFFFFFFFFull ? (int)0xFFFFFFFF : (int)(unsigned)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, range, 0x00020000);
 }
 
 __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
