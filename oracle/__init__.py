@@ -61,6 +61,8 @@ def _load():
         lib.oracle_group_sum_correction.argtypes = [P, P, P, I, I, I, I, P]
         lib.oracle_w4a8.restype = I
         lib.oracle_w4a8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P]
+        lib.oracle_quantize_rows_int8.restype = None
+        lib.oracle_quantize_rows_int8.argtypes = [P, I, I, P, P]
         _lib = lib
     return _lib
 
@@ -215,3 +217,15 @@ def w4a8(Aq, a_scale, q, s, offsets, g, fold=True, want_acc=True):
     if rc != 0:
         raise MemoryError("oracle_w4a8 allocation failed")
     return C, acc
+
+
+def quantize_rows_int8(A):
+    """Per-row int8 codes of fp16 activations [M,K] (float16 or uint16 bits).
+    Returns (codes int8 [M,K], a_scale float32 [M])."""
+    A, pa = _c(_bits16(A), np.uint16)
+    M, K = A.shape
+    codes = np.empty((M, K), dtype=np.int8)
+    sc = np.empty(M, dtype=np.float32)
+    _load().oracle_quantize_rows_int8(pa, M, K, codes.ctypes.data_as(ctypes.c_void_p),
+                                      sc.ctypes.data_as(ctypes.c_void_p))
+    return codes, sc

@@ -306,3 +306,37 @@ int oracle_w4a8(const int8_t *Aq, const float *a_scale, const uint8_t *q,
     free(qc); free(sc); free(row_acc);
     return 0;
 }
+
+/* ---- [HyperQwen] "why int8 activation quantization (W4A8) is worth doing":
+ * the activations of the W4A8 path are quantized per token (per row) to int8.
+ * The page names no rule; this is the plain symmetric absmax one:
+ *     a_scale[m] = max_k |A[m,k]| / 127
+ *     A_q[m,k]   = clamp(round_half_even(A[m,k] / a_scale[m]), -127, 127)
+ * and a row of zeros gets a_scale 0 and codes 0.  Floating point decides the
+ * integer codes here, so the precision is part of the definition: both
+ * divisions are single IEEE binary32 operations rounded to nearest even (the
+ * precision the GPU kernel takes them in).  binary16 values convert to
+ * binary32 exactly.                                                          */
+void oracle_quantize_rows_int8(const uint16_t *A, int M, int K, int8_t *Aq, float *a_scale)
+{
+    for (int m = 0; m < M; ++m) {
+        const uint16_t *a = A + (size_t)m * K;
+        float amax = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            float v = fabsf((float)oracle_f16_to_f64(a[k]));
+            if (v > amax) amax = v;
+        }
+        float sc = amax / 127.0f;
+        a_scale[m] = sc;
+        for (int k = 0; k < K; ++k) {
+            int8_t c = 0;
+            if (sc > 0.0f) {
+                float r = rintf((float)oracle_f16_to_f64(a[k]) / sc);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                c = (int8_t)r;
+            }
+            Aq[(size_t)m * K + k] = c;
+        }
+    }
+}

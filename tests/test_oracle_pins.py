@@ -269,3 +269,75 @@ def test_quantize_rows_int8():
     assert sc[1] == 0 and np.all(codes[1] == 0)
     assert codes[0, 1] == -127 and codes[2, 0] == 127
     assert np.all(np.abs(codes) <= 127)
+
+
+# ------------------------------------------- per-row int8 quantization ---
+def test_quantize_ties_half_even_unit_scale(oracle_lib):
+    """max|row| = 127 gives a_scale = 1 exactly, so the codes are the row
+    itself rounded half to even (hand-worked)."""
+    A = _h([[127, 2.5, 3.5, -2.5, 0.5, -0.5, 1.5, 126.5, -1.5, 0.25]])
+    codes, sc = oracle_lib.quantize_rows_int8(A)
+    assert sc.dtype == np.float32 and sc[0] == 1.0
+    assert codes.tolist() == [[127, 2, 4, -2, 0, 0, 2, 126, -2, 0]]
+
+
+def test_quantize_power_of_two_scale(oracle_lib):
+    """max|row| = 127/64 gives a_scale = 1/64 exactly: A = j/64 maps to code j,
+    and (j + 1/2)/64 to the even neighbour."""
+    j = np.arange(-127, 128)
+    A = np.concatenate([j / 64.0, (np.arange(-126, 126) + 0.5) / 64.0])[None, :]
+    codes, sc = oracle_lib.quantize_rows_int8(_h(A))
+    assert sc[0] == np.float32(1 / 64)
+    assert np.array_equal(codes[0, :255], j)
+    half = np.arange(-126, 126) + 0.5
+    even = np.where(np.floor(half) % 2 == 0, np.floor(half), np.ceil(half))
+    assert np.array_equal(codes[0, 255:], even)
+
+
+def test_quantize_zero_row_and_single_entry(oracle_lib):
+    A = np.zeros((3, 16), np.float16)
+    A[1, 5] = -3.0
+    A[2, :] = 1e-7                      # binary16 subnormals: a tiny positive scale
+    codes, sc = oracle_lib.quantize_rows_int8(A)
+    assert sc[0] == 0 and np.all(codes[0] == 0)
+    assert codes[1, 5] == -127 and np.count_nonzero(codes[1]) == 1
+    assert sc[2] > 0 and np.all(codes[2] == 127)
+
+
+def test_quantize_against_exact_rationals(oracle_lib):
+    """Random rows: a_scale is max|row|/127 correctly rounded to binary32
+    (within half an ulp of the exact quotient), the argmax maps to +-127, and
+    every code is the exact quotient A/a_scale rounded half to even, except
+    within binary32 rounding of a half-integer (counted: there are few)."""
+    rng = np.random.default_rng(5)
+    A = (rng.standard_normal((6, 300)) * np.array([[1e-3], [1], [30], [1], [5e3], [0.1]])).astype(np.float16)
+    codes, sc = oracle_lib.quantize_rows_int8(A)
+    A64 = A.astype(np.float64)
+    near_half = 0
+    for m in range(A.shape[0]):
+        amax = Fraction(float(np.max(np.abs(A64[m]))))
+        s = Fraction(float(sc[m]))
+        ulp = Fraction(float(np.spacing(sc[m])))
+        assert abs(s - amax / 127) <= ulp / 2
+        am = int(np.argmax(np.abs(A64[m])))
+        assert codes[m, am] == (127 if A64[m, am] > 0 else -127)
+        for k in range(A.shape[1]):
+            x = Fraction(float(A64[m, k])) / s
+            fl = x.numerator // x.denominator
+            frac = x - fl
+            if abs(frac - Fraction(1, 2)) < Fraction(1, 1 << 16):
+                near_half += 1
+                assert codes[m, k] in (fl, fl + 1)
+                continue
+            r = fl + 1 if frac > Fraction(1, 2) else fl
+            assert codes[m, k] == max(-127, min(127, r))
+    assert near_half < 10
+
+
+def test_quantize_matches_input_preparation(oracle_lib):
+    """The W4A8 inputs are prepared with the same rule (an independent
+    implementation in the input generator): identical codes and scales."""
+    A = synth.w4a8_case(E=2, rows_per_expert=7, K=256, N=128, g=128).A16
+    c1, s1 = oracle_lib.quantize_rows_int8(A)
+    c2, s2 = synth.quantize_rows_int8(A)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
