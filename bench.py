@@ -288,7 +288,10 @@ def add_fractions(r, ach):
     """Fractions of one case against the measured achievable rates."""
     if ach is None:
         return
-    r["frac_achievable_hbm_weight"] = r["weight_gbps"] / ach["hbm_read_gbps"]
+    if "weight_gbps" in r:
+        r["frac_achievable_hbm_weight"] = r["weight_gbps"] / ach["hbm_read_gbps"]
+    else:
+        r["frac_achievable_hbm"] = r["alg_gbps"] / ach["hbm_read_gbps"]
     if "tflops" in r:
         r["frac_achievable_fp16_mfma"] = r["tflops"] / ach["mfma_f16_tflops"]
     if "tops" in r:
@@ -310,12 +313,54 @@ def cpu_baseline(case):
                        f"asym ({dt:.2f} s wall, fp64 dequant + naive m-k-n loop)")
 
 
+def bench_quantize(name, steps, warmup, A16, gemm=None):
+    """Per-row int8 quantization of the fp16 activations A16 [M,K]; with
+    `gemm` (the W4A8 case) also the quantizer followed by the W4A8 GEMM, the
+    step of an fp16-input W4A8 layer.  Inputs rotate over >= ROTATE_BYTES of
+    copies, so the rate is HBM's and not a cache's."""
+    import numpy as np
+    import torch
+
+    import int4_weight_only_uint32_amd as qg
+
+    M, K = A16.shape
+    alg = M * K * 2 + M * K + M * 4
+    R = max(1, math.ceil(ROTATE_BYTES / alg))
+    A0 = torch.from_numpy(np.ascontiguousarray(A16)).cuda()
+    As = [A0] + [A0.clone() for _ in range(R - 1)]
+    Qs = [torch.empty((M, K), dtype=torch.int8, device="cuda") for _ in range(R)]
+    Ss = [torch.empty((M,), dtype=torch.float32, device="cuda") for _ in range(R)]
+
+    def call(i):
+        qg.quantize_rows_int8(As[i], M, K, Qs[i], Ss[i])
+
+    ms, ms_graph, ms_eager = time_best(call, R, steps, warmup)
+    res = dict(name=name, M=M, K=K, us_per_call=ms * 1e3, alg_bytes=alg,
+               alg_gbps=alg / (ms * 1e-3) / 1e9, rotated_copies=R,
+               us_per_call_graph=ms_graph * 1e3 if ms_graph else None,
+               us_per_call_eager=ms_eager * 1e3)
+    res["pct_hbm"] = 100.0 * res["alg_gbps"] / HBM_PEAK_GBPS
+    if gemm is not None:
+        W, S, off, E, mr, N, g, C = gemm
+
+        def step(i):
+            qg.quantize_rows_int8(As[i], M, K, Qs[i], Ss[i])
+            qg.qgemm_w4a8(Qs[i], Ss[i], W, S, off, E, M, mr, N, K, g, C)
+
+        ms2, _, _ = time_best(step, R, steps, warmup)
+        res["us_quantize_plus_w4a8"] = ms2 * 1e3
+    del As, Qs, Ss
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
               f"(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
     import int4_weight_only_uint32_amd as qg
     import synth
@@ -368,6 +413,30 @@ def main():
                 r = bench_w4a8(nm, steps, warmup)
                 log(json.dumps(r))
                 cases.append(r)
+        qn = "quantize-rows-int8-E8x64-K2048+w4a8"
+        if not want or qn in want:
+            c = synth.workload("w4a8-moe-E8x64-K2048-N7168-g128")
+            dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+            packs = [qg.pack(dev(c.q[e]), dev(c.s[e]), None, c.g, fold=True) for e in range(c.E)]
+            W = torch.stack([p.w for p in packs]).contiguous()
+            S = torch.stack([p.scale for p in packs]).contiguous()
+            C = torch.empty((c.M_total, c.N), dtype=torch.float16, device="cuda")
+            mr = int(np.max(np.diff(c.offsets)))
+            gemm = (W, S, dev(c.offsets), c.E, mr, c.N, c.g, C)
+            r = bench_quantize(qn, steps, warmup, c.A16, gemm)
+            log(json.dumps(r))
+            cases.append(r)
+            del packs, W, S, C, gemm
+        qn = "quantize-rows-int8-M16-K5120"
+        if not want or qn in want:
+            r = bench_quantize(qn, steps, warmup, pcase.A)
+            log(json.dumps(r))
+            cases.append(r)
+        qn = "quantize-rows-int8-M4096-K5120"
+        if not want or qn in want:
+            r = bench_quantize(qn, steps, warmup, synth.activations(4096, 5120))
+            log(json.dumps(r))
+            cases.append(r)
 
     ach = None
     if not args.no_probes:

@@ -179,6 +179,22 @@ int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed
                uint16_t *C, int32_t *acc_debug, void *workspace, size_t workspace_bytes,
                unsigned flags, void *stream);
 
+/* ---- per-token int8 activation quantization, the input stage of
+ *      qgemm_w4a8 ([HyperQwen] "why int8 activation quantization (W4A8) is
+ *      worth doing": activations are quantized per token to int8) ----
+ * A        [M,K] fp16 activations, 16-byte aligned; K % 8 == 0 (else
+ *          QG_ERR_UNSUPPORTED).
+ * A_q      [M,K] int8 out, 8-byte aligned; a_scale [M] fp32 out:
+ *            a_scale[m] = max_k |A[m,k]| / 127
+ *            A_q[m,k]   = clamp(round_half_even(A[m,k] / a_scale[m]), -127, 127)
+ *          both divisions single IEEE binary32 operations (round to nearest
+ *          even); a row of zeros gets a_scale 0 and codes 0.  The outputs
+ *          are exactly qgemm_w4a8's A_q and a_scale.  Non-finite inputs give
+ *          unspecified codes.
+ * One kernel on `stream`. No workspace.                                     */
+int quantize_rows_int8(const uint16_t *A, int M, int K, int8_t *A_q, float *a_scale,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,7 +38,8 @@ QG_OP_GROUP_SUM_CORRECTION = 3
 QG_OP_PACK = 4
 
 EXPORTED = ("qg_device_supported", "qg_status_string", "qg_last_error", "qg_workspace_bytes",
-            "pack_int4_weights", "qgemm_w4a16", "group_sum_correction", "qgemm_w4a8")
+            "pack_int4_weights", "qgemm_w4a16", "group_sum_correction", "qgemm_w4a8",
+            "quantize_rows_int8")
 
 
 class QGemmError(RuntimeError):
@@ -75,6 +76,8 @@ def lib():
         L.group_sum_correction.argtypes = [P, P, P, I, I, I, I, P, Z, P]
         L.qgemm_w4a8.restype = I
         L.qgemm_w4a8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, Z, U, P]
+        L.quantize_rows_int8.restype = I
+        L.quantize_rows_int8.argtypes = [P, I, I, P, P, P]
         _lib = L
     return _lib
 
@@ -220,3 +223,22 @@ def w4a8(A_q: torch.Tensor, a_scale: torch.Tensor, w_packed: torch.Tensor, w_sca
     qgemm_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts, M_total,
                max_rows_per_expert, N, K, group_size, C, acc_debug)
     return C
+
+
+def quantize_rows_int8(A, M, K, A_q, a_scale):
+    _check(lib().quantize_rows_int8(_ptr(A, torch.float16, "A"), M, K, _ptr(A_q, torch.int8, "A_q"),
+                                    _ptr(a_scale, torch.float32, "a_scale"), _stream(A)))
+
+
+def quantize_rows(A: torch.Tensor, A_q: Optional[torch.Tensor] = None,
+                  a_scale: Optional[torch.Tensor] = None):
+    """Per-row int8 codes and fp32 scales of fp16 activations [M,K]."""
+    M, K = A.shape
+    if A_q is None:
+        A_q = torch.empty((M, K), dtype=torch.int8, device=A.device)
+    if a_scale is None:
+        a_scale = torch.empty((M,), dtype=torch.float32, device=A.device)
+    if tuple(A_q.shape) != (M, K) or tuple(a_scale.shape) != (M,):
+        raise ValueError(f"A_q must be [{M},{K}] and a_scale [{M}]")
+    quantize_rows_int8(A, M, K, A_q, a_scale)
+    return A_q, a_scale

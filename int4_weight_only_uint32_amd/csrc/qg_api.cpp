@@ -270,4 +270,21 @@ int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed
     return launch_status(e, "qgemm_w4a8");
 }
 
+int quantize_rows_int8(const uint16_t *A, int M, int K, int8_t *A_q, float *a_scale,
+                       void *stream)
+{
+    if (!A || !A_q || !a_scale)
+        return fail(QG_ERR_INVALID_ARG, "quantize_rows_int8: NULL A/A_q/a_scale");
+    if (M < 1 || K < 1)
+        return fail(QG_ERR_INVALID_ARG, "quantize_rows_int8: M and K must be >= 1 (got %d, %d)", M, K);
+    if (K % 8)
+        return fail(QG_ERR_UNSUPPORTED, "quantize_rows_int8: K must be a multiple of 8 (got %d)", K);
+    if (!aligned(A, 16) || !aligned(A_q, 8) || !aligned(a_scale, 4))
+        return fail(QG_ERR_INVALID_ARG, "quantize_rows_int8: misaligned pointer");
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = qg::launch_quantize_rows_int8(A, M, K, A_q, a_scale, (hipStream_t)stream);
+    return launch_status(e, "quantize_rows_int8");
+}
+
 } // extern "C"

@@ -149,6 +149,11 @@ def w4a8_case(E, rows_per_expert, K, N, g, signed_scales=False, stream=4, case_i
 WORKLOADS = {}
 
 
+def activations(M, K, stream=5, case_id=0) -> np.ndarray:
+    """Seeded fp16 N(0,1) activations [M,K] (the quantizer's prefill-size input)."""
+    return rng_for(stream, case_id).standard_normal((M, K), dtype=np.float32).astype(np.float16)
+
+
 def _add(name, kind, stream, case_id, **spec):
     WORKLOADS[name] = dict(kind=kind, stream=stream, case_id=case_id, spec=spec)
 

@@ -188,3 +188,17 @@ def test_product_path_does_not_import_the_oracle():
                 txt = open(os.path.join(dp, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
                 assert "qgemm_oracle" not in txt and "liboracle" not in txt, f
+
+
+def test_quantize_rows_validation():
+    # every case fails validation, before the device check and any launch
+    L = qg.lib()
+    assert L.quantize_rows_int8(None, 4, 1024, FAKE, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.quantize_rows_int8(FAKE, 4, 1024, None, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.quantize_rows_int8(FAKE, 0, 1024, FAKE, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.quantize_rows_int8(FAKE, 4, 0, FAKE, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.quantize_rows_int8(FAKE, 4, 1020, FAKE, FAKE, None) == qg.QG_ERR_UNSUPPORTED
+    assert L.quantize_rows_int8(P(0x10008), 4, 1024, FAKE, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.quantize_rows_int8(FAKE, 4, 1024, P(0x10004), FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.quantize_rows_int8(FAKE, 4, 1024, FAKE, P(0x10002), None) == qg.QG_ERR_INVALID_ARG
+    assert b"quantize_rows_int8" in L.qg_last_error()
