@@ -60,7 +60,7 @@ def _load():
         lib.oracle_group_sum_correction.restype = I
         lib.oracle_group_sum_correction.argtypes = [P, P, P, I, I, I, I, P]
         lib.oracle_w4a8.restype = I
-        lib.oracle_w4a8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P]
+        lib.oracle_w4a8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P]
         lib.oracle_quantize_rows_int8.restype = None
         lib.oracle_quantize_rows_int8.argtypes = [P, I, I, P, P]
         _lib = lib
@@ -198,13 +198,17 @@ def group_sum_correction(A, delta_bits, C_in, g):
     return out
 
 
-def w4a8(Aq, a_scale, q, s, offsets, g, fold=True, want_acc=True):
-    """Grouped W4A8.  q: [E,K,N] u8, s: [E,G,N] fp16 bits, offsets: [E+1].
+def w4a8(Aq, a_scale, q, s, offsets, g, fold=True, want_acc=True, z=None):
+    """Grouped W4A8.  q: [E,K,N] u8, s: [E,G,N] fp16 bits, offsets: [E+1];
+    z: [E,G,N] fp16 zeros for asymmetric weights (never folded), or None.
     Returns (C fp64 [M_total,N], acc int64 [M_total,G,N] or None)."""
     Aq, pa = _c(Aq, np.int8)
     a_scale, psc = _c(a_scale, np.float32)
     q, pq = _c(q, np.uint8)
     s, ps = _c(_bits16(s), np.uint16)
+    pz = None
+    if z is not None:
+        z, pz = _c(_bits16(z), np.uint16)
     offsets, po = _c(offsets, np.int32)
     E, K, N = q.shape
     M_total = Aq.shape[0]
@@ -212,7 +216,7 @@ def w4a8(Aq, a_scale, q, s, offsets, g, fold=True, want_acc=True):
     C = np.empty((M_total, N), dtype=np.float64)
     acc = np.zeros((M_total, G, N), dtype=np.int64) if want_acc else None
     pacc = acc.ctypes.data_as(ctypes.c_void_p) if want_acc else None
-    rc = _load().oracle_w4a8(pa, psc, pq, ps, po, E, M_total, N, K, int(g), int(bool(fold)),
+    rc = _load().oracle_w4a8(pa, psc, pq, ps, pz, po, E, M_total, N, K, int(g), int(bool(fold)),
                              pacc, C.ctypes.data_as(ctypes.c_void_p))
     if rc != 0:
         raise MemoryError("oracle_w4a8 allocation failed")

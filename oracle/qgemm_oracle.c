@@ -264,46 +264,71 @@ int oracle_group_sum_correction(const uint16_t *A, const uint16_t *delta,
 
 /* ---- [HyperQwen] "why int8 activation quantization (W4A8) is worth doing" ----
  * Grouped W4A8: expert e owns rows offsets[e] .. offsets[e+1]-1 of A_q and its
- * own symmetric 4-bit weights (codes q_e [K,N], scales s_e [G,N]).  Per row m
- * of expert e, per group g and column n, the integer partial product
+ * own 4-bit weights (codes q_e [K,N], scales s_e [G,N]; zeros z_e [G,N] for
+ * an asymmetric weight, z == NULL for a symmetric one).  Per row m of expert
+ * e, per group g and column n, the integer partial product
  *     acc[m,g,n] = sum_{k in g} A_q[m,k] * (v_e[k,n] - 8)
  * is exact (int64 here), and the output is
- *     C[m,n] = a_scale[m] * sum_g s_e[g,n] * acc[m,g,n]       (fp64).
- * Negative scales are folded first when fold != 0, as for W4A16.
- * acc may be NULL.  Returns 0, or -1 on allocation failure.                  */
+ *     symmetric:   C[m,n] = a_scale[m] * sum_g s_e[g,n] * acc[m,g,n]
+ *     asymmetric:  C[m,n] = a_scale[m] * sum_k A_q[m,k] * (v_e[k,n] s_e[g,n] + z_e[g,n])
+ *                         = a_scale[m] * sum_g (s_e[g,n] P[m,g,n] + z_e[g,n] Q[m,g])
+ * with the exact integer sums P = sum_{k in g} A_q v and Q = sum_{k in g} A_q
+ * (the asymmetric form is [HyperQwen] "how to verify", point 2: zero-point
+ * uint4 weights with int8 activations), all in fp64.  Negative scales are
+ * folded first when fold != 0, for a symmetric weight only (an asymmetric
+ * weight is never folded).  acc may be NULL.  Returns 0, or -1 on allocation
+ * failure.                                                                   */
 int oracle_w4a8(const int8_t *Aq, const float *a_scale, const uint8_t *q,
-                const uint16_t *s, const int32_t *offsets, int E, int M_total,
-                int N, int K, int g, int fold, int64_t *acc, double *C)
+                const uint16_t *s, const uint16_t *z, const int32_t *offsets, int E,
+                int M_total, int N, int K, int g, int fold, int64_t *acc, double *C)
 {
     int G = n_groups(K, g);
     size_t KN = (size_t)K * N, GN = (size_t)G * N;
     uint8_t *qc = (uint8_t *)malloc(KN);
     uint16_t *sc = (uint16_t *)malloc(GN * sizeof(uint16_t));
-    int64_t *row_acc = (int64_t *)malloc((size_t)G * N * sizeof(int64_t));
-    if (!qc || !sc || !row_acc) { free(qc); free(sc); free(row_acc); return -1; }
+    int64_t *row_acc = (int64_t *)malloc(GN * sizeof(int64_t));
+    int64_t *row_p = (int64_t *)malloc(GN * sizeof(int64_t));
+    int64_t *row_q = (int64_t *)malloc((size_t)G * sizeof(int64_t));
+    if (!qc || !sc || !row_acc || !row_p || !row_q) {
+        free(qc); free(sc); free(row_acc); free(row_p); free(row_q);
+        return -1;
+    }
     (void)M_total;
     for (int e = 0; e < E; ++e) {
+        const uint16_t *ze = z ? z + (size_t)e * GN : NULL;
         memcpy(qc, q + (size_t)e * KN, KN);
         memcpy(sc, s + (size_t)e * GN, GN * sizeof(uint16_t));
-        if (fold) oracle_fold_negative_scales(qc, sc, K, N, g);
+        if (fold && !ze) oracle_fold_negative_scales(qc, sc, K, N, g);
         for (int m = offsets[e]; m < offsets[e + 1]; ++m) {
-            for (size_t i = 0; i < GN; ++i) row_acc[i] = 0;
+            for (size_t i = 0; i < GN; ++i) row_acc[i] = row_p[i] = 0;
+            for (int gi = 0; gi < G; ++gi) row_q[gi] = 0;
             for (int k = 0; k < K; ++k) {
                 int64_t a = Aq[(size_t)m * K + k];
                 int64_t *ra = row_acc + (size_t)(k / g) * N;
+                int64_t *rp = row_p + (size_t)(k / g) * N;
                 const uint8_t *qr = qc + (size_t)k * N;
-                for (int n = 0; n < N; ++n) ra[n] += a * ((int64_t)qr[n] - 8);
+                row_q[k / g] += a;
+                for (int n = 0; n < N; ++n) {
+                    ra[n] += a * ((int64_t)qr[n] - 8);
+                    rp[n] += a * (int64_t)qr[n];
+                }
             }
             if (acc) memcpy(acc + (size_t)m * GN, row_acc, GN * sizeof(int64_t));
             for (int n = 0; n < N; ++n) {
                 double t = 0.0;
-                for (int gi = 0; gi < G; ++gi)
-                    t += oracle_f16_to_f64(sc[(size_t)gi * N + n]) * (double)row_acc[(size_t)gi * N + n];
+                for (int gi = 0; gi < G; ++gi) {
+                    size_t i = (size_t)gi * N + n;
+                    double sv = oracle_f16_to_f64(sc[i]);
+                    if (ze)
+                        t += sv * (double)row_p[i] + oracle_f16_to_f64(ze[i]) * (double)row_q[gi];
+                    else
+                        t += sv * (double)row_acc[i];
+                }
                 C[(size_t)m * N + n] = (double)a_scale[m] * t;
             }
         }
     }
-    free(qc); free(sc); free(row_acc);
+    free(qc); free(sc); free(row_acc); free(row_p); free(row_q);
     return 0;
 }
 

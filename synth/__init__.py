@@ -100,6 +100,7 @@ class W4A8Case:
     offsets: np.ndarray      # int32 [E + 1]
     g: int
     name: str = ""
+    z: Optional[np.ndarray] = None   # fp16 [E, G, N] zero-points, or None (symmetric)
 
     @property
     def E(self):
@@ -119,8 +120,10 @@ class W4A8Case:
 
 
 def w4a8_case(E, rows_per_expert, K, N, g, signed_scales=False, stream=4, case_id=0,
-              rows=None, name="") -> W4A8Case:
-    """rows: optional explicit per-expert row counts (ragged groups)."""
+              rows=None, name="", asym=False) -> W4A8Case:
+    """rows: optional explicit per-expert row counts (ragged groups).
+    asym: also zero-points z = fp16(-zp * s), zp ~ U{0..15} per group and
+    column (an AWQ-style integer zero-point), drawn after everything else."""
     if rows is None:
         rows = [rows_per_expert] * E
     assert len(rows) == E
@@ -136,7 +139,12 @@ def w4a8_case(E, rows_per_expert, K, N, g, signed_scales=False, stream=4, case_i
         neg = r.random((E, G, N)) < 0.5
         s = np.where(neg, -s, s).astype(np.float16)
     Aq, a_scale = quantize_rows_int8(A16)
-    return W4A8Case(A16=A16, Aq=Aq, a_scale=a_scale, q=q, s=s, offsets=offsets, g=g, name=name)
+    z = None
+    if asym:
+        zp = r.integers(0, 16, size=(E, G, N))
+        z = (-zp * s.astype(np.float64)).astype(np.float16)
+    return W4A8Case(A16=A16, Aq=Aq, a_scale=a_scale, q=q, s=s, offsets=offsets, g=g, name=name,
+                    z=z)
 
 
 # The named workloads: shapes, value recipe and seed stream of each.

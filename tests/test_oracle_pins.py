@@ -341,3 +341,57 @@ def test_quantize_matches_input_preparation(oracle_lib):
     c1, s1 = oracle_lib.quantize_rows_int8(A)
     c2, s2 = synth.quantize_rows_int8(A)
     assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+# ------------------------------------------- W4A8 with zero-points ---------
+def _w4a8_asym_case(**kw):
+    return synth.w4a8_case(E=2, rows_per_expert=5, K=256, N=128, g=128, asym=True, **kw)
+
+
+def test_w4a8_asym_reduces_to_symmetric(oracle_lib):
+    """z = -8s (exact in binary16) makes q s + z = (q - 8) s: the symmetric
+    product, and the same integer accumulators."""
+    c = _w4a8_asym_case()
+    z8 = (-8.0 * c.s.astype(np.float64)).astype(np.float16)
+    assert np.array_equal(z8.astype(np.float64), -8.0 * c.s.astype(np.float64))
+    Ca, acc_a = oracle_lib.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, 128, z=z8)
+    Cs, acc_s = oracle_lib.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, 128, fold=False)
+    np.testing.assert_allclose(Ca, Cs, rtol=1e-12, atol=1e-12 * np.abs(Cs).max())
+    assert np.array_equal(acc_a, acc_s)
+
+
+def test_w4a8_asym_one_hot_rows_pick_weight_rows(oracle_lib):
+    """A row with a single 1 at k and a_scale 1 returns row k of the
+    dequantized asymmetric weight q s + z of its expert (orientation, the
+    zero-point term and the expert's own weights)."""
+    c = _w4a8_asym_case()
+    rng = np.random.default_rng(2)
+    ks = rng.integers(0, 256, size=c.M_total)
+    Aq = np.zeros((c.M_total, 256), np.int8)
+    Aq[np.arange(c.M_total), ks] = 1
+    C, _ = oracle_lib.w4a8(Aq, np.ones(c.M_total, np.float32), c.q, c.s, c.offsets, 128, z=c.z)
+    for e in range(c.E):
+        W = oracle_lib.dequant_asym(c.q[e], c.s[e], c.z[e], 128)
+        for m in range(c.offsets[e], c.offsets[e + 1]):
+            np.testing.assert_allclose(C[m], W[ks[m]], rtol=1e-15, atol=0)
+
+
+def test_w4a8_asym_linear_in_zero_points(oracle_lib):
+    """C(z) - C(z') = a_scale * sum_g Q[m,g] (z - z')[g,n], Q the integer
+    group sums of A_q: the zero-point term alone, in closed form."""
+    c = _w4a8_asym_case()
+    z2 = np.zeros_like(c.z)
+    C1, _ = oracle_lib.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, 128, z=c.z)
+    C0, _ = oracle_lib.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, 128, z=z2)
+    Q = c.Aq.astype(np.int64).reshape(c.M_total, 2, 128).sum(axis=2)
+    for e in range(c.E):
+        rows = slice(c.offsets[e], c.offsets[e + 1])
+        d = (Q[rows].astype(np.float64) @ c.z[e].astype(np.float64)) * c.a_scale[rows, None].astype(np.float64)
+        np.testing.assert_allclose(C1[rows] - C0[rows], d, rtol=1e-9, atol=1e-12 * np.abs(C1).max())
+
+
+def test_w4a8_asym_is_never_folded(oracle_lib):
+    c = _w4a8_asym_case(signed_scales=True)
+    Cf, _ = oracle_lib.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, 128, fold=True, z=c.z)
+    Cn, _ = oracle_lib.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, 128, fold=False, z=c.z)
+    assert np.array_equal(Cf, Cn)
