@@ -165,33 +165,39 @@ def bench_w4a16(name, steps, warmup, flags=0, label=None):
     return res, c
 
 
-def bench_w4a8(name, steps, warmup):
+def bench_w4a8(name, steps, warmup, case=None):
     import numpy as np
     import torch
 
     import int4_weight_only_uint32_amd as qg
     import synth
 
-    c = synth.workload(name)
+    c = case if case is not None else synth.workload(name)
+    asym = c.z is not None
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    packs = [qg.pack(dev(c.q[e]), dev(c.s[e]), None, c.g, fold=True) for e in range(c.E)]
+    packs = [qg.pack(dev(c.q[e]), dev(c.s[e]), dev(c.z[e]) if asym else None, c.g, fold=True)
+             for e in range(c.E)]
     W = torch.stack([p.w for p in packs]).contiguous()
     S = torch.stack([p.scale for p in packs]).contiguous()
-    wb = c.E * weight_bytes(c.K, c.N, c.g, False)
+    D = torch.stack([p.delta for p in packs]).contiguous() if asym else None
+    wb = c.E * weight_bytes(c.K, c.N, c.g, asym)
     R = max(1, math.ceil(ROTATE_BYTES / wb))
     Ws = [W] + [W.clone() for _ in range(R - 1)]
     Ss = [S] + [S.clone() for _ in range(R - 1)]
+    Ds = [D] + [D.clone() for _ in range(R - 1)] if asym else [None] * R
     Aq, asc, off = dev(c.Aq), dev(c.a_scale), dev(c.offsets)
     C = torch.empty((c.M_total, c.N), dtype=torch.float16, device="cuda")
     mr = int(np.max(np.diff(c.offsets)))
 
     def call(i):
-        qg.qgemm_w4a8(Aq, asc, Ws[i], Ss[i], off, c.E, c.M_total, mr, c.N, c.K, c.g, C)
+        qg.qgemm_w4a8(Aq, asc, Ws[i], Ss[i], off, c.E, c.M_total, mr, c.N, c.K, c.g, C,
+                      w_delta=Ds[i])
 
     ms, ms_graph, ms_eager = time_best(call, R, steps, warmup)
     ops = 2.0 * c.M_total * c.N * c.K
     alg = wb + c.M_total * c.K + c.M_total * 4 + c.M_total * c.N * 2
     res = dict(name=name, E=c.E, rows_per_expert=mr, K=c.K, N=c.N, group=c.g,
+               mode="asym" if asym else "sym",
                us_per_call=ms * 1e3, tops=ops / (ms * 1e-3) / 1e12,
                weight_gbps=wb / (ms * 1e-3) / 1e9, total_alg_gbps=alg / (ms * 1e-3) / 1e9,
                weight_bytes=wb, rotated_copies=R,
@@ -199,7 +205,7 @@ def bench_w4a8(name, steps, warmup):
                us_per_call_eager=ms_eager * 1e3)
     res["pct_hbm_weight"] = 100.0 * res["weight_gbps"] / HBM_PEAK_GBPS
     res["pct_int8_mfma"] = 100.0 * res["tops"] / INT8_PEAK_TOPS
-    del Ws, Ss, W, S
+    del Ws, Ss, Ds, W, S, D
     torch.cuda.empty_cache()
     return res
 
@@ -413,6 +419,14 @@ def main():
                 r = bench_w4a8(nm, steps, warmup)
                 log(json.dumps(r))
                 cases.append(r)
+        an = "w4a8-moe-asym-E8x64-K2048-N7168-g128"
+        if not want or an in want:
+            # the expert batch's A, codes and scales, with AWQ-style zero-points
+            ca = synth.w4a8_case(8, 64, 2048, 7168, 128, stream=4, case_id=0, asym=True, name=an)
+            r = bench_w4a8(an, steps, warmup, case=ca)
+            log(json.dumps(r))
+            cases.append(r)
+            del ca
         qn = "quantize-rows-int8-E8x64-K2048+w4a8"
         if not want or qn in want:
             c = synth.workload("w4a8-moe-E8x64-K2048-N7168-g128")

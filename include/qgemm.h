@@ -158,10 +158,15 @@ int group_sum_correction(const uint16_t *A, const uint16_t *delta, uint16_t *C,
                          size_t workspace_bytes, void *stream);
 
 /* ---- grouped W4A8 GEMM ([HyperQwen] "why int8 activation quantization
- *      (W4A8) is worth doing") ----
- * A_q          [M_total,K] int8 per-token codes; a_scale [M_total] fp32.
- * w_packed     E stacked packs (each K*N/8 uint32, symmetric weights).
+ *      (W4A8) is worth doing"; zero-point weights: its verification section,
+ *      point 2) ----
+ * A_q          [M_total,K] int8 per-token codes; a_scale [M_total] fp32
+ *              (quantize_rows_int8 makes both from fp16 activations).
+ * w_packed     E stacked packs (each K*N/8 uint32).
  * w_scale      E stacked [G,N] fp16 scales (the packs' scale_out).
+ * w_delta      NULL for symmetric weights; for asymmetric (zero-point) ones
+ *              the E stacked [G,N] fp16 deltas (the packs' delta_out,
+ *              delta = zero + 8*scale).
  * expert_offsets  DEVICE int32[E+1], non-decreasing, offsets[0] = 0,
  *              offsets[E] = M_total: expert e owns rows offsets[e] ..
  *              offsets[e+1]-1.  NULL means one expert owning all rows (E must
@@ -169,12 +174,17 @@ int group_sum_correction(const uint16_t *A, const uint16_t *delta, uint16_t *C,
  * max_rows_per_expert  an upper bound of offsets[e+1]-offsets[e] over e; rows
  *              of an expert beyond this bound are NOT computed.
  * C            [M_total,N] fp16 out, overwritten:
- *              C[m,n] = a_scale[m] * sum_g scale_e[g,n] * acc[m,g,n]
+ *              C[m,n] = a_scale[m] * sum_g (scale_e[g,n] * acc[m,g,n]
+ *                                           + delta_e[g,n] * qsum[m,g])
  *              acc[m,g,n] = sum_{k in g} A_q[m,k] * (v_e[k,n] - 8)  (int32, exact)
+ *              qsum[m,g]  = sum_{k in g} A_q[m,k]                    (int32, exact)
+ *              (the delta term only with w_delta), in fp32, one rounding to
+ *              fp16 at the end.
  * acc_debug    NULL, or [M_total,G,N] int32 out receiving acc exactly.
  * No workspace (pass NULL, 0).                                              */
 int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed,
-               const uint16_t *w_scale, const int32_t *expert_offsets, int num_experts,
+               const uint16_t *w_scale, const uint16_t *w_delta,
+               const int32_t *expert_offsets, int num_experts,
                int M_total, int max_rows_per_expert, int N, int K, int group_size,
                uint16_t *C, int32_t *acc_debug, void *workspace, size_t workspace_bytes,
                unsigned flags, void *stream);

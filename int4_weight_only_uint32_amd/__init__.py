@@ -75,7 +75,7 @@ def lib():
         L.group_sum_correction.restype = I
         L.group_sum_correction.argtypes = [P, P, P, I, I, I, I, P, Z, P]
         L.qgemm_w4a8.restype = I
-        L.qgemm_w4a8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, Z, U, P]
+        L.qgemm_w4a8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, Z, U, P]
         L.quantize_rows_int8.restype = I
         L.quantize_rows_int8.argtypes = [P, I, I, P, P, P]
         _lib = L
@@ -203,10 +203,11 @@ def correct(A: torch.Tensor, delta: torch.Tensor, C: torch.Tensor, group_size: i
 
 
 def qgemm_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts, M_total,
-               max_rows_per_expert, N, K, group_size, C, acc_debug=None, flags=0):
+               max_rows_per_expert, N, K, group_size, C, acc_debug=None, flags=0, w_delta=None):
     _check(lib().qgemm_w4a8(_ptr(A_q, torch.int8, "A_q"), _ptr(a_scale, torch.float32, "a_scale"),
                             _ptr(w_packed, torch.int32, "w_packed"),
                             _ptr(w_scale, torch.float16, "w_scale"),
+                            _ptr(w_delta, torch.float16, "w_delta"),
                             _ptr(expert_offsets, torch.int32, "expert_offsets"), num_experts,
                             M_total, max_rows_per_expert, N, K, group_size,
                             _ptr(C, torch.float16, "C"), _ptr(acc_debug, torch.int32, "acc_debug"),
@@ -216,12 +217,14 @@ def qgemm_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts, M_t
 def w4a8(A_q: torch.Tensor, a_scale: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor,
          expert_offsets: Optional[torch.Tensor], num_experts: int, max_rows_per_expert: int,
          N: int, group_size: int, C: Optional[torch.Tensor] = None,
-         acc_debug: Optional[torch.Tensor] = None) -> torch.Tensor:
+         acc_debug: Optional[torch.Tensor] = None,
+         w_delta: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Grouped W4A8; w_delta (stacked deltas of asymmetric packs) or None."""
     M_total, K = A_q.shape
     if C is None:
         C = torch.empty((M_total, N), dtype=torch.float16, device=A_q.device)
     qgemm_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts, M_total,
-               max_rows_per_expert, N, K, group_size, C, acc_debug)
+               max_rows_per_expert, N, K, group_size, C, acc_debug, w_delta=w_delta)
     return C
 
 

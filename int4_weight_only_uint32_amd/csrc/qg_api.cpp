@@ -236,7 +236,8 @@ int group_sum_correction(const uint16_t *A, const uint16_t *delta, uint16_t *C, 
 }
 
 int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed,
-               const uint16_t *w_scale, const int32_t *expert_offsets, int num_experts,
+               const uint16_t *w_scale, const uint16_t *w_delta,
+               const int32_t *expert_offsets, int num_experts,
                int M_total, int max_rows_per_expert, int N, int K, int group_size, uint16_t *C,
                int32_t *acc_debug, void *workspace, size_t workspace_bytes, unsigned flags,
                void *stream)
@@ -259,13 +260,14 @@ int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed
     if (K > 131072)
         return fail(QG_ERR_UNSUPPORTED, "qgemm_w4a8: K > 131072 would overflow int32 accumulators");
     if (!aligned(A_q, 8) || !aligned(a_scale, 4) || !aligned(w_packed, 16) ||
-        !aligned(w_scale, 2) || !aligned(C, 2) || (acc_debug && !aligned(acc_debug, 4)) ||
+        !aligned(w_scale, 2) || (w_delta && !aligned(w_delta, 2)) || !aligned(C, 2) ||
+        (acc_debug && !aligned(acc_debug, 4)) ||
         (expert_offsets && !aligned(expert_offsets, 4)))
         return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: misaligned pointer");
     if (flags != 0) return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: unknown flags 0x%x", flags);
     if ((rc = check_device())) return rc;
     int max_rows = max_rows_per_expert > M_total ? M_total : max_rows_per_expert;
-    hipError_t e = qg::launch_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts,
+    hipError_t e = qg::launch_w4a8(A_q, a_scale, w_packed, w_scale, w_delta, expert_offsets, num_experts,
                                    M_total, max_rows, N, K, g, C, acc_debug, (hipStream_t)stream);
     return launch_status(e, "qgemm_w4a8");
 }

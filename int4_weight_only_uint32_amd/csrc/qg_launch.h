@@ -66,10 +66,11 @@ hipError_t launch_group_sum_correction(const uint16_t *A, const uint16_t *D, uin
                                        int M, int N, int K, int g, float *a_sum,
                                        hipStream_t st);
 
+// D: stacked [E,G,N] fp16 deltas of asymmetric weights, or nullptr.
 hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
-                       const uint16_t *S, const int32_t *offsets, int E, int M_total,
-                       int max_rows, int N, int K, int g, uint16_t *C, int32_t *acc_debug,
-                       hipStream_t st);
+                       const uint16_t *S, const uint16_t *D, const int32_t *offsets, int E,
+                       int M_total, int max_rows, int N, int K, int g, uint16_t *C,
+                       int32_t *acc_debug, hipStream_t st);
 
 // Per-row int8 codes and fp32 scales of fp16 activations (K % 8 == 0, A
 // 16-byte and Aq 8-byte aligned).

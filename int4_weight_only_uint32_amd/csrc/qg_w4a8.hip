@@ -1,6 +1,11 @@
-// Grouped W4A8 GEMM: 4-bit symmetric weights x per-token int8 activations on
-// int8 MFMA with exact int32 accumulation per weight group, then per-group and
-// per-token scaling in fp32.
+// Grouped W4A8 GEMM: 4-bit weights x per-token int8 activations on int8 MFMA
+// with exact int32 accumulation per weight group, then per-group and
+// per-token scaling in fp32.  Symmetric weights, (v - 8) s, or asymmetric
+// zero-point ones, v s + z = (v - 8) s + delta with delta = z + 8 s: the
+// delta term needs only the integer group sums of A, taken exactly on the
+// same int8 MFMAs against an all-ones operand (the HyperQwen article's
+// verification section, point 2: zero-point uint4 weights with int8
+// activations).
 //
 // Method: the HyperQwen W4A8 article, section on why int8 activation
 // quantization is worth doing (weights stay int4, activations are quantized per
@@ -31,12 +36,15 @@ namespace qg {
 // fragments, codes and group scales of the next P tiles wait in a register
 // ring whose loads are unconditional (indices clamped to the last tile), so
 // every wait covers only the slot being consumed -- a scale loaded just before
-// its use would wait for every load issued before it.
-template <int NT, int P, bool DEBUG, bool G1>
+// its use would wait for every load issued before it.  DELTA: the group
+// deltas ride in the ring beside the scales, and two more MFMAs per 16-row
+// tile and k-tile sum the tile's activations per row.
+template <int NT, int P, bool DEBUG, bool G1, bool DELTA>
 __global__ __launch_bounds__(256, 2) void w4a8_kernel(
     const int8_t *__restrict__ Aq, const float *__restrict__ a_scale,
     const uint4v *__restrict__ Wall, const uint16_t *__restrict__ Sall,
-    const int32_t *__restrict__ offsets, int M_total, int N, int K, int g,
+    const uint16_t *__restrict__ Dall, const int32_t *__restrict__ offsets, int M_total,
+    int N, int K, int g,
     uint16_t *__restrict__ C, int32_t *__restrict__ acc_debug)
 {
     constexpr int MT = 4;                                  // 64 rows
@@ -61,6 +69,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
     const int nt0 = (blockIdx.x * 4 + wave) * NT;
     const uint4v *W = Wall + (size_t)e * KT * (N / NTILE) * 64;
     const uint16_t *S = Sall + (size_t)e * G * N;
+    const uint16_t *D = DELTA ? Dall + (size_t)e * G * N : nullptr;
     const int sh = 16 * (c & 1);
 
     // ---- A staging: thread t copies 2 x 16 bytes: row t/4 (of 64), bytes
@@ -90,18 +99,21 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
 
     float4v accf[MT][NT];
     int4v acci[MT][NT];
+    int4v qsum[MT];   // DELTA: the group's activation sums, rows 4 kq + r
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt) {
+        qsum[mt] = int4v{0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             accf[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
             acci[mt][t] = int4v{0, 0, 0, 0};
         }
+    }
 
     // register ring: activations, codes, group scales (32-bit pair holding
     // this lane's column, half c & 1)
     uint4v ra[P][2], rw[P][NT];
-    uint32_t rs[P][NT];
+    uint32_t rs[P][NT], rd[P][NT];
     auto load = [&](int kt, int sl) {
         const int k = kt < KT ? kt : KT - 1;
         ra[sl][0] = *reinterpret_cast<const uint4v *>(asrc + k * KTILE);
@@ -112,20 +124,27 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
         const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
 #pragma unroll
         for (int t = 0; t < NT; ++t) rs[sl][t] = srow[8 * t];
+        if (DELTA) {
+            const uint32_t *drow = reinterpret_cast<const uint32_t *>(D + (size_t)gi * N + (col0 & ~1));
+#pragma unroll
+            for (int t = 0; t < NT; ++t) rd[sl][t] = drow[8 * t];
+        }
     };
 
     auto step = [&](int kt, int sl) {
         const int st = kt & 1;
         store_a(st, ra[sl]);
         CodeOpsI8 b[NT];
-        float sv[NT];
+        float sv[NT], dv[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             b[t] = split_codes_i8(rw[sl][t]);
             sv[t] = h2f((uint16_t)(rs[sl][t] >> sh));
+            dv[t] = DELTA ? h2f((uint16_t)(rd[sl][t] >> sh)) : 0.0f;
             pin(b[t].op[0]);
             pin(b[t].op[1]);
             pin(sv[t]);
+            if (DELTA) pin(dv[t]);
         }
         load(kt + P, sl);
         __syncthreads();
@@ -139,6 +158,16 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
         // G1 (one k-tile per group): each tile's group sum starts from a zero
         // MFMA operand, so nothing is reset and nothing stays live across tiles
         const int4v zero4 = {0, 0, 0, 0};
+        if (DELTA) {
+            // sum over k of A[row, k] * 1: every column of the product holds
+            // the row's sum, so each lane gets its own rows' sums
+            const int4v ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                qsum[mt] = mfma_i8(alo[mt], ones, G1 ? zero4 : qsum[mt]);
+                qsum[mt] = mfma_i8(ahi[mt], ones, qsum[mt]);
+            }
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -168,9 +197,14 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
                     } else {
                         accf[mt][t] += sv16 * __builtin_convertvector(acci[mt][t], float4v);
                     }
+                    // the delta term: |qsum| <= 127 g < 2^24, exact in fp32
+                    if (DELTA) accf[mt][t] += dv[t] * __builtin_convertvector(qsum[mt], float4v);
                     if (!G1) acci[mt][t] = int4v{0, 0, 0, 0};
                 }
             }
+            if (DELTA && !G1)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) qsum[mt] = int4v{0, 0, 0, 0};
         }
     };
 
@@ -204,33 +238,46 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
         }
 }
 
-template <int NT, int P, bool DEBUG, bool G1>
+template <int NT, int P, bool DEBUG, bool G1, bool DELTA>
 static hipError_t run_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
-                           const uint16_t *S, const int32_t *offsets, int E, int M_total,
-                           int max_rows, int N, int K, int g, uint16_t *C, int32_t *acc_debug,
-                           hipStream_t st)
+                           const uint16_t *S, const uint16_t *D, const int32_t *offsets, int E,
+                           int M_total, int max_rows, int N, int K, int g, uint16_t *C,
+                           int32_t *acc_debug, hipStream_t st)
 {
     const int NT16 = N / NTILE;
     dim3 grid((unsigned)((NT16 + 4 * NT - 1) / (4 * NT)), (unsigned)((max_rows + 63) / 64), (unsigned)E);
-    hipLaunchKernelGGL((w4a8_kernel<NT, P, DEBUG, G1>), grid, dim3(256), 0, st, Aq, a_scale,
-                       reinterpret_cast<const uint4v *>(W), S, offsets, M_total, N, K, g, C,
+    hipLaunchKernelGGL((w4a8_kernel<NT, P, DEBUG, G1, DELTA>), grid, dim3(256), 0, st, Aq, a_scale,
+                       reinterpret_cast<const uint4v *>(W), S, D, offsets, M_total, N, K, g, C,
                        acc_debug);
     return hipGetLastError();
 }
 
-hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
-                       const uint16_t *S, const int32_t *offsets, int E, int M_total,
-                       int max_rows, int N, int K, int g, uint16_t *C, int32_t *acc_debug,
-                       hipStream_t st)
+template <bool DEBUG, bool G1>
+static hipError_t run_w4a8_d(const int8_t *Aq, const float *a_scale, const uint32_t *W,
+                             const uint16_t *S, const uint16_t *D, const int32_t *offsets, int E,
+                             int M_total, int max_rows, int N, int K, int g, uint16_t *C,
+                             int32_t *acc_debug, hipStream_t st)
 {
     // N % 128 == 0 -> the n-tile count is a multiple of 8: NT = 2 tiles the
-    // columns exactly (4 waves x 2 n-tiles = 128 columns per workgroup)
+    // columns exactly (4 waves x 2 n-tiles = 128 columns per workgroup).
+    // With deltas and groups of several k-tiles the group's activation sums
+    // stay live across tiles too: a ring of 2 (204 VGPRs) instead of 3, which
+    // would spill at two workgroups per CU.
+    return D ? run_w4a8<2, G1 ? 3 : 2, DEBUG, G1, true>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)
+             : run_w4a8<2, 3, DEBUG, G1, false>(Aq, a_scale, W, S, nullptr, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
+}
+
+hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
+                       const uint16_t *S, const uint16_t *D, const int32_t *offsets, int E,
+                       int M_total, int max_rows, int N, int K, int g, uint16_t *C,
+                       int32_t *acc_debug, hipStream_t st)
+{
     const bool g1 = g == KTILE;
     if (acc_debug)
-        return g1 ? run_w4a8<2, 3, true, true>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)
-                  : run_w4a8<2, 3, true, false>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
-    return g1 ? run_w4a8<2, 3, false, true>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st)
-              : run_w4a8<2, 3, false, false>(Aq, a_scale, W, S, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st);
+        return g1 ? run_w4a8_d<true, true>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)
+                  : run_w4a8_d<true, false>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
+    return g1 ? run_w4a8_d<false, true>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st)
+              : run_w4a8_d<false, false>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st);
 }
 
 } // namespace qg

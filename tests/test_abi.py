@@ -114,7 +114,7 @@ def test_pack_validation():
 
 def test_w4a8_validation():
     L = qg.lib()
-    args = lambda **kw: [kw.get("A", FAKE), FAKE, FAKE, FAKE, kw.get("off", None), kw.get("E", 1),
+    args = lambda **kw: [kw.get("A", FAKE), FAKE, FAKE, FAKE, kw.get("D", None), kw.get("off", None), kw.get("E", 1),
                          kw.get("M", 64), kw.get("mr", 64), 1024, kw.get("K", 1024), 128, FAKE,
                          None, None, 0, kw.get("flags", 0), None]
     assert L.qgemm_w4a8(*args(E=2)) == qg.QG_ERR_INVALID_ARG          # offsets needed
@@ -123,6 +123,7 @@ def test_w4a8_validation():
     assert L.qgemm_w4a8(*args(flags=1)) == qg.QG_ERR_INVALID_ARG
     assert L.qgemm_w4a8(*args(A=P(0x10004))) == qg.QG_ERR_INVALID_ARG
     assert L.qgemm_w4a8(*args(K=1000)) == qg.QG_ERR_UNSUPPORTED
+    assert L.qgemm_w4a8(*args(D=P(0x10001))) == qg.QG_ERR_INVALID_ARG  # misaligned deltas
 
 
 def test_group_sum_correction_validation():

@@ -329,28 +329,38 @@ def test_group_sum_correction(M, K, N, g):
 
 
 # ------------------------------------------------------------------ W4A8 --
-def _run_w4a8(case, max_rows=None, offsets=True, fold=True):
-    E, K, N, g = case.E, case.K, case.N, case.g
-    ws, ss = [], []
-    for e in range(E):
-        pw = qg.pack(dev(case.q[e]), dev(case.s[e]), None, g, fold=fold)
+def _pack_w4a8(case, fold=True):
+    """Stacked packs of the experts' weights: (W, S, D), D None if symmetric."""
+    ws, ss, ds = [], [], []
+    for e in range(case.E):
+        z = dev(case.z[e]) if case.z is not None else None
+        pw = qg.pack(dev(case.q[e]), dev(case.s[e]), z, case.g, fold=fold)
         ws.append(pw.w)
         ss.append(pw.scale)
-    W = torch.stack(ws).contiguous()
-    S = torch.stack(ss).contiguous()
+        ds.append(pw.delta)
+    D = torch.stack(ds).contiguous() if case.z is not None else None
+    return torch.stack(ws).contiguous(), torch.stack(ss).contiguous(), D
+
+
+def _run_w4a8(case, max_rows=None, offsets=True, fold=True, debug=True):
+    E, K, N, g = case.E, case.K, case.N, case.g
+    W, S, D = _pack_w4a8(case, fold)
     G = K // g
-    acc = torch.full((case.M_total, G, N), -7, dtype=torch.int32, device="cuda")
+    acc = torch.full((case.M_total, G, N), -7, dtype=torch.int32, device="cuda") if debug else None
     off = dev(case.offsets) if offsets else None
     mr = max_rows if max_rows is not None else int(np.max(np.diff(case.offsets)))
-    C = qg.w4a8(dev(case.Aq), dev(case.a_scale), W, S, off, E, max(mr, 1), N, g, acc_debug=acc)
+    C = qg.w4a8(dev(case.Aq), dev(case.a_scale), W, S, off, E, max(mr, 1), N, g, acc_debug=acc,
+                w_delta=D)
     torch.cuda.synchronize()
-    return host(C).astype(np.float64), host(acc)
+    return host(C).astype(np.float64), host(acc) if debug else None
 
 
 def _check_w4a8(case, **kw):
-    note(f"w4a8 {case.name} E={case.E} rows={np.diff(case.offsets).tolist()} K={case.K} N={case.N}")
+    note(f"w4a8 {case.name} E={case.E} rows={np.diff(case.offsets).tolist()} K={case.K} N={case.N}"
+         f" asym={case.z is not None}")
     got, acc = _run_w4a8(case, **kw)
-    ref, ref_acc = oracle.w4a8(case.Aq, case.a_scale, case.q, case.s, case.offsets, case.g, fold=True)
+    ref, ref_acc = oracle.w4a8(case.Aq, case.a_scale, case.q, case.s, case.offsets, case.g, fold=True,
+                               z=case.z)
     assert np.array_equal(acc.astype(np.int64), ref_acc)
     err = rel_fro(got, ref)
     assert err <= W4A8_TOL, err
@@ -375,3 +385,62 @@ def test_w4a8_single_expert_no_offsets():
     _check_w4a8(c, offsets=False)
     c2 = synth.w4a8_case(1, 7, 768, 128, 768, stream=85, case_id=2)
     _check_w4a8(c2, offsets=False)
+
+
+# ------------------------------------------------ W4A8 with zero-points --
+def test_w4a8_moe_asym():
+    """The expert-batch workload with AWQ-style zero-points (the same A, codes
+    and scales): exact accumulators, the output within the W4A8 tolerance of
+    the oracle (which uses the zeros themselves, not the fp16 deltas), and the
+    accumulator-debug and plain instantiations bit-identical."""
+    c = synth.w4a8_case(8, 64, 2048, 7168, 128, stream=4, case_id=0, asym=True,
+                        name="w4a8-moe-asym")
+    err = _check_w4a8(c)
+    note(f"w4a8 moe asym rel_fro = {err:.3e}")
+    plain, _ = _run_w4a8(c, debug=False)
+    dbg, _ = _run_w4a8(c, debug=True)
+    assert np.array_equal(plain, dbg)
+
+
+def test_w4a8_asym_ragged_group256_signed():
+    """Group 256 (two k-tiles per group: the sums carry across tiles), ragged
+    experts, and negative scales that an asymmetric weight never folds."""
+    c = synth.w4a8_case(4, 0, 1024, 256, 256, signed_scales=True, stream=85, case_id=2,
+                        rows=[33, 0, 70, 5], asym=True, name="w4a8-asym-g256")
+    _check_w4a8(c)
+    plain, _ = _run_w4a8(c, debug=False)
+    dbg, _ = _run_w4a8(c, debug=True)
+    assert np.array_equal(plain, dbg)
+
+
+def test_w4a8_asym_zero_delta_equals_symmetric():
+    """z = -8s makes every delta exactly 0: the asymmetric call returns the
+    symmetric call's output."""
+    c = synth.w4a8_case(2, 48, 512, 256, 128, stream=85, case_id=3, asym=True)
+    z8 = (-8.0 * c.s.astype(np.float64)).astype(np.float16)
+    assert np.array_equal(z8.astype(np.float64), -8.0 * c.s.astype(np.float64))
+    c.z = z8
+    got_a, acc_a = _run_w4a8(c)
+    c.z = None
+    got_s, acc_s = _run_w4a8(c, fold=False)
+    assert np.array_equal(acc_a, acc_s)
+    assert np.array_equal(got_a, got_s)
+
+
+def test_w4a8_asym_integer_exact():
+    """Scale 1, integer zero-points, unit token scales and sparse +-1
+    activations: every output is an integer below 2048, which the fp32
+    arithmetic and the fp16 store represent exactly -- the GPU must match the
+    oracle bit for bit, both instantiations."""
+    c = synth.w4a8_case(2, 40, 256, 128, 128, stream=85, case_id=4, asym=True)
+    rng = np.random.default_rng(9)
+    c.s = np.ones_like(c.s)
+    c.z = rng.integers(-8, 8, size=c.z.shape).astype(np.float16)
+    Aq = rng.choice(np.array([-1, 0, 0, 0, 0, 0, 0, 0, 1], np.int8), size=c.Aq.shape)
+    c.Aq = Aq
+    c.a_scale = np.ones_like(c.a_scale)
+    ref, _ = oracle.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, c.g, z=c.z)
+    assert np.all(np.abs(ref) < 2048) and np.array_equal(ref, np.round(ref))
+    for debug in (True, False):
+        got, _ = _run_w4a8(c, debug=debug)
+        assert np.array_equal(got, ref)
