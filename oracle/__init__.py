@@ -62,6 +62,8 @@ def _load():
         lib.oracle_w4a8.restype = I
         lib.oracle_w4a8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P]
         lib.oracle_quantize_rows_int8.restype = None
+        lib.oracle_silu_mul.restype = None
+        lib.oracle_silu_mul.argtypes = [P, I, I, P]
         lib.oracle_quantize_rows_int8.argtypes = [P, I, I, P, P]
         _lib = lib
     return _lib
@@ -233,3 +235,18 @@ def quantize_rows_int8(A):
     _load().oracle_quantize_rows_int8(pa, M, K, codes.ctypes.data_as(ctypes.c_void_p),
                                       sc.ctypes.data_as(ctypes.c_void_p))
     return codes, sc
+
+
+def silu_mul(C):
+    """H = silu(C[:, :N]) * C[:, N:] for C fp64 [M, 2N]."""
+    C, pc = _c(C, np.float64)
+    M, N2 = C.shape
+    H = np.empty((M, N2 // 2), dtype=np.float64)
+    _load().oracle_silu_mul(pc, M, N2 // 2, H.ctypes.data_as(ctypes.c_void_p))
+    return H
+
+
+def w4a16_swiglu(A, q, s, z, g, fold=True):
+    """SwiGLU of a gate/up pair held as one weight [K, 2N] (gate columns
+    first): silu(A . W_gate) * (A . W_up), fp64 [M, N]."""
+    return silu_mul(w4a16(A, q, s, z, g, fold=fold))

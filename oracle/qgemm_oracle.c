@@ -365,3 +365,19 @@ void oracle_quantize_rows_int8(const uint16_t *A, int M, int K, int8_t *Aq, floa
         }
     }
 }
+
+/* ---- [Marlin-Ada] "Gaps and follow-ups": the fused SwiGLU of an MLP's gate
+ * and up projections (mlp_gate and mlp_up in one kernel).  The page does not
+ * define it; the standard definition is used:
+ *     H[m,n] = silu(G[m,n]) * U[m,n],   silu(x) = x / (1 + exp(-x))
+ * where G = C[:, 0:N] and U = C[:, N:2N] are the two halves of the product
+ * C = A . [W_gate | W_up]  ([M, 2N], row-major, fp64).                      */
+void oracle_silu_mul(const double *C, int M, int N, double *H)
+{
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n) {
+            double g = C[(size_t)m * 2 * N + n];
+            double u = C[(size_t)m * 2 * N + N + n];
+            H[(size_t)m * N + n] = g / (1.0 + exp(-g)) * u;
+        }
+}

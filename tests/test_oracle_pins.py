@@ -395,3 +395,52 @@ def test_w4a8_asym_is_never_folded(oracle_lib):
     Cf, _ = oracle_lib.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, 128, fold=True, z=c.z)
     Cn, _ = oracle_lib.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, 128, fold=False, z=c.z)
     assert np.array_equal(Cf, Cn)
+
+
+# ---------------------------------------------------------- SwiGLU ---------
+def test_silu_mul_closed_forms(oracle_lib):
+    """With the up half 1, H = silu(x): silu(x) - silu(-x) = x (sigmoid(x) +
+    sigmoid(-x) = 1), silu(ln 3) = (3/4) ln 3 (sigmoid(ln 3) = 3/4), silu(0) =
+    0, silu(40) = 40 and silu(-40) vanishes in fp64."""
+    x = np.concatenate([np.linspace(-12, 12, 97), [np.log(3.0), 40.0, -40.0, 0.0]])
+    C = np.stack([np.concatenate([x, np.ones_like(x)]), np.concatenate([-x, np.ones_like(x)])])
+    H = oracle_lib.silu_mul(C)
+    np.testing.assert_allclose(H[0] - H[1], x, rtol=1e-14, atol=1e-14)
+    n = len(x)
+    assert abs(H[0, n - 4] - 0.75 * np.log(3.0)) < 1e-15
+    assert H[0, n - 3] == 40.0 and abs(H[0, n - 2]) < 1e-15 and H[0, n - 1] == 0.0
+
+
+def test_silu_mul_gate_is_the_first_half(oracle_lib):
+    """Zero gate or zero up gives 0; [x | 1] gives silu(x) while [1 | x] gives
+    silu(1) x -- the halves are not interchangeable."""
+    x = np.linspace(-3, 3, 13)            # holds 1.0 at index 8
+    one, zero = np.ones_like(x), np.zeros_like(x)
+    H = oracle_lib.silu_mul(np.stack([np.concatenate([zero, x]), np.concatenate([x, zero]),
+                                      np.concatenate([x, one]), np.concatenate([one, x])]))
+    assert np.all(H[0] == 0) and np.all(H[1] == 0)
+    silu1 = H[2, 8]
+    np.testing.assert_allclose(H[3], silu1 * x, rtol=1e-15, atol=0)
+    assert not np.allclose(H[2], H[3])
+
+
+def test_w4a16_swiglu_halves(oracle_lib):
+    """The pair's product is the two plain products side by side: with a
+    gate whose product is 0 (codes 8, symmetric) the output is 0, and with up
+    codes 9 at scale 1 (W_up = 1 everywhere) the output is silu of the gate
+    product times the row sums of A."""
+    rng = np.random.default_rng(4)
+    M, K, N, g = 3, 256, 32, 128
+    A = (rng.standard_normal((M, K)) * 0.05).astype(np.float16)
+    qg_ = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    s = rng.uniform(1e-3, 2e-2, size=(K // g, 2 * N)).astype(np.float16)
+    q = np.concatenate([np.full((K, N), 8, np.uint8), qg_], axis=1)
+    H0 = oracle_lib.w4a16_swiglu(A, q, s, None, g)
+    assert np.all(H0 == 0)
+    q = np.concatenate([qg_, np.full((K, N), 9, np.uint8)], axis=1)
+    s1 = s.copy()
+    s1[:, N:] = 1.0
+    H = oracle_lib.w4a16_swiglu(A, q, s1, None, g)
+    Cg = oracle_lib.w4a16(A, qg_, s[:, :N], None, g)
+    rows = A.astype(np.float64).sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(H, Cg / (1 + np.exp(-Cg)) * rows, rtol=1e-12, atol=1e-15)
