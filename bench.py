@@ -319,6 +319,52 @@ def cpu_baseline(case):
                        f"asym ({dt:.2f} s wall, fp64 dequant + naive m-k-n loop)")
 
 
+def bench_swiglu(name, steps, warmup, M, K, N, g):
+    """SwiGLU of a gate/up pair (one packed [K, 2N] weight) against the plain
+    GEMM of the same pair (its [M, 2N] product, no activation)."""
+    import numpy as np
+    import torch
+
+    import int4_weight_only_uint32_amd as qg
+    import synth
+
+    c = synth.w4a16_case(M, K, 2 * N, g, asym=True, stream=91, case_id=99)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    pair = qg.pack(dev(c.q), dev(c.s), dev(c.z), g)
+    wb = weight_bytes(K, 2 * N, g, True)
+    R = max(1, math.ceil(ROTATE_BYTES / wb))
+    copies = [pair] + [qg.PackedWeight(w=pair.w.clone(), scale=pair.scale.clone(),
+                                       delta=pair.delta.clone(), K=K, N=2 * N, group_size=g)
+                       for _ in range(R - 1)]
+    A = dev(c.A)
+    H = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    Y = torch.empty((M, 2 * N), dtype=torch.float16, device="cuda")
+    n = max(qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, M, N, K, g, 1, 0),
+            qg.qg_workspace_bytes(qg.QG_OP_W4A16, M, 2 * N, K, g, 1, 0), 256)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+
+    def fused(i):
+        p = copies[i]
+        qg.qgemm_w4a16_swiglu(A, p.w, p.scale, p.delta, H, M, N, K, g, 0, ws)
+
+    def gemm(i):
+        p = copies[i]
+        qg.qgemm_w4a16(A, p.w, p.scale, p.delta, Y, M, 2 * N, K, g, 0, ws)
+
+    ms, ms_graph, ms_eager = time_best(fused, R, steps, warmup)
+    ms_gemm, _, _ = time_best(gemm, R, steps, warmup)
+    res = dict(name=name, M=M, K=K, N=N, group=g, mode="asym", us_per_call=ms * 1e3,
+               weight_bytes=wb, weight_gbps=wb / (ms * 1e-3) / 1e9,
+               tflops=4.0 * M * N * K / (ms * 1e-3) / 1e12, rotated_copies=R,
+               us_pair_gemm_only=ms_gemm * 1e3,
+               us_per_call_graph=ms_graph * 1e3 if ms_graph else None,
+               us_per_call_eager=ms_eager * 1e3)
+    res["pct_hbm_weight"] = 100.0 * res["weight_gbps"] / HBM_PEAK_GBPS
+    del copies, A, H, Y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_quantize(name, steps, warmup, A16, gemm=None):
     """Per-row int8 quantization of the fp16 activations A16 [M,K]; with
     `gemm` (the W4A8 case) also the quantizer followed by the W4A8 GEMM, the
@@ -427,6 +473,11 @@ def main():
             log(json.dumps(r))
             cases.append(r)
             del ca
+        sn = "w4a16-swiglu-decode-M16-K5120-N17408x2-g128-asym"
+        if not want or sn in want:
+            r = bench_swiglu(sn, steps, warmup, 16, 5120, 17408, 128)
+            log(json.dumps(r))
+            cases.append(r)
         qn = "quantize-rows-int8-E8x64-K2048+w4a8"
         if not want or qn in want:
             c = synth.workload("w4a8-moe-E8x64-K2048-N7168-g128")

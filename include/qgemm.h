@@ -87,6 +87,7 @@ extern "C" {
 #define QG_OP_W4A8                  2
 #define QG_OP_GROUP_SUM_CORRECTION  3
 #define QG_OP_PACK                  4
+#define QG_OP_W4A16_SWIGLU          5
 
 /* 1 if HIP device `device` is a gfx950 GPU this library has kernels for,
  * else 0 (also 0 when the device does not exist).  The analogue of the pages'
@@ -146,6 +147,30 @@ int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *sca
                 const uint16_t *delta, uint16_t *C, int M, int N, int K,
                 int group_size, unsigned flags, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/* ---- SwiGLU of an MLP's gate and up projections in one call ([Marlin-Ada]
+ *      "Gaps and follow-ups": the fused mlp_gate + mlp_up dispatch) ----
+ * The pair is ONE packed weight of shape [K, 2N]: pack_int4_weights on the
+ * codes [W_gate | W_up] (gate columns 0..N-1, up columns N..2N-1) and their
+ * [G, 2N] scales (and zeros) concatenated the same way.
+ * A        [M,K] fp16, 16-byte aligned.
+ * w_packed, scale, delta: the pair's pack (delta NULL for symmetric weights).
+ * H        [M,N] fp16 out, 16-byte aligned, OVERWRITTEN with
+ *            H[m,n] = silu(G[m,n]) * U[m,n],  silu(x) = x / (1 + exp(-x)),
+ *          G = A . W_gate and U = A . W_up with their delta terms fused.
+ *          M <= 16 (when the decode kernel takes the pair): one launch, G and
+ *          U in fp32 and H rounded once; otherwise G and U are stored as fp16
+ *          in the workspace and a second kernel forms H (two roundings).
+ * N % 128 == 0 (the output width), K and group_size as for qgemm_w4a16.
+ * flags    must be 0.
+ * workspace/workspace_bytes: qg_workspace_bytes(QG_OP_W4A16_SWIGLU, M, N, K,
+ *          group_size, 1, 0) bytes, 256-byte aligned (NULL when 0); it starts
+ *          with the same counter region as a W4A16 workspace (zero-filled
+ *          once, left at zero by every call), so one workspace of the larger
+ *          size serves both kinds of call on one stream.                    */
+int qgemm_w4a16_swiglu(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,
+                       const uint16_t *delta, uint16_t *H, int M, int N, int K, int group_size,
+                       unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---- asymmetric correction as its own two stages ([Marlin-Ada] "The
  *      pipeline, end to end", a_group_sum and correction_accum) ----

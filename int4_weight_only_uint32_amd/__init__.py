@@ -36,10 +36,11 @@ QG_OP_W4A16 = 1
 QG_OP_W4A8 = 2
 QG_OP_GROUP_SUM_CORRECTION = 3
 QG_OP_PACK = 4
+QG_OP_W4A16_SWIGLU = 5
 
 EXPORTED = ("qg_device_supported", "qg_status_string", "qg_last_error", "qg_workspace_bytes",
             "pack_int4_weights", "qgemm_w4a16", "group_sum_correction", "qgemm_w4a8",
-            "quantize_rows_int8")
+            "quantize_rows_int8", "qgemm_w4a16_swiglu")
 
 
 class QGemmError(RuntimeError):
@@ -76,6 +77,8 @@ def lib():
         L.group_sum_correction.argtypes = [P, P, P, I, I, I, I, P, Z, P]
         L.qgemm_w4a8.restype = I
         L.qgemm_w4a8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, Z, U, P]
+        L.qgemm_w4a16_swiglu.restype = I
+        L.qgemm_w4a16_swiglu.argtypes = [P, P, P, P, P, I, I, I, I, U, P, Z, P]
         L.quantize_rows_int8.restype = I
         L.quantize_rows_int8.argtypes = [P, I, I, P, P, P]
         _lib = L
@@ -245,3 +248,29 @@ def quantize_rows(A: torch.Tensor, A_q: Optional[torch.Tensor] = None,
         raise ValueError(f"A_q must be [{M},{K}] and a_scale [{M}]")
     quantize_rows_int8(A, M, K, A_q, a_scale)
     return A_q, a_scale
+
+
+def qgemm_w4a16_swiglu(A, w_packed, scale, delta, H, M, N, K, group_size, flags=0, workspace=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().qgemm_w4a16_swiglu(_ptr(A, torch.float16, "A"), _ptr(w_packed, torch.int32, "w_packed"),
+                                    _ptr(scale, torch.float16, "scale"), _ptr(delta, torch.float16, "delta"),
+                                    _ptr(H, torch.float16, "H"), M, N, K, group_size, flags,
+                                    _ptr(workspace, None, "workspace"), nbytes, _stream(A)))
+
+
+def w4a16_swiglu(A: torch.Tensor, pair: PackedWeight, H: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """silu(A . W_gate) * (A . W_up) for a gate/up pair packed as one [K, 2N]
+    weight (gate columns first)."""
+    M, K = A.shape
+    N = pair.N // 2
+    if H is None:
+        H = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    if tuple(H.shape) != (M, N):
+        raise ValueError(f"H must be [{M},{N}]")
+    if workspace is None:
+        n = qg_workspace_bytes(QG_OP_W4A16_SWIGLU, M, N, K, pair.group_size, 1, 0)
+        if n > 0:
+            workspace = workspace_for(A.device, n)
+    qgemm_w4a16_swiglu(A, pair.w, pair.scale, pair.delta, H, M, N, K, pair.group_size, 0, workspace)
+    return H

@@ -142,6 +142,10 @@ size_t qg_workspace_bytes(int op, int M, int N, int K, int group_size, int num_e
     case QG_OP_W4A16:
         if (check_shape("qg_workspace_bytes", M, N, K, &g) != QG_OK) return (size_t)-1;
         return w4a16_ws_bytes(M, N, K, g, (flags & QG_CORR_SEPARATE) != 0);
+    case QG_OP_W4A16_SWIGLU:
+        if (check_shape("qg_workspace_bytes", M, N, K, &g) != QG_OK) return (size_t)-1;
+        if (N > 0x3FFFFFFF) return (size_t)-1;
+        return qg::swiglu_workspace_bytes(M, N, K);
     case QG_OP_GROUP_SUM_CORRECTION:
         if (check_shape("qg_workspace_bytes", M, N, K, &g) != QG_OK) return (size_t)-1;
         return corr_ws_bytes(M, K, g);
@@ -210,6 +214,36 @@ int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *sca
         e = qg::launch_group_sum_correction(A, delta, C, M, N, K, g,
                                             (float *)((char *)workspace + align256(gemm_ws)), st);
     return launch_status(e, "qgemm_w4a16");
+}
+
+int qgemm_w4a16_swiglu(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,
+                       const uint16_t *delta, uint16_t *H, int M, int N, int K, int group_size,
+                       unsigned flags, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int g = group_size;
+    int rc = check_shape("qgemm_w4a16_swiglu", M, N, K, &g);
+    if (rc) return rc;
+    if (N > 0x3FFFFFFF || (size_t)K * 2 * (size_t)N / 8 > 0x7FFFFFFFull * 16)
+        return fail(QG_ERR_UNSUPPORTED, "qgemm_w4a16_swiglu: shape too large");
+    if (!A || !w_packed || !scale || !H)
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16_swiglu: NULL A/w_packed/scale/H");
+    if (!aligned(A, 16) || !aligned(w_packed, 16) || !aligned(scale, 2) || !aligned(H, 16) ||
+        (delta && !aligned(delta, 2)))
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16_swiglu: misaligned pointer");
+    if (flags != 0)
+        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16_swiglu: unknown flags 0x%x", flags);
+    const size_t need = qg::swiglu_workspace_bytes(M, N, K);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(QG_ERR_WORKSPACE, "qgemm_w4a16_swiglu: workspace of %zu bytes needed, got %zu",
+                        need, workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 256))
+            return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16_swiglu: workspace must be 256-byte aligned");
+    }
+    if ((rc = check_device())) return rc;
+    hipError_t e = qg::launch_w4a16_swiglu(A, w_packed, scale, delta, H, M, N, K, g,
+                                           need ? workspace : nullptr, (hipStream_t)stream);
+    return launch_status(e, "qgemm_w4a16_swiglu");
 }
 
 int group_sum_correction(const uint16_t *A, const uint16_t *delta, uint16_t *C, int M, int N,

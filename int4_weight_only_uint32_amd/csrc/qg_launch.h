@@ -61,6 +61,15 @@ hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                         const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                         bool fuse_delta, void *ws, hipStream_t st);
 
+// H = silu(A . W[:, :N]) * (A . W[:, N:]) for a gate/up pair packed as one
+// [K, 2N] weight; `ws` of swiglu_workspace_bytes(M, N, K) bytes (counters
+// first, zero-filled once, as for the W4A16 workspace).
+bool swiglu_uses_decode(int M, int N, int K);
+size_t swiglu_workspace_bytes(int M, int N, int K);
+hipError_t launch_w4a16_swiglu(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                               const uint16_t *D, uint16_t *H, int M, int N, int K, int g,
+                               void *ws, hipStream_t st);
+
 // a_sum[M, K/g] (fp32) into `a_sum`, then C += a_sum @ delta.
 hipError_t launch_group_sum_correction(const uint16_t *A, const uint16_t *D, uint16_t *C,
                                        int M, int N, int K, int g, float *a_sum,

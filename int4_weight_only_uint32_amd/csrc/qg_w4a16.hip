@@ -235,7 +235,12 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
 // accesses touch the shared slots, so no cache-wide fence is needed; the
 // workspace counters must be zero before the first call and stay zero
 // between calls.
-template <int NT, int P, int WV, bool DELTA>
+// GATED: W is a gate/up pair packed as one [K, N] weight (gate columns
+// 0 .. N/2-1, up columns N/2 .. N-1) and C receives silu(gate) * up [M, N/2].
+// Waves 0, 1 of workgroup cg take gate n-tiles 2cg, 2cg+1, waves 2, 3 the up
+// n-tiles of the same columns; after the (split-K) sums, the up waves hand
+// their values to the gate waves through LDS.
+template <int NT, int P, int WV, bool DELTA, bool GATED = false>
 __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g,
@@ -243,9 +248,11 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
 {
     static_assert(NT == 1, "the scale table holds one column per lane");
     static_assert(WV == 4 || WV == 8, "4 or 8 waves per workgroup");
+    static_assert(!GATED || WV == 4, "the gate/up pairing takes 4 waves");
     constexpr int COLS = 16 * WV;            // columns per workgroup
     __shared__ __attribute__((aligned(16))) _Float16 As[2][16 * KTILE];
     __shared__ unsigned arrived;
+    __shared__ float xch[GATED ? 2 * 4 * 64 : 1];   // up values for the gate waves
     // (scale | delta << 16) of this workgroup's 64 columns for every group its
     // k-range touches: filled once, read once per k-tile (an LDS read instead
     // of two global loads per k-tile)
@@ -258,8 +265,10 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const int kt_beg = (sp * KT) / nsplit, kt_end = ((sp + 1) * KT) / nsplit;
     const int n = kt_end - kt_beg;
     const int last = kt_end - 1;
-    const int nt0 = (cg * WV + wave) * NT;
-    const int col0 = nt0 * NTILE + c;
+    const int Nh = N / 2;                    // GATED: output width
+    const int nt0 = GATED ? (wave < 2 ? 2 * cg + wave : Nh / NTILE + 2 * cg + wave - 2)
+                          : (cg * WV + wave) * NT;
+    const int col0 = GATED ? 32 * cg + 16 * (wave & 1) + c : nt0 * NTILE + c;
 
     // scale table: its loads are issued first (the oldest in flight), and,
     // when it fits in TB words per thread, written to LDS only after the
@@ -270,8 +279,12 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const int ng = n > 0 ? ((kt_end - 1) * KTILE) / g - gi0 + 1 : 0;
     const int total = ng * (COLS / 2);
     const bool tfast = total <= TB * 64 * WV;
-    const uint32_t *s32 = reinterpret_cast<const uint32_t *>(S) + (size_t)gi0 * (N / 2) + cg * (COLS / 2);
-    const uint32_t *d32 = DELTA ? reinterpret_cast<const uint32_t *>(D) + (size_t)gi0 * (N / 2) + cg * (COLS / 2) : nullptr;
+    // scale pairs of the table's COLS columns: contiguous, or (GATED) the 32
+    // gate columns 32cg.. and the 32 up columns Nh + 32cg..
+    const int pbase = GATED ? 16 * cg : cg * (COLS / 2);
+    const int pgap = GATED ? Nh / 2 - 16 : 0;   // added to pairs 16.. (GATED)
+    const uint32_t *s32 = reinterpret_cast<const uint32_t *>(S) + (size_t)gi0 * (N / 2) + pbase;
+    const uint32_t *d32 = DELTA ? reinterpret_cast<const uint32_t *>(D) + (size_t)gi0 * (N / 2) + pbase : nullptr;
     uint32_t tsv[TB], tdv[TB];
     if (n > 0) {
         if (tfast) {
@@ -281,14 +294,16 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
                 int idx = tid + i * 64 * WV;
                 idx = idx < total ? idx : total - 1;
                 const int gl = idx / (COLS / 2), pr = idx % (COLS / 2);
-                tsv[i] = s32[(size_t)gl * (N / 2) + pr];
-                tdv[i] = DELTA ? d32[(size_t)gl * (N / 2) + pr] : 0u;
+                const int sp2 = pr + (GATED && pr >= 16 ? pgap : 0);
+                tsv[i] = s32[(size_t)gl * (N / 2) + sp2];
+                tdv[i] = DELTA ? d32[(size_t)gl * (N / 2) + sp2] : 0u;
             }
         } else {
             for (int idx = tid; idx < total; idx += 64 * WV) {
                 const int gl = idx / (COLS / 2), pr = idx % (COLS / 2);
-                const uint32_t s2 = s32[(size_t)gl * (N / 2) + pr];
-                const uint32_t d2 = DELTA ? d32[(size_t)gl * (N / 2) + pr] : 0u;
+                const int sp2 = pr + (GATED && pr >= 16 ? pgap : 0);
+                const uint32_t s2 = s32[(size_t)gl * (N / 2) + sp2];
+                const uint32_t d2 = DELTA ? d32[(size_t)gl * (N / 2) + sp2] : 0u;
                 sdt[gl * COLS + 2 * pr] = (s2 & 0xFFFFu) | (d2 << 16);
                 sdt[gl * COLS + 2 * pr + 1] = (s2 >> 16) | (d2 & 0xFFFF0000u);
             }
@@ -403,15 +418,34 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
             if (j + i < n) step(kt_beg + j + i, i, last);
     }
 
-    // C rows 4 kq + r, columns (nt0 + t) * 16 + c
-    if (nsplit == 1) {
+    // C rows 4 kq + r, columns (nt0 + t) * 16 + c; GATED: silu(gate) * up
+    // into C [M, Nh] by the gate waves (reached by every thread of the
+    // workgroup, or of none: the barrier is uniform)
+    auto store = [&](const float4v (&v)[NT]) {
+        if (GATED) {
+            if (wave >= 2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xch[(wave - 2) * 256 + r * 64 + lane] = v[0][r];
+            __syncthreads();
+            if (wave < 2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * kq + r;
+                    const float gv = v[0][r], u = xch[wave * 256 + r * 64 + lane];
+                    if (row < M) C[(size_t)row * Nh + col0] = f2h(gv / (1.0f + __builtin_expf(-gv)) * u);
+                }
+            return;
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 4 * kq + r;
-                if (row < M) C[(size_t)row * N + col0 + 16 * t] = f2h(acc[t][r]);
+                if (row < M) C[(size_t)row * N + col0 + 16 * t] = f2h(v[t][r]);
             }
+    };
+    if (nsplit == 1) {
+        store(acc);
         return;
     }
     // slot layout: [cg][split][wave][t][r][lane] fp32
@@ -442,13 +476,7 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
                                         : __hip_atomic_load(base + (size_t)s2 * WV * PER_WAVE + (t * 4 + r) * 64,
                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 4 * kq + r;
-            if (row < M) C[(size_t)row * N + col0 + 16 * t] = f2h(tot[t][r]);
-        }
+    store(tot);
     if (tid == 0) __hip_atomic_store(&counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -531,7 +559,7 @@ size_t decode_workspace_bytes(int M, int N, int K)
     return W4A16_WS_COUNTER_BYTES + ncg * ns * 16 * decode::COLS * sizeof(float);
 }
 
-template <bool DELTA>
+template <bool DELTA, bool GATED = false>
 static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                              const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                              int nsplit, void *ws, hipStream_t st)
@@ -544,7 +572,7 @@ static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_
         partials = reinterpret_cast<float *>(static_cast<char *>(ws) + W4A16_WS_COUNTER_BYTES);
     }
     const size_t table = (size_t)decode_max_groups(K, g, nsplit) * decode::COLS * sizeof(uint32_t);
-    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA>),
+    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED>),
                        dim3(ncg * nsplit), dim3(64 * decode::WV), table, st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M,
                        N, K, g, nsplit, counters, partials);
     return hipGetLastError();
@@ -1431,6 +1459,74 @@ hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                                    st);
     return launch_w4a16_skinny_cfg(skinny_config(M, N, K), A, W, S, D, C, M, N, K, g,
                                    fuse_delta, ws, st);
+}
+
+// ---- SwiGLU of a gate/up pair ("Gaps and follow-ups": mlp_gate and mlp_up
+//      in one kernel) ----
+// The pair is one packed [K, 2N] weight, gate columns first.  Decode batches
+// (M <= 16) run the gated decode kernel: one launch, the product of both
+// halves kept in fp32 and silu(gate) * up rounded once.  Other batches run
+// the GEMM of the whole pair into the workspace ([M, 2N] fp16 after the
+// counter region), then swiglu_kernel.
+
+// silu(Y[m, n]) * Y[m, N + n] for Y [M, 2N] fp16; 8 outputs per thread
+__global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *__restrict__ Y,
+                                                     uint16_t *__restrict__ H, int M, int N)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;   // 8-column chunk
+    const size_t per_row = (size_t)N / 8;
+    if (i >= (size_t)M * per_row) return;
+    const size_t m = i / per_row, n8 = (i % per_row) * 8;
+    const uint4v gv = *reinterpret_cast<const uint4v *>(Y + m * 2 * N + n8);
+    const uint4v uv = *reinterpret_cast<const uint4v *>(Y + m * 2 * N + N + n8);
+    unsigned out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        unsigned o = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float gf = h2f((uint16_t)(gv[j] >> (16 * h)));
+            const float uf = h2f((uint16_t)(uv[j] >> (16 * h)));
+            o |= (unsigned)f2h(gf / (1.0f + __builtin_expf(-gf)) * uf) << (16 * h);
+        }
+        out[j] = o;
+    }
+    *reinterpret_cast<uint4v *>(H + m * N + n8) = uint4v{out[0], out[1], out[2], out[3]};
+}
+
+bool swiglu_uses_decode(int M, int N, int K) { return M <= 16 && use_decode_kernel(M, 2 * N, K); }
+
+size_t swiglu_workspace_bytes(int M, int N, int K)
+{
+    if (swiglu_uses_decode(M, N, K)) return decode_workspace_bytes(M, 2 * N, K);
+    // counters first (the layout every W4A16 workspace shares), then the GEMM's
+    // own workspace, then the pair's product
+    const size_t gemm = w4a16_workspace_bytes(M, 2 * N, K);
+    const size_t head = (gemm > W4A16_WS_COUNTER_BYTES ? gemm : W4A16_WS_COUNTER_BYTES);
+    return (head + 255) / 256 * 256 + (size_t)M * 2 * N * sizeof(uint16_t);
+}
+
+hipError_t launch_w4a16_swiglu(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                               const uint16_t *D, uint16_t *H, int M, int N, int K, int g,
+                               void *ws, hipStream_t st)
+{
+    const int N2 = 2 * N;
+    if (swiglu_uses_decode(M, N, K)) {
+        const int ns = decode_workspace_bytes(M, N2, K) ? decode_splits(N2, K) : 1;
+        if (ns > 1 && !ws) return hipErrorInvalidValue;
+        return D ? run_decode<true, true>(A, W, S, D, H, M, N2, K, g, ns, ws, st)
+                 : run_decode<false, true>(A, W, S, nullptr, H, M, N2, K, g, ns, ws, st);
+    }
+    if (!ws) return hipErrorInvalidValue;
+    const size_t gemm = w4a16_workspace_bytes(M, N2, K);
+    const size_t head = (gemm > W4A16_WS_COUNTER_BYTES ? gemm : W4A16_WS_COUNTER_BYTES);
+    uint16_t *Y = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + (head + 255) / 256 * 256);
+    hipError_t e = launch_w4a16(A, W, S, D, Y, M, N2, K, g, true, gemm ? ws : nullptr, st);
+    if (e != hipSuccess) return e;
+    const size_t chunks = (size_t)M * N / 8;
+    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, Y, H,
+                       M, N);
+    return hipGetLastError();
 }
 
 // ---- two-stage correction ("The pipeline, end to end": a_group_sum then

@@ -203,3 +203,19 @@ def test_quantize_rows_validation():
     assert L.quantize_rows_int8(FAKE, 4, 1024, P(0x10004), FAKE, None) == qg.QG_ERR_INVALID_ARG
     assert L.quantize_rows_int8(FAKE, 4, 1024, FAKE, P(0x10002), None) == qg.QG_ERR_INVALID_ARG
     assert b"quantize_rows_int8" in L.qg_last_error()
+
+
+def test_swiglu_validation():
+    # every case fails validation, before the device check and any launch
+    L = qg.lib()
+    ok = lambda **kw: [kw.get("A", FAKE), FAKE, FAKE, None, kw.get("H", FAKE), kw.get("M", 64), kw.get("N", 1024),
+                       kw.get("K", 1024), 128, kw.get("flags", 0), kw.get("ws", FAKE), kw.get("wsb", 1 << 30), None]
+    assert L.qgemm_w4a16_swiglu(*ok(A=None)) == qg.QG_ERR_INVALID_ARG
+    assert L.qgemm_w4a16_swiglu(*ok(H=P(0x10008))) == qg.QG_ERR_INVALID_ARG      # H 16-byte aligned
+    assert L.qgemm_w4a16_swiglu(*ok(flags=1)) == qg.QG_ERR_INVALID_ARG
+    assert L.qgemm_w4a16_swiglu(*ok(N=1000)) == qg.QG_ERR_UNSUPPORTED
+    assert L.qgemm_w4a16_swiglu(*ok(ws=None, wsb=0)) == qg.QG_ERR_WORKSPACE       # M=64 needs the pair's product
+    need = qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 64, 1024, 1024, 128, 1, 0)
+    assert need == CTR + 64 * 2048 * 2
+    assert L.qgemm_w4a16_swiglu(*ok(wsb=need - 1)) == qg.QG_ERR_WORKSPACE
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 16, 17408, 5120, 128, 1, 0) == 0

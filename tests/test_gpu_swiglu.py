@@ -1,0 +1,83 @@
+"""GPU parity of the SwiGLU of a gate/up pair (one packed [K, 2N] weight,
+gate columns first) against the oracle's silu(A . W_gate) * (A . W_up):
+the gated decode kernel (M <= 16, one launch, split-K included), and the
+GEMM-then-elementwise path of every other batch (skinny, mid and tiled GEMM
+kernels), symmetric and asymmetric weights."""
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_uint32_amd as qg
+import oracle
+import synth
+from tests.gpu_util import dev, elementwise_guard, host, note, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available()
+    assert qg.qg_device_supported(0), "GPU visible but not gfx950"
+    oracle.build(force=False)
+
+
+def _check(M, K, N, g, asym=True, signed=False, case_id=0):
+    c = synth.w4a16_case(M, K, 2 * N, g, asym=asym, signed_scales=signed, stream=91,
+                         case_id=case_id)
+    note(f"swiglu M={M} K={K} N={N} g={g} asym={asym} signed={signed}")
+    pair = qg.pack(dev(c.q), dev(c.s), dev(c.z) if asym else None, g, fold=True)
+    H = qg.w4a16_swiglu(dev(c.A), pair)
+    torch.cuda.synchronize()
+    got = host(H).astype(np.float64)
+    ref = oracle.w4a16_swiglu(c.A, c.q, c.s, c.z if asym else None, c.g, fold=True)
+    err = rel_fro(got, ref)
+    assert err <= TOL, err
+    assert elementwise_guard(got, ref) <= 0
+    return err
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_swiglu_decode_mlp_shape(M):
+    """The gate and up projections of the MLP, K 5120 -> N 17408 each."""
+    err = _check(M, 5120, 17408, 128, case_id=M)
+    note(f"rel_fro {err:.3e}")
+
+
+@pytest.mark.parametrize("M,K,N,g", [(16, 17408, 5120, 128), (9, 16384, 2048, -1)])
+def test_swiglu_decode_split_k(M, K, N, g):
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, M, N, K, g, 1, 0) > 0
+    _check(M, K, N, g, case_id=20 + M)
+
+
+def test_swiglu_decode_symmetric_signed():
+    _check(8, 4096, 2048, 128, asym=False, signed=True, case_id=30)
+
+
+@pytest.mark.parametrize("M,K,N,g", [(1, 1024, 512, 128), (33, 1024, 1024, 256),
+                                     (256, 2048, 1024, -1), (300, 1024, 2048, 128)])
+def test_swiglu_unfused_batches(M, K, N, g):
+    _check(M, K, N, g, case_id=40 + M)
+
+
+def test_swiglu_shares_a_workspace_with_w4a16():
+    """One zero-filled workspace serves SwiGLU and W4A16 calls in turn (the
+    counter region is common and left at zero)."""
+    M, K, N, g = 16, 17408, 5120, 128
+    c = synth.w4a16_case(M, K, 2 * N, g, stream=91, case_id=50)
+    pair = qg.pack(dev(c.q), dev(c.s), dev(c.z), g)
+    n = max(qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, M, N, K, g, 1, 0),
+            qg.qg_workspace_bytes(qg.QG_OP_W4A16, M, 2 * N, K, g, 1, 0))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    A = dev(c.A)
+    H1 = qg.w4a16_swiglu(A, pair, workspace=ws)
+    Y = qg.w4a16(A, pair, workspace=ws)
+    H2 = qg.w4a16_swiglu(A, pair, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(H1, H2)
+    Yf = Y.float()
+    Hy = (Yf[:, :N] * torch.sigmoid(Yf[:, :N]) * Yf[:, N:]).cpu().numpy()
+    assert rel_fro(host(H1).astype(np.float64), Hy.astype(np.float64)) <= TOL
+    assert int(ws[:qg.QG_W4A16_WS_COUNTER_BYTES].count_nonzero()) == 0
