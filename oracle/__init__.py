@@ -181,7 +181,7 @@ def w4a16_cells(A, q, s, z, g, rows, cols, fold=True):
 def group_sum(A, g):
     A, pa = _c(_bits16(A), np.uint16)
     M, K = A.shape
-    out = np.empty((M, K // g), dtype=np.float64)
+    out = np.empty((M, -(-K // g)), dtype=np.float64)
     _load().oracle_group_sum(pa, M, K, int(g), out.ctypes.data_as(ctypes.c_void_p))
     return out
 

@@ -74,7 +74,11 @@ uint16_t oracle_f64_to_f16(double x)
     return (uint16_t)(sign | (uint16_t)(biased << 10) | (uint16_t)frac);
 }
 
-static int n_groups(int K, int g) { return K / g; }
+/* Groups of g consecutive k: k belongs to group k / g, and when g does not
+ * divide K the last group is partial (K not a multiple of 128 is a supported
+ * shape; the pages' dispatcher requires the multiple, so a partial group is
+ * this library's own reading of "one scale per group of g k").            */
+static int n_groups(int K, int g) { return (K + g - 1) / g; }
 
 /* ---- [HyperQwen] section "hidden landmine: the negative group scale bug" ----
  * For every (group, column) whose scale is strictly negative, flip the scale's
@@ -91,7 +95,7 @@ long oracle_fold_negative_scales(uint8_t *q, uint16_t *s, int K, int N, int g)
             double sv = oracle_f16_to_f64(s[(size_t)gi * N + n]);
             if (!(sv < 0.0)) continue;          /* strict: -0.0 is not folded */
             s[(size_t)gi * N + n] ^= 0x8000;    /* s -> -s (exact in binary16) */
-            for (int k = gi * g; k < (gi + 1) * g; ++k) {
+            for (int k = gi * g; k < (gi + 1) * g && k < K; ++k) {
                 int v = q[(size_t)k * N + n];
                 int nv = 16 - v;
                 if (nv > 15) { nv = 15; ++clamped; }
@@ -235,7 +239,7 @@ void oracle_group_sum(const uint16_t *A, int M, int K, int g, double *a_sum)
     for (int m = 0; m < M; ++m)
         for (int gi = 0; gi < G; ++gi) {
             double acc = 0.0;
-            for (int k = gi * g; k < (gi + 1) * g; ++k)
+            for (int k = gi * g; k < (gi + 1) * g && k < K; ++k)
                 acc += oracle_f16_to_f64(A[(size_t)m * K + k]);
             a_sum[(size_t)m * G + gi] = acc;
         }

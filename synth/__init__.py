@@ -58,8 +58,7 @@ def w4a16_case(M, K, N, g, asym=True, signed_scales=False, stream=0, case_id=0,
                name="") -> W4A16Case:
     if g == -1:
         g = K
-    assert K % g == 0
-    G = K // g
+    G = -(-K // g)            # groups of g consecutive k; the last may be partial
     r = rng_for(stream, case_id)
     A = r.standard_normal((M, K)).astype(np.float16)
     q = r.integers(0, 16, size=(K, N), dtype=np.uint8)

@@ -86,6 +86,8 @@ def _exact_w4a16(A, q, s, z, g, fold):
     (3, 256, 8, 64, False, True),
     (2, 256, 8, 256, False, False),
     (1, 256, 16, 128, False, True),
+    (1, 130, 8, 128, True, False),      # K tail: a partial last group of 2
+    (2, 200, 8, 64, False, True),       # groups of 64, the last of 8
 ])
 def test_w4a16_matches_exact_rationals(oracle_lib, M, K, N, g, asym, signed):
     c = synth.w4a16_case(M, K, N, g, asym=asym, signed_scales=signed, stream=90, case_id=K + N + M)
@@ -444,3 +446,27 @@ def test_w4a16_swiglu_halves(oracle_lib):
     Cg = oracle_lib.w4a16(A, qg_, s[:, :N], None, g)
     rows = A.astype(np.float64).sum(axis=1, keepdims=True)
     np.testing.assert_allclose(H, Cg / (1 + np.exp(-Cg)) * rows, rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------- shapes with tails -------
+def test_w4a16_k_tail_is_zero_padding(oracle_lib):
+    """K not a multiple of 128: the product equals the product over K padded
+    to 128 with zero activations and arbitrary codes in the padding (the
+    groups, and so the scales, are the same)."""
+    c = synth.w4a16_case(3, 1000, 40, 128, asym=True, stream=90, case_id=500)
+    C = oracle_lib.w4a16(c.A, c.q, c.s, c.z, 128)
+    rng = np.random.default_rng(1)
+    Ap = np.concatenate([c.A, np.zeros((3, 24), np.float16)], axis=1)
+    qp = np.concatenate([c.q, rng.integers(0, 16, size=(24, 40), dtype=np.uint8)], axis=0)
+    Cp = oracle_lib.w4a16(Ap, qp, c.s, c.z, 128)
+    assert np.array_equal(C, Cp)
+
+
+def test_w4a16_n_tail_columns_are_independent(oracle_lib):
+    """N not a multiple of 128: each column is its own product, so the first
+    300 columns of a 384-column problem are the 300-column problem."""
+    c = synth.w4a16_case(2, 256, 384, 128, asym=False, signed_scales=True, stream=90, case_id=501)
+    C = oracle_lib.w4a16(c.A, c.q, c.s, None, 128)
+    C3 = oracle_lib.w4a16(c.A, np.ascontiguousarray(c.q[:, :300]), np.ascontiguousarray(c.s[:, :300]),
+                          None, 128)
+    assert np.array_equal(C[:, :300], C3)
