@@ -111,14 +111,14 @@ def time_best(fn, n_copies, steps, warmup):
     return (min(ms_graph, ms_eager) if ms_graph else ms_eager), ms_graph, ms_eager
 
 
-def bench_w4a16(name, steps, warmup, flags=0, label=None):
+def bench_w4a16(name, steps, warmup, flags=0, label=None, case=None):
     import numpy as np
     import torch
 
     import int4_weight_only_uint32_amd as qg
     import synth
 
-    c = synth.workload(name)
+    c = case if case is not None else synth.workload(name)
     M, K, N, g = c.M, c.K, c.N, c.g
     asym = c.z is not None
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -473,6 +473,14 @@ def main():
             log(json.dumps(r))
             cases.append(r)
             del ca
+        vn = "w4a16-vocab-head-M16-K5120-N50257-g128-asym"
+        if not want or vn in want:
+            # a vocabulary of 50257 (N padded to 50304 in the pack, C cropped)
+            cv = synth.w4a16_case(16, 5120, 50257, 128, asym=True, stream=92, case_id=1016)
+            r, _ = bench_w4a16(vn, steps, warmup, case=cv)
+            log(json.dumps(r))
+            cases.append(r)
+            del cv
         sn = "w4a16-swiglu-decode-M16-K5120-N17408x2-g128-asym"
         if not want or sn in want:
             r = bench_swiglu(sn, steps, warmup, 16, 5120, 17408, 128)

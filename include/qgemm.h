@@ -45,6 +45,9 @@
  *   - Shapes: K % 128 == 0 and N % 128 == 0 (the tile multiples the pages'
  *     dispatcher requires), M >= 1.  group_size must divide K and be a multiple
  *     of 128, or equal K; -1 is accepted as an alias of K (per-column scales).
+ *     pack_int4_weights and qgemm_w4a16 also take any K, N >= 1 ("tails"):
+ *     group_size is then a multiple of 128 (the last group of g consecutive k
+ *     may be partial: G = ceil(K / g)), K, or -1; see qg_padded_shape.
  *   - A, C, scale, zero and delta must be 2-byte aligned; w_packed 16-byte
  *     aligned; A 16-byte aligned for the W4A16 GEMM, A_q 8-byte aligned for
  *     W4A8.
@@ -101,6 +104,14 @@ const char *qg_status_string(int status);
  * pointer stays valid until the next library call on that thread.          */
 const char *qg_last_error(void);
 
+/* Padded shape of a pack of [K,N] codes with this group size (any K, N >= 1):
+ * the packed weight holds K_padded * N_padded / 8 uint32, scale_out and
+ * delta_out are [groups, N_padded] fp16.  K_padded = K rounded up to a whole
+ * group (to 128 when group_size is K or -1), N_padded = N rounded up to 128,
+ * groups = ceil(K / group_size) (1 per column).  Equal to K, N, K/g for shapes
+ * without tails.  Any output pointer may be NULL.  Returns a QG_* status.  */
+int qg_padded_shape(int K, int N, int group_size, int *K_padded, int *N_padded, int *groups);
+
 /* Bytes of workspace `op` needs for this shape (0 when none). Returns
  * (size_t)-1 when the arguments are invalid.                                */
 size_t qg_workspace_bytes(int op, int M, int N, int K, int group_size,
@@ -110,15 +121,18 @@ size_t qg_workspace_bytes(int op, int M, int N, int K, int group_size,
  *      [HyperQwen] negative group-scale section) ----
  * q         [K,N] uint8, one code (0..15) per byte; larger values are an
  *           error the kernel cannot report and give unspecified codes.
- * scale     [G,N] fp16, G = K / group_size.
+ * scale     [G,N] fp16, G = ceil(K / group_size) (qg_padded_shape).
  * zero      [G,N] fp16, or NULL for a symmetric weight.
  * flags     QG_PACK_FOLD_NEG_SCALES: for a symmetric weight, every (g,n) with
  *           scale < 0 (strictly; -0.0 is left alone) gets scale -> -scale and
  *           codes v -> min(16 - v, 15) over that group.
- * w_packed  [K*N/8] uint32 out, in this library's MFMA-operand tile order
- *           (private layout; the only consumers are qgemm_w4a16/qgemm_w4a8).
- * scale_out [G,N] fp16 out: the (folded) scale.  May alias `scale`.
- * delta_out [G,N] fp16 out, required iff zero != NULL:
+ * w_packed  [K_padded*N_padded/8] uint32 out, in this library's MFMA-operand
+ *           tile order (private layout; the only consumers are the GEMMs);
+ *           padding codes are 8.
+ * scale_out [G,N_padded] fp16 out: the (folded) scale, 0 in padded columns.
+ *           May alias `scale` when N % 128 == 0.
+ * delta_out [G,N_padded] fp16 out, required iff zero != NULL (0 in padded
+ *           columns):
  *           delta = round_to_nearest_even_fp16(zero + 8*scale), with the
  *           pre-fold scale and the sum formed exactly.
  * Runs one or two kernels on `stream`. No workspace.                        */
@@ -138,6 +152,10 @@ int pack_int4_weights(const uint8_t *q, const uint16_t *scale, const uint16_t *z
  *          the GEMM epilogue (one launch).
  *          QG_CORR_SEPARATE: C is first stored as the symmetric product and
  *          then corrected in place by group_sum_correction (needs workspace).
+ * Tails (K or N not a multiple of 128, from a tail pack): A is copied into
+ *          the workspace with zero columns up to K_padded, the GEMM runs on
+ *          the padded shape and its product is cropped into C; the delta term
+ *          is fused; QG_CORR_SEPARATE is QG_ERR_UNSUPPORTED.
  * workspace/workspace_bytes: qg_workspace_bytes(QG_OP_W4A16, ...) bytes,
  *          256-byte aligned (NULL when that is 0).  For M <= 16 the K range
  *          is split over several workgroups whose fp32 partial sums meet in

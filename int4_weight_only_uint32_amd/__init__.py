@@ -40,7 +40,7 @@ QG_OP_W4A16_SWIGLU = 5
 
 EXPORTED = ("qg_device_supported", "qg_status_string", "qg_last_error", "qg_workspace_bytes",
             "pack_int4_weights", "qgemm_w4a16", "group_sum_correction", "qgemm_w4a8",
-            "quantize_rows_int8", "qgemm_w4a16_swiglu")
+            "quantize_rows_int8", "qgemm_w4a16_swiglu", "qg_padded_shape")
 
 
 class QGemmError(RuntimeError):
@@ -77,6 +77,8 @@ def lib():
         L.group_sum_correction.argtypes = [P, P, P, I, I, I, I, P, Z, P]
         L.qgemm_w4a8.restype = I
         L.qgemm_w4a8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, Z, U, P]
+        L.qg_padded_shape.restype = I
+        L.qg_padded_shape.argtypes = [I, I, I, P, P, P]
         L.qgemm_w4a16_swiglu.restype = I
         L.qgemm_w4a16_swiglu.argtypes = [P, P, P, P, P, I, I, I, I, U, P, Z, P]
         L.quantize_rows_int8.restype = I
@@ -138,14 +140,24 @@ def pack_int4_weights(q, scale, zero, K, N, group_size, flags, w_packed, scale_o
                                    _ptr(delta_out, torch.float16, "delta_out"), _stream(q)))
 
 
+def padded_shape(K: int, N: int, group_size: int):
+    """(K_padded, N_padded, groups) of a pack of [K, N] codes."""
+    kp, np_, gs = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().qg_padded_shape(K, N, group_size, ctypes.byref(kp), ctypes.byref(np_),
+                                 ctypes.byref(gs)))
+    return kp.value, np_.value, gs.value
+
+
 def pack(q: torch.Tensor, scale: torch.Tensor, zero: Optional[torch.Tensor] = None,
          group_size: int = 128, fold: bool = True) -> PackedWeight:
-    """Allocate outputs (torch) and run pack_int4_weights."""
+    """Allocate outputs (torch) and run pack_int4_weights (any K, N: shapes
+    with tails get a padded pack, see qg_padded_shape)."""
     K, N = q.shape
     g = K if group_size == -1 else group_size
-    w = torch.empty(K * N // 8, dtype=torch.int32, device=q.device)
-    s_out = torch.empty_like(scale)
-    d_out = torch.empty_like(scale) if zero is not None else None
+    Kp, Np, G = padded_shape(K, N, group_size)
+    w = torch.empty(Kp * Np // 8, dtype=torch.int32, device=q.device)
+    s_out = torch.empty((G, Np), dtype=torch.float16, device=q.device)
+    d_out = torch.empty((G, Np), dtype=torch.float16, device=q.device) if zero is not None else None
     pack_int4_weights(q, scale, zero, K, N, group_size,
                       QG_PACK_FOLD_NEG_SCALES if fold else 0, w, s_out, d_out)
     return PackedWeight(w=w, scale=s_out, delta=d_out, K=K, N=N, group_size=g)

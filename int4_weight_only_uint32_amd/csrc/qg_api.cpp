@@ -70,6 +70,28 @@ int check_shape(const char *what, int M, int N, int K, int *g)
     return QG_OK;
 }
 
+// Shape rules of the entry points that take tails (pack_int4_weights,
+// qgemm_w4a16): K and N any positive size; group_size a multiple of 128 (the
+// last group may be partial), K, or -1 (normalised to K).
+int check_shape_tail(const char *what, int M, int N, int K, int *g)
+{
+    if (M < 1 || N < 1 || K < 1)
+        return fail(QG_ERR_INVALID_ARG, "%s: M, N, K must be >= 1 (got %d, %d, %d)", what, M, N, K);
+    if (*g == -1) *g = K;
+    if (*g < 1)
+        return fail(QG_ERR_INVALID_ARG, "%s: group_size %d", what, *g);
+    if (*g != K && *g % 128 != 0) {
+        if (K % *g != 0)
+            return fail(QG_ERR_INVALID_ARG, "%s: group_size %d does not divide K=%d", what, *g, K);
+        return fail(QG_ERR_UNSUPPORTED,
+                    "%s: group_size %d unsupported (must be a multiple of 128, K, or -1)", what, *g);
+    }
+    if (K > (1 << 28) || N > (1 << 28) || (long long)M * K > (1ll << 40) ||
+        (long long)K * N > (1ll << 40))
+        return fail(QG_ERR_UNSUPPORTED, "%s: shape too large", what);
+    return QG_OK;
+}
+
 size_t corr_ws_bytes(int M, int K, int g) { return (size_t)M * (size_t)(K / g) * sizeof(float); }
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
@@ -95,6 +117,19 @@ size_t w4a16_ws_bytes(int M, int N, int K, int g, bool separate)
 } // namespace
 
 extern "C" {
+
+int qg_padded_shape(int K, int N, int group_size, int *K_padded, int *N_padded, int *groups)
+{
+    int g = group_size;
+    int rc = check_shape_tail("qg_padded_shape", 1, N, K, &g);
+    if (rc) return rc;
+    int Kp, Np, gp;
+    qg::padded_shape(K, N, g, &Kp, &Np, &gp);
+    if (K_padded) *K_padded = Kp;
+    if (N_padded) *N_padded = Np;
+    if (groups) *groups = Kp / gp;
+    return ok();
+}
 
 int qg_device_supported(int device)
 {
@@ -140,7 +175,14 @@ size_t qg_workspace_bytes(int op, int M, int N, int K, int group_size, int num_e
     int g = group_size;
     switch (op) {
     case QG_OP_W4A16:
-        if (check_shape("qg_workspace_bytes", M, N, K, &g) != QG_OK) return (size_t)-1;
+        if (check_shape_tail("qg_workspace_bytes", M, N, K, &g) != QG_OK) return (size_t)-1;
+        if (qg::is_tail_shape(N, K, g)) {
+            if (flags & QG_CORR_SEPARATE) {
+                fail(QG_ERR_UNSUPPORTED, "qg_workspace_bytes: QG_CORR_SEPARATE needs K, N multiples of 128");
+                return (size_t)-1;
+            }
+            return qg::tail_workspace_bytes(M, N, K, g);
+        }
         return w4a16_ws_bytes(M, N, K, g, (flags & QG_CORR_SEPARATE) != 0);
     case QG_OP_W4A16_SWIGLU:
         if (check_shape("qg_workspace_bytes", M, N, K, &g) != QG_OK) return (size_t)-1;
@@ -164,7 +206,7 @@ int pack_int4_weights(const uint8_t *q, const uint16_t *scale, const uint16_t *z
                       uint16_t *scale_out, uint16_t *delta_out, void *stream)
 {
     int g = group_size;
-    int rc = check_shape("pack_int4_weights", 1, N, K, &g);
+    int rc = check_shape_tail("pack_int4_weights", 1, N, K, &g);
     if (rc) return rc;
     if (!q || !scale || !w_packed || !scale_out)
         return fail(QG_ERR_INVALID_ARG, "pack_int4_weights: NULL q/scale/w_packed/scale_out");
@@ -175,6 +217,9 @@ int pack_int4_weights(const uint8_t *q, const uint16_t *scale, const uint16_t *z
         return fail(QG_ERR_INVALID_ARG, "pack_int4_weights: misaligned pointer");
     if (flags & ~QG_PACK_FOLD_NEG_SCALES)
         return fail(QG_ERR_INVALID_ARG, "pack_int4_weights: unknown flags 0x%x", flags);
+    if (N % 128 != 0 && (const void *)scale_out == (const void *)scale)
+        return fail(QG_ERR_INVALID_ARG,
+                    "pack_int4_weights: scale_out may alias scale only when N %% 128 == 0");
     if ((rc = check_device())) return rc;
     hipError_t e = qg::launch_pack(q, scale, zero, K, N, g, (flags & QG_PACK_FOLD_NEG_SCALES) != 0,
                                    w_packed, scale_out, zero ? delta_out : nullptr,
@@ -187,7 +232,7 @@ int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *sca
                 unsigned flags, void *workspace, size_t workspace_bytes, void *stream)
 {
     int g = group_size;
-    int rc = check_shape("qgemm_w4a16", M, N, K, &g);
+    int rc = check_shape_tail("qgemm_w4a16", M, N, K, &g);
     if (rc) return rc;
     if (!A || !w_packed || !scale || !C)
         return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16: NULL A/w_packed/scale/C");
@@ -197,7 +242,10 @@ int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *sca
     if (flags & ~QG_CORR_SEPARATE)
         return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16: unknown flags 0x%x", flags);
     const bool separate = (flags & QG_CORR_SEPARATE) && delta;
-    const size_t need = w4a16_ws_bytes(M, N, K, g, separate);
+    const bool tail = qg::is_tail_shape(N, K, g);
+    if (tail && separate)
+        return fail(QG_ERR_UNSUPPORTED, "qgemm_w4a16: QG_CORR_SEPARATE needs K, N multiples of 128");
+    const size_t need = tail ? qg::tail_workspace_bytes(M, N, K, g) : w4a16_ws_bytes(M, N, K, g, separate);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(QG_ERR_WORKSPACE, "qgemm_w4a16: workspace of %zu bytes needed, got %zu",
@@ -207,6 +255,10 @@ int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *sca
     }
     if ((rc = check_device())) return rc;
     hipStream_t st = (hipStream_t)stream;
+    if (tail)
+        return launch_status(qg::launch_w4a16_tail(A, w_packed, scale, delta, C, M, N, K, g, true,
+                                                   workspace, st),
+                             "qgemm_w4a16");
     const size_t gemm_ws = w4a16_gemm_ws_bytes(M, N, K, separate);
     hipError_t e = qg::launch_w4a16(A, w_packed, scale, delta, C, M, N, K, g, !separate,
                                     qg::w4a16_workspace_bytes(M, N, K) ? workspace : nullptr, st);

@@ -7,6 +7,19 @@
 
 namespace qg {
 
+// Padded shape of a pack: Kp (K up to a whole group, or to 128 for one group
+// per column, g == K), Np (N up to 128), gp (the group size in the padded
+// layout: g, or Kp when g == K).  Kp == K and Np == N for aligned shapes.
+void padded_shape(int K, int N, int g, int *Kp, int *Np, int *gp);
+
+// W4A16 on a shape with tails (is_tail_shape): A padded and C cropped through
+// `ws` (tail_workspace_bytes), the GEMM on the padded shape.
+bool is_tail_shape(int N, int K, int g);
+size_t tail_workspace_bytes(int M, int N, int K, int g);
+hipError_t launch_w4a16_tail(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                             bool fuse_delta, void *ws, hipStream_t st);
+
 hipError_t launch_pack(const uint8_t *q, const uint16_t *s, const uint16_t *z, int K, int N,
                        int g, bool fold, uint32_t *w, uint16_t *s_out, uint16_t *d_out,
                        hipStream_t st);

@@ -52,17 +52,19 @@ __device__ inline uint16_t f64_to_f16_rne(double x)
     return (uint16_t)(sign | (uint16_t)r);          // subnormal (r == 1024 -> 2^-14)
 }
 
-// One thread per packed uint32.
+// One thread per packed uint32 of the padded [Kp, Np] weight; codes outside
+// the logical [K, N] are 8 (zero weight for a symmetric pack; the GEMM pads
+// the activations with zeros and drops the extra columns anyway).
 __global__ void pack_codes_kernel(const uint8_t *__restrict__ q, const uint16_t *__restrict__ s,
-                                  int K, int N, int g, int fold, uint32_t *__restrict__ out,
-                                  size_t total)
+                                  int K, int N, int Kp, int g, int fold,
+                                  uint32_t *__restrict__ out, size_t total)
 {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total) return;
     size_t tile = i >> 8;
     int within = (int)(i & 255);
     int lane = within >> 2, j = within & 3;
-    int KT = K / KTILE;
+    int KT = Kp / KTILE;
     int nt = (int)(tile / KT), kt = (int)(tile % KT);
     int n = nt * NTILE + (lane & 15);
     int kq = lane >> 4;
@@ -70,26 +72,48 @@ __global__ void pack_codes_kernel(const uint8_t *__restrict__ q, const uint16_t 
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         int k = kt * KTILE + tile_k(kq, j, p);
-        unsigned v = q[(size_t)k * N + n] & 15u;
-        if (fold && f16_is_negative(s[(size_t)(k / g) * N + n])) {
-            v = 16u - v;
-            if (v > 15u) v = 15u;
+        unsigned v = 8u;
+        if (k < K && n < N) {
+            v = q[(size_t)k * N + n] & 15u;
+            if (fold && f16_is_negative(s[(size_t)(k / g) * N + n])) {
+                v = 16u - v;
+                if (v > 15u) v = 15u;
+            }
         }
         word |= v << (4 * p);
     }
     out[i] = word;
 }
 
-// One thread per (group, column): folded scale and delta.
+// One thread per (group, column) of the padded [G, Np] outputs: folded scale
+// and delta; 0 in the columns past N.
 __global__ void pack_scales_kernel(const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
-                                   int fold, uint16_t *s_out, uint16_t *__restrict__ d_out,
-                                   size_t total)
+                                   int N, int Np, int fold, uint16_t *s_out,
+                                   uint16_t *__restrict__ d_out, size_t total)
 {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total) return;
-    uint16_t sb = s[i];
-    if (z) d_out[i] = f64_to_f16_rne(f16_bits_to_f64(z[i]) + 8.0 * f16_bits_to_f64(sb));
+    const size_t gi = i / Np;
+    const int n = (int)(i % Np);
+    if (n >= N) {
+        if (z) d_out[i] = 0;
+        s_out[i] = 0;
+        return;
+    }
+    const size_t src = gi * N + n;
+    uint16_t sb = s[src];
+    if (z) d_out[i] = f64_to_f16_rne(f16_bits_to_f64(z[src]) + 8.0 * f16_bits_to_f64(sb));
     s_out[i] = (fold && f16_is_negative(sb)) ? (uint16_t)(sb ^ 0x8000u) : sb;
+}
+
+void padded_shape(int K, int N, int g, int *Kp, int *Np, int *gp)
+{
+    // g == K: one group per column, padded with K to a multiple of 128;
+    // otherwise g is a multiple of 128 and K is padded to a whole group
+    const int kp = g == K ? (K + KTILE - 1) / KTILE * KTILE : (K + g - 1) / g * g;
+    *Kp = kp;
+    *Np = (N + 127) / 128 * 128;
+    *gp = g == K ? kp : g;
 }
 
 hipError_t launch_pack(const uint8_t *q, const uint16_t *s, const uint16_t *z, int K, int N,
@@ -98,16 +122,18 @@ hipError_t launch_pack(const uint8_t *q, const uint16_t *s, const uint16_t *z, i
 {
     // the fold only applies to symmetric weights
     int f = (fold && z == nullptr) ? 1 : 0;
-    size_t total = (size_t)K * N / 8;
+    int Kp, Np, gp;
+    padded_shape(K, N, g, &Kp, &Np, &gp);
+    size_t total = (size_t)Kp * Np / 8;
     int bs = 256;
     // codes first: they read the original scales, which s_out may overwrite
     hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)((total + bs - 1) / bs)), dim3(bs), 0, st,
-                       q, s, K, N, g, f, w, total);
+                       q, s, K, N, Kp, g, f, w, total);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    size_t gt = (size_t)(K / g) * N;
+    size_t gt = (size_t)(Kp / gp) * Np;
     hipLaunchKernelGGL(pack_scales_kernel, dim3((unsigned)((gt + bs - 1) / bs)), dim3(bs), 0, st,
-                       s, z, f, s_out, d_out, gt);
+                       s, z, N, Np, f, s_out, d_out, gt);
     return hipGetLastError();
 }
 

@@ -1461,6 +1461,84 @@ hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                                    fuse_delta, ws, st);
 }
 
+// ---- shapes with tails: K or N not a multiple of 128 (the pages' dispatcher
+//      requires both; "Gaps and follow-ups" lists the head projection's N
+//      as the gap) ----
+// The pack pads the weight to [Kp, Np] (codes 8, scales 0); a call copies A
+// into the workspace with zero columns up to Kp, runs the GEMM on the padded
+// shape, and crops the padded product to C.  All in the workspace after the
+// counter region: [counters | GEMM workspace][A padded][C padded].
+__global__ __launch_bounds__(256) void pad_cols_kernel(const uint16_t *__restrict__ A,
+                                                       uint16_t *__restrict__ Ap, int M, int K,
+                                                       int Kp)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)M * Kp) return;
+    const size_t m = i / Kp;
+    const int k = (int)(i % Kp);
+    Ap[i] = k < K ? A[m * K + k] : (uint16_t)0;
+}
+
+__global__ __launch_bounds__(256) void crop_cols_kernel(const uint16_t *__restrict__ Cp,
+                                                        uint16_t *__restrict__ C, int M, int N,
+                                                        int Np)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)M * N) return;
+    const size_t m = i / N;
+    const int n = (int)(i % N);
+    C[i] = Cp[m * Np + n];
+}
+
+static size_t al256(size_t n) { return (n + 255) / 256 * 256; }
+
+bool is_tail_shape(int N, int K, int g)
+{
+    int Kp, Np, gp;
+    padded_shape(K, N, g, &Kp, &Np, &gp);
+    return Kp != K || Np != N;
+}
+
+size_t tail_workspace_bytes(int M, int N, int K, int g)
+{
+    int Kp, Np, gp;
+    padded_shape(K, N, g, &Kp, &Np, &gp);
+    const size_t gemm = w4a16_workspace_bytes(M, Np, Kp);
+    size_t off = al256(gemm > W4A16_WS_COUNTER_BYTES ? gemm : W4A16_WS_COUNTER_BYTES);
+    if (Kp != K) off += al256((size_t)M * Kp * sizeof(uint16_t));
+    if (Np != N) off += (size_t)M * Np * sizeof(uint16_t);
+    return off;
+}
+
+hipError_t launch_w4a16_tail(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                             bool fuse_delta, void *ws, hipStream_t st)
+{
+    if (!ws) return hipErrorInvalidValue;
+    int Kp, Np, gp;
+    padded_shape(K, N, g, &Kp, &Np, &gp);
+    const size_t gemm = w4a16_workspace_bytes(M, Np, Kp);
+    char *p = static_cast<char *>(ws) + al256(gemm > W4A16_WS_COUNTER_BYTES ? gemm : W4A16_WS_COUNTER_BYTES);
+    const uint16_t *Ause = A;
+    if (Kp != K) {
+        uint16_t *Ap = reinterpret_cast<uint16_t *>(p);
+        p += al256((size_t)M * Kp * sizeof(uint16_t));
+        const size_t n = (size_t)M * Kp;
+        hipLaunchKernelGGL(pad_cols_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A,
+                           Ap, M, K, Kp);
+        Ause = Ap;
+    }
+    uint16_t *Cuse = Np != N ? reinterpret_cast<uint16_t *>(p) : C;
+    hipError_t e = launch_w4a16(Ause, W, S, D, Cuse, M, Np, Kp, gp, fuse_delta, gemm ? ws : nullptr, st);
+    if (e != hipSuccess) return e;
+    if (Np != N) {
+        const size_t n = (size_t)M * N;
+        hipLaunchKernelGGL(crop_cols_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Cuse,
+                           C, M, N, Np);
+    }
+    return hipGetLastError();
+}
+
 // ---- SwiGLU of a gate/up pair ("Gaps and follow-ups": mlp_gate and mlp_up
 //      in one kernel) ----
 // The pair is one packed [K, 2N] weight, gate columns first.  Decode batches

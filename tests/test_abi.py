@@ -67,8 +67,10 @@ def _w4a16(M=16, N=1024, K=1024, g=128, A=FAKE, W=FAKE, S=FAKE, D=None, C=FAKE, 
 
 
 @pytest.mark.parametrize("kw,rc", [
-    (dict(K=1000), qg.QG_ERR_UNSUPPORTED),
-    (dict(N=1000), qg.QG_ERR_UNSUPPORTED),
+    (dict(K=1000), qg.QG_ERR_WORKSPACE),               # tails: A padded / C cropped in the workspace
+    (dict(N=1000), qg.QG_ERR_WORKSPACE),
+    (dict(K=1000, D=FAKE, flags=qg.QG_CORR_SEPARATE), qg.QG_ERR_UNSUPPORTED),
+    (dict(K=1000, g=384), qg.QG_ERR_WORKSPACE),        # a partial last group
     (dict(M=0), qg.QG_ERR_INVALID_ARG),
     (dict(g=100), qg.QG_ERR_INVALID_ARG),
     (dict(g=64), qg.QG_ERR_UNSUPPORTED),
@@ -107,7 +109,10 @@ def test_split_k_workspace_is_required_and_sized():
 def test_pack_validation():
     L = qg.lib()
     assert L.pack_int4_weights(FAKE, FAKE, FAKE, 1024, 1024, 128, 1, FAKE, FAKE, None, None) == qg.QG_ERR_INVALID_ARG
-    assert L.pack_int4_weights(FAKE, FAKE, None, 1024, 1000, 128, 1, FAKE, FAKE, None, None) == qg.QG_ERR_UNSUPPORTED
+    # N tail: the padded scale_out cannot alias scale
+    assert L.pack_int4_weights(FAKE, FAKE, None, 1024, 1000, 128, 1, FAKE, FAKE, None, None) == qg.QG_ERR_INVALID_ARG
+    assert b"alias" in L.qg_last_error()
+    assert L.pack_int4_weights(FAKE, FAKE, None, 1024, 1000, 100, 1, FAKE, P(0x20000), None, None) == qg.QG_ERR_INVALID_ARG
     assert L.pack_int4_weights(FAKE, FAKE, None, 1024, 1024, 128, 4, FAKE, FAKE, None, None) == qg.QG_ERR_INVALID_ARG
     assert L.pack_int4_weights(None, FAKE, None, 1024, 1024, 128, 1, FAKE, FAKE, None, None) == qg.QG_ERR_INVALID_ARG
 
@@ -171,7 +176,9 @@ def test_workspace_bytes():
     assert qg.qg_workspace_bytes(qg.QG_OP_GROUP_SUM_CORRECTION, 3, 1024, 1024, -1) == 3 * 4
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 64, 7168, 2048, 128, 8) == 0
     with pytest.raises(qg.QGemmError):
-        qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1000, 128)
+        qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1000, 100)     # 100 neither divides K nor is a multiple of 128
+    with pytest.raises(qg.QGemmError):
+        qg.qg_workspace_bytes(qg.QG_OP_W4A8, 16, 1024, 1000, 128)      # W4A8 keeps K % 128 == 0
     with pytest.raises(qg.QGemmError):
         qg.qg_workspace_bytes(99, 16, 1024, 1024, 128)
 
@@ -219,3 +226,25 @@ def test_swiglu_validation():
     assert need == CTR + 64 * 2048 * 2
     assert L.qgemm_w4a16_swiglu(*ok(wsb=need - 1)) == qg.QG_ERR_WORKSPACE
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 16, 17408, 5120, 128, 1, 0) == 0
+
+
+def test_padded_shape():
+    assert qg.padded_shape(5120, 17408, 128) == (5120, 17408, 40)
+    assert qg.padded_shape(5120, 50257, 128) == (5120, 50304, 40)
+    assert qg.padded_shape(1000, 300, 128) == (1024, 384, 8)
+    assert qg.padded_shape(1000, 300, -1) == (1024, 384, 1)
+    assert qg.padded_shape(1000, 128, 384) == (1152, 128, 3)
+    assert qg.padded_shape(130, 1, 128) == (256, 128, 2)
+    with pytest.raises(qg.QGemmError):
+        qg.padded_shape(1000, 300, 100)
+
+
+def test_tail_workspace_sizes():
+    # counters, then A padded (K tail), then the padded product (N tail)
+    al = lambda n: (n + 255) // 256 * 256
+    ws = lambda M, N, K, g: qg.qg_workspace_bytes(qg.QG_OP_W4A16, M, N, K, g, 1, 0)
+    assert ws(300, 1000, 1024, 128) == CTR + 300 * 1024 * 2
+    assert ws(300, 1024, 1000, 128) == CTR + al(300 * 1024 * 2)
+    assert ws(300, 1000, 1000, 128) == CTR + al(300 * 1024 * 2) + 300 * 1024 * 2
+    with pytest.raises(qg.QGemmError):
+        qg.qg_workspace_bytes(qg.QG_OP_W4A16, 4, 1000, 1000, 128, 1, qg.QG_CORR_SEPARATE)

@@ -1,0 +1,72 @@
+"""GPU parity on shapes whose K or N is not a multiple of 128 (the padded
+pack; A padded and C cropped through the workspace): a 50257-wide vocabulary
+head on sampled cells, and dense checks of K tails with a partial last group,
+per-column scales, and every GEMM kernel the padded shape selects."""
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_uint32_amd as qg
+import oracle
+import synth
+from tests.gpu_util import dev, elementwise_guard, host, note, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available()
+    assert qg.qg_device_supported(0), "GPU visible but not gfx950"
+    oracle.build(force=False)
+
+
+def _run(c, asym):
+    pw = qg.pack(dev(c.q), dev(c.s), dev(c.z) if asym else None, c.g, fold=True)
+    C = qg.w4a16(dev(c.A), pw)
+    torch.cuda.synchronize()
+    return pw, host(C).astype(np.float64)
+
+
+@pytest.mark.parametrize("M,K,N,g,asym,signed", [
+    (3, 1000, 300, 128, True, False),      # K and N tails, partial last group (104 of 128)
+    (7, 1000, 300, -1, True, False),       # one group per column over a K tail
+    (16, 1000, 1024, 384, False, True),    # groups of 384, the last of 232; decode batch
+    (16, 130, 200, 128, True, False),      # a group of 2
+    (64, 1000, 1000, 128, True, False),    # mid batch
+    (300, 1000, 520, 256, False, True),    # tiled kernels
+])
+def test_tails_dense(M, K, N, g, asym, signed):
+    c = synth.w4a16_case(M, K, N, g, asym=asym, signed_scales=signed, stream=92,
+                         case_id=M * 7 + N)
+    note(f"tails M={M} K={K} N={N} g={g} asym={asym}")
+    pw, got = _run(c, asym)
+    ref = oracle.w4a16(c.A, c.q, c.s, c.z if asym else None, c.g, fold=True)
+    assert got.shape == (M, N)
+    assert rel_fro(got, ref) <= TOL
+    assert elementwise_guard(got, ref) <= 0
+    Np = pw.scale.shape[1]
+    if Np > N:   # padded columns hold scale 0
+        assert int(pw.scale[:, N:].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_vocab_head_sampled(M):
+    """K 5120 -> a 50257-token vocabulary (N = 50304 padded), asymmetric g128:
+    all rows at 1200 columns -- the first 64, the last 200 (the tail tile and
+    its neighbours) and 936 drawn at random."""
+    K, N = 5120, 50257
+    c = synth.w4a16_case(M, K, N, 128, asym=True, stream=92, case_id=1000 + M)
+    note(f"vocab head M={M} K={K} N={N}")
+    _, got = _run(c, True)
+    rng = np.random.default_rng(M)
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(N - 200, N),
+                                     rng.choice(N, 936, replace=False)]))
+    rows = np.repeat(np.arange(M), cols.size)
+    cc = np.tile(cols, M)
+    ref = oracle.w4a16_cells(c.A, c.q, c.s, c.z, 128, rows, cc, fold=True)
+    g = got[rows, cc]
+    assert rel_fro(g, ref) <= TOL
+    assert elementwise_guard(g, ref) <= 0
