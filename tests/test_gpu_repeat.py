@@ -30,7 +30,7 @@ def _device():
 
 # one shape per kernel path: decode split 8 ways, decode unsplit, skinny,
 # mid-size M, 64x128 tiles with the fused delta, 128x256 symmetric tiles with
-# the row split, and the separate correction launch
+# the row split, the separate correction launch, and two shapes with tails
 CASES = [
     (16, 16384, 4096, 128, True, 0),
     (4, 1024, 32768, 128, False, 0),
@@ -39,6 +39,8 @@ CASES = [
     (512, 1024, 8192, 128, True, 0),
     (1000, 640, 16256, 128, False, 0),
     (16, 1024, 1024, 128, True, 1),
+    (16, 1000, 1000, 128, True, 0),        # tails: A padded, C cropped
+    (300, 1000, 520, 256, False, 0),
 ]
 
 
@@ -89,6 +91,59 @@ def test_w4a8_repeats_bitwise_across_streams():
     for i in range(REPEATS):
         with torch.cuda.stream(streams[i % len(streams)]):
             outs.append(qg.w4a8(Aq, asc, W, S, off, c.E, 64, c.N, c.g))
+    torch.cuda.synchronize()
+    want = host(first)
+    for i, o in enumerate(outs):
+        assert np.array_equal(host(o), want), f"repeat {i} differs"
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 17408, 5120), (64, 1024, 1024)])
+def test_swiglu_repeats_bitwise_across_streams(M, K, N):
+    """The gated decode kernel (split-K) and the GEMM-then-elementwise path."""
+    note(f"repeat swiglu M={M} K={K} N={N}")
+    c = synth.w4a16_case(M, K, 2 * N, 128, asym=True, stream=91, case_id=7000 + M)
+    pair = qg.pack(dev(c.q), dev(c.s), dev(c.z), 128)
+    A = dev(c.A)
+    first = qg.w4a16_swiglu(A, pair)
+    torch.cuda.synchronize()
+    ref = oracle.w4a16_swiglu(c.A, c.q, c.s, c.z, 128)
+    assert rel_fro(host(first).astype(np.float64), ref) <= 2e-3
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = []
+    for i in range(REPEATS):
+        with torch.cuda.stream(streams[i % len(streams)]):
+            outs.append(qg.w4a16_swiglu(A, pair))
+    torch.cuda.synchronize()
+    want = host(first)
+    for i, o in enumerate(outs):
+        assert np.array_equal(host(o), want), f"repeat {i} differs"
+
+
+def test_quantize_then_w4a8_asym_repeats_bitwise_across_streams():
+    """The quantizer and the zero-point W4A8 GEMM, chained on each stream."""
+    c = synth.w4a8_case(8, 64, 2048, 1024, 128, stream=92, case_id=1, asym=True)
+    note(f"repeat quantize + w4a8 asym E={c.E} K={c.K} N={c.N}")
+    packs = [qg.pack(dev(c.q[e]), dev(c.s[e]), dev(c.z[e]), c.g) for e in range(c.E)]
+    W = torch.stack([p.w for p in packs]).contiguous()
+    S = torch.stack([p.scale for p in packs]).contiguous()
+    D = torch.stack([p.delta for p in packs]).contiguous()
+    A16, off = dev(c.A16), dev(c.offsets)
+
+    def run():
+        Aq, asc = qg.quantize_rows(A16)
+        return qg.w4a8(Aq, asc, W, S, off, c.E, 64, c.N, c.g, w_delta=D)
+
+    first = run()
+    torch.cuda.synchronize()
+    ref, _ = oracle.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, c.g, z=c.z)
+    assert rel_fro(host(first).astype(np.float64), ref) <= 1e-2
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = []
+    for i in range(REPEATS):
+        with torch.cuda.stream(streams[i % len(streams)]):
+            outs.append(run())
     torch.cuda.synchronize()
     want = host(first)
     for i, o in enumerate(outs):
