@@ -179,9 +179,11 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
             const int gi = (kt * KTILE) / g;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                // acci is exactly 16x the group's integer product (|acci| < 2^24,
-                // so its fp32 conversion is exact); scaling it by s/16 (exact)
-                // gives the same fma result as scaling acci >> 4 by s
+                // acci is exactly 16x the group's integer product; for groups of
+                // up to 1024 k, |acci| <= 16 * 127 * 8 * g < 2^24 and its fp32
+                // conversion is exact, so scaling it by s/16 (exact) gives the
+                // same fma result as scaling acci >> 4 by s (longer groups, e.g.
+                // one per column, round that conversion once: 2^-24 relative)
                 const float sv16 = sv[t] * 0.0625f;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
