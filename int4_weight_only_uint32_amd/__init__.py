@@ -106,6 +106,18 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t: Optional[torch.Tensor], n: int, name: str):
+    """Element count a call will touch: a smaller tensor would be read or
+    written out of bounds on the device, so it is refused here."""
+    if t is not None and isinstance(t, torch.Tensor) and t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
+
+
+def _groups(K: int, group_size: int) -> int:
+    g = K if group_size == -1 else group_size
+    return -(-K // g) if g > 0 else 0
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -133,6 +145,13 @@ class PackedWeight:
 
 def pack_int4_weights(q, scale, zero, K, N, group_size, flags, w_packed, scale_out, delta_out):
     """Same arguments as the C entry point, as device tensors (zero/delta_out may be None)."""
+    Kp, Np, G = padded_shape(K, N, group_size)
+    _need(q, K * N, "q")
+    for t, nm in ((scale, "scale"), (zero, "zero")):
+        _need(t, G * N, nm)
+    _need(w_packed, Kp * Np // 8, "w_packed")
+    for t, nm in ((scale_out, "scale_out"), (delta_out, "delta_out")):
+        _need(t, G * Np, nm)
     _check(lib().pack_int4_weights(_ptr(q, torch.uint8, "q"), _ptr(scale, torch.float16, "scale"),
                                    _ptr(zero, torch.float16, "zero"), K, N, group_size, flags,
                                    _ptr(w_packed, torch.int32, "w_packed"),
@@ -164,6 +183,12 @@ def pack(q: torch.Tensor, scale: torch.Tensor, zero: Optional[torch.Tensor] = No
 
 
 def qgemm_w4a16(A, w_packed, scale, delta, C, M, N, K, group_size, flags=0, workspace=None):
+    Kp, Np, G = padded_shape(K, N, group_size)
+    _need(A, M * K, "A")
+    _need(C, M * N, "C")
+    _need(w_packed, Kp * Np // 8, "w_packed")
+    _need(scale, G * Np, "scale")
+    _need(delta, G * Np, "delta")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qgemm_w4a16(_ptr(A, torch.float16, "A"), _ptr(w_packed, torch.int32, "w_packed"),
                              _ptr(scale, torch.float16, "scale"),
@@ -201,6 +226,9 @@ def w4a16(A: torch.Tensor, pw: PackedWeight, C: Optional[torch.Tensor] = None, f
 
 
 def group_sum_correction(A, delta, C, M, N, K, group_size, workspace):
+    _need(A, M * K, "A")
+    _need(delta, _groups(K, group_size) * N, "delta")
+    _need(C, M * N, "C")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().group_sum_correction(_ptr(A, torch.float16, "A"), _ptr(delta, torch.float16, "delta"),
                                       _ptr(C, torch.float16, "C"), M, N, K, group_size,
@@ -219,6 +247,15 @@ def correct(A: torch.Tensor, delta: torch.Tensor, C: torch.Tensor, group_size: i
 
 def qgemm_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts, M_total,
                max_rows_per_expert, N, K, group_size, C, acc_debug=None, flags=0, w_delta=None):
+    G = _groups(K, group_size)
+    _need(A_q, M_total * K, "A_q")
+    _need(a_scale, M_total, "a_scale")
+    _need(w_packed, num_experts * K * N // 8, "w_packed")
+    _need(w_scale, num_experts * G * N, "w_scale")
+    _need(w_delta, num_experts * G * N, "w_delta")
+    _need(expert_offsets, num_experts + 1, "expert_offsets")
+    _need(C, M_total * N, "C")
+    _need(acc_debug, M_total * G * N, "acc_debug")
     _check(lib().qgemm_w4a8(_ptr(A_q, torch.int8, "A_q"), _ptr(a_scale, torch.float32, "a_scale"),
                             _ptr(w_packed, torch.int32, "w_packed"),
                             _ptr(w_scale, torch.float16, "w_scale"),
@@ -244,6 +281,9 @@ def w4a8(A_q: torch.Tensor, a_scale: torch.Tensor, w_packed: torch.Tensor, w_sca
 
 
 def quantize_rows_int8(A, M, K, A_q, a_scale):
+    _need(A, M * K, "A")
+    _need(A_q, M * K, "A_q")
+    _need(a_scale, M, "a_scale")
     _check(lib().quantize_rows_int8(_ptr(A, torch.float16, "A"), M, K, _ptr(A_q, torch.int8, "A_q"),
                                     _ptr(a_scale, torch.float32, "a_scale"), _stream(A)))
 
@@ -263,6 +303,12 @@ def quantize_rows(A: torch.Tensor, A_q: Optional[torch.Tensor] = None,
 
 
 def qgemm_w4a16_swiglu(A, w_packed, scale, delta, H, M, N, K, group_size, flags=0, workspace=None):
+    G = _groups(K, group_size)
+    _need(A, M * K, "A")
+    _need(w_packed, K * 2 * N // 8, "w_packed")
+    _need(scale, G * 2 * N, "scale")
+    _need(delta, G * 2 * N, "delta")
+    _need(H, M * N, "H")
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().qgemm_w4a16_swiglu(_ptr(A, torch.float16, "A"), _ptr(w_packed, torch.int32, "w_packed"),
                                     _ptr(scale, torch.float16, "scale"), _ptr(delta, torch.float16, "delta"),

@@ -248,3 +248,25 @@ def test_tail_workspace_sizes():
     assert ws(300, 1000, 1000, 128) == CTR + al(300 * 1024 * 2) + 300 * 1024 * 2
     with pytest.raises(qg.QGemmError):
         qg.qg_workspace_bytes(qg.QG_OP_W4A16, 4, 1000, 1000, 128, 1, qg.QG_CORR_SEPARATE)
+
+
+def test_binding_refuses_undersized_tensors():
+    """The Python layer checks element counts before any call: a tensor too
+    small for the sizes passed would be read or written out of bounds."""
+    import torch
+    t = lambda n, dt=torch.float16: torch.zeros(n, dtype=dt)
+    with pytest.raises(ValueError, match="C holds"):
+        qg.qgemm_w4a16(t(16 * 1024), t(1024 * 1024 // 8, torch.int32), t(8 * 1024), None,
+                       t(16 * 1024 - 1), 16, 1024, 1024, 128)
+    with pytest.raises(ValueError, match="w_packed"):
+        qg.qgemm_w4a16(t(16 * 1000), t(1000 * 1000 // 8, torch.int32), t(8 * 1024), None,
+                       t(16 * 1000), 16, 1000, 1000, 128)    # the padded pack is 1024 x 1024
+    with pytest.raises(ValueError, match="a_scale"):
+        qg.quantize_rows_int8(t(4 * 64), 4, 64, t(4 * 64, torch.int8), t(3, torch.float32))
+    with pytest.raises(ValueError, match="acc_debug"):
+        qg.qgemm_w4a8(t(64 * 1024, torch.int8), t(64, torch.float32), t(1024 * 1024 // 8, torch.int32),
+                      t(8 * 1024), None, 1, 64, 64, 1024, 1024, 128, t(64 * 1024),
+                      acc_debug=t(10, torch.int32))
+    with pytest.raises(ValueError, match="H holds"):
+        qg.qgemm_w4a16_swiglu(t(16 * 1024), t(1024 * 2048 // 8, torch.int32), t(8 * 2048), None,
+                              t(16 * 1023), 16, 1024, 1024, 128)
