@@ -444,3 +444,12 @@ def test_w4a8_asym_integer_exact():
     for debug in (True, False):
         got, _ = _run_w4a8(c, debug=debug)
         assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_w4a8_large_ragged_experts(asym):
+    """Experts of 700 and 300 rows: many 64-row blocks per expert, a ragged
+    last block, the grid sized by the larger expert."""
+    c = synth.w4a8_case(2, 0, 1024, 512, 128, signed_scales=not asym, stream=85, case_id=6,
+                        rows=[700, 300], asym=asym, name="w4a8-large")
+    _check_w4a8(c)
