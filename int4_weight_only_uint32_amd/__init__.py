@@ -1,14 +1,16 @@
 """Python binding of the packed-int4 weight GEMM library (libqgemm.so, gfx950).
 
 Argument marshalling only: each function checks that it was given device
-tensors of the right dtype, passes their pointers and the current HIP stream to
-the C ABI declared in include/qgemm.h, and raises QGemmError on a non-zero
-status.  Every step of the computation runs in the library's HIP kernels; there
-is no fallback of any kind -- if libqgemm.so is missing, importing works but
-every call raises.
+tensors of the right dtype and of at least the sizes the call touches, passes
+their pointers and the current HIP stream to the C ABI declared in
+include/qgemm.h, and raises QGemmError on a non-zero status.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback of any
+kind -- if libqgemm.so is missing, importing works but every call raises.
 
-Names follow the C ABI: pack_int4_weights, qgemm_w4a16, group_sum_correction,
-qgemm_w4a8 (plus qg_device_supported, qg_workspace_bytes).
+Names follow the C ABI: pack_int4_weights, qgemm_w4a16, qgemm_w4a16_swiglu,
+group_sum_correction, quantize_rows_int8, qgemm_w4a8 (plus qg_device_supported,
+qg_workspace_bytes, qg_padded_shape); pack, w4a16, w4a16_swiglu, correct,
+quantize_rows and w4a8 are the same calls with torch-allocated outputs.
 """
 import ctypes
 import os
