@@ -214,7 +214,7 @@ def w4a8(Aq, a_scale, q, s, offsets, g, fold=True, want_acc=True, z=None):
     offsets, po = _c(offsets, np.int32)
     E, K, N = q.shape
     M_total = Aq.shape[0]
-    G = K // g
+    G = -(-K // g)
     C = np.empty((M_total, N), dtype=np.float64)
     acc = np.zeros((M_total, G, N), dtype=np.int64) if want_acc else None
     pacc = acc.ctypes.data_as(ctypes.c_void_p) if want_acc else None

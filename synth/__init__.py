@@ -129,7 +129,7 @@ def w4a8_case(E, rows_per_expert, K, N, g, signed_scales=False, stream=4, case_i
     offsets = np.zeros(E + 1, dtype=np.int32)
     offsets[1:] = np.cumsum(rows)
     M_total = int(offsets[-1])
-    G = K // g
+    G = -(-K // g)
     r = rng_for(stream, case_id)
     A16 = r.standard_normal((M_total, K)).astype(np.float16)
     q = r.integers(0, 16, size=(E, K, N), dtype=np.uint8)

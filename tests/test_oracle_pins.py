@@ -470,3 +470,15 @@ def test_w4a16_n_tail_columns_are_independent(oracle_lib):
     C3 = oracle_lib.w4a16(c.A, np.ascontiguousarray(c.q[:, :300]), np.ascontiguousarray(c.s[:, :300]),
                           None, 128)
     assert np.array_equal(C[:, :300], C3)
+
+
+def test_w4a8_k_tail_is_zero_padding(oracle_lib):
+    """W4A8 over K = 1000 (a partial last group) equals the same product with
+    A_q padded by zero columns to K = 1024 and arbitrary padding codes."""
+    c = synth.w4a8_case(2, 3, 1000, 40, 128, stream=90, case_id=502, asym=True)
+    C, acc = oracle_lib.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, 128, z=c.z)
+    rng = np.random.default_rng(2)
+    Aq = np.concatenate([c.Aq, np.zeros((c.M_total, 24), np.int8)], axis=1)
+    q = np.concatenate([c.q, rng.integers(0, 16, size=(2, 24, 40), dtype=np.uint8)], axis=1)
+    Cp, accp = oracle_lib.w4a8(Aq, c.a_scale, q, c.s, c.offsets, 128, z=c.z)
+    assert np.array_equal(C, Cp) and np.array_equal(acc, accp)
