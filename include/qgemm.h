@@ -45,7 +45,8 @@
  *   - Shapes: K % 128 == 0 and N % 128 == 0 (the tile multiples the pages'
  *     dispatcher requires), M >= 1.  group_size must divide K and be a multiple
  *     of 128, or equal K; -1 is accepted as an alias of K (per-column scales).
- *     pack_int4_weights and qgemm_w4a16 also take any K, N >= 1 ("tails"):
+ *     pack_int4_weights, qgemm_w4a16 and qgemm_w4a8 also take any K, N >= 1
+ *     ("tails"):
  *     group_size is then a multiple of 128 (the last group of g consecutive k
  *     may be partial: G = ceil(K / g)), K, or -1; see qg_padded_shape.
  *   - A, C, scale, zero and delta must be 2-byte aligned; w_packed 16-byte
@@ -224,7 +225,14 @@ int group_sum_correction(const uint16_t *A, const uint16_t *delta, uint16_t *C,
  *              (the delta term only with w_delta), in fp32, one rounding to
  *              fp16 at the end.
  * acc_debug    NULL, or [M_total,G,N] int32 out receiving acc exactly.
- * No workspace (pass NULL, 0).                                              */
+ * Tails (K or N not a multiple of 128, packs from pack_int4_weights of that
+ *              shape: each [K_padded*N_padded/8], scales [G,N_padded]): A_q
+ *              is copied with zero columns into the workspace, the product is
+ *              formed on the padded shape and cropped into C; acc_debug is
+ *              then QG_ERR_UNSUPPORTED.
+ * workspace/workspace_bytes: qg_workspace_bytes(QG_OP_W4A8, M_total, N, K,
+ *              group_size, E, 0) bytes, 256-byte aligned: 0 (pass NULL, 0)
+ *              unless the shape has tails.                                  */
 int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed,
                const uint16_t *w_scale, const uint16_t *w_delta,
                const int32_t *expert_offsets, int num_experts,

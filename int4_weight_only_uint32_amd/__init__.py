@@ -248,13 +248,14 @@ def correct(A: torch.Tensor, delta: torch.Tensor, C: torch.Tensor, group_size: i
 
 
 def qgemm_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts, M_total,
-               max_rows_per_expert, N, K, group_size, C, acc_debug=None, flags=0, w_delta=None):
-    G = _groups(K, group_size)
+               max_rows_per_expert, N, K, group_size, C, acc_debug=None, flags=0, w_delta=None,
+               workspace=None):
+    Kp, Np, G = padded_shape(K, N, group_size)
     _need(A_q, M_total * K, "A_q")
     _need(a_scale, M_total, "a_scale")
-    _need(w_packed, num_experts * K * N // 8, "w_packed")
-    _need(w_scale, num_experts * G * N, "w_scale")
-    _need(w_delta, num_experts * G * N, "w_delta")
+    _need(w_packed, num_experts * Kp * Np // 8, "w_packed")
+    _need(w_scale, num_experts * G * Np, "w_scale")
+    _need(w_delta, num_experts * G * Np, "w_delta")
     _need(expert_offsets, num_experts + 1, "expert_offsets")
     _need(C, M_total * N, "C")
     _need(acc_debug, M_total * G * N, "acc_debug")
@@ -265,7 +266,9 @@ def qgemm_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts, M_t
                             _ptr(expert_offsets, torch.int32, "expert_offsets"), num_experts,
                             M_total, max_rows_per_expert, N, K, group_size,
                             _ptr(C, torch.float16, "C"), _ptr(acc_debug, torch.int32, "acc_debug"),
-                            None, 0, flags, _stream(A_q)))
+                            _ptr(workspace, None, "workspace"),
+                            workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                            flags, _stream(A_q)))
 
 
 def w4a8(A_q: torch.Tensor, a_scale: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor,
@@ -277,8 +280,12 @@ def w4a8(A_q: torch.Tensor, a_scale: torch.Tensor, w_packed: torch.Tensor, w_sca
     M_total, K = A_q.shape
     if C is None:
         C = torch.empty((M_total, N), dtype=torch.float16, device=A_q.device)
+    ws = None
+    n = qg_workspace_bytes(QG_OP_W4A8, M_total, N, K, group_size, num_experts, 0)
+    if n > 0:
+        ws = workspace_for(A_q.device, n)
     qgemm_w4a8(A_q, a_scale, w_packed, w_scale, expert_offsets, num_experts, M_total,
-               max_rows_per_expert, N, K, group_size, C, acc_debug, w_delta=w_delta)
+               max_rows_per_expert, N, K, group_size, C, acc_debug, w_delta=w_delta, workspace=ws)
     return C
 
 

@@ -192,6 +192,8 @@ size_t qg_workspace_bytes(int op, int M, int N, int K, int group_size, int num_e
         if (check_shape("qg_workspace_bytes", M, N, K, &g) != QG_OK) return (size_t)-1;
         return corr_ws_bytes(M, K, g);
     case QG_OP_W4A8:
+        if (check_shape_tail("qg_workspace_bytes", M < 1 ? 1 : M, N, K, &g) != QG_OK) return (size_t)-1;
+        return qg::is_tail_shape(N, K, g) ? qg::w4a8_tail_workspace_bytes(M < 1 ? 1 : M, N, K, g) : 0;
     case QG_OP_PACK:
         if (check_shape("qg_workspace_bytes", M < 1 ? 1 : M, N, K, &g) != QG_OK) return (size_t)-1;
         return 0;
@@ -328,11 +330,10 @@ int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed
                int32_t *acc_debug, void *workspace, size_t workspace_bytes, unsigned flags,
                void *stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     int g = group_size;
-    int rc = check_shape("qgemm_w4a8", M_total, N, K, &g);
+    int rc = check_shape_tail("qgemm_w4a8", M_total, N, K, &g);
     if (rc) return rc;
+    const bool tail = qg::is_tail_shape(N, K, g);
     if (!A_q || !a_scale || !w_packed || !w_scale || !C)
         return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: NULL A_q/a_scale/w_packed/w_scale/C");
     if (num_experts < 1 || num_experts > 65535)
@@ -351,8 +352,23 @@ int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed
         (expert_offsets && !aligned(expert_offsets, 4)))
         return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: misaligned pointer");
     if (flags != 0) return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: unknown flags 0x%x", flags);
+    if (tail) {
+        if (acc_debug)
+            return fail(QG_ERR_UNSUPPORTED, "qgemm_w4a8: acc_debug needs K, N multiples of 128");
+        const size_t need = qg::w4a8_tail_workspace_bytes(M_total, N, K, g);
+        if (!workspace || workspace_bytes < need)
+            return fail(QG_ERR_WORKSPACE, "qgemm_w4a8: workspace of %zu bytes needed, got %zu", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 256))
+            return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: workspace must be 256-byte aligned");
+    }
     if ((rc = check_device())) return rc;
     int max_rows = max_rows_per_expert > M_total ? M_total : max_rows_per_expert;
+    if (tail)
+        return launch_status(qg::launch_w4a8_tail(A_q, a_scale, w_packed, w_scale, w_delta,
+                                                  expert_offsets, num_experts, M_total, max_rows,
+                                                  N, K, g, C, workspace, (hipStream_t)stream),
+                             "qgemm_w4a8");
     hipError_t e = qg::launch_w4a8(A_q, a_scale, w_packed, w_scale, w_delta, expert_offsets, num_experts,
                                    M_total, max_rows, N, K, g, C, acc_debug, (hipStream_t)stream);
     return launch_status(e, "qgemm_w4a8");

@@ -20,6 +20,17 @@ hipError_t launch_w4a16_tail(const uint16_t *A, const uint32_t *W, const uint16_
                              const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                              bool fuse_delta, void *ws, hipStream_t st);
 
+// C [M, N] from the first N columns of Cp [M, Np].
+hipError_t launch_crop_cols(const uint16_t *Cp, uint16_t *C, int M, int N, int Np, hipStream_t st);
+
+// Grouped W4A8 on a shape with tails (A_q padded and C cropped through `ws`
+// of w4a8_tail_workspace_bytes bytes, the kernel on the padded shape).
+size_t w4a8_tail_workspace_bytes(int M_total, int N, int K, int g);
+hipError_t launch_w4a8_tail(const int8_t *Aq, const float *a_scale, const uint32_t *W,
+                            const uint16_t *S, const uint16_t *D, const int32_t *offsets, int E,
+                            int M_total, int max_rows, int N, int K, int g, uint16_t *C, void *ws,
+                            hipStream_t st);
+
 hipError_t launch_pack(const uint8_t *q, const uint16_t *s, const uint16_t *z, int K, int N,
                        int g, bool fold, uint32_t *w, uint16_t *s_out, uint16_t *d_out,
                        hipStream_t st);

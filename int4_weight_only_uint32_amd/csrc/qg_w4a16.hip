@@ -1492,6 +1492,14 @@ __global__ __launch_bounds__(256) void crop_cols_kernel(const uint16_t *__restri
 
 static size_t al256(size_t n) { return (n + 255) / 256 * 256; }
 
+hipError_t launch_crop_cols(const uint16_t *Cp, uint16_t *C, int M, int N, int Np, hipStream_t st)
+{
+    const size_t n = (size_t)M * N;
+    hipLaunchKernelGGL(crop_cols_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Cp, C,
+                       M, N, Np);
+    return hipGetLastError();
+}
+
 bool is_tail_shape(int N, int K, int g)
 {
     int Kp, Np, gp;

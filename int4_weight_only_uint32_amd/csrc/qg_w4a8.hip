@@ -269,6 +269,29 @@ static hipError_t run_w4a8_d(const int8_t *Aq, const float *a_scale, const uint3
              : run_w4a8<2, 3, DEBUG, G1, false>(Aq, a_scale, W, S, nullptr, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
 }
 
+// ---- shapes with tails (K or N not a multiple of 128): the packs are padded
+//      to [Kp, Np] (pack_int4_weights); A_q is copied with zero columns up to
+//      Kp into the workspace, the kernel runs on the padded shape into a
+//      padded product there, which is cropped to C.  Workspace:
+//      [A_q padded, 256-aligned][C padded]. ----
+__global__ __launch_bounds__(256) void pad_cols_i8_kernel(const int8_t *__restrict__ A,
+                                                          int8_t *__restrict__ Ap, int M, int K,
+                                                          int Kp)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)M * Kp) return;
+    const size_t m = i / Kp;
+    const int k = (int)(i % Kp);
+    Ap[i] = k < K ? A[m * K + k] : (int8_t)0;
+}
+
+size_t w4a8_tail_workspace_bytes(int M_total, int N, int K, int g)
+{
+    int Kp, Np, gp;
+    padded_shape(K, N, g, &Kp, &Np, &gp);
+    return ((size_t)M_total * Kp + 255) / 256 * 256 + (size_t)M_total * Np * sizeof(uint16_t);
+}
+
 hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
                        const uint16_t *S, const uint16_t *D, const int32_t *offsets, int E,
                        int M_total, int max_rows, int N, int K, int g, uint16_t *C,
@@ -280,6 +303,31 @@ hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W
                   : run_w4a8_d<true, false>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
     return g1 ? run_w4a8_d<false, true>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st)
               : run_w4a8_d<false, false>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st);
+}
+
+} // namespace qg
+
+namespace qg {
+
+hipError_t launch_w4a8_tail(const int8_t *Aq, const float *a_scale, const uint32_t *W,
+                            const uint16_t *S, const uint16_t *D, const int32_t *offsets, int E,
+                            int M_total, int max_rows, int N, int K, int g, uint16_t *C, void *ws,
+                            hipStream_t st)
+{
+    if (!ws) return hipErrorInvalidValue;
+    int Kp, Np, gp;
+    padded_shape(K, N, g, &Kp, &Np, &gp);
+    int8_t *Ap = static_cast<int8_t *>(ws);
+    uint16_t *Cp = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) +
+                                                ((size_t)M_total * Kp + 255) / 256 * 256);
+    const size_t n = (size_t)M_total * Kp;
+    hipLaunchKernelGGL(pad_cols_i8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Aq,
+                       Ap, M_total, K, Kp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_w4a8(Ap, a_scale, W, S, D, offsets, E, M_total, max_rows, Np, Kp, gp, Cp, nullptr, st);
+    if (e != hipSuccess) return e;
+    return launch_crop_cols(Cp, C, M_total, N, Np, st);
 }
 
 } // namespace qg

@@ -127,7 +127,11 @@ def test_w4a8_validation():
     assert L.qgemm_w4a8(*args(mr=32)) == qg.QG_ERR_INVALID_ARG        # one expert must cover all rows
     assert L.qgemm_w4a8(*args(flags=1)) == qg.QG_ERR_INVALID_ARG
     assert L.qgemm_w4a8(*args(A=P(0x10004))) == qg.QG_ERR_INVALID_ARG
-    assert L.qgemm_w4a8(*args(K=1000)) == qg.QG_ERR_UNSUPPORTED
+    assert L.qgemm_w4a8(*args(K=1000)) == qg.QG_ERR_WORKSPACE        # tails: A_q padded in the workspace
+    tail_acc = args(K=1000)
+    tail_acc[13] = FAKE                                                # acc_debug with a tail
+    tail_acc[14], tail_acc[15] = P(0x100000), 1 << 30
+    assert L.qgemm_w4a8(*tail_acc) == qg.QG_ERR_UNSUPPORTED
     assert L.qgemm_w4a8(*args(D=P(0x10001))) == qg.QG_ERR_INVALID_ARG  # misaligned deltas
 
 
@@ -177,8 +181,8 @@ def test_workspace_bytes():
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 64, 7168, 2048, 128, 8) == 0
     with pytest.raises(qg.QGemmError):
         qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1000, 100)     # 100 neither divides K nor is a multiple of 128
-    with pytest.raises(qg.QGemmError):
-        qg.qg_workspace_bytes(qg.QG_OP_W4A8, 16, 1024, 1000, 128)      # W4A8 keeps K % 128 == 0
+    al = lambda n: (n + 255) // 256 * 256
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 16, 1000, 1000, 128, 2) == al(16 * 1024) + 16 * 1024 * 2
     with pytest.raises(qg.QGemmError):
         qg.qg_workspace_bytes(99, 16, 1024, 1024, 128)
 

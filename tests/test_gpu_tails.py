@@ -70,3 +70,25 @@ def test_vocab_head_sampled(M):
     g = got[rows, cc]
     assert rel_fro(g, ref) <= TOL
     assert elementwise_guard(g, ref) <= 0
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_w4a8_tails(asym):
+    """Grouped W4A8 with K = 1000 (a partial last group) and N = 300 over
+    ragged experts (one empty): padded packs, A_q padded and C cropped through
+    the workspace."""
+    c = synth.w4a8_case(3, 0, 1000, 300, 128, signed_scales=not asym, stream=92, case_id=2000,
+                        rows=[40, 0, 75], asym=asym)
+    note(f"w4a8 tails asym={asym} rows={np.diff(c.offsets).tolist()} K=1000 N=300")
+    packs = [qg.pack(dev(c.q[e]), dev(c.s[e]), dev(c.z[e]) if asym else None, c.g, fold=True)
+             for e in range(c.E)]
+    W = torch.stack([p.w for p in packs]).contiguous()
+    S = torch.stack([p.scale for p in packs]).contiguous()
+    D = torch.stack([p.delta for p in packs]).contiguous() if asym else None
+    C = qg.w4a8(dev(c.Aq), dev(c.a_scale), W, S, dev(c.offsets), c.E, 75, c.N, c.g, w_delta=D)
+    torch.cuda.synchronize()
+    got = host(C).astype(np.float64)
+    ref, _ = oracle.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, c.g, fold=True, z=c.z,
+                         want_acc=False)
+    assert rel_fro(got, ref) <= 1e-2
+    assert elementwise_guard(got, ref) <= 0
