@@ -50,6 +50,17 @@ int launch_status(hipError_t e, const char *what)
     return ok();
 }
 
+// The kernels address a tile's activation rows and a scale row with 32-bit
+// byte offsets: K < 2^22 and ceil(K/g) * N * 2 < 2^31 keep every one in
+// range (far beyond any layer; larger shapes are refused, not miscomputed).
+int check_offsets(const char *what, int N, int K, int g)
+{
+    const long long groups = (K + (long long)g - 1) / g;
+    if (K >= (1 << 22) || groups * N * 2 >= (1ll << 31))
+        return fail(QG_ERR_UNSUPPORTED, "%s: K=%d, N=%d too large for 32-bit offsets", what, K, N);
+    return QG_OK;
+}
+
 // Shape rules shared by every GEMM-like entry point.  Normalises the per-column
 // sentinel -1 to K.
 int check_shape(const char *what, int M, int N, int K, int *g)
@@ -67,7 +78,7 @@ int check_shape(const char *what, int M, int N, int K, int *g)
                     "%s: group_size %d unsupported (must be a multiple of 128, K, or -1)", what, *g);
     if ((long long)M * K > (1ll << 40) || (long long)K * N > (1ll << 40))
         return fail(QG_ERR_UNSUPPORTED, "%s: shape too large", what);
-    return QG_OK;
+    return check_offsets(what, N, K, *g);
 }
 
 // Shape rules of the entry points that take tails (pack_int4_weights,
@@ -89,7 +100,7 @@ int check_shape_tail(const char *what, int M, int N, int K, int *g)
     if (K > (1 << 28) || N > (1 << 28) || (long long)M * K > (1ll << 40) ||
         (long long)K * N > (1ll << 40))
         return fail(QG_ERR_UNSUPPORTED, "%s: shape too large", what);
-    return QG_OK;
+    return check_offsets(what, N, K, *g);
 }
 
 size_t corr_ws_bytes(int M, int K, int g) { return (size_t)M * (size_t)(K / g) * sizeof(float); }
@@ -279,6 +290,7 @@ int qgemm_w4a16_swiglu(const uint16_t *A, const uint32_t *w_packed, const uint16
     if (rc) return rc;
     if (N > 0x3FFFFFFF || (size_t)K * 2 * (size_t)N / 8 > 0x7FFFFFFFull * 16)
         return fail(QG_ERR_UNSUPPORTED, "qgemm_w4a16_swiglu: shape too large");
+    if ((rc = check_offsets("qgemm_w4a16_swiglu", 2 * N, K, g))) return rc;   // the pair's width
     if (!A || !w_packed || !scale || !H)
         return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16_swiglu: NULL A/w_packed/scale/H");
     if (!aligned(A, 16) || !aligned(w_packed, 16) || !aligned(scale, 2) || !aligned(H, 16) ||

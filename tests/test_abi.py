@@ -274,3 +274,12 @@ def test_binding_refuses_undersized_tensors():
     with pytest.raises(ValueError, match="H holds"):
         qg.qgemm_w4a16_swiglu(t(16 * 1024), t(1024 * 2048 // 8, torch.int32), t(8 * 2048), None,
                               t(16 * 1023), 16, 1024, 1024, 128)
+
+
+def test_offset_limits_refused():
+    # shapes whose 32-bit in-kernel offsets would overflow are refused on the host
+    with pytest.raises(qg.QGemmError):
+        qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1 << 22, 128)
+    with pytest.raises(qg.QGemmError):
+        qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1 << 20, 1 << 18, 128)   # 2048 groups x 2^20 columns
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 262144, 65536, 128) >= 0
