@@ -49,6 +49,9 @@
  *     ("tails"):
  *     group_size is then a multiple of 128 (the last group of g consecutive k
  *     may be partial: G = ceil(K / g)), K, or -1; see qg_padded_shape.
+ *     Limits: K < 2^22 and ceil(K / g) * N * 2 < 2^31 (the kernels' 32-bit
+ *     offsets; qgemm_w4a16_swiglu counts the pair's 2N), else
+ *     QG_ERR_UNSUPPORTED.
  *   - A, C, scale, zero and delta must be 2-byte aligned; w_packed 16-byte
  *     aligned; A 16-byte aligned for the W4A16 GEMM, A_q 8-byte aligned for
  *     W4A8.
