@@ -218,8 +218,10 @@ int group_sum_correction(const uint16_t *A, const uint16_t *delta, uint16_t *C,
  *              offsets[E] = M_total: expert e owns rows offsets[e] ..
  *              offsets[e+1]-1.  NULL means one expert owning all rows (E must
  *              be 1).  Rows are clipped to [0, M_total) in the kernel.
- * max_rows_per_expert  an upper bound of offsets[e+1]-offsets[e] over e; rows
- *              of an expert beyond this bound are NOT computed.
+ * max_rows_per_expert  the expected largest offsets[e+1]-offsets[e]; it only
+ *              sizes the launch (ceil(max_rows_per_expert / 64) row blocks per
+ *              expert, each taking every further 64-row block of its expert in
+ *              turn), so a bound below the true count is slower, never wrong.
  * C            [M_total,N] fp16 out, overwritten:
  *              C[m,n] = a_scale[m] * sum_g (scale_e[g,n] * acc[m,g,n]
  *                                           + delta_e[g,n] * qsum[m,g])
@@ -235,7 +237,11 @@ int group_sum_correction(const uint16_t *A, const uint16_t *delta, uint16_t *C,
  *              then QG_ERR_UNSUPPORTED.
  * workspace/workspace_bytes: qg_workspace_bytes(QG_OP_W4A8, M_total, N, K,
  *              group_size, E, 0) bytes, 256-byte aligned: 0 (pass NULL, 0)
- *              unless the shape has tails.                                  */
+ *              unless the shape has tails.  The first
+ *              QG_W4A16_WS_COUNTER_BYTES bytes are never touched (they are
+ *              the W4A16 split-K counters' place), so one zero-filled
+ *              workspace may serve W4A16 and W4A8 calls in turn on one
+ *              stream.                                                      */
 int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed,
                const uint16_t *w_scale, const uint16_t *w_delta,
                const int32_t *expert_offsets, int num_experts,

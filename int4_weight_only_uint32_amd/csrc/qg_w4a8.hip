@@ -59,9 +59,6 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
         r0 = r0 < 0 ? 0 : (r0 > M_total ? M_total : r0);
         r1 = r1 < r0 ? r0 : (r1 > M_total ? M_total : r1);
     }
-    const int m0 = r0 + blockIdx.y * 16 * MT;
-    if (m0 >= r1) return;   // uniform over the workgroup, before any barrier
-
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, kq = lane >> 4;
@@ -72,172 +69,185 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
     const uint16_t *D = DELTA ? Dall + (size_t)e * G * N : nullptr;
     const int sh = 16 * (c & 1);
 
-    // ---- A staging: thread t copies 2 x 16 bytes: row t/4 (of 64), bytes
-    // 32 (t%4) .. 32 (t%4) + 31 of the 128-k tile.  Rows past the expert's
-    // last row read that last row (never stored).
-    int arow = m0 + (tid >> 2);
-    arow = arow < r1 ? arow : r1 - 1;
-    const int8_t *asrc = Aq + (size_t)arow * K + 32 * (tid & 3);
-    // the 32 bytes k0 .. k0+31 (k0 = 32 (t%4)) split into four 8-byte pieces:
-    // piece j holds k = k0 + 8j .. k0 + 8j + 7 -> operand op = k0 / 64, slot
-    // kq = j, half = (k0 / 32) % 2
-    auto slot = [&](int row, int op, int q) { return row * 8 + op * 4 + (q ^ ((row >> 1) & 3)); };
-    auto store_a = [&](int st, const uint4v (&areg)[2]) {
-        const int row = tid >> 2, k0 = 32 * (tid & 3);
-        const int op = k0 / 64, half = (k0 / 32) & 1;
-        unsigned d[8] = {areg[0].x, areg[0].y, areg[0].z, areg[0].w,
-                         areg[1].x, areg[1].y, areg[1].z, areg[1].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint2v piece = {swap_mid_bytes(d[2 * j]), swap_mid_bytes(d[2 * j + 1])};
-            *reinterpret_cast<uint2v *>(reinterpret_cast<char *>(&As[st][slot(row, op, j)]) + 8 * half) = piece;
-        }
-    };
+    // The grid's y extent comes from the caller's bound on rows per expert,
+    // which the host cannot check against the device offsets: a workgroup
+    // takes row blocks y, y + gridDim.y, ... until the expert's rows run out,
+    // so an understated bound costs time, never rows.  The exit test is
+    // uniform over the workgroup and comes before any barrier of the block.
+    for (int mb = blockIdx.y;; mb += gridDim.y) {
+        const int m0 = r0 + mb * 16 * MT;
+        if (m0 >= r1) break;
 
-    const uint4v *wp = W + (size_t)nt0 * KT * 64 + lane;
-    const int col0 = nt0 * NTILE + c;
+        // ---- A staging: thread t copies 2 x 16 bytes: row t/4 (of 64), bytes
+        // 32 (t%4) .. 32 (t%4) + 31 of the 128-k tile.  Rows past the expert's
+        // last row read that last row (never stored).
+        int arow = m0 + (tid >> 2);
+        arow = arow < r1 ? arow : r1 - 1;
+        const int8_t *asrc = Aq + (size_t)arow * K + 32 * (tid & 3);
+        // the 32 bytes k0 .. k0+31 (k0 = 32 (t%4)) split into four 8-byte pieces:
+        // piece j holds k = k0 + 8j .. k0 + 8j + 7 -> operand op = k0 / 64, slot
+        // kq = j, half = (k0 / 32) % 2
+        auto slot = [&](int row, int op, int q) { return row * 8 + op * 4 + (q ^ ((row >> 1) & 3)); };
+        auto store_a = [&](int st, const uint4v (&areg)[2]) {
+            const int row = tid >> 2, k0 = 32 * (tid & 3);
+            const int op = k0 / 64, half = (k0 / 32) & 1;
+            unsigned d[8] = {areg[0].x, areg[0].y, areg[0].z, areg[0].w,
+                             areg[1].x, areg[1].y, areg[1].z, areg[1].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint2v piece = {swap_mid_bytes(d[2 * j]), swap_mid_bytes(d[2 * j + 1])};
+                *reinterpret_cast<uint2v *>(reinterpret_cast<char *>(&As[st][slot(row, op, j)]) + 8 * half) = piece;
+            }
+        };
 
-    float4v accf[MT][NT];
-    int4v acci[MT][NT];
-    int4v qsum[MT];   // DELTA: the group's activation sums, rows 4 kq + r
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        qsum[mt] = int4v{0, 0, 0, 0};
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            accf[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
-            acci[mt][t] = int4v{0, 0, 0, 0};
-        }
-    }
+        const uint4v *wp = W + (size_t)nt0 * KT * 64 + lane;
+        const int col0 = nt0 * NTILE + c;
 
-    // register ring: activations, codes, group scales (32-bit pair holding
-    // this lane's column, half c & 1)
-    uint4v ra[P][2], rw[P][NT];
-    uint32_t rs[P][NT], rd[P][NT];
-    auto load = [&](int kt, int sl) {
-        const int k = kt < KT ? kt : KT - 1;
-        ra[sl][0] = *reinterpret_cast<const uint4v *>(asrc + k * KTILE);
-        ra[sl][1] = *reinterpret_cast<const uint4v *>(asrc + k * KTILE + 16);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) rw[sl][t] = wp[((size_t)t * KT + k) * 64];
-        const int gi = (k * KTILE) / g;
-        const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) rs[sl][t] = srow[8 * t];
-        if (DELTA) {
-            const uint32_t *drow = reinterpret_cast<const uint32_t *>(D + (size_t)gi * N + (col0 & ~1));
-#pragma unroll
-            for (int t = 0; t < NT; ++t) rd[sl][t] = drow[8 * t];
-        }
-    };
-
-    auto step = [&](int kt, int sl) {
-        const int st = kt & 1;
-        store_a(st, ra[sl]);
-        CodeOpsI8 b[NT];
-        float sv[NT], dv[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            b[t] = split_codes_i8(rw[sl][t]);
-            sv[t] = h2f((uint16_t)(rs[sl][t] >> sh));
-            dv[t] = DELTA ? h2f((uint16_t)(rd[sl][t] >> sh)) : 0.0f;
-            pin(b[t].op[0]);
-            pin(b[t].op[1]);
-            pin(sv[t]);
-            if (DELTA) pin(dv[t]);
-        }
-        load(kt + P, sl);
-        __syncthreads();
-        int4v alo[MT], ahi[MT];
+        float4v accf[MT][NT];
+        int4v acci[MT][NT];
+        int4v qsum[MT];   // DELTA: the group's activation sums, rows 4 kq + r
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int row = 16 * mt + c;
-            alo[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 0, kq)]);
-            ahi[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 1, kq)]);
-        }
-        // G1 (one k-tile per group): each tile's group sum starts from a zero
-        // MFMA operand, so nothing is reset and nothing stays live across tiles
-        const int4v zero4 = {0, 0, 0, 0};
-        if (DELTA) {
-            // sum over k of A[row, k] * 1: every column of the product holds
-            // the row's sum, so each lane gets its own rows' sums
-            const int4v ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                qsum[mt] = mfma_i8(alo[mt], ones, G1 ? zero4 : qsum[mt]);
-                qsum[mt] = mfma_i8(ahi[mt], ones, qsum[mt]);
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                acci[mt][t] = mfma_i8(alo[mt], b[t].op[0], G1 ? zero4 : acci[mt][t]);
-                acci[mt][t] = mfma_i8(ahi[mt], b[t].op[1], acci[mt][t]);
-            }
-        if (G1 || ((kt + 1) * KTILE) % g == 0) {   // end of a weight group
-            const int gi = (kt * KTILE) / g;
+            qsum[mt] = int4v{0, 0, 0, 0};
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                // acci is exactly 16x the group's integer product; for groups of
-                // up to 1024 k, |acci| <= 16 * 127 * 8 * g < 2^24 and its fp32
-                // conversion is exact, so scaling it by s/16 (exact) gives the
-                // same fma result as scaling acci >> 4 by s (longer groups, e.g.
-                // one per column, round that conversion once: 2^-24 relative)
-                const float sv16 = sv[t] * 0.0625f;
+                accf[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
+                acci[mt][t] = int4v{0, 0, 0, 0};
+            }
+        }
+
+        // register ring: activations, codes, group scales (32-bit pair holding
+        // this lane's column, half c & 1)
+        uint4v ra[P][2], rw[P][NT];
+        uint32_t rs[P][NT], rd[P][NT];
+        auto load = [&](int kt, int sl) {
+            const int k = kt < KT ? kt : KT - 1;
+            ra[sl][0] = *reinterpret_cast<const uint4v *>(asrc + k * KTILE);
+            ra[sl][1] = *reinterpret_cast<const uint4v *>(asrc + k * KTILE + 16);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) rw[sl][t] = wp[((size_t)t * KT + k) * 64];
+            const int gi = (k * KTILE) / g;
+            const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
+#pragma unroll
+            for (int t = 0; t < NT; ++t) rs[sl][t] = srow[8 * t];
+            if (DELTA) {
+                const uint32_t *drow = reinterpret_cast<const uint32_t *>(D + (size_t)gi * N + (col0 & ~1));
+#pragma unroll
+                for (int t = 0; t < NT; ++t) rd[sl][t] = drow[8 * t];
+            }
+        };
+
+        auto step = [&](int kt, int sl) {
+            const int st = kt & 1;
+            store_a(st, ra[sl]);
+            CodeOpsI8 b[NT];
+            float sv[NT], dv[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                b[t] = split_codes_i8(rw[sl][t]);
+                sv[t] = h2f((uint16_t)(rs[sl][t] >> sh));
+                dv[t] = DELTA ? h2f((uint16_t)(rd[sl][t] >> sh)) : 0.0f;
+                pin(b[t].op[0]);
+                pin(b[t].op[1]);
+                pin(sv[t]);
+                if (DELTA) pin(dv[t]);
+            }
+            load(kt + P, sl);
+            __syncthreads();
+            int4v alo[MT], ahi[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int row = 16 * mt + c;
+                alo[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 0, kq)]);
+                ahi[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 1, kq)]);
+            }
+            // G1 (one k-tile per group): each tile's group sum starts from a zero
+            // MFMA operand, so nothing is reset and nothing stays live across tiles
+            const int4v zero4 = {0, 0, 0, 0};
+            if (DELTA) {
+                // sum over k of A[row, k] * 1: every column of the product holds
+                // the row's sum, so each lane gets its own rows' sums
+                const int4v ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    if (DEBUG) {
-                        const int4v qv = acci[mt][t] >> 4;   // exact: terms are multiples of 16
-                        accf[mt][t] += sv[t] * __builtin_convertvector(qv, float4v);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int row = m0 + 16 * mt + 4 * kq + r;
-                            if (row < r1)
-                                acc_debug[((size_t)row * G + gi) * N + col0 + 16 * t] = qv[r];
-                        }
-                    } else {
-                        accf[mt][t] += sv16 * __builtin_convertvector(acci[mt][t], float4v);
-                    }
-                    // the delta term: |qsum| <= 127 g < 2^24, exact in fp32
-                    if (DELTA) accf[mt][t] += dv[t] * __builtin_convertvector(qsum[mt], float4v);
-                    if (!G1) acci[mt][t] = int4v{0, 0, 0, 0};
+                    qsum[mt] = mfma_i8(alo[mt], ones, G1 ? zero4 : qsum[mt]);
+                    qsum[mt] = mfma_i8(ahi[mt], ones, qsum[mt]);
                 }
             }
-            if (DELTA && !G1)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) qsum[mt] = int4v{0, 0, 0, 0};
-        }
-    };
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    acci[mt][t] = mfma_i8(alo[mt], b[t].op[0], G1 ? zero4 : acci[mt][t]);
+                    acci[mt][t] = mfma_i8(ahi[mt], b[t].op[1], acci[mt][t]);
+                }
+            if (G1 || ((kt + 1) * KTILE) % g == 0) {   // end of a weight group
+                const int gi = (kt * KTILE) / g;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    // acci is exactly 16x the group's integer product; for groups of
+                    // up to 1024 k, |acci| <= 16 * 127 * 8 * g < 2^24 and its fp32
+                    // conversion is exact, so scaling it by s/16 (exact) gives the
+                    // same fma result as scaling acci >> 4 by s (longer groups, e.g.
+                    // one per column, round that conversion once: 2^-24 relative)
+                    const float sv16 = sv[t] * 0.0625f;
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        if (DEBUG) {
+                            const int4v qv = acci[mt][t] >> 4;   // exact: terms are multiples of 16
+                            accf[mt][t] += sv[t] * __builtin_convertvector(qv, float4v);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int row = m0 + 16 * mt + 4 * kq + r;
+                                if (row < r1)
+                                    acc_debug[((size_t)row * G + gi) * N + col0 + 16 * t] = qv[r];
+                            }
+                        } else {
+                            accf[mt][t] += sv16 * __builtin_convertvector(acci[mt][t], float4v);
+                        }
+                        // the delta term: |qsum| <= 127 g < 2^24, exact in fp32
+                        if (DELTA) accf[mt][t] += dv[t] * __builtin_convertvector(qsum[mt], float4v);
+                        if (!G1) acci[mt][t] = int4v{0, 0, 0, 0};
+                    }
+                }
+                if (DELTA && !G1)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) qsum[mt] = int4v{0, 0, 0, 0};
+            }
+        };
 
 #pragma unroll
-    for (int i = 0; i < P; ++i) load(i, i);
-    int kt = 0;
-    for (; kt + P <= KT; kt += P) {
+        for (int i = 0; i < P; ++i) load(i, i);
+        int kt = 0;
+        for (; kt + P <= KT; kt += P) {
 #pragma unroll
-        for (int i = 0; i < P; ++i) {
-            step(kt + i, i);
-            // keep each refill ahead of the loop's back edge and the next
-            // slot's work out of this step (the compiler would otherwise fold
-            // the last slot's loads into the top of the loop)
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < P; ++i) {
+                step(kt + i, i);
+                // keep each refill ahead of the loop's back edge and the next
+                // slot's work out of this step (the compiler would otherwise fold
+                // the last slot's loads into the top of the loop)
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
+#pragma unroll
+        for (int i = 0; i < P - 1; ++i)
+            if (kt + i < KT) step(kt + i, i);
+
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + 16 * mt + 4 * kq + r;
+                if (row >= r1) continue;
+                const float as = a_scale[row];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) C[(size_t)row * N + col0 + 16 * t] = f2h(as * accf[mt][t][r]);
+            }
+        // the next row block restarts the LDS buffers at stage 0: every wave must
+        // be done reading this block's last stage first
+        __syncthreads();
     }
-#pragma unroll
-    for (int i = 0; i < P - 1; ++i)
-        if (kt + i < KT) step(kt + i, i);
-
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = m0 + 16 * mt + 4 * kq + r;
-            if (row >= r1) continue;
-            const float as = a_scale[row];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) C[(size_t)row * N + col0 + 16 * t] = f2h(as * accf[mt][t][r]);
-        }
 }
 
 template <int NT, int P, bool DEBUG, bool G1, bool DELTA>
@@ -273,7 +283,11 @@ static hipError_t run_w4a8_d(const int8_t *Aq, const float *a_scale, const uint3
 //      to [Kp, Np] (pack_int4_weights); A_q is copied with zero columns up to
 //      Kp into the workspace, the kernel runs on the padded shape into a
 //      padded product there, which is cropped to C.  Workspace:
-//      [A_q padded, 256-aligned][C padded]. ----
+//      [counter region, untouched][A_q padded, 256-aligned][C padded].  The
+//      leading region is the W4A16 split-K counters' place in every
+//      workspace: W4A8 never writes it, so one workspace can serve W4A16 and
+//      W4A8 calls in turn on one stream without a W4A8 call leaving nonzero
+//      counters behind for the next split-K W4A16 call. ----
 __global__ __launch_bounds__(256) void pad_cols_i8_kernel(const int8_t *__restrict__ A,
                                                           int8_t *__restrict__ Ap, int M, int K,
                                                           int Kp)
@@ -289,7 +303,8 @@ size_t w4a8_tail_workspace_bytes(int M_total, int N, int K, int g)
 {
     int Kp, Np, gp;
     padded_shape(K, N, g, &Kp, &Np, &gp);
-    return ((size_t)M_total * Kp + 255) / 256 * 256 + (size_t)M_total * Np * sizeof(uint16_t);
+    return W4A16_WS_COUNTER_BYTES + ((size_t)M_total * Kp + 255) / 256 * 256 +
+           (size_t)M_total * Np * sizeof(uint16_t);
 }
 
 hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
@@ -317,9 +332,9 @@ hipError_t launch_w4a8_tail(const int8_t *Aq, const float *a_scale, const uint32
     if (!ws) return hipErrorInvalidValue;
     int Kp, Np, gp;
     padded_shape(K, N, g, &Kp, &Np, &gp);
-    int8_t *Ap = static_cast<int8_t *>(ws);
-    uint16_t *Cp = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) +
-                                                ((size_t)M_total * Kp + 255) / 256 * 256);
+    char *base = static_cast<char *>(ws) + W4A16_WS_COUNTER_BYTES;   // past the counters
+    int8_t *Ap = reinterpret_cast<int8_t *>(base);
+    uint16_t *Cp = reinterpret_cast<uint16_t *>(base + ((size_t)M_total * Kp + 255) / 256 * 256);
     const size_t n = (size_t)M_total * Kp;
     hipLaunchKernelGGL(pad_cols_i8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, Aq,
                        Ap, M_total, K, Kp);

@@ -55,7 +55,11 @@ class W4A16Case:
 
 
 def w4a16_case(M, K, N, g, asym=True, signed_scales=False, stream=0, case_id=0,
-               name="") -> W4A16Case:
+               name="", zero_points="noise") -> W4A16Case:
+    """zero_points (asymmetric cases): "noise", z = fp16(-8 s + N(0, 1e-3)),
+    the configs' recipe (delta = z + 8 s is tiny); or "awq", an integer
+    zero-point per group and column, z = fp16(-zp * s) with zp ~ U{0..15}
+    drawn in place of the noise (delta as large as 8 |s|)."""
     if g == -1:
         g = K
     G = -(-K // g)            # groups of g consecutive k; the last may be partial
@@ -68,7 +72,11 @@ def w4a16_case(M, K, N, g, asym=True, signed_scales=False, stream=0, case_id=0,
         neg = r.random((G, N)) < 0.5
         s = np.where(neg, -s, s).astype(np.float16)
     z = None
-    if asym:
+    if asym and zero_points == "awq":
+        zp = r.integers(0, 16, size=(G, N))
+        z = (-zp * s.astype(np.float64)).astype(np.float16)
+    elif asym:
+        assert zero_points == "noise", zero_points
         noise = r.standard_normal((G, N)) * 1e-3
         z = (-8.0 * s.astype(np.float64) + noise).astype(np.float16)
     return W4A16Case(A=A, q=q, s=s, z=z, g=g, name=name)

@@ -182,7 +182,8 @@ def test_workspace_bytes():
     with pytest.raises(qg.QGemmError):
         qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1000, 100)     # 100 neither divides K nor is a multiple of 128
     al = lambda n: (n + 255) // 256 * 256
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 16, 1000, 1000, 128, 2) == al(16 * 1024) + 16 * 1024 * 2
+    # the counter region first (never written by W4A8), then A_q and C padded
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 16, 1000, 1000, 128, 2) == CTR + al(16 * 1024) + 16 * 1024 * 2
     with pytest.raises(qg.QGemmError):
         qg.qg_workspace_bytes(99, 16, 1024, 1024, 128)
 

@@ -210,24 +210,40 @@ def test_w4a16_midbatch(name):
     _check_w4a16(c, flags=qg.QG_CORR_SEPARATE)
 
 
-def test_w4a16_prefill_sampled():
+def test_w4a16_prefill_every_tile():
     """Full prefill shape (M=4096, K=5120, N=17408, random-sign scales, fold on)
-    in the benchmark's launch shape; the oracle evaluates sampled cells
-    one by one (every row and column band is hit)."""
+    in the benchmark's launch shape: 128x256 tiles over rows 0..3839 and a
+    second launch of 64x128 tiles over the last 256 rows.  Against the oracle:
+    (a) one row of every 16-row m-tile crossed with one column of every
+    16-column n-tile (row 16i + i%16, column 16j + j%16), 256 x 1088 cells:
+    128 in every 128x256 output tile, at least one in every 16x16 MFMA tile of
+    every wave, at varying positions inside it; (b) the first and the last
+    128 rows densely over all N (every n-tile of both launches, the full
+    40 k-tiles)."""
     c = synth.workload("w4a16-prefill-M4096-K5120-N17408-g128-sym-signed")
     note(f"w4a16 prefill M={c.M} K={c.K} N={c.N}")
     got, _ = run_w4a16(c)
-    r = np.random.default_rng(5)
-    rows = np.concatenate([r.integers(0, c.M, 3000), [0, c.M - 1, 0, c.M - 1]])
-    cols = np.concatenate([r.integers(0, c.N, 3000), [0, 0, c.N - 1, c.N - 1]])
-    ref = oracle.w4a16_cells(c.A, c.q, c.s, None, c.g, rows, cols, fold=True)
-    g = got[rows, cols]
+    assert np.all(np.isfinite(got))
+    i = np.arange(c.M // 16)
+    j = np.arange(c.N // 16)
+    rows = 16 * i + i % 16
+    cols = 16 * j + j % 16
+    ref = oracle.w4a16(c.A[rows], c.q[:, cols], c.s[:, cols],
+                       None, c.g, fold=True)
+    g = got[np.ix_(rows, cols)]
     assert rel_fro(g, ref) <= W4A16_TOL
     assert elementwise_guard(g, ref) <= 0
-    assert np.all(np.isfinite(got))
+    for band in (np.arange(0, 128), np.arange(c.M - 128, c.M)):
+        note(f"w4a16 prefill dense rows {band[0]}..{band[-1]}")
+        ref = oracle.w4a16(c.A[band], c.q, c.s, None, c.g, fold=True)
+        assert rel_fro(got[band], ref) <= W4A16_TOL
+        assert elementwise_guard(got[band], ref) <= 0
     # the fold matters at this distribution: the unfolded product is far off
-    ref_nofold = oracle.w4a16_cells(c.A, c.q, c.s, None, c.g, rows, cols, fold=False)
-    assert rel_fro(ref_nofold, ref) > 10 * W4A16_TOL
+    r = np.random.default_rng(5)
+    rr, cc = r.integers(0, c.M, 500), r.integers(0, c.N, 500)
+    ref_f = oracle.w4a16_cells(c.A, c.q, c.s, None, c.g, rr, cc, fold=True)
+    ref_nofold = oracle.w4a16_cells(c.A, c.q, c.s, None, c.g, rr, cc, fold=False)
+    assert rel_fro(ref_nofold, ref_f) > 10 * W4A16_TOL
 
 
 def test_w4a16_prefill_dense_slice():
@@ -453,3 +469,25 @@ def test_w4a8_large_ragged_experts(asym):
     c = synth.w4a8_case(2, 0, 1024, 512, 128, signed_scales=not asym, stream=85, case_id=6,
                         rows=[700, 300], asym=asym, name="w4a8-large")
     _check_w4a8(c)
+
+
+@pytest.mark.parametrize("max_rows", [1, 64, 300])
+def test_w4a8_understated_row_bound(max_rows):
+    """max_rows_per_expert below the true row count (700 and 300 rows): the
+    bound only sizes the launch, every row of every expert is still computed
+    (C starts as NaN so a row left unwritten fails)."""
+    c = synth.w4a8_case(2, 0, 1024, 512, 128, stream=85, case_id=7, rows=[700, 300],
+                        name="w4a8-understated")
+    note(f"w4a8 understated bound max_rows={max_rows} rows=[700, 300]")
+    W, S, _ = _pack_w4a8(c)
+    C = torch.full((c.M_total, c.N), float("nan"), dtype=torch.float16, device="cuda")
+    acc = torch.full((c.M_total, c.K // c.g, c.N), -7, dtype=torch.int32, device="cuda")
+    qg.w4a8(dev(c.Aq), dev(c.a_scale), W, S, dev(c.offsets), c.E, max_rows, c.N, c.g, C=C,
+            acc_debug=acc)
+    torch.cuda.synchronize()
+    ref, ref_acc = oracle.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, c.g)
+    got = host(C).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert np.array_equal(host(acc).astype(np.int64), ref_acc)
+    assert rel_fro(got, ref) <= W4A8_TOL
+    assert elementwise_guard(got, ref) <= 0

@@ -53,23 +53,18 @@ def test_tails_dense(M, K, N, g, asym, signed):
 
 
 @pytest.mark.parametrize("M", [1, 16])
-def test_vocab_head_sampled(M):
-    """K 5120 -> a 50257-token vocabulary (N = 50304 padded), asymmetric g128:
-    all rows at 1200 columns -- the first 64, the last 200 (the tail tile and
-    its neighbours) and 936 drawn at random."""
+def test_vocab_head_dense(M):
+    """K 5120 -> a 50257-token vocabulary (N = 50304 padded), asymmetric g128,
+    in the benchmark's launch shape, checked densely: every output, so every
+    column group of the decode kernel, both of its k-splits and the cropped
+    tail tile."""
     K, N = 5120, 50257
     c = synth.w4a16_case(M, K, N, 128, asym=True, stream=92, case_id=1000 + M)
     note(f"vocab head M={M} K={K} N={N}")
     _, got = _run(c, True)
-    rng = np.random.default_rng(M)
-    cols = np.unique(np.concatenate([np.arange(64), np.arange(N - 200, N),
-                                     rng.choice(N, 936, replace=False)]))
-    rows = np.repeat(np.arange(M), cols.size)
-    cc = np.tile(cols, M)
-    ref = oracle.w4a16_cells(c.A, c.q, c.s, c.z, 128, rows, cc, fold=True)
-    g = got[rows, cc]
-    assert rel_fro(g, ref) <= TOL
-    assert elementwise_guard(g, ref) <= 0
+    ref = oracle.w4a16(c.A, c.q, c.s, c.z, 128, fold=True)
+    assert rel_fro(got, ref) <= TOL
+    assert elementwise_guard(got, ref) <= 0
 
 
 @pytest.mark.parametrize("asym", [False, True])
@@ -92,3 +87,31 @@ def test_w4a8_tails(asym):
                          want_acc=False)
     assert rel_fro(got, ref) <= 1e-2
     assert elementwise_guard(got, ref) <= 0
+
+
+def test_w4a8_tail_then_split_k_decode_shared_workspace():
+    """A W4A8 call on a tail shape and a split-K W4A16 decode call share the
+    binding's cached workspace on one stream: the W4A8 call must leave the
+    split-K counters (the workspace's first QG_W4A16_WS_COUNTER_BYTES) at
+    zero, or the decode call's partial sums never meet and C is not written."""
+    c8 = synth.w4a8_case(3, 0, 1000, 300, 128, stream=92, case_id=2001, rows=[40, 0, 75])
+    packs = [qg.pack(dev(c8.q[e]), dev(c8.s[e]), None, c8.g, fold=True) for e in range(c8.E)]
+    W = torch.stack([p.w for p in packs]).contiguous()
+    S = torch.stack([p.scale for p in packs]).contiguous()
+    c16 = synth.workload("w4a16-decode-M16-K5120-N17408-g128-asym")
+    pw = qg.pack(dev(c16.q), dev(c16.s), dev(c16.z), c16.g, fold=True)
+    A16 = dev(c16.A)
+    ref16 = oracle.w4a16(c16.A, c16.q, c16.s, c16.z, c16.g)
+    ref8, _ = oracle.w4a8(c8.Aq, c8.a_scale, c8.q, c8.s, c8.offsets, c8.g, want_acc=False)
+    for rep in range(2):
+        note(f"shared workspace: w4a8 tail then split-K decode, rep {rep}")
+        C8 = qg.w4a8(dev(c8.Aq), dev(c8.a_scale), W, S, dev(c8.offsets), c8.E, 75, c8.N, c8.g)
+        C16 = torch.full((c16.M, c16.N), float("nan"), dtype=torch.float16, device="cuda")
+        qg.w4a16(A16, pw, C=C16)
+        torch.cuda.synchronize()
+        got8 = host(C8).astype(np.float64)
+        got16 = host(C16).astype(np.float64)
+        assert rel_fro(got8, ref8) <= 1e-2
+        assert np.all(np.isfinite(got16))
+        assert rel_fro(got16, ref16) <= TOL
+        assert elementwise_guard(got16, ref16) <= 0
