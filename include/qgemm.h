@@ -170,6 +170,27 @@ int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *sca
                 int group_size, unsigned flags, void *workspace,
                 size_t workspace_bytes, void *stream);
 
+/* ---- W4A16 GEMM without a workspace argument, for callers that cannot
+ *      allocate device memory (code under HIP graph capture, tight serving
+ *      loops, harnesses that forbid allocation) ----
+ * Same arguments, checks, kernels and results as qgemm_w4a16 minus the
+ * workspace: the scratch a call needs (split-K partial sums and counters,
+ * the separate correction's group sums, a tail shape's padded A and C) is a
+ * static device array of QG_NOALLOC_SCRATCH_BYTES bytes inside the library,
+ * one per GPU, held until the process ends.  No device memory is allocated
+ * or freed by the call.  A call whose scratch need
+ * (qg_workspace_bytes(QG_OP_W4A16, ...)) exceeds QG_NOALLOC_SCRATCH_BYTES
+ * returns QG_ERR_WORKSPACE before anything is launched.  The first call on a
+ * device clears the scratch's counter region with a small kernel on
+ * `stream`; every call leaves it at zero again.  Every call on a GPU uses
+ * that GPU's one array, which keeps the last call's contents: calls that may
+ * overlap in time on one GPU (different streams, threads or graphs) race and
+ * must be ordered by the caller.                                            */
+#define QG_NOALLOC_SCRATCH_BYTES 8388608u
+int qgemm_w4a16_noalloc(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,
+                        const uint16_t *delta, uint16_t *C, int M, int N, int K,
+                        int group_size, unsigned flags, void *stream);
+
 /* ---- SwiGLU of an MLP's gate and up projections in one call ([Marlin-Ada]
  *      "Gaps and follow-ups": the fused mlp_gate + mlp_up dispatch) ----
  * The pair is ONE packed weight of shape [K, 2N]: pack_int4_weights on the

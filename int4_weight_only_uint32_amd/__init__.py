@@ -7,10 +7,11 @@ include/qgemm.h, and raises QGemmError on a non-zero status.  Every step of the
 computation runs in the library's HIP kernels; there is no fallback of any
 kind -- if libqgemm.so is missing, importing works but every call raises.
 
-Names follow the C ABI: pack_int4_weights, qgemm_w4a16, qgemm_w4a16_swiglu,
-group_sum_correction, quantize_rows_int8, qgemm_w4a8 (plus qg_device_supported,
-qg_workspace_bytes, qg_padded_shape); pack, w4a16, w4a16_swiglu, correct,
-quantize_rows and w4a8 are the same calls with torch-allocated outputs.
+Names follow the C ABI: pack_int4_weights, qgemm_w4a16, qgemm_w4a16_noalloc,
+qgemm_w4a16_swiglu, group_sum_correction, quantize_rows_int8, qgemm_w4a8 (plus
+qg_device_supported, qg_workspace_bytes, qg_padded_shape); pack, w4a16,
+w4a16_swiglu, correct, quantize_rows and w4a8 are the same calls with
+torch-allocated outputs.
 """
 import ctypes
 import os
@@ -33,6 +34,7 @@ QG_PACK_FOLD_NEG_SCALES = 0x1
 QG_CORR_SEPARATE = 0x1
 
 QG_W4A16_WS_COUNTER_BYTES = 65536
+QG_NOALLOC_SCRATCH_BYTES = 8388608
 
 QG_OP_W4A16 = 1
 QG_OP_W4A8 = 2
@@ -42,7 +44,8 @@ QG_OP_W4A16_SWIGLU = 5
 
 EXPORTED = ("qg_device_supported", "qg_status_string", "qg_last_error", "qg_workspace_bytes",
             "pack_int4_weights", "qgemm_w4a16", "group_sum_correction", "qgemm_w4a8",
-            "quantize_rows_int8", "qgemm_w4a16_swiglu", "qg_padded_shape")
+            "quantize_rows_int8", "qgemm_w4a16_swiglu", "qg_padded_shape",
+            "qgemm_w4a16_noalloc")
 
 
 class QGemmError(RuntimeError):
@@ -75,6 +78,8 @@ def lib():
         L.pack_int4_weights.argtypes = [P, P, P, I, I, I, U, P, P, P, P]
         L.qgemm_w4a16.restype = I
         L.qgemm_w4a16.argtypes = [P, P, P, P, P, I, I, I, I, U, P, Z, P]
+        L.qgemm_w4a16_noalloc.restype = I
+        L.qgemm_w4a16_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, U, P]
         L.group_sum_correction.restype = I
         L.group_sum_correction.argtypes = [P, P, P, I, I, I, I, P, Z, P]
         L.qgemm_w4a8.restype = I
@@ -197,6 +202,23 @@ def qgemm_w4a16(A, w_packed, scale, delta, C, M, N, K, group_size, flags=0, work
                              _ptr(delta, torch.float16, "delta"), _ptr(C, torch.float16, "C"),
                              M, N, K, group_size, flags, _ptr(workspace, None, "workspace"),
                              ws_bytes, _stream(A)))
+
+
+def qgemm_w4a16_noalloc(A, w_packed, scale, delta, C, M, N, K, group_size, flags=0):
+    """qgemm_w4a16 with the library's static scratch instead of a workspace
+    (no device allocation; calls that overlap on one GPU race)."""
+    Kp, Np, G = padded_shape(K, N, group_size)
+    _need(A, M * K, "A")
+    _need(C, M * N, "C")
+    _need(w_packed, Kp * Np // 8, "w_packed")
+    _need(scale, G * Np, "scale")
+    _need(delta, G * Np, "delta")
+    _check(lib().qgemm_w4a16_noalloc(_ptr(A, torch.float16, "A"),
+                                     _ptr(w_packed, torch.int32, "w_packed"),
+                                     _ptr(scale, torch.float16, "scale"),
+                                     _ptr(delta, torch.float16, "delta"),
+                                     _ptr(C, torch.float16, "C"), M, N, K, group_size, flags,
+                                     _stream(A)))
 
 
 _workspaces = {}

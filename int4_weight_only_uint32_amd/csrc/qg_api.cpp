@@ -125,6 +125,58 @@ size_t w4a16_ws_bytes(int M, int N, int K, int g, bool separate)
     return align256(gemm) + corr_ws_bytes(M, K, g);
 }
 
+// Host checks of a W4A16 call shared by qgemm_w4a16 and qgemm_w4a16_noalloc:
+// shape, pointers, alignment and flags; fills the group size, the path and
+// the scratch bytes the call needs.
+struct W4A16Call {
+    int g;
+    bool separate, tail;
+    size_t need;
+};
+
+int w4a16_check(const char *what, const uint16_t *A, const uint32_t *w_packed,
+                const uint16_t *scale, const uint16_t *delta, const uint16_t *C, int M, int N,
+                int K, int group_size, unsigned flags, W4A16Call *call)
+{
+    int g = group_size;
+    int rc = check_shape_tail(what, M, N, K, &g);
+    if (rc) return rc;
+    if (!A || !w_packed || !scale || !C)
+        return fail(QG_ERR_INVALID_ARG, "%s: NULL A/w_packed/scale/C", what);
+    if (!aligned(A, 16) || !aligned(w_packed, 16) || !aligned(scale, 2) || !aligned(C, 2) ||
+        (delta && !aligned(delta, 2)))
+        return fail(QG_ERR_INVALID_ARG, "%s: misaligned pointer", what);
+    if (flags & ~QG_CORR_SEPARATE)
+        return fail(QG_ERR_INVALID_ARG, "%s: unknown flags 0x%x", what, flags);
+    call->g = g;
+    call->separate = (flags & QG_CORR_SEPARATE) && delta;
+    call->tail = qg::is_tail_shape(N, K, g);
+    if (call->tail && call->separate)
+        return fail(QG_ERR_UNSUPPORTED, "%s: QG_CORR_SEPARATE needs K, N multiples of 128", what);
+    call->need = call->tail ? qg::tail_workspace_bytes(M, N, K, g)
+                            : w4a16_ws_bytes(M, N, K, g, call->separate);
+    return QG_OK;
+}
+
+// The launches of a checked W4A16 call; `workspace` holds call.need bytes.
+int w4a16_launch(const char *what, const W4A16Call &call, const uint16_t *A,
+                 const uint32_t *w_packed, const uint16_t *scale, const uint16_t *delta,
+                 uint16_t *C, int M, int N, int K, void *workspace, hipStream_t st)
+{
+    const int g = call.g;
+    if (call.tail)
+        return launch_status(qg::launch_w4a16_tail(A, w_packed, scale, delta, C, M, N, K, g, true,
+                                                   workspace, st),
+                             what);
+    const size_t gemm_ws = w4a16_gemm_ws_bytes(M, N, K, call.separate);
+    hipError_t e = qg::launch_w4a16(A, w_packed, scale, delta, C, M, N, K, g, !call.separate,
+                                    qg::w4a16_workspace_bytes(M, N, K) ? workspace : nullptr, st);
+    if (e == hipSuccess && call.separate)
+        e = qg::launch_group_sum_correction(A, delta, C, M, N, K, g,
+                                            (float *)((char *)workspace + align256(gemm_ws)), st);
+    return launch_status(e, what);
+}
+
 } // namespace
 
 extern "C" {
@@ -244,41 +296,45 @@ int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *sca
                 const uint16_t *delta, uint16_t *C, int M, int N, int K, int group_size,
                 unsigned flags, void *workspace, size_t workspace_bytes, void *stream)
 {
-    int g = group_size;
-    int rc = check_shape_tail("qgemm_w4a16", M, N, K, &g);
+    W4A16Call call;
+    int rc = w4a16_check("qgemm_w4a16", A, w_packed, scale, delta, C, M, N, K, group_size, flags,
+                         &call);
     if (rc) return rc;
-    if (!A || !w_packed || !scale || !C)
-        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16: NULL A/w_packed/scale/C");
-    if (!aligned(A, 16) || !aligned(w_packed, 16) || !aligned(scale, 2) || !aligned(C, 2) ||
-        (delta && !aligned(delta, 2)))
-        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16: misaligned pointer");
-    if (flags & ~QG_CORR_SEPARATE)
-        return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16: unknown flags 0x%x", flags);
-    const bool separate = (flags & QG_CORR_SEPARATE) && delta;
-    const bool tail = qg::is_tail_shape(N, K, g);
-    if (tail && separate)
-        return fail(QG_ERR_UNSUPPORTED, "qgemm_w4a16: QG_CORR_SEPARATE needs K, N multiples of 128");
-    const size_t need = tail ? qg::tail_workspace_bytes(M, N, K, g) : w4a16_ws_bytes(M, N, K, g, separate);
-    if (need > 0) {
-        if (!workspace || workspace_bytes < need)
+    if (call.need > 0) {
+        if (!workspace || workspace_bytes < call.need)
             return fail(QG_ERR_WORKSPACE, "qgemm_w4a16: workspace of %zu bytes needed, got %zu",
-                        need, workspace ? workspace_bytes : (size_t)0);
+                        call.need, workspace ? workspace_bytes : (size_t)0);
         if (!aligned(workspace, 256))
             return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16: workspace must be 256-byte aligned");
     }
     if ((rc = check_device())) return rc;
-    hipStream_t st = (hipStream_t)stream;
-    if (tail)
-        return launch_status(qg::launch_w4a16_tail(A, w_packed, scale, delta, C, M, N, K, g, true,
-                                                   workspace, st),
-                             "qgemm_w4a16");
-    const size_t gemm_ws = w4a16_gemm_ws_bytes(M, N, K, separate);
-    hipError_t e = qg::launch_w4a16(A, w_packed, scale, delta, C, M, N, K, g, !separate,
-                                    qg::w4a16_workspace_bytes(M, N, K) ? workspace : nullptr, st);
-    if (e == hipSuccess && separate)
-        e = qg::launch_group_sum_correction(A, delta, C, M, N, K, g,
-                                            (float *)((char *)workspace + align256(gemm_ws)), st);
-    return launch_status(e, "qgemm_w4a16");
+    return w4a16_launch("qgemm_w4a16", call, A, w_packed, scale, delta, C, M, N, K, workspace,
+                        (hipStream_t)stream);
+}
+
+int qgemm_w4a16_noalloc(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,
+                        const uint16_t *delta, uint16_t *C, int M, int N, int K, int group_size,
+                        unsigned flags, void *stream)
+{
+    W4A16Call call;
+    int rc = w4a16_check("qgemm_w4a16_noalloc", A, w_packed, scale, delta, C, M, N, K, group_size,
+                         flags, &call);
+    if (rc) return rc;
+    if (call.need > QG_NOALLOC_SCRATCH_BYTES)
+        return fail(QG_ERR_WORKSPACE,
+                    "qgemm_w4a16_noalloc: this call needs %zu bytes of scratch, more than the "
+                    "library's static scratch of %zu bytes (use qgemm_w4a16 with a workspace)",
+                    call.need, (size_t)QG_NOALLOC_SCRATCH_BYTES);
+    if ((rc = check_device())) return rc;
+    void *ws = nullptr;
+    if (call.need > 0) {
+        hipError_t e = qg::noalloc_scratch((hipStream_t)stream, &ws);
+        if (e != hipSuccess)
+            return fail(QG_ERR_LAUNCH, "qgemm_w4a16_noalloc: static scratch unavailable: %s",
+                        hipGetErrorString(e));
+    }
+    return w4a16_launch("qgemm_w4a16_noalloc", call, A, w_packed, scale, delta, C, M, N, K, ws,
+                        (hipStream_t)stream);
 }
 
 int qgemm_w4a16_swiglu(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,

@@ -105,6 +105,11 @@ hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W
                        int M_total, int max_rows, int N, int K, int g, uint16_t *C,
                        int32_t *acc_debug, hipStream_t st);
 
+// Device address of the static scratch of qgemm_w4a16_noalloc on the current
+// device (looked up once per device; the first call also clears its counter
+// region on `st`).
+hipError_t noalloc_scratch(hipStream_t st, void **out);
+
 // Per-row int8 codes and fp32 scales of fp16 activations (K % 8 == 0, A
 // 16-byte and Aq 8-byte aligned).
 hipError_t launch_quantize_rows_int8(const uint16_t *A, int M, int K, int8_t *Aq,

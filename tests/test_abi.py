@@ -284,3 +284,23 @@ def test_offset_limits_refused():
     with pytest.raises(qg.QGemmError):
         qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1 << 20, 1 << 18, 128)   # 2048 groups x 2^20 columns
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 262144, 65536, 128) >= 0
+
+
+def test_noalloc_refuses_shapes_beyond_the_scratch():
+    """qgemm_w4a16_noalloc refuses a call needing more scratch than the
+    library's static array holds, on the host, before any device call (the
+    pointers are never dereferenced), naming the sizes."""
+    L = qg.lib()
+    M, K, N = 4096, 1000, 1000        # a tail shape: padded A and C need ~16 MB
+    need = qg.qg_workspace_bytes(qg.QG_OP_W4A16, M, N, K, 128)
+    assert need > qg.QG_NOALLOC_SCRATCH_BYTES
+    assert L.qgemm_w4a16_noalloc(FAKE, FAKE, FAKE, None, FAKE, M, N, K, 128, 0, None) == \
+        qg.QG_ERR_WORKSPACE
+    assert b"static scratch" in L.qg_last_error()
+    # the other host checks come first, as for qgemm_w4a16
+    assert L.qgemm_w4a16_noalloc(None, FAKE, FAKE, None, FAKE, 16, 1024, 1024, 128, 0, None) == \
+        qg.QG_ERR_INVALID_ARG
+    assert L.qgemm_w4a16_noalloc(FAKE, FAKE, FAKE, None, FAKE, 16, 1024, 1024, 64, 0, None) == \
+        qg.QG_ERR_UNSUPPORTED
+    assert L.qgemm_w4a16_noalloc(FAKE, FAKE, FAKE, None, FAKE, 16, 1024, 1024, 128, 4, None) == \
+        qg.QG_ERR_INVALID_ARG
