@@ -326,7 +326,7 @@ def cpu_baseline(case):
                        f"naive m-k-n loop)")
 
 
-def bench_swiglu(name, steps, warmup, M, K, N, g):
+def bench_swiglu(name, steps, warmup, M, K, N, g, asym=True):
     """SwiGLU of a gate/up pair (one packed [K, 2N] weight) against the plain
     GEMM of the same pair (its [M, 2N] product, no activation)."""
     import numpy as np
@@ -335,13 +335,14 @@ def bench_swiglu(name, steps, warmup, M, K, N, g):
     import int4_weight_only_uint32_amd as qg
     import synth
 
-    c = synth.w4a16_case(M, K, 2 * N, g, asym=True, stream=91, case_id=99)
+    c = synth.w4a16_case(M, K, 2 * N, g, asym=asym, signed_scales=not asym, stream=91, case_id=99)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    pair = qg.pack(dev(c.q), dev(c.s), dev(c.z), g)
-    wb = weight_bytes(K, 2 * N, g, True)
+    pair = qg.pack(dev(c.q), dev(c.s), dev(c.z) if asym else None, g)
+    wb = weight_bytes(K, 2 * N, g, asym)
     R = max(1, math.ceil(ROTATE_BYTES / wb))
     copies = [pair] + [qg.PackedWeight(w=pair.w.clone(), scale=pair.scale.clone(),
-                                       delta=pair.delta.clone(), K=K, N=2 * N, group_size=g)
+                                       delta=None if pair.delta is None else pair.delta.clone(),
+                                       K=K, N=2 * N, group_size=g)
                        for _ in range(R - 1)]
     A = dev(c.A)
     H = torch.empty((M, N), dtype=torch.float16, device="cuda")
@@ -360,13 +361,15 @@ def bench_swiglu(name, steps, warmup, M, K, N, g):
 
     ms, ms_graph, ms_eager = time_best(fused, R, steps, warmup)
     ms_gemm, _, _ = time_best(gemm, R, steps, warmup)
-    res = dict(name=name, M=M, K=K, N=N, group=g, mode="asym", us_per_call=ms * 1e3,
+    res = dict(name=name, M=M, K=K, N=N, group=g, mode="asym" if asym else "sym-fold",
+               us_per_call=ms * 1e3,
                weight_bytes=wb, weight_gbps=wb / (ms * 1e-3) / 1e9,
                tflops=4.0 * M * N * K / (ms * 1e-3) / 1e12, rotated_copies=R,
                us_pair_gemm_only=ms_gemm * 1e3,
                us_per_call_graph=ms_graph * 1e3 if ms_graph else None,
                us_per_call_eager=ms_eager * 1e3)
     res["pct_hbm_weight"] = 100.0 * res["weight_gbps"] / HBM_PEAK_GBPS
+    res["pct_fp16_mfma"] = 100.0 * res["tflops"] / FP16_PEAK_TFLOPS
     del copies, A, H, Y, ws
     torch.cuda.empty_cache()
     return res
@@ -491,6 +494,12 @@ def main():
         sn = "w4a16-swiglu-decode-M16-K5120-N17408x2-g128-asym"
         if not want or sn in want:
             r = bench_swiglu(sn, steps, warmup, 16, 5120, 17408, 128)
+            log(json.dumps(r))
+            cases.append(r)
+        sn = "w4a16-swiglu-prefill-M4096-K5120-N17408x2-g128-sym-signed"
+        if not want or sn in want:
+            st = max(5, steps // 20)
+            r = bench_swiglu(sn, st, min(warmup, st), 4096, 5120, 17408, 128, asym=False)
             log(json.dumps(r))
             cases.append(r)
         qn = "quantize-rows-int8-E8x64-K2048+w4a8"

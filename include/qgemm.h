@@ -201,16 +201,16 @@ int qgemm_w4a16_noalloc(const uint16_t *A, const uint32_t *w_packed, const uint1
  * H        [M,N] fp16 out, 16-byte aligned, OVERWRITTEN with
  *            H[m,n] = silu(G[m,n]) * U[m,n],  silu(x) = x / (1 + exp(-x)),
  *          G = A . W_gate and U = A . W_up with their delta terms fused.
- *          M <= 16 (when the decode kernel takes the pair): one launch, G and
- *          U in fp32 and H rounded once; otherwise G and U are stored as fp16
- *          in the workspace and a second kernel forms H (two roundings).
+ *          One launch for every M: the kernel holds G and U of the same
+ *          output columns in fp32 and rounds H once.
  * N % 128 == 0 (the output width), K and group_size as for qgemm_w4a16.
  * flags    must be 0.
  * workspace/workspace_bytes: qg_workspace_bytes(QG_OP_W4A16_SWIGLU, M, N, K,
- *          group_size, 1, 0) bytes, 256-byte aligned (NULL when 0); it starts
- *          with the same counter region as a W4A16 workspace (zero-filled
- *          once, left at zero by every call), so one workspace of the larger
- *          size serves both kinds of call on one stream.                    */
+ *          group_size, 1, 0) bytes, 256-byte aligned (NULL when 0: every
+ *          shape but the split-K decode batches); it starts with the same
+ *          counter region as a W4A16 workspace (zero-filled once, left at
+ *          zero by every call), so one workspace of the larger size serves
+ *          both kinds of call on one stream.                                */
 int qgemm_w4a16_swiglu(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,
                        const uint16_t *delta, uint16_t *H, int M, int N, int K, int group_size,
                        unsigned flags, void *workspace, size_t workspace_bytes, void *stream);

@@ -104,6 +104,23 @@ __device__ inline unsigned swap_mid_bytes(unsigned x)
     return (x & 0xFF0000FFu) | ((x >> 8) & 0x0000FF00u) | ((x << 8) & 0x00FF0000u);
 }
 
+// The gated activation of a gate/up pair, silu(g) * u with silu(x) = x / (1 +
+// e^-x), in fp32 (the device library's expf).
+__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __builtin_expf(-g)) * u; }
+
+// Gate/up pairs in the GEMM kernels (GATED): the pair is one packed [K, 2Nh]
+// weight, gate columns first.  A kernel runs over the pair's 2Nh columns in a
+// virtual order that interleaves the two halves by 16-column tile -- virtual
+// tile 2j is gate tile j, 2j + 1 is up tile j (physical tile Nh/16 + j) -- so
+// every wave that owns an even run of virtual tiles holds both products of
+// the same output columns, and its epilogue stores silu(gate) * up.  Given
+// the run's first virtual tile v0 (even), tile t of the run is physical tile
+// gated_tile(v0, t, Nh16) = v0 / 2 + t / 2 + (t odd ? Nh16 : 0).
+__host__ __device__ inline int gated_tile(int v0, int t, int Nh16)
+{
+    return v0 / 2 + (t >> 1) + ((t & 1) ? Nh16 : 0);
+}
+
 // Materialize a staged value here.  In a register ring the compiler may sink
 // pure arithmetic on a slot (code splitting, scale conversion) below the
 // refill load of that slot; the old registers then stay live across the
@@ -114,6 +131,21 @@ template <class T>
 __device__ inline void pin(T &x)
 {
     asm volatile("" : "+v"(x));
+}
+
+// Buffer resource over [p, p + bytes) for raw (unstructured) buffer loads:
+// base address, stride 0, range in bytes (clamped to 32 bits), and the fixed
+// third-word value of this GPU family for raw dword access.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, size_t bytes)
+{
+    const int range = bytes > 0xFFFFFFFFull ? (int)0xFFFFFFFF : (int)(unsigned)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, range, 0x00020000);
+}
+
+// s_waitcnt immediate: vmcnt n (6 bits, split), expcnt and lgkmcnt not waited
+constexpr unsigned waitcnt_vm(int n)
+{
+    return (unsigned)((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 __device__ inline float4v mfma_f16(half8 a, half8 b, float4v c)

@@ -44,21 +44,24 @@ struct SkinnyCfg {
     int MT, NT, P, nw, S;
 };
 SkinnyCfg skinny_config(int M, int N, int K);
+// gated: W is a gate/up pair [K, N] (gate columns first) and C the [M, N/2]
+// output silu(A W_gate) * (A W_up), both products kept in fp32 (N / 2 a
+// multiple of 128).
 hipError_t launch_w4a16_skinny_cfg(const SkinnyCfg &c, const uint16_t *A, const uint32_t *W,
                                    const uint16_t *S, const uint16_t *D, uint16_t *C, int M,
                                    int N, int K, int g, bool fuse_delta, void *ws,
-                                   hipStream_t st);
+                                   hipStream_t st, bool gated = false);
 hipError_t launch_w4a16_mid(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
-                            bool fuse_delta, hipStream_t st);
+                            bool fuse_delta, hipStream_t st, bool gated = false);
 int tiled_config(int M, int N);
 int tiled_row_split(int M, int N);
 hipError_t launch_w4a16_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W,
                                   const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
-                                  int K, int g, bool fuse_delta, hipStream_t st);
+                                  int K, int g, bool fuse_delta, hipStream_t st, bool gated = false);
 hipError_t launch_w4a16_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                               const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
-                              bool fuse_delta, hipStream_t st);
+                              bool fuse_delta, hipStream_t st, bool gated = false);
 
 // Every non-empty W4A16 workspace starts with this many bytes of split-K
 // counters.  Only the decode kernel writes them and it leaves them at zero, so

@@ -26,7 +26,7 @@
 
 namespace qg {
 
-template <int MT, int NT, int P, int NWMAX, bool DELTA>
+template <int MT, int NT, int P, int NWMAX, bool DELTA, bool GATED>
 __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g, int nw)
@@ -42,6 +42,12 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
     const int c = lane & 15, kq = lane >> 4;
     const int KT = K / KTILE;
     const int nt0 = blockIdx.x * NT;
+    // GATED: the NT (virtual) n-tiles are NT/2 gate/up pairs of the [K, N]
+    // pair weight, and C is the [M, N/2] output
+    const int Nh16 = N / (2 * NTILE);
+    const int pt0 = GATED ? gated_tile(nt0, 0, Nh16) : nt0;   // first physical tile
+    // physical tile of n-tile t, relative to pt0
+    auto trel = [&](int t) { return GATED ? gated_tile(nt0, t, Nh16) - pt0 : t; };
     const int m0 = blockIdx.y * 16 * MT;
     const int kt_beg = (wave * KT) / nw, kt_end = ((wave + 1) * KT) / nw;
     const int n = kt_end - kt_beg;
@@ -62,8 +68,8 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
         asrc[j] = reinterpret_cast<const uint4v *>(A + (size_t)row * K) + (lane & 15);
         adst[j] = r * KTILE + 8 * ((lane & 15) ^ (r & 15));
     }
-    const uint4v *wbase = W + (size_t)nt0 * KT * 64 + lane;
-    const int col0 = nt0 * NTILE + c;
+    const uint4v *wbase = W + (size_t)pt0 * KT * 64 + lane;
+    const int col0 = pt0 * NTILE + c;
 
     float4v acc[MT][NT];
 #pragma unroll
@@ -89,15 +95,15 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
 #pragma unroll
         for (int j = 0; j < MT * 4; ++j) a[j] = asrc[j][kt * (KTILE / 8)];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) w[t] = wbase[((size_t)t * KT + kt) * 64];
+        for (int t = 0; t < NT; ++t) w[t] = wbase[((size_t)trel(t) * KT + kt) * 64];
         const int gi = (kt * KTILE) / g;
         const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
 #pragma unroll
-        for (int t = 0; t < NT; ++t) sv[t] = srow[8 * t];
+        for (int t = 0; t < NT; ++t) sv[t] = srow[8 * trel(t)];
         if (DELTA) {
             const uint32_t *drow = reinterpret_cast<const uint32_t *>(D + (size_t)gi * N + (col0 & ~1));
 #pragma unroll
-            for (int t = 0; t < NT; ++t) dv[t] = drow[8 * t];
+            for (int t = 0; t < NT; ++t) dv[t] = drow[8 * trel(t)];
         }
     };
     // Consuming a slot happens in two halves: `stage` moves the slot's
@@ -206,13 +212,20 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
                 red[((size_t)wave * E4 + (mt * NT + t) * 4 + r) * 64 + lane] = acc[mt][t][r];
     __syncthreads();
     for (int idx = threadIdx.x; idx < E4 * 64; idx += blockDim.x) {
-        float v = 0.f;
-        for (int w = 0; w < nw; ++w) v += red[(size_t)w * E4 * 64 + idx];
         const int e = idx >> 6, l = idx & 63;
         const int r = e & 3, t = (e >> 2) % NT, mt = (e >> 2) / NT;
+        if (GATED && (t & 1)) continue;                   // an up tile: read with its gate
+        float v = 0.f;
+        for (int w = 0; w < nw; ++w) v += red[(size_t)w * E4 * 64 + idx];
         const int row = m0 + 16 * mt + 4 * (l >> 4) + r;
-        const int cc = (nt0 + t) * NTILE + (l & 15);
-        if (row < M) C[(size_t)row * N + cc] = f2h(v);
+        if (row >= M) continue;
+        if (GATED) {
+            float u = 0.f;   // the up element of the same output: tile t + 1
+            for (int w = 0; w < nw; ++w) u += red[(size_t)w * E4 * 64 + idx + 4 * 64];
+            C[(size_t)row * (N / 2) + (pt0 + trel(t)) * NTILE + (l & 15)] = f2h(silu_mul(v, u));
+        } else {
+            C[(size_t)row * N + (nt0 + t) * NTILE + (l & 15)] = f2h(v);
+        }
     }
 }
 
@@ -588,7 +601,7 @@ hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint1
     return run_decode<false>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st);
 }
 
-template <int MT, int NT, int P, int NWMAX, bool DELTA>
+template <int MT, int NT, int P, int NWMAX, bool DELTA, bool GATED>
 static hipError_t run_skinny(const SkinnyCfg &cf, const uint16_t *A, const uint32_t *W,
                              const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
                              int K, int g, hipStream_t st)
@@ -599,7 +612,7 @@ static hipError_t run_skinny(const SkinnyCfg &cf, const uint16_t *A, const uint3
     const size_t lds = ring > sum ? ring : sum;
     if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
     if (cf.nw < 1 || cf.nw > NWMAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((w4a16_skinny_kernel<MT, NT, P, NWMAX, DELTA>), grid, dim3(64 * cf.nw), lds,
+    hipLaunchKernelGGL((w4a16_skinny_kernel<MT, NT, P, NWMAX, DELTA, GATED>), grid, dim3(64 * cf.nw), lds,
                        st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g, cf.nw);
     return hipGetLastError();
 }
@@ -660,16 +673,7 @@ __device__ inline half8 dequant_scaled(uint4v w, half2v s2)
     return __builtin_bit_cast(half8, uint4v{out[0], out[1], out[2], out[3]});
 }
 
-// Buffer resource over [p, p + bytes) for raw (unstructured) buffer loads:
-// base address, stride 0, range in bytes (clamped to 32 bits), and the fixed
-// third-word value of this GPU family for raw dword access.
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, size_t bytes)
-{
-    const int range = bytes > 0xFFFFFFFFull ? (int)0xFFFFFFFF : (int)(unsigned)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, range, 0x00020000);
-}
-
-template <int WM, int WN, bool DELTA>
+template <int WM, int WN, bool DELTA, bool GATED>
 __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g)
@@ -690,6 +694,13 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
     const int n0 = blockIdx.x * BN + wave * 16 * WN;   // this wave's first column
     const bool active = n0 < N;
     const int ntile0 = n0 / NTILE;
+    // GATED: the wave's WN (virtual) n-tiles are WN/2 gate/up pairs: n-tile t
+    // is tile t/2 of the gate run starting at ntile0/2 (t even) or of the up
+    // run starting at N/32 + ntile0/2 (t odd); each run has its resources
+    static_assert(!GATED || WN % 2 == 0, "gate/up pairs need an even WN");
+    const int Nh16 = N / (2 * NTILE);
+    auto odd = [](int t) { return GATED && (t & 1); };
+    auto rel = [](int t) { return GATED ? (t >> 1) : t; };
 
     // ---- A: global -> LDS directly.  One wave instruction fills 1 KB = 4
     // rows; lane i lands at position i of that block, i.e. row 4b + i/16,
@@ -731,16 +742,26 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
     uint4v wreg[WN];
     uint16_t sreg[WN];
     const int ntw = active ? ntile0 : 0;   // (inactive waves load nothing)
-    const __amdgpu_buffer_rsrc_t w_rs = buffer_rsrc(W + (size_t)ntw * KT * 64, (size_t)(N / NTILE - ntw) * KT * 1024);
-    const __amdgpu_buffer_rsrc_t s_rs = buffer_rsrc(S + ntw * NTILE, ((size_t)G * N - ntw * NTILE) * 2);
+    // first physical tile of the (gate, up) runs; resources in plain
+    // variables (a target builtin given an argument whose type depends on a
+    // template parameter loses the kernel's host launch stub)
+    const int pb0 = GATED ? gated_tile(ntw, 0, Nh16) : ntw, pb1 = GATED ? gated_tile(ntw, 1, Nh16) : ntw;
+    auto ptile = [&](int t) { return (odd(t) ? pb1 : pb0) + rel(t); };
+    const __amdgpu_buffer_rsrc_t w_rs0 = buffer_rsrc(W + (size_t)pb0 * KT * 64, (size_t)(N / NTILE - pb0) * KT * 1024);
+    const __amdgpu_buffer_rsrc_t w_rs1 = buffer_rsrc(W + (size_t)pb1 * KT * 64, (size_t)(N / NTILE - pb1) * KT * 1024);
+    const __amdgpu_buffer_rsrc_t s_rs0 = buffer_rsrc(S + pb0 * NTILE, ((size_t)G * N - pb0 * NTILE) * 2);
+    const __amdgpu_buffer_rsrc_t s_rs1 = buffer_rsrc(S + pb1 * NTILE, ((size_t)G * N - pb1 * NTILE) * 2);
     const unsigned w_off = (unsigned)lane * 16u, s_off = (unsigned)c * 2u;
     auto load_w = [&](int kt) {
         if (!active) return;
         const int gb = ((kt * KTILE) / g) * N * 2;
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
-            wreg[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off, (t * KT + kt) * 1024, 0));
-            sreg[t] = __builtin_amdgcn_raw_buffer_load_b16(s_rs, s_off, gb + 32 * t, 0);
+            const __amdgpu_buffer_rsrc_t wr = odd(t) ? w_rs1 : w_rs0;
+            const __amdgpu_buffer_rsrc_t sr = odd(t) ? s_rs1 : s_rs0;
+            const int wo = (rel(t) * KT + kt) * 1024, so = gb + 32 * rel(t);
+            wreg[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off, wo, 0));
+            sreg[t] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off, so, 0);
         }
     };
 
@@ -762,7 +783,7 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
         half8 be[WN];
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
-            const int colx = n0 + 16 * t + c;
+            const int colx = ptile(t) * NTILE + c;
 #pragma unroll
             for (int s8 = 0; s8 < 8; ++s8) {
                 const int gg = gw0 + 8 * (kq & 1) + s8;
@@ -864,11 +885,16 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
 #pragma unroll
     for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-        for (int t = 0; t < WN; ++t)
+        for (int t = 0; t < WN; t += (GATED ? 2 : 1))
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + 16 * mt + 4 * kq + r;
-                if (row < M) C[(size_t)row * N + n0 + 16 * t + c] = f2h(acc[mt][t][r]);
+                if (row >= M) continue;
+                if (GATED)
+                    C[(size_t)row * (N / 2) + ptile(t) * NTILE + c] =
+                        f2h(silu_mul(acc[mt][t][r], acc[mt][t + 1][r]));
+                else
+                    C[(size_t)row * N + n0 + 16 * t + c] = f2h(acc[mt][t][r]);
             }
 }
 
@@ -912,6 +938,7 @@ __device__ inline half8 dequant_scaled_ao(uint4v w, half2v s2, unsigned magic)
     return __builtin_bit_cast(half8, uint4v{out[0], out[1], out[2], out[3]});
 }
 
+template <bool GATED>
 __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     uint16_t *__restrict__ C, int M, int N, int K, int g)
@@ -931,6 +958,12 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
     const int n0c = active ? n0 : N - 16 * WN;
     const int ntile0 = n0c / NTILE;
     const int sh = 16 * (c & 1);
+    // GATED: n-tile t is tile t/2 of the gate run at ntile0/2 (t even) or of
+    // the up run at N/32 + ntile0/2 (t odd), each with its own resources
+    const int Nh16 = N / (2 * NTILE);
+    auto odd = [](int t) { return GATED && (t & 1); };
+    auto rel = [](int t) { return GATED ? (t >> 1) : t; };
+    const int pb0 = GATED ? gated_tile(ntile0, 0, Nh16) : ntile0, pb1 = GATED ? gated_tile(ntile0, 1, Nh16) : ntile0;
 
     // Buffer loads: a workgroup-uniform resource, a fixed per-lane byte
     // offset and the k-dependent byte offset in a scalar register (no
@@ -961,18 +994,29 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
     };
     uint4v wreg[WN];
     uint32_t sreg[WN];   // aligned scale pair holding this lane's column (half c & 1)
-    const __amdgpu_buffer_rsrc_t w_rs = buffer_rsrc(W + (size_t)ntile0 * KT * 64, (size_t)(N / NTILE - ntile0) * KT * 1024);
-    const __amdgpu_buffer_rsrc_t s_rs = buffer_rsrc(S + n0c, ((size_t)(K / g) * N - n0c) * 2);
+    // (resources in plain variables: a target builtin given an argument whose
+    // type depends on a template parameter loses the kernel's host launch stub)
+    const __amdgpu_buffer_rsrc_t w_rs0 = buffer_rsrc(W + (size_t)pb0 * KT * 64, (size_t)(N / NTILE - pb0) * KT * 1024);
+    const __amdgpu_buffer_rsrc_t w_rs1 = buffer_rsrc(W + (size_t)pb1 * KT * 64, (size_t)(N / NTILE - pb1) * KT * 1024);
+    const __amdgpu_buffer_rsrc_t s_rs0 = buffer_rsrc(S + pb0 * NTILE, ((size_t)(K / g) * N - pb0 * NTILE) * 2);
+    const __amdgpu_buffer_rsrc_t s_rs1 = buffer_rsrc(S + pb1 * NTILE, ((size_t)(K / g) * N - pb1 * NTILE) * 2);
     const unsigned w_off = (unsigned)lane * 16u;      // this lane's 16 bytes of a code tile
     const unsigned s_off = ((unsigned)c >> 1) * 4u;   // this lane's scale pair within 16 columns
     auto load_w = [&](int kt) {
         const int k = kt < KT ? kt : KT - 1;
         const int gb = ((k * KTILE) / g) * N * 2;      // byte offset of this k-tile's group row
 #pragma unroll
-        for (int t = 0; t < WN; ++t)
-            wreg[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off, (t * KT + k) * 1024, 0));
+        for (int t = 0; t < WN; ++t) {
+            const __amdgpu_buffer_rsrc_t wr = odd(t) ? w_rs1 : w_rs0;
+            const int wo = (rel(t) * KT + k) * 1024;
+            wreg[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off, wo, 0));
+        }
 #pragma unroll
-        for (int t = 0; t < WN; ++t) sreg[t] = __builtin_amdgcn_raw_buffer_load_b32(s_rs, s_off, gb + 32 * t, 0);
+        for (int t = 0; t < WN; ++t) {
+            const __amdgpu_buffer_rsrc_t sr = odd(t) ? s_rs1 : s_rs0;
+            const int so = gb + 32 * rel(t);
+            sreg[t] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_off, so, 0);
+        }
     };
 
     float4v acc[WM][WN];
@@ -1053,22 +1097,27 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
 #pragma unroll
     for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-        for (int t = 0; t < WN; ++t)
+        for (int t = 0; t < WN; t += (GATED ? 2 : 1))
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + 16 * mt + 4 * kq + r;
-                if (row < M) C[(size_t)row * N + n0 + 16 * t + c] = f2h(acc[mt][t][r]);
+                if (row >= M) continue;
+                if (GATED)
+                    C[(size_t)row * (N / 2) + (pb0 + rel(t)) * NTILE + c] =
+                        f2h(silu_mul(acc[mt][t][r], acc[mt][t + 1][r]));
+                else
+                    C[(size_t)row * N + n0 + 16 * t + c] = f2h(acc[mt][t][r]);
             }
 }
 
-template <int WM, int WN, bool DELTA>
+template <int WM, int WN, bool DELTA, bool GATED>
 static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                             hipStream_t st)
 {
     constexpr int BM = 16 * WM, BN = 64 * WN;
     dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-    hipLaunchKernelGGL((w4a16_tiled_kernel<WM, WN, DELTA>), grid, dim3(256), 0, st, A,
+    hipLaunchKernelGGL((w4a16_tiled_kernel<WM, WN, DELTA, GATED>), grid, dim3(256), 0, st, A,
                        reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g);
     return hipGetLastError();
 }
@@ -1098,13 +1147,7 @@ static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t
 // after which the slot used by the previous k-tile is refilled.
 constexpr int MID_STAGES = 4;
 
-constexpr unsigned waitcnt_vm(int n)
-{
-    // s_waitcnt immediate: vmcnt n (6 bits, split), expcnt and lgkmcnt not waited
-    return (unsigned)((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-template <int SG, bool DELTA, int GK>
+template <int SG, bool DELTA, int GK, bool GATED>
 __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g)
@@ -1123,6 +1166,11 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
     const int ntile0 = blockIdx.x * (BN / NTILE) + WN * nw;
     const int col0 = ntile0 * NTILE + c;
     const int sh = 16 * (c & 1);
+    // GATED: the wave's two (virtual) n-tiles are the gate tile ntile0 / 2
+    // and the up tile N / 32 + ntile0 / 2 of the [K, N] pair weight; each
+    // takes its own resources (parity p of n-tile t = t & 1)
+    const int Nh16 = N / (2 * NTILE);
+    auto pbase = [&](int p) { return GATED ? gated_tile(ntile0, p, Nh16) : ntile0; };
 
     // Every load below is a buffer load: a workgroup-uniform resource (base
     // address), a fixed per-lane byte offset and the k-dependent byte offset
@@ -1148,9 +1196,20 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
                 a_off[i], kt * KTILE * 2, 0, 0);
         }
     };
-    const __amdgpu_buffer_rsrc_t w_rs = buffer_rsrc(W + (size_t)ntile0 * KT * 64, (size_t)(N / NTILE - ntile0) * KT * 1024);
-    const __amdgpu_buffer_rsrc_t s_rs = buffer_rsrc(S + ntile0 * NTILE, ((size_t)(K / g) * N - ntile0 * NTILE) * 2);
-    const __amdgpu_buffer_rsrc_t d_rs = buffer_rsrc(DELTA ? D + ntile0 * NTILE : S, DELTA ? ((size_t)(K / g) * N - ntile0 * NTILE) * 2 : 4);
+    // (plain variables of a fixed type: a target builtin given an argument
+    // whose type depends on a template parameter loses the kernel's host
+    // launch stub)
+    const int pt0 = pbase(0), pt1 = pbase(1);
+    const __amdgpu_buffer_rsrc_t w_rs0 = buffer_rsrc(W + (size_t)pt0 * KT * 64, (size_t)(N / NTILE - pt0) * KT * 1024);
+    const __amdgpu_buffer_rsrc_t w_rs1 = buffer_rsrc(W + (size_t)pt1 * KT * 64, (size_t)(N / NTILE - pt1) * KT * 1024);
+    const __amdgpu_buffer_rsrc_t s_rs0 = buffer_rsrc(S + pt0 * NTILE, ((size_t)(K / g) * N - pt0 * NTILE) * 2);
+    const __amdgpu_buffer_rsrc_t s_rs1 = buffer_rsrc(S + pt1 * NTILE, ((size_t)(K / g) * N - pt1 * NTILE) * 2);
+    const __amdgpu_buffer_rsrc_t d_rs0 = buffer_rsrc(DELTA ? D + pt0 * NTILE : S, DELTA ? ((size_t)(K / g) * N - pt0 * NTILE) * 2 : 4);
+    const __amdgpu_buffer_rsrc_t d_rs1 = buffer_rsrc(DELTA ? D + pt1 * NTILE : S, DELTA ? ((size_t)(K / g) * N - pt1 * NTILE) * 2 : 4);
+    // n-tile t: the up resources at tile 0 for odd t (GATED), else the first
+    // resources at tile t
+    auto odd = [](int t) { return GATED && (t & 1); };
+    auto rel = [](int t) { return GATED ? 0 : t; };
     uint4v rw[SG][WN];
     uint32_t rs[SG][WN], rd[SG][WN];   // aligned scale / delta pairs (half c & 1)
     const unsigned w_off = (unsigned)lane * 16u;      // this lane's 16 bytes of a code tile
@@ -1161,14 +1220,25 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
         const int k = kt < KT ? kt : KT - 1;
         load_a(k, slot);
 #pragma unroll
-        for (int t = 0; t < WN; ++t)
-            rw[slot][t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off, (t * KT + k) * 1024, 0));
+        for (int t = 0; t < WN; ++t) {
+            const __amdgpu_buffer_rsrc_t wr = odd(t) ? w_rs1 : w_rs0;
+            const int wo = (rel(t) * KT + k) * 1024;
+            rw[slot][t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off, wo, 0));
+        }
         const int gb = ((k * KTILE) / g) * N * 2;      // byte offset of this k-tile's group row
 #pragma unroll
-        for (int t = 0; t < WN; ++t) rs[slot][t] = __builtin_amdgcn_raw_buffer_load_b32(s_rs, s_off, gb + 32 * t, 0);
+        for (int t = 0; t < WN; ++t) {
+            const __amdgpu_buffer_rsrc_t sr = odd(t) ? s_rs1 : s_rs0;
+            const int so = gb + 32 * rel(t);
+            rs[slot][t] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_off, so, 0);
+        }
         if (DELTA) {
 #pragma unroll
-            for (int t = 0; t < WN; ++t) rd[slot][t] = __builtin_amdgcn_raw_buffer_load_b32(d_rs, s_off, gb + 32 * t, 0);
+            for (int t = 0; t < WN; ++t) {
+                const __amdgpu_buffer_rsrc_t dr = odd(t) ? d_rs1 : d_rs0;
+                const int so = gb + 32 * rel(t);
+                rd[slot][t] = __builtin_amdgcn_raw_buffer_load_b32(dr, s_off, so, 0);
+            }
         }
     };
 
@@ -1288,27 +1358,31 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
 #pragma unroll
     for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-        for (int t = 0; t < WN; ++t)
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + 32 * mw + 16 * mt + 4 * kq + r;
+            if (row >= M) continue;
+            if (GATED) {
+                C[(size_t)row * (N / 2) + pbase(0) * NTILE + c] = f2h(silu_mul(acc[mt][0][r], acc[mt][1][r]));
+            } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + 32 * mw + 16 * mt + 4 * kq + r;
-                if (row < M) C[(size_t)row * N + col0 + 16 * t] = f2h(acc[mt][t][r]);
+                for (int t = 0; t < WN; ++t) C[(size_t)row * N + col0 + 16 * t] = f2h(acc[mt][t][r]);
             }
+        }
 }
 
-template <bool DELTA, int GK>
+template <bool DELTA, int GK, bool GATED>
 static hipError_t run_mid(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                           const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                           hipStream_t st)
 {
     dim3 grid((unsigned)(N / 64), (unsigned)((M + 63) / 64));
     const size_t lds = (size_t)MID_STAGES * 64 * KTILE * sizeof(_Float16);
-    hipLaunchKernelGGL((w4a16_mid_kernel<MID_STAGES, DELTA, GK>), grid, dim3(256), lds, st, A,
+    hipLaunchKernelGGL((w4a16_mid_kernel<MID_STAGES, DELTA, GK, GATED>), grid, dim3(256), lds, st, A,
                        reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g);
     return hipGetLastError();
 }
 
-template <bool DELTA>
+template <bool DELTA, bool GATED>
 static hipError_t run_mid_g(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                             hipStream_t st)
@@ -1316,17 +1390,21 @@ static hipError_t run_mid_g(const uint16_t *A, const uint32_t *W, const uint16_t
     // the two-k-tile form needs groups of exactly 2 k-tiles (MID_STAGES even:
     // group parity follows the ring slot)
     static_assert(MID_STAGES % 2 == 0, "k-tile parity must follow the ring slot");
-    if (g == K) return run_mid<DELTA, 0>(A, W, S, D, C, M, N, K, g, st);
-    if (g == 2 * KTILE) return run_mid<DELTA, 2>(A, W, S, D, C, M, N, K, g, st);
-    return run_mid<DELTA, 1>(A, W, S, D, C, M, N, K, g, st);
+    if (g == K) return run_mid<DELTA, 0, GATED>(A, W, S, D, C, M, N, K, g, st);
+    if (g == 2 * KTILE) return run_mid<DELTA, 2, GATED>(A, W, S, D, C, M, N, K, g, st);
+    return run_mid<DELTA, 1, GATED>(A, W, S, D, C, M, N, K, g, st);
 }
 
 hipError_t launch_w4a16_mid(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
-                            bool fuse_delta, hipStream_t st)
+                            bool fuse_delta, hipStream_t st, bool gated)
 {
-    if (D && fuse_delta) return run_mid_g<true>(A, W, S, D, C, M, N, K, g, st);
-    return run_mid_g<false>(A, W, S, nullptr, C, M, N, K, g, st);
+    const bool dl = D && fuse_delta;
+    if (gated)
+        return dl ? run_mid_g<true, true>(A, W, S, D, C, M, N, K, g, st)
+                  : run_mid_g<false, true>(A, W, S, nullptr, C, M, N, K, g, st);
+    return dl ? run_mid_g<true, false>(A, W, S, D, C, M, N, K, g, st)
+              : run_mid_g<false, false>(A, W, S, nullptr, C, M, N, K, g, st);
 }
 
 // Configuration for M >= MID_MIN_M: 0 = mid kernel (64 x 64 tiles),
@@ -1344,21 +1422,30 @@ int tiled_config(int M, int N)
     return 0;
 }
 
-hipError_t launch_w4a16_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W,
-                                  const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
-                                  int K, int g, bool fuse_delta, hipStream_t st)
+template <bool GATED>
+static hipError_t run_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                                const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                                bool fuse_delta, hipStream_t st)
 {
     const bool dl = D && fuse_delta;
-    if (cfg == 0) return launch_w4a16_mid(A, W, S, D, C, M, N, K, g, fuse_delta, st);
+    if (cfg == 0) return launch_w4a16_mid(A, W, S, D, C, M, N, K, g, fuse_delta, st, GATED);
     if (cfg == 1) {
-        if (dl) return run_tiled<4, 2, true>(A, W, S, D, C, M, N, K, g, st);
-        return run_tiled<4, 2, false>(A, W, S, nullptr, C, M, N, K, g, st);
+        if (dl) return run_tiled<4, 2, true, GATED>(A, W, S, D, C, M, N, K, g, st);
+        return run_tiled<4, 2, false, GATED>(A, W, S, nullptr, C, M, N, K, g, st);
     }
-    if (dl) return run_tiled<8, 4, true>(A, W, S, D, C, M, N, K, g, st);
+    if (dl) return run_tiled<8, 4, true, GATED>(A, W, S, D, C, M, N, K, g, st);
     dim3 grid((unsigned)((N + 255) / 256), (unsigned)((M + 127) / 128));
-    hipLaunchKernelGGL(w4a16_tiled_sym_kernel, grid, dim3(256), 0, st, A,
+    hipLaunchKernelGGL(w4a16_tiled_sym_kernel<GATED>, grid, dim3(256), 0, st, A,
                        reinterpret_cast<const uint4v *>(W), S, C, M, N, K, g);
     return hipGetLastError();
+}
+
+hipError_t launch_w4a16_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W,
+                                  const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
+                                  int K, int g, bool fuse_delta, hipStream_t st, bool gated)
+{
+    return gated ? run_tiled_cfg<true>(cfg, A, W, S, D, C, M, N, K, g, fuse_delta, st)
+                 : run_tiled_cfg<false>(cfg, A, W, S, D, C, M, N, K, g, fuse_delta, st);
 }
 
 // Rows of the first launch when the 128 x 256 tiles would end in a partly
@@ -1379,20 +1466,21 @@ int tiled_row_split(int M, int N)
 
 hipError_t launch_w4a16_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                               const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
-                              bool fuse_delta, hipStream_t st)
+                              bool fuse_delta, hipStream_t st, bool gated)
 {
     const int cfg = tiled_config(M, N);
     if (cfg == 2) {
         const int m1 = tiled_row_split(M, N);
         if (m1 < M) {
-            hipError_t e = launch_w4a16_tiled_cfg(2, A, W, S, D, C, m1, N, K, g, fuse_delta, st);
+            hipError_t e = launch_w4a16_tiled_cfg(2, A, W, S, D, C, m1, N, K, g, fuse_delta, st, gated);
             if (e != hipSuccess) return e;
             const int m2 = M - m1;
+            const int ldc = gated ? N / 2 : N;   // row stride of the output
             return launch_w4a16_tiled_cfg(tiled_config(m2, N), A + (size_t)m1 * K, W, S, D,
-                                          C + (size_t)m1 * N, m2, N, K, g, fuse_delta, st);
+                                          C + (size_t)m1 * ldc, m2, N, K, g, fuse_delta, st, gated);
         }
     }
-    return launch_w4a16_tiled_cfg(cfg, A, W, S, D, C, M, N, K, g, fuse_delta, st);
+    return launch_w4a16_tiled_cfg(cfg, A, W, S, D, C, M, N, K, g, fuse_delta, st, gated);
 }
 
 // Heuristic choice of the skinny configuration (also sizes the workspace).
@@ -1424,7 +1512,7 @@ size_t w4a16_workspace_bytes(int M, int N, int K)
     return decode_workspace_bytes(M, N, K);
 }
 
-template <bool DELTA>
+template <bool DELTA, bool GATED>
 static hipError_t dispatch_skinny(const SkinnyCfg &c, const uint16_t *A, const uint32_t *W,
                                   const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
                                   int K, int g, hipStream_t st)
@@ -1432,7 +1520,7 @@ static hipError_t dispatch_skinny(const SkinnyCfg &c, const uint16_t *A, const u
     if (c.S != 1) return hipErrorInvalidConfiguration;
 #define QG_SK(MT_, NT_, P_, NWMAX_)                                                             \
     if (c.MT == MT_ && c.NT == NT_ && c.P == P_ && c.nw <= NWMAX_)                              \
-        return run_skinny<MT_, NT_, P_, NWMAX_, DELTA>(c, A, W, S, D, C, M, N, K, g, st);
+        return run_skinny<MT_, NT_, P_, NWMAX_, DELTA, GATED>(c, A, W, S, D, C, M, N, K, g, st);
     QG_SK(1, 2, 2, 8) QG_SK(2, 4, 2, 4) QG_SK(4, 2, 2, 4)
 #undef QG_SK
     return hipErrorInvalidConfiguration;
@@ -1441,11 +1529,15 @@ static hipError_t dispatch_skinny(const SkinnyCfg &c, const uint16_t *A, const u
 hipError_t launch_w4a16_skinny_cfg(const SkinnyCfg &c, const uint16_t *A, const uint32_t *W,
                                    const uint16_t *S, const uint16_t *D, uint16_t *C, int M,
                                    int N, int K, int g, bool fuse_delta, void *ws,
-                                   hipStream_t st)
+                                   hipStream_t st, bool gated)
 {
     (void)ws;
-    if (D && fuse_delta) return dispatch_skinny<true>(c, A, W, S, D, C, M, N, K, g, st);
-    return dispatch_skinny<false>(c, A, W, S, nullptr, C, M, N, K, g, st);
+    const bool dl = D && fuse_delta;
+    if (gated)
+        return dl ? dispatch_skinny<true, true>(c, A, W, S, D, C, M, N, K, g, st)
+                  : dispatch_skinny<false, true>(c, A, W, S, nullptr, C, M, N, K, g, st);
+    return dl ? dispatch_skinny<true, false>(c, A, W, S, D, C, M, N, K, g, st)
+              : dispatch_skinny<false, false>(c, A, W, S, nullptr, C, M, N, K, g, st);
 }
 
 hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
@@ -1549,47 +1641,18 @@ hipError_t launch_w4a16_tail(const uint16_t *A, const uint32_t *W, const uint16_
 
 // ---- SwiGLU of a gate/up pair ("Gaps and follow-ups": mlp_gate and mlp_up
 //      in one kernel) ----
-// The pair is one packed [K, 2N] weight, gate columns first.  Decode batches
-// (M <= 16) run the gated decode kernel: one launch, the product of both
-// halves kept in fp32 and silu(gate) * up rounded once.  Other batches run
-// the GEMM of the whole pair into the workspace ([M, 2N] fp16 after the
-// counter region), then swiglu_kernel.
-
-// silu(Y[m, n]) * Y[m, N + n] for Y [M, 2N] fp16; 8 outputs per thread
-__global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *__restrict__ Y,
-                                                     uint16_t *__restrict__ H, int M, int N)
-{
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;   // 8-column chunk
-    const size_t per_row = (size_t)N / 8;
-    if (i >= (size_t)M * per_row) return;
-    const size_t m = i / per_row, n8 = (i % per_row) * 8;
-    const uint4v gv = *reinterpret_cast<const uint4v *>(Y + m * 2 * N + n8);
-    const uint4v uv = *reinterpret_cast<const uint4v *>(Y + m * 2 * N + N + n8);
-    unsigned out[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        unsigned o = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float gf = h2f((uint16_t)(gv[j] >> (16 * h)));
-            const float uf = h2f((uint16_t)(uv[j] >> (16 * h)));
-            o |= (unsigned)f2h(gf / (1.0f + __builtin_expf(-gf)) * uf) << (16 * h);
-        }
-        out[j] = o;
-    }
-    *reinterpret_cast<uint4v *>(H + m * N + n8) = uint4v{out[0], out[1], out[2], out[3]};
-}
+// The pair is one packed [K, 2N] weight, gate columns first.  Every batch
+// runs one launch whose kernel holds the gate and the up product of the same
+// output columns in fp32 and stores silu(gate) * up once: the gated decode
+// kernel (M <= 16 where it is chosen), otherwise the skinny, mid or tiled
+// kernel with the gated epilogue (gated_tile pairs their n-tiles).
 
 bool swiglu_uses_decode(int M, int N, int K) { return M <= 16 && use_decode_kernel(M, 2 * N, K); }
 
 size_t swiglu_workspace_bytes(int M, int N, int K)
 {
-    if (swiglu_uses_decode(M, N, K)) return decode_workspace_bytes(M, 2 * N, K);
-    // counters first (the layout every W4A16 workspace shares), then the GEMM's
-    // own workspace, then the pair's product
-    const size_t gemm = w4a16_workspace_bytes(M, 2 * N, K);
-    const size_t head = (gemm > W4A16_WS_COUNTER_BYTES ? gemm : W4A16_WS_COUNTER_BYTES);
-    return (head + 255) / 256 * 256 + (size_t)M * 2 * N * sizeof(uint16_t);
+    // only the decode kernel's split-K needs a workspace
+    return swiglu_uses_decode(M, N, K) ? decode_workspace_bytes(M, 2 * N, K) : 0;
 }
 
 hipError_t launch_w4a16_swiglu(const uint16_t *A, const uint32_t *W, const uint16_t *S,
@@ -1603,16 +1666,9 @@ hipError_t launch_w4a16_swiglu(const uint16_t *A, const uint32_t *W, const uint1
         return D ? run_decode<true, true>(A, W, S, D, H, M, N2, K, g, ns, ws, st)
                  : run_decode<false, true>(A, W, S, nullptr, H, M, N2, K, g, ns, ws, st);
     }
-    if (!ws) return hipErrorInvalidValue;
-    const size_t gemm = w4a16_workspace_bytes(M, N2, K);
-    const size_t head = (gemm > W4A16_WS_COUNTER_BYTES ? gemm : W4A16_WS_COUNTER_BYTES);
-    uint16_t *Y = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + (head + 255) / 256 * 256);
-    hipError_t e = launch_w4a16(A, W, S, D, Y, M, N2, K, g, true, gemm ? ws : nullptr, st);
-    if (e != hipSuccess) return e;
-    const size_t chunks = (size_t)M * N / 8;
-    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, Y, H,
-                       M, N);
-    return hipGetLastError();
+    if (M >= TILED_MIN_M) return launch_w4a16_tiled(A, W, S, D, H, M, N2, K, g, true, st, true);
+    return launch_w4a16_skinny_cfg(skinny_config(M, N2, K), A, W, S, D, H, M, N2, K, g, true,
+                                   nullptr, st, true);
 }
 
 // ---- two-stage correction ("The pipeline, end to end": a_group_sum then

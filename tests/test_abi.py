@@ -226,11 +226,16 @@ def test_swiglu_validation():
     assert L.qgemm_w4a16_swiglu(*ok(H=P(0x10008))) == qg.QG_ERR_INVALID_ARG      # H 16-byte aligned
     assert L.qgemm_w4a16_swiglu(*ok(flags=1)) == qg.QG_ERR_INVALID_ARG
     assert L.qgemm_w4a16_swiglu(*ok(N=1000)) == qg.QG_ERR_UNSUPPORTED
-    assert L.qgemm_w4a16_swiglu(*ok(ws=None, wsb=0)) == qg.QG_ERR_WORKSPACE       # M=64 needs the pair's product
-    need = qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 64, 1024, 1024, 128, 1, 0)
-    assert need == CTR + 64 * 2048 * 2
-    assert L.qgemm_w4a16_swiglu(*ok(wsb=need - 1)) == qg.QG_ERR_WORKSPACE
+    # every batch is one fused launch: only the decode kernel's split-K (here
+    # M = 16, K 17408 -> N 5120 per half: 3 splits) takes a workspace
+    for M in (17, 64, 256, 4096):
+        assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, M, 1024, 1024, 128, 1, 0) == 0
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 16, 17408, 5120, 128, 1, 0) == 0
+    need = qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 16, 5120, 17408, 128, 1, 0)
+    assert need == CTR + 160 * 3 * 4096
+    split = lambda **kw: ok(M=16, N=5120, K=17408, **kw)
+    assert L.qgemm_w4a16_swiglu(*split(ws=None, wsb=0)) == qg.QG_ERR_WORKSPACE
+    assert L.qgemm_w4a16_swiglu(*split(wsb=need - 1)) == qg.QG_ERR_WORKSPACE
 
 
 def test_padded_shape():

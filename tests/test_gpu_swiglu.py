@@ -1,8 +1,10 @@
 """GPU parity of the SwiGLU of a gate/up pair (one packed [K, 2N] weight,
-gate columns first) against the oracle's silu(A . W_gate) * (A . W_up):
-the gated decode kernel (M <= 16, one launch, split-K included), and the
-GEMM-then-elementwise path of every other batch (skinny, mid and tiled GEMM
-kernels), symmetric and asymmetric weights."""
+gate columns first) against the oracle's silu(A . W_gate) * (A . W_up): one
+launch at every batch size, the gate and up products of the same columns
+held in fp32 and H rounded once -- the gated decode kernel (M <= 16, split-K
+included) and the gated epilogues of the skinny, mid and tiled kernels
+(64x128, 128x256 with fused delta, the symmetric 128x256 kernel, and the
+prefill-size pair with its row split), symmetric and asymmetric weights."""
 import numpy as np
 import pytest
 import torch
@@ -24,18 +26,23 @@ def _device():
     oracle.build(force=False)
 
 
-def _check(M, K, N, g, asym=True, signed=False, case_id=0):
+def _check(M, K, N, g, asym=True, signed=False, case_id=0, rows=None):
+    """rows: the output rows compared with the oracle (all by default)."""
     c = synth.w4a16_case(M, K, 2 * N, g, asym=asym, signed_scales=signed, stream=91,
                          case_id=case_id)
     note(f"swiglu M={M} K={K} N={N} g={g} asym={asym} signed={signed}")
     pair = qg.pack(dev(c.q), dev(c.s), dev(c.z) if asym else None, g, fold=True)
-    H = qg.w4a16_swiglu(dev(c.A), pair)
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, M, N, K, g, 1, 0) == 0 or M <= 16
+    H = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    qg.w4a16_swiglu(dev(c.A), pair, H=H)
     torch.cuda.synchronize()
     got = host(H).astype(np.float64)
-    ref = oracle.w4a16_swiglu(c.A, c.q, c.s, c.z if asym else None, c.g, fold=True)
-    err = rel_fro(got, ref)
+    assert np.all(np.isfinite(got))
+    rows = np.arange(M) if rows is None else rows
+    ref = oracle.w4a16_swiglu(c.A[rows], c.q, c.s, c.z if asym else None, c.g, fold=True)
+    err = rel_fro(got[rows], ref)
     assert err <= TOL, err
-    assert elementwise_guard(got, ref) <= 0
+    assert elementwise_guard(got[rows], ref) <= 0
     return err
 
 
@@ -56,10 +63,37 @@ def test_swiglu_decode_symmetric_signed():
     _check(8, 4096, 2048, 128, asym=False, signed=True, case_id=30)
 
 
+# skinny (M = 1 where the decode kernel is not chosen, M = 33), mid (per-column
+# and g128 with a ragged last row tile)
 @pytest.mark.parametrize("M,K,N,g", [(1, 1024, 512, 128), (33, 1024, 1024, 256),
                                      (256, 2048, 1024, -1), (300, 1024, 2048, 128)])
-def test_swiglu_unfused_batches(M, K, N, g):
+def test_swiglu_fused_small_batches(M, K, N, g):
     _check(M, K, N, g, case_id=40 + M)
+
+
+def _band_rows(M, every):
+    """One row of every `every`-row band, at a varying offset in the band."""
+    i = np.arange((M + every - 1) // every)
+    return np.minimum(every * i + i % every, M - 1)
+
+
+# tiled kernels: 64x128 tiles (fused delta, and symmetric), 128x256 tiles with
+# the fused delta, the symmetric 128x256 kernel (random-sign scales, folded)
+@pytest.mark.parametrize("M,K,N,asym", [(512, 2048, 4096, True), (512, 1024, 4096, False),
+                                        (2048, 1024, 8192, True), (2048, 1024, 8192, False)])
+def test_swiglu_fused_tiled(M, K, N, asym):
+    _check(M, K, N, 128, asym=asym, signed=not asym, case_id=60 + M + asym,
+           rows=_band_rows(M, 16))
+
+
+def test_swiglu_fused_prefill_pair():
+    """The MLP pair at prefill size (M 4096, K 5120 -> N 17408 per half,
+    symmetric, random-sign scales): 128x256 tiles over the first 3840 rows
+    and a second launch over the rest, checked on one row of every 64-row
+    band plus one row of every 16-row band of the second launch."""
+    M = 4096
+    rows = np.unique(np.concatenate([_band_rows(M, 64), 3840 + _band_rows(256, 16)]))
+    _check(M, 5120, 17408, 128, asym=False, signed=True, case_id=80, rows=rows)
 
 
 def test_swiglu_shares_a_workspace_with_w4a16():
