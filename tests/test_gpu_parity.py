@@ -491,3 +491,23 @@ def test_w4a8_understated_row_bound(max_rows):
     assert np.array_equal(host(acc).astype(np.int64), ref_acc)
     assert rel_fro(got, ref) <= W4A8_TOL
     assert elementwise_guard(got, ref) <= 0
+
+
+# The 8-wave mid-batch kernel (K split between two groups of waves inside the
+# workgroup; taken when (N/128) * ceil(M/64) >= 256): every group form, both
+# weight kinds, k-tile counts that split unevenly (9: 5 + 4; 10 with groups
+# of two k-tiles: 6 + 4; 5 per-column: 3 + 2), the shortest K it takes (4
+# k-tiles), and ragged rows.
+@pytest.mark.parametrize("M,K,N,g,asym", [
+    (256, 1152, 8192, 128, True),
+    (256, 1280, 8192, 256, True),
+    (256, 640, 8192, -1, True),
+    (200, 512, 8192, 128, False),
+    (256, 1536, 8192, 256, False),
+    (130, 1024, 16384, 512, True),
+])
+def test_w4a16_mid_kernel_ksplit(M, K, N, g, asym):
+    gg = K if g == -1 else g
+    c = synth.w4a16_case(M, K, N, gg, asym=asym, signed_scales=not asym, stream=96,
+                         case_id=M + K + gg + asym, name="mid-ksplit")
+    _check_w4a16(c)

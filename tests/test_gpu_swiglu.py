@@ -77,6 +77,12 @@ def _band_rows(M, every):
     return np.minimum(every * i + i % every, M - 1)
 
 
+# the 8-wave mid-batch kernel (K split inside the workgroup), gated
+@pytest.mark.parametrize("M,K,N,g", [(256, 2048, 4096, 256), (192, 1152, 8192, 128)])
+def test_swiglu_fused_mid_ksplit(M, K, N, g):
+    _check(M, K, N, g, case_id=50 + M + K)
+
+
 # tiled kernels: 64x128 tiles (fused delta, and symmetric), 128x256 tiles with
 # the fused delta, the symmetric 128x256 kernel (random-sign scales, folded)
 @pytest.mark.parametrize("M,K,N,asym", [(512, 2048, 4096, True), (512, 1024, 4096, False),
