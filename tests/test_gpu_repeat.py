@@ -136,7 +136,8 @@ def test_quantize_then_w4a8_asym_repeats_bitwise_across_streams():
 
     first = run()
     torch.cuda.synchronize()
-    ref, _ = oracle.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, c.g, z=c.z)
+    ref_q, ref_s = oracle.quantize_rows_int8(c.A16)
+    ref, _ = oracle.w4a8(ref_q, ref_s, c.q, c.s, c.offsets, c.g, z=c.z)
     assert rel_fro(host(first).astype(np.float64), ref) <= 1e-2
     streams = [torch.cuda.current_stream(), torch.cuda.Stream(), torch.cuda.Stream()]
     torch.cuda.synchronize()
