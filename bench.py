@@ -51,6 +51,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--only-primary", action="store_true", help="skip the secondary cases")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-full", action="store_true",
+                   help="run the oracle on every row of every workload (prefill: minutes)")
+    p.add_argument("--cpu-only", action="store_true",
+                   help="only the CPU oracle baseline (no GPU needed)")
     p.add_argument("--cases", default="all", help="comma list of case names, or 'all'")
     p.add_argument("--eager", action="store_true", help="time plain launches instead of a graph replay")
     p.add_argument("--no-probes", action="store_true", help="skip the achievable-peak probes")
@@ -304,11 +308,58 @@ def add_fractions(r, ach):
         r["frac_achievable_int8_mfma"] = r["tops"] / ach["mfma_i8_16x16x64_tops"]
 
 
-def cpu_baseline(case):
-    """The oracle (fp64 dequant + naive loop, OpenMP) on the primary workload:
-    whole calls repeated until at least 10 s have passed (at most 40 calls);
-    returns the mean TFLOP/s and the thread count it used."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_case(oracle, nm, rows, full):
+    """One oracle call on a named workload: every row when `full` or when the
+    workload has at most `rows` rows, else its first `rows` rows (W4A8: the
+    first rows of each expert).  Returns the per-case record."""
+    import numpy as np
+    import synth
+    c = synth.workload(nm)
+    if nm.startswith("w4a8"):
+        per = np.diff(c.offsets)
+        take = per if full else np.minimum(per, rows)
+        idx = np.concatenate([np.arange(o, o + t) for o, t in zip(c.offsets[:-1], take)])
+        off = np.concatenate([[0], np.cumsum(take)]).astype(np.int32)
+        M, total, K, N = int(take.sum()), int(per.sum()), c.K, c.N
+        wb = c.E * (K * N // 2 + (K // c.g) * N * 2)
+        t0 = time.perf_counter()
+        oracle.w4a8(c.Aq[idx], c.a_scale[idx], c.q, c.s, off, c.g, fold=True, want_acc=False)
+        dt = time.perf_counter() - t0
+    else:
+        total, K, N = c.M, c.K, c.N
+        M = total if full else min(total, rows)
+        wb = weight_bytes(K, N, c.g, c.z is not None)
+        t0 = time.perf_counter()
+        oracle.w4a16(c.A[:M], c.q, c.s, c.z, c.g, fold=True)
+        dt = time.perf_counter() - t0
+    flops = 2.0 * M * N * K
+    return {"case": nm, "rows": M, "rows_total": total, "s": round(dt, 3),
+            "gflops": round(flops / dt / 1e9, 3),
+            "weight_gbps": round(wb / dt / 1e9, 3),
+            "full_call_s_linear": round(dt * total / M, 2)}
+
+
+def cpu_baseline(case, full=False):
+    """The oracle (fp64 dequant + naive loop, OpenMP) on this host.  Primary
+    workload: whole calls repeated until at least 8 s have passed (at most 40
+    calls); returns the mean TFLOP/s and the thread count it used.  Then one
+    oracle call per named workload: whole for the decode shapes, the first 64
+    rows for M >= 256 (all rows with `full`), the first 8 rows of every expert
+    for the W4A8 batch; each with its seconds, GFLOP/s, weight GB/s and the
+    seconds a whole call would take if the time grew linearly in the rows."""
     import oracle
+    import synth
     oracle.build(force=False)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     calls = 0
@@ -317,13 +368,22 @@ def cpu_baseline(case):
         oracle.w4a16(case.A, case.q, case.s, case.z, case.g, fold=True)
         calls += 1
         dt = time.perf_counter() - t0
-        if dt >= 10.0 or calls >= 40:
+        if dt >= 8.0 or calls >= 40:
             break
     flops = 2.0 * case.M * case.N * case.K * calls
+    per_case = []
+    for nm in synth.WORKLOADS:
+        if nm == case.name:
+            continue
+        r = _oracle_case(oracle, nm, 8 if nm.startswith("w4a8") else 64, full)
+        log(json.dumps(r))
+        per_case.append(r)
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                cpu=cpu_model(),
                 sample=f"{calls} whole oracle calls on M={case.M} K={case.K} N={case.N} g={case.g} "
                        f"asym ({dt:.1f} s wall, {dt / calls:.2f} s per call; fp64 dequant + "
-                       f"naive m-k-n loop)")
+                       f"naive m-k-n loop)",
+                cases=per_case)
 
 
 def bench_swiglu(name, steps, warmup, M, K, N, g, asym=True):
@@ -423,9 +483,14 @@ def main():
               f"(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
+    import synth
+    if args.cpu_only:
+        print(json.dumps({"cpu_baseline": cpu_baseline(
+            synth.workload("w4a16-decode-M16-K5120-N17408-g128-asym"), full=args.cpu_full)}),
+              flush=True)
+        return
     import torch
     import int4_weight_only_uint32_amd as qg
-    import synth
     global GRAPH
     GRAPH = not args.eager
     if not torch.cuda.is_available():
@@ -536,7 +601,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(pcase)
+        cpu = cpu_baseline(pcase, full=args.cpu_full)
         log(json.dumps(cpu))
 
     launch_us = primary["us_per_call"]
