@@ -76,7 +76,12 @@ bool use_decode_kernel(int M, int N, int K);
 size_t decode_workspace_bytes(int M, int N, int K);
 hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                                const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
-                               bool fuse_delta, int nsplit, void *ws, hipStream_t st);
+                               bool fuse_delta, int nsplit, void *ws, hipStream_t st,
+                               bool gated = false);
+
+// Rows from which the tiled/mid kernels take over from the skinny one (the mid
+// kernel measured faster from about M = 80 on).
+constexpr int TILED_MIN_M = 81;
 
 // Bytes of workspace the W4A16 GEMM kernels need for this shape (0 = none).
 size_t w4a16_workspace_bytes(int M, int N, int K);

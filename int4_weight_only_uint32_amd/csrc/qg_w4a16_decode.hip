@@ -1,0 +1,390 @@
+// W4A16 decode kernel (M <= 16): activation tile shared through LDS, split-K
+// with a last-arriver reduction.  Arithmetic as in the skinny kernel
+// ("Marlin INT4 on Ada - how it works", "The core mismatch: symmetric vs
+// asymmetric"): codes as exact fp16 subnormals in the MFMAs, group scale and
+// delta applied on the fp32 accumulators.
+#include "qg_device.h"
+#include "qg_launch.h"
+
+#include <type_traits>
+
+namespace qg {
+
+// ---- decode kernel (M <= 16) ----
+// A workgroup of 4 waves owns 4*NT consecutive 16-column strips (wave w the
+// strips 4*NT*cg + NT*w .. +NT-1) and one of `nsplit` contiguous ranges of
+// 128-k tiles.  Each k-tile of A (16 rows x 128 k, 4 KB) is fetched once per
+// workgroup -- one 16-byte load per thread, rows past M reading row M-1 --
+// and shared through LDS (double buffered, one barrier per k-tile), so the
+// activation traffic is one tile per workgroup instead of one per wave.
+// Each wave streams its codes, scales and deltas through a P-deep register
+// ring; the MFMA and scaling steps are those of the skinny kernel.
+//
+// nsplit > 1: the workgroups of a column group each hold fp32 partial sums
+// for the same outputs.  Each writes them to its slot of the workspace with
+// device-coherent stores, waits for them to complete, and increments the
+// column group's counter (device-scope atomic).  The one that sees
+// nsplit - 1 adds the slots in split order (deterministic), converts to
+// fp16, stores C and puts the counter back to zero.  Only device-coherent
+// accesses touch the shared slots, so no cache-wide fence is needed; the
+// workspace counters must be zero before the first call and stay zero
+// between calls.
+// GATED: W is a gate/up pair packed as one [K, N] weight (gate columns
+// 0 .. N/2-1, up columns N/2 .. N-1) and C receives silu(gate) * up [M, N/2].
+// Waves 0, 1 of workgroup cg take gate n-tiles 2cg, 2cg+1, waves 2, 3 the up
+// n-tiles of the same columns; after the (split-K) sums, the up waves hand
+// their values to the gate waves through LDS.
+template <int NT, int P, int WV, bool DELTA, bool GATED = false>
+__global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
+    const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
+    const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g,
+    int nsplit, unsigned *__restrict__ counters, float *__restrict__ partials)
+{
+    static_assert(NT == 1, "the scale table holds one column per lane");
+    static_assert(WV == 4 || WV == 8, "4 or 8 waves per workgroup");
+    static_assert(!GATED || WV == 4, "the gate/up pairing takes 4 waves");
+    constexpr int COLS = 16 * WV;            // columns per workgroup
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][16 * KTILE];
+    __shared__ unsigned arrived;
+    __shared__ float xch[GATED ? 2 * 4 * 64 : 1];   // up values for the gate waves
+    // (scale | delta << 16) of this workgroup's 64 columns for every group its
+    // k-range touches: filled once, read once per k-tile (an LDS read instead
+    // of two global loads per k-tile)
+    extern __shared__ uint32_t sdt[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, kq = lane >> 4;
+    const int KT = K / KTILE;
+    const int cg = blockIdx.x / nsplit, sp = blockIdx.x - cg * nsplit;
+    const int kt_beg = (sp * KT) / nsplit, kt_end = ((sp + 1) * KT) / nsplit;
+    const int n = kt_end - kt_beg;
+    const int last = kt_end - 1;
+    const int Nh = N / 2;                    // GATED: output width
+    const int nt0 = GATED ? (wave < 2 ? 2 * cg + wave : Nh / NTILE + 2 * cg + wave - 2)
+                          : (cg * WV + wave) * NT;
+    const int col0 = GATED ? 32 * cg + 16 * (wave & 1) + c : nt0 * NTILE + c;
+
+    // scale table: its loads are issued first (the oldest in flight), and,
+    // when it fits in TB words per thread, written to LDS only after the
+    // ring's first loads are out, so its latency overlaps theirs instead of
+    // preceding them
+    constexpr int TB = 4;
+    const int gi0 = (kt_beg * KTILE) / g;
+    const int ng = n > 0 ? ((kt_end - 1) * KTILE) / g - gi0 + 1 : 0;
+    const int total = ng * (COLS / 2);
+    const bool tfast = total <= TB * 64 * WV;
+    // scale pairs of the table's COLS columns: contiguous, or (GATED) the 32
+    // gate columns 32cg.. and the 32 up columns Nh + 32cg..
+    const int pbase = GATED ? 16 * cg : cg * (COLS / 2);
+    const int pgap = GATED ? Nh / 2 - 16 : 0;   // added to pairs 16.. (GATED)
+    const uint32_t *s32 = reinterpret_cast<const uint32_t *>(S) + (size_t)gi0 * (N / 2) + pbase;
+    const uint32_t *d32 = DELTA ? reinterpret_cast<const uint32_t *>(D) + (size_t)gi0 * (N / 2) + pbase : nullptr;
+    uint32_t tsv[TB], tdv[TB];
+    if (n > 0) {
+        if (tfast) {
+            // unconditional, clamped: the waits for these count exactly
+#pragma unroll
+            for (int i = 0; i < TB; ++i) {
+                int idx = tid + i * 64 * WV;
+                idx = idx < total ? idx : total - 1;
+                const int gl = idx / (COLS / 2), pr = idx % (COLS / 2);
+                const int sp2 = pr + (GATED && pr >= 16 ? pgap : 0);
+                tsv[i] = s32[(size_t)gl * (N / 2) + sp2];
+                tdv[i] = DELTA ? d32[(size_t)gl * (N / 2) + sp2] : 0u;
+            }
+        } else {
+            for (int idx = tid; idx < total; idx += 64 * WV) {
+                const int gl = idx / (COLS / 2), pr = idx % (COLS / 2);
+                const int sp2 = pr + (GATED && pr >= 16 ? pgap : 0);
+                const uint32_t s2 = s32[(size_t)gl * (N / 2) + sp2];
+                const uint32_t d2 = DELTA ? d32[(size_t)gl * (N / 2) + sp2] : 0u;
+                sdt[gl * COLS + 2 * pr] = (s2 & 0xFFFFu) | (d2 << 16);
+                sdt[gl * COLS + 2 * pr + 1] = (s2 >> 16) | (d2 & 0xFFFF0000u);
+            }
+        }
+    }
+
+    // activation tile (16 rows x 256 bytes): with 4 waves thread t fetches
+    // row t/16, 16-byte chunk t%16; with 8 waves row t/32, 8-byte piece t%32.
+    // A 16-byte chunk lands at position chunk ^ row within its 256-byte LDS
+    // row so the 16 rows an MFMA operand reads fall in distinct banks.
+    using AVec = typename std::conditional<WV == 4, uint4v, uint2v>::type;
+    constexpr int APR = 256 / sizeof(AVec);      // pieces per row
+    const int arow_i = tid / APR, apc = tid % APR;
+    const int arow = arow_i < M ? arow_i : M - 1;
+    const AVec *asrc = reinterpret_cast<const AVec *>(A + (size_t)arow * K) + apc;
+    const int ach = apc * (int)sizeof(AVec) / 16, asub = (apc * (int)sizeof(AVec) % 16) / 2;
+    const int adst = arow_i * KTILE + 8 * (ach ^ (arow_i & 15)) + asub;
+    const uint4v *wbase = W + (size_t)nt0 * KT * 64 + lane;
+    const int gbase = (kt_beg * KTILE) / g;
+
+    float4v acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
+    const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    const float4v fzero = {0.f, 0.f, 0.f, 0.f};
+
+    AVec ra[P];
+    uint4v rw[P][NT];
+    auto load = [&](int kt, AVec &a, uint4v (&w)[NT]) {
+        a = asrc[(size_t)kt * (KTILE * 2 / sizeof(AVec))];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) w[t] = wbase[((size_t)t * KT + kt) * 64];
+    };
+    auto finish = [&](int buf, int kt, const CodeOps (&ops)[NT]) {
+        half8 a[4];
+#pragma unroll
+        for (int o = 0; o < 4; ++o)
+            a[o] = *reinterpret_cast<const half8 *>(&As[buf][c * KTILE + 8 * ((4 * o + kq) ^ c)]);
+        const uint32_t sd = sdt[((kt * KTILE) / g - gbase) * COLS + 16 * wave + c];
+        float4v as = mfma_f16(a[0], ones, fzero);
+        as = mfma_f16(a[1], ones, as);
+        as = mfma_f16(a[2], ones, as);
+        as = mfma_f16(a[3], ones, as);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float s = h2f((uint16_t)(sd & 0xFFFFu));
+            const float d = DELTA ? h2f((uint16_t)(sd >> 16)) : 0.f;
+            const float c1 = s * 0x1p20f, c16 = s * 0x1p24f;
+            const float c2 = DELTA ? (d - 8.0f * s) : (-8.0f * s);
+            float4v xl = mfma_f16(a[0], ops[t].lo[0], fzero);
+            xl = mfma_f16(a[1], ops[t].lo[1], xl);
+            float4v xh = mfma_f16(a[2], ops[t].hi[0], fzero);
+            xh = mfma_f16(a[3], ops[t].hi[1], xh);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = __builtin_fmaf(c16, xl[r], acc[t][r]);
+                v = __builtin_fmaf(c1, xh[r], v);
+                acc[t][r] = __builtin_fmaf(c2, as[r], v);
+            }
+        }
+    };
+    auto step = [&](int kt, int slot, int kt_next) {
+        const int buf = (kt - kt_beg) & 1;
+        *reinterpret_cast<AVec *>(&As[buf][adst]) = ra[slot];
+        CodeOps ops[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            ops[t] = split_codes(rw[slot][t]);
+            pin(ops[t].lo[0]); pin(ops[t].lo[1]); pin(ops[t].hi[0]); pin(ops[t].hi[1]);
+        }
+        // unconditional (clamped) refill: a conditional load would make every
+        // later wait assume it might be missing and wait for everything
+        load(kt_next, ra[slot], rw[slot]);
+        __syncthreads();
+        finish(buf, kt, ops);
+    };
+
+    if (n > 0) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int kt = kt_beg + i;
+            load(kt < last ? kt : last, ra[i], rw[i]);
+            // slot by slot, in the order the loop refills them (the waits in
+            // the loop are computed for both orders)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (tfast) {
+#pragma unroll
+            for (int i = 0; i < TB; ++i) {
+                const int idx = tid + i * 64 * WV;
+                if (idx < total) {
+                    const int gl = idx / (COLS / 2), pr = idx % (COLS / 2);
+                    sdt[gl * COLS + 2 * pr] = (tsv[i] & 0xFFFFu) | (tdv[i] << 16);
+                    sdt[gl * COLS + 2 * pr + 1] = (tsv[i] >> 16) | (tdv[i] & 0xFFFF0000u);
+                }
+            }
+        }
+        int j = 0;
+        for (; j + P <= n; j += P) {
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                const int kt = kt_beg + j + i + P;
+                step(kt_beg + j + i, i, kt < last ? kt : last);
+                // keep each refill ahead of the loop's back edge (see the
+                // skinny kernel) and the next slot's work out of this step
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < P - 1; ++i)
+            if (j + i < n) step(kt_beg + j + i, i, last);
+    }
+
+    // C rows 4 kq + r, columns (nt0 + t) * 16 + c; GATED: silu(gate) * up
+    // into C [M, Nh] by the gate waves (reached by every thread of the
+    // workgroup, or of none: the barrier is uniform)
+    auto store = [&](const float4v (&v)[NT]) {
+        if (GATED) {
+            if (wave >= 2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xch[(wave - 2) * 256 + r * 64 + lane] = v[0][r];
+            __syncthreads();
+            if (wave < 2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * kq + r;
+                    const float gv = v[0][r], u = xch[wave * 256 + r * 64 + lane];
+                    if (row < M) C[(size_t)row * Nh + col0] = f2h(gv / (1.0f + __builtin_expf(-gv)) * u);
+                }
+            return;
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * kq + r;
+                if (row < M) C[(size_t)row * N + col0 + 16 * t] = f2h(v[t][r]);
+            }
+    };
+    if (nsplit == 1) {
+        store(acc);
+        return;
+    }
+    // slot layout: [cg][split][wave][t][r][lane] fp32
+    constexpr int PER_WAVE = NT * 4 * 64;
+    float *mine = partials + ((size_t)cg * nsplit + sp) * WV * PER_WAVE + wave * PER_WAVE + lane;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            __hip_atomic_store(mine + (t * 4 + r) * 64, acc[t][r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);          // this thread's slot stores are complete
+    __syncthreads();                        // ... and every thread's
+    if (tid == 0)
+        arrived = __hip_atomic_fetch_add(&counters[cg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived != (unsigned)(nsplit - 1)) return;
+    float4v tot[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) tot[t] = fzero;
+    const float *base = partials + (size_t)cg * nsplit * WV * PER_WAVE + wave * PER_WAVE + lane;
+    for (int s2 = 0; s2 < nsplit; ++s2) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                tot[t][r] += (s2 == sp) ? acc[t][r]
+                                        : __hip_atomic_load(base + (size_t)s2 * WV * PER_WAVE + (t * 4 + r) * 64,
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    store(tot);
+    if (tid == 0) __hip_atomic_store(&counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+namespace decode {
+constexpr int NT = 1, P = 2, WV = 4;      // 8 waves measured slower
+constexpr int COLS = WV * NT * NTILE;    // columns per workgroup
+}
+
+// Groups the k-range of one split touches (at most): the size of the decode
+// kernel's scale table in 64-column rows.
+int decode_max_groups(int K, int g, int nsplit)
+{
+    const int KT = K / KTILE;
+    const int span = (KT + nsplit - 1) / nsplit;          // k-tiles per split, at most
+    const int per_group = g / KTILE > 0 ? g / KTILE : 1;  // k-tiles per group
+    return (span + per_group - 1) / per_group + 1;
+}
+
+// Split count of the decode kernel.  All workgroups are resident at once, and
+// a CU holding one workgroup more than the others finishes last, so the count
+// that keeps every CU at <= 2 workgroups (512 slots on 256 CUs) is taken when
+// it still fills >= 7/8 of the slots (at K = 17408, N = 5120: 6 splits, 480
+// workgroups, 6-12 % faster than 8 splits and 640 workgroups).  Otherwise the
+// smallest power of two giving at least 512 workgroups.  Both keep >= 2
+// k-tiles per split and <= 16 splits; more splits while one split's scale
+// table would exceed 32 KB of LDS.
+// The two-per-CU split count when it applies (see decode_splits), else 0.
+static int decode_balanced_splits(int N, int K)
+{
+    const int KT = K / KTILE, ncg = N / decode::COLS;
+    const int fit = 512 / ncg;
+    return (fit >= 2 && fit <= 16 && ncg * fit >= 448 && KT / fit >= 2) ? fit : 0;
+}
+
+int decode_splits(int N, int K)
+{
+    const int KT = K / KTILE, ncg = N / decode::COLS;
+    int ns = 1;
+    if ((size_t)ncg * sizeof(unsigned) > W4A16_WS_COUNTER_BYTES) return 1;   // no counter for it
+    if (const int fit = decode_balanced_splits(N, K))
+        ns = fit;
+    else
+        while (ns < 16 && (long)ncg * ns < 512 && KT / (2 * ns) >= 2) ns *= 2;
+    while (ns < 1024 && (size_t)decode_max_groups(K, KTILE, ns) * decode::COLS * 4 > 32768) ns *= 2;
+    return ns;
+}
+
+// Decode workspace: the fixed counter region (W4A16_WS_COUNTER_BYTES, shared
+// by every W4A16 layout and written by nothing but the counters), then the
+// partial-sum slots.  0 when the shape is not split.
+// Whether M <= 16 runs the decode kernel rather than the skinny one (which
+// splits K between the 8 waves of a workgroup of 32 columns and needs no
+// cross-workgroup step).  Measured on MI355X (M = 4-16, interleaved repeats):
+// * two or fewer decode splits (wide N): the decode kernel;
+// * more than 256 skinny workgroups (some CUs hold two, the rest one) on
+//   weights of >= 32 M elements: the decode kernel (K = 4096: N = 10240
+//   9.6 against 13.2 us, N = 12288 12.0 against 13.9);
+// * otherwise the decode kernel only when the skinny kernel leaves CUs idle
+//   (< 256 workgroups) and each decode split still streams >= 16 k-tiles
+//   (K = 16384, N = 4096: 14.8 against 17.4 us; K = 17408, N = 5120); with
+//   shorter splits its fixed costs (scale table, split-K epilogue) lose
+//   (K = 4096, N = 4096-8192: 9.2-10 against 7.2-8.5 us; K = N = 8192: 12.7
+//   against 11.7).
+bool use_decode_kernel(int M, int N, int K)
+{
+    if (M > 16 || N % decode::COLS) return false;
+    const int ns = decode_splits(N, K);
+    if (ns <= 2) return true;
+    const long skinny_wgs = N / 32;
+    if (skinny_wgs > 256) return (long long)K * N >= (1ll << 25);
+    return skinny_wgs < 256 && (K / KTILE) / ns >= 16;
+}
+
+size_t decode_workspace_bytes(int M, int N, int K)
+{
+    if (!use_decode_kernel(M, N, K)) return 0;
+    const int ns = decode_splits(N, K);
+    if (ns == 1) return 0;
+    const size_t ncg = (size_t)(N / decode::COLS);
+    return W4A16_WS_COUNTER_BYTES + ncg * ns * 16 * decode::COLS * sizeof(float);
+}
+
+template <bool DELTA, bool GATED = false>
+static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                             int nsplit, void *ws, hipStream_t st)
+{
+    const int ncg = N / decode::COLS;
+    unsigned *counters = nullptr;
+    float *partials = nullptr;
+    if (nsplit > 1) {
+        counters = static_cast<unsigned *>(ws);
+        partials = reinterpret_cast<float *>(static_cast<char *>(ws) + W4A16_WS_COUNTER_BYTES);
+    }
+    const size_t table = (size_t)decode_max_groups(K, g, nsplit) * decode::COLS * sizeof(uint32_t);
+    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED>),
+                       dim3(ncg * nsplit), dim3(64 * decode::WV), table, st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M,
+                       N, K, g, nsplit, counters, partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
+                               const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
+                               bool fuse_delta, int nsplit, void *ws, hipStream_t st,
+                               bool gated)
+{
+    if (M > 16 || N % decode::COLS || nsplit < 1 || (nsplit > 1 && !ws))
+        return hipErrorInvalidValue;
+    const bool dl = D && fuse_delta;
+    if (gated)
+        return dl ? run_decode<true, true>(A, W, S, D, C, M, N, K, g, nsplit, ws, st)
+                  : run_decode<false, true>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st);
+    return dl ? run_decode<true>(A, W, S, D, C, M, N, K, g, nsplit, ws, st)
+              : run_decode<false>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st);
+}
+
+} // namespace qg
