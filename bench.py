@@ -216,7 +216,7 @@ def bench_w4a8(name, steps, warmup, case=None):
 
 def _committed(name):
     """A committed rocprofv3 counter record under profiles/, if neither the
-    kernel source nor the build flags have changed since it was taken."""
+    kernel sources nor the build script have changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", name)
 
@@ -226,33 +226,45 @@ def _committed(name):
     try:
         with open(path) as f:
             rec = json.load(f)
-        same = (sha(rec["source"]) == rec["source_sha256_16"]
-                and sha(rec["build"]) == rec["build_sha256_16"])
+        same = all(sha(p) == h for p, h in {**rec["sources"], **rec["build"]}.items())
     except (OSError, ValueError, KeyError):
         return None
     return rec if same else None
 
 
-def measured_traffic():
-    """HBM bytes per launch of the decode kernel (FETCH_SIZE + WRITE_SIZE,
-    copy-calibrated) from the committed counter summary, or None."""
-    rec = _committed("w4a16_decode_M16_K5120_N17408_traffic.json")
-    return rec["traffic_bytes"] if rec else None
+# case name -> committed counter record of the kernels it runs
+COUNTER_RECORDS = {
+    "w4a16-decode-M16-K5120-N17408-g128-asym": "w4a16_decode_M16_K5120_N17408_counters.json",
+    "w4a16-midbatch-M256-K4096-N8192-g256-asym": "w4a16_mid_M256_K4096_N8192_counters.json",
+    "w4a16-midbatch-M256-K4096-N8192-percol-asym": "w4a16_mid_M256_K4096_N8192_counters.json",
+    "w4a16-prefill-M4096-K5120-N17408-g128-sym-signed": "w4a16_prefill_M4096_K5120_N17408_counters.json",
+    "w4a8-moe-E8x64-K2048-N7168-g128": "w4a8_E8x64_K2048_N7168_counters.json",
+    "w4a8-moe-asym-E8x64-K2048-N7168-g128": "w4a8_E8x64_K2048_N7168_counters.json",
+    "w4a16-swiglu-decode-M16-K5120-N17408x2-g128-asym": "w4a16_swiglu_decode_M16_K5120_N17408x2_counters.json",
+    "quantize-rows-int8-M4096-K5120": "quantize_rows_int8_M4096_K5120_counters.json",
+}
+COUNTER_FIELDS = ("duration_us_under_counters", "mfma_busy_of_grbm_cycles", "grbm_clock_ghz",
+                  "other_valu_per_mfma", "traffic_bytes", "algorithmic_bytes",
+                  "traffic_over_algorithmic")
 
 
-def prefill_counters():
-    """Clock, matrix-core busy and fabric traffic of the prefill kernels from
-    the committed counter summary, or None."""
-    rec = _committed("w4a16_prefill_M4096_K5120_N17408_counters.json")
+def case_counters(name):
+    """Counter figures (rocprofv3 --pmc) of the kernels a case runs, from the
+    committed record while its sources are unchanged, else None."""
+    fn = COUNTER_RECORDS.get(name)
+    rec = _committed(fn) if fn else None
     if not rec:
         return None
-    out = {}
-    for k, v in rec["kernels"].items():
-        if "w4a16" in k:
-            out[k] = {f: v[f] for f in ("duration_us", "clock_ghz", "mfma_busy", "traffic_bytes",
-                                        "algorithmic_bytes") if f in v}
-    out["source"] = "profiles/w4a16_prefill_M4096_K5120_N17408_clock.md (rocprofv3 --pmc)"
+    out = {k: {f: v[f] for f in COUNTER_FIELDS if f in v} for k, v in rec["kernels"].items()}
+    out["source"] = "profiles/" + fn[:-5] + ".md"
     return out
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode kernel (FETCH_SIZE + WRITE_SIZE,
+    copy-calibrated) from the committed counter record, or None."""
+    rec = _committed(COUNTER_RECORDS["w4a16-decode-M16-K5120-N17408-g128-asym"])
+    return next(iter(rec["kernels"].values()))["traffic_bytes"] if rec else None
 
 
 def achievable(primary_bytes):
@@ -592,6 +604,11 @@ def main():
             log(json.dumps(r))
             cases.append(r)
 
+    for r in [primary] + cases:
+        cc = case_counters(r["name"])
+        if cc:
+            r["counters"] = cc
+
     ach = None
     if not args.no_probes:
         ach = achievable(primary["weight_bytes"])
@@ -645,7 +662,7 @@ def main():
                                 "pct_fp16_mfma": prefill[0]["pct_fp16_mfma"],
                                 "frac_achievable_fp16_mfma": prefill[0].get("frac_achievable_fp16_mfma"),
                                 "us_per_call": prefill[0]["us_per_call"],
-                                "counters": prefill_counters()}
+                                "counters": prefill[0].get("counters")}
     print(json.dumps(out), flush=True)
 
 
