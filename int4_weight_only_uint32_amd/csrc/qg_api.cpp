@@ -1,6 +1,6 @@
 // C ABI of the packed-int4 GEMM library: host-side validation, then launches.
 // Nothing is launched and nothing is written unless every check passes.
-#include "../../include/qgemm.h"
+#include "qgemm.h"
 
 #include <hip/hip_runtime.h>
 

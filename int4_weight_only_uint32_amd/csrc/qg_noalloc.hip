@@ -13,7 +13,7 @@
 // graph); every W4A16 call leaves those counters at zero again.  All calls on
 // one GPU share the one array, which keeps the last call's contents: calls
 // that overlap in time on one GPU race.
-#include "../../include/qgemm.h"
+#include "qgemm.h"
 #include "qg_launch.h"
 
 #include <mutex>
