@@ -33,7 +33,7 @@ long long qgprobe_mfma_flops(int shape, int workgroups, int iters);
 
 /* Streaming read of `bytes` (rounded down to whole KiB) from `buf`:
  * `workgroups` workgroups of 4 waves, each wave reading one contiguous run of
- * 1 KiB blocks in batches of `unroll` (1, 2 or 4) blocks, one batch in flight
+ * 1 KiB blocks in batches of `unroll` (1, 2, 4, 8 or 16) blocks, one batch in flight
  * ahead of the one it consumes.  `out` receives one word per lane
  * (workgroups * 256 words, caller-allocated). */
 int qgprobe_hbm_read(const void *buf, size_t bytes, unsigned *out, int workgroups, int unroll, void *stream);

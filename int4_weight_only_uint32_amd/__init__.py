@@ -22,6 +22,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+DEBUG_SYNC_LIB_PATH = os.path.join(_HERE, "libqgemm_debugsync.so")
 
 QG_OK = 0
 QG_ERR_INVALID_ARG = 1
@@ -55,43 +56,59 @@ class QGemmError(RuntimeError):
 
 
 _lib = None
+_debug_lib = None
 
 
 def lib():
     """Load libqgemm.so (built by __graft_entry__.build() or build.py)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
-                               "(python int4_weight_only_uint32_amd/build.py)")
-        L = ctypes.CDLL(LIB_PATH)
-        P, I, U, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
-        L.qg_device_supported.restype = I
-        L.qg_device_supported.argtypes = [I]
-        L.qg_status_string.restype = ctypes.c_char_p
-        L.qg_status_string.argtypes = [I]
-        L.qg_last_error.restype = ctypes.c_char_p
-        L.qg_last_error.argtypes = []
-        L.qg_workspace_bytes.restype = Z
-        L.qg_workspace_bytes.argtypes = [I, I, I, I, I, I, U]
-        L.pack_int4_weights.restype = I
-        L.pack_int4_weights.argtypes = [P, P, P, I, I, I, U, P, P, P, P]
-        L.qgemm_w4a16.restype = I
-        L.qgemm_w4a16.argtypes = [P, P, P, P, P, I, I, I, I, U, P, Z, P]
-        L.qgemm_w4a16_noalloc.restype = I
-        L.qgemm_w4a16_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, U, P]
-        L.group_sum_correction.restype = I
-        L.group_sum_correction.argtypes = [P, P, P, I, I, I, I, P, Z, P]
-        L.qgemm_w4a8.restype = I
-        L.qgemm_w4a8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, Z, U, P]
-        L.qg_padded_shape.restype = I
-        L.qg_padded_shape.argtypes = [I, I, I, P, P, P]
-        L.qgemm_w4a16_swiglu.restype = I
-        L.qgemm_w4a16_swiglu.argtypes = [P, P, P, P, P, I, I, I, I, U, P, Z, P]
-        L.quantize_rows_int8.restype = I
-        L.quantize_rows_int8.argtypes = [P, I, I, P, P, P]
-        _lib = L
+        _lib = open_library(LIB_PATH)
     return _lib
+
+
+def debug_sync_lib():
+    """libqgemm_debugsync.so: the same entry points built with QG_DEBUG_SYNC=1
+    (every pipeline stage waits for all outstanding memory operations, every
+    call waits for its kernels), for race checks against lib()."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = open_library(DEBUG_SYNC_LIB_PATH)
+    return _debug_lib
+
+
+def open_library(path):
+    """A built library with the argument types of every entry point set."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first "
+                           "(python int4_weight_only_uint32_amd/build.py)")
+    L = ctypes.CDLL(path)
+    P, I, U, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+    L.qg_device_supported.restype = I
+    L.qg_device_supported.argtypes = [I]
+    L.qg_status_string.restype = ctypes.c_char_p
+    L.qg_status_string.argtypes = [I]
+    L.qg_last_error.restype = ctypes.c_char_p
+    L.qg_last_error.argtypes = []
+    L.qg_workspace_bytes.restype = Z
+    L.qg_workspace_bytes.argtypes = [I, I, I, I, I, I, U]
+    L.pack_int4_weights.restype = I
+    L.pack_int4_weights.argtypes = [P, P, P, I, I, I, U, P, P, P, P]
+    L.qgemm_w4a16.restype = I
+    L.qgemm_w4a16.argtypes = [P, P, P, P, P, I, I, I, I, U, P, Z, P]
+    L.qgemm_w4a16_noalloc.restype = I
+    L.qgemm_w4a16_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, U, P]
+    L.group_sum_correction.restype = I
+    L.group_sum_correction.argtypes = [P, P, P, I, I, I, I, P, Z, P]
+    L.qgemm_w4a8.restype = I
+    L.qgemm_w4a8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, Z, U, P]
+    L.qg_padded_shape.restype = I
+    L.qg_padded_shape.argtypes = [I, I, I, P, P, P]
+    L.qgemm_w4a16_swiglu.restype = I
+    L.qgemm_w4a16_swiglu.argtypes = [P, P, P, P, P, I, I, I, I, U, P, Z, P]
+    L.quantize_rows_int8.restype = I
+    L.quantize_rows_int8.argtypes = [P, I, I, P, P, P]
+    return L
 
 
 def _check(rc):

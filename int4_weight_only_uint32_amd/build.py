@@ -8,6 +8,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqgemm.so")
+# the same sources with QG_DEBUG_SYNC=1 (every pipeline stage waits for all
+# outstanding memory operations): a race check compares its results with
+# libqgemm.so's, bit for bit
+DEBUG_SYNC_LIB = os.path.join(HERE, "libqgemm_debugsync.so")
 PROBE_LIB = os.path.join(HERE, "libqgprobe.so")
 PROBE_SRC = [os.path.join(HERE, "probe", "qg_probe.hip")]
 
@@ -30,9 +34,9 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "qg_api.cpp")]
 
 
-def _hipcc(srcs, out, verbose):
+def _hipcc(srcs, out, verbose, defines=()):
     tmp = out + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(HERE, "..", "include")] + srcs + ["-o", tmp]
+    cmd = [HIPCC] + FLAGS + list(defines) + ["-I", os.path.join(HERE, "..", "include")] + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,9 +53,15 @@ def _hipcc(srcs, out, verbose):
 
 
 def build(verbose=False):
-    """Build both libraries; returns the path of libqgemm.so."""
-    _hipcc(PROBE_SRC, PROBE_LIB, verbose)
-    return _hipcc(sources(), LIB, verbose)
+    """Build the three libraries (in parallel); returns the path of libqgemm.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(3) as ex:
+        jobs = [ex.submit(_hipcc, PROBE_SRC, PROBE_LIB, verbose),
+                ex.submit(_hipcc, sources(), DEBUG_SYNC_LIB, verbose, ["-DQG_DEBUG_SYNC=1"]),
+                ex.submit(_hipcc, sources(), LIB, verbose)]
+        for j in jobs:
+            j.result()
+    return LIB
 
 
 if __name__ == "__main__":

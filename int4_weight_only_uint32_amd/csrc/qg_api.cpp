@@ -6,8 +6,11 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <set>
+#include <string>
 
 #include "qg_launch.h"
 
@@ -43,11 +46,50 @@ int check_device()
     return QG_OK;
 }
 
-int launch_status(hipError_t e, const char *what)
+// QG_DEBUG_SYNC: the library built with it set (libqgemm_debugsync.so, for
+// race checks) also waits for each call's kernels and reports a failed kernel
+// as that call's error; it must not be used under stream capture.
+#ifndef QG_DEBUG_SYNC
+#define QG_DEBUG_SYNC 0
+#endif
+
+int launch_status(hipError_t e, const char *what, hipStream_t st)
 {
     if (e != hipSuccess)
         return fail(QG_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    if (QG_DEBUG_SYNC) {
+        e = hipStreamSynchronize(st);
+        if (e != hipSuccess)
+            return fail(QG_ERR_LAUNCH, "%s: kernel failed: %s", what, hipGetErrorString(e));
+    }
     return ok();
+}
+
+// With QGEMM_LOG set (and not "0"): one stderr line for the first successful
+// launch of each distinct call description, as the pages' integration logs its
+// first dispatch ("Marlin INT4 on Ada - how it works", "End-to-end result on
+// RTX 4090").
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char *e = getenv("QGEMM_LOG");
+        return e && *e && strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
+void log_first(const char *fmt, ...)
+{
+    if (!log_enabled()) return;
+    char line[320];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(line, sizeof(line), fmt, ap);
+    va_end(ap);
+    static std::mutex mu;
+    static std::set<std::string> seen;
+    std::lock_guard<std::mutex> lk(mu);
+    if (seen.insert(line).second) fprintf(stderr, "[qgemm] first dispatch ok: %s\n", line);
 }
 
 // The kernels address a tile's activation rows and a scale row with 32-bit
@@ -164,17 +206,32 @@ int w4a16_launch(const char *what, const W4A16Call &call, const uint16_t *A,
                  uint16_t *C, int M, int N, int K, void *workspace, hipStream_t st)
 {
     const int g = call.g;
-    if (call.tail)
-        return launch_status(qg::launch_w4a16_tail(A, w_packed, scale, delta, C, M, N, K, g, true,
-                                                   workspace, st),
-                             what);
-    const size_t gemm_ws = w4a16_gemm_ws_bytes(M, N, K, call.separate);
-    hipError_t e = qg::launch_w4a16(A, w_packed, scale, delta, C, M, N, K, g, !call.separate,
-                                    qg::w4a16_workspace_bytes(M, N, K) ? workspace : nullptr, st);
-    if (e == hipSuccess && call.separate)
-        e = qg::launch_group_sum_correction(A, delta, C, M, N, K, g,
-                                            (float *)((char *)workspace + align256(gemm_ws)), st);
-    return launch_status(e, what);
+    int rc;
+    if (call.tail) {
+        rc = launch_status(qg::launch_w4a16_tail(A, w_packed, scale, delta, C, M, N, K, g, true,
+                                                 workspace, st),
+                           what, st);
+    } else {
+        const size_t gemm_ws = w4a16_gemm_ws_bytes(M, N, K, call.separate);
+        hipError_t e = qg::launch_w4a16(A, w_packed, scale, delta, C, M, N, K, g, !call.separate,
+                                        qg::w4a16_workspace_bytes(M, N, K) ? workspace : nullptr, st);
+        if (e == hipSuccess && call.separate)
+            e = qg::launch_group_sum_correction(A, delta, C, M, N, K, g,
+                                                (float *)((char *)workspace + align256(gemm_ws)), st);
+        rc = launch_status(e, what, st);
+    }
+    if (rc == QG_OK && log_enabled()) {
+        int Kp = K, Np = N, gp = g;
+        if (call.tail) qg::padded_shape(K, N, g, &Kp, &Np, &gp);
+        char kern[160];
+        qg::describe_w4a16(M, Np, Kp, delta && !call.separate, false, kern, sizeof(kern));
+        log_first("%s M=%d N=%d K=%d gs=%d %s: %s%s%s", what, M, N, K, g,
+                  delta ? (call.separate ? "asymmetric (separate correction)" : "asymmetric")
+                        : "symmetric",
+                  call.tail ? "padded shape, " : "", kern,
+                  call.separate ? " + group sums + correction" : "");
+    }
+    return rc;
 }
 
 } // namespace
@@ -289,7 +346,11 @@ int pack_int4_weights(const uint8_t *q, const uint16_t *scale, const uint16_t *z
     hipError_t e = qg::launch_pack(q, scale, zero, K, N, g, (flags & QG_PACK_FOLD_NEG_SCALES) != 0,
                                    w_packed, scale_out, zero ? delta_out : nullptr,
                                    (hipStream_t)stream);
-    return launch_status(e, "pack_int4_weights");
+    rc = launch_status(e, "pack_int4_weights", (hipStream_t)stream);
+    if (rc == QG_OK)
+        log_first("pack_int4_weights K=%d N=%d gs=%d %s%s", K, N, g, zero ? "asymmetric" : "symmetric",
+                  (flags & QG_PACK_FOLD_NEG_SCALES) ? ", negative scales folded" : "");
+    return rc;
 }
 
 int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,
@@ -365,7 +426,14 @@ int qgemm_w4a16_swiglu(const uint16_t *A, const uint32_t *w_packed, const uint16
     if ((rc = check_device())) return rc;
     hipError_t e = qg::launch_w4a16_swiglu(A, w_packed, scale, delta, H, M, N, K, g,
                                            need ? workspace : nullptr, (hipStream_t)stream);
-    return launch_status(e, "qgemm_w4a16_swiglu");
+    rc = launch_status(e, "qgemm_w4a16_swiglu", (hipStream_t)stream);
+    if (rc == QG_OK && log_enabled()) {
+        char kern[160];
+        qg::describe_w4a16(M, N, K, delta != nullptr, true, kern, sizeof(kern));
+        log_first("qgemm_w4a16_swiglu M=%d N=%d (pair %d) K=%d gs=%d %s: %s", M, N, 2 * N, K, g,
+                  delta ? "asymmetric" : "symmetric", kern);
+    }
+    return rc;
 }
 
 int group_sum_correction(const uint16_t *A, const uint16_t *delta, uint16_t *C, int M, int N,
@@ -388,7 +456,9 @@ int group_sum_correction(const uint16_t *A, const uint16_t *delta, uint16_t *C, 
     if ((rc = check_device())) return rc;
     hipError_t e = qg::launch_group_sum_correction(A, delta, C, M, N, K, g, (float *)workspace,
                                                    (hipStream_t)stream);
-    return launch_status(e, "group_sum_correction");
+    rc = launch_status(e, "group_sum_correction", (hipStream_t)stream);
+    if (rc == QG_OK) log_first("group_sum_correction M=%d N=%d K=%d gs=%d", M, N, K, g);
+    return rc;
 }
 
 int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed,
@@ -432,14 +502,18 @@ int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed
     }
     if ((rc = check_device())) return rc;
     int max_rows = max_rows_per_expert > M_total ? M_total : max_rows_per_expert;
-    if (tail)
-        return launch_status(qg::launch_w4a8_tail(A_q, a_scale, w_packed, w_scale, w_delta,
-                                                  expert_offsets, num_experts, M_total, max_rows,
-                                                  N, K, g, C, workspace, (hipStream_t)stream),
-                             "qgemm_w4a8");
-    hipError_t e = qg::launch_w4a8(A_q, a_scale, w_packed, w_scale, w_delta, expert_offsets, num_experts,
-                                   M_total, max_rows, N, K, g, C, acc_debug, (hipStream_t)stream);
-    return launch_status(e, "qgemm_w4a8");
+    const hipError_t e =
+        tail ? qg::launch_w4a8_tail(A_q, a_scale, w_packed, w_scale, w_delta, expert_offsets,
+                                    num_experts, M_total, max_rows, N, K, g, C, workspace,
+                                    (hipStream_t)stream)
+             : qg::launch_w4a8(A_q, a_scale, w_packed, w_scale, w_delta, expert_offsets, num_experts,
+                               M_total, max_rows, N, K, g, C, acc_debug, (hipStream_t)stream);
+    rc = launch_status(e, "qgemm_w4a8", (hipStream_t)stream);
+    if (rc == QG_OK)
+        log_first("qgemm_w4a8 experts=%d M_total=%d max_rows=%d N=%d K=%d gs=%d %s%s%s", num_experts,
+                  M_total, max_rows_per_expert, N, K, g, w_delta ? "zero-points" : "symmetric",
+                  tail ? ", padded shape" : "", acc_debug ? ", acc_debug" : "");
+    return rc;
 }
 
 int quantize_rows_int8(const uint16_t *A, int M, int K, int8_t *A_q, float *a_scale,
@@ -456,7 +530,9 @@ int quantize_rows_int8(const uint16_t *A, int M, int K, int8_t *A_q, float *a_sc
     int rc = check_device();
     if (rc) return rc;
     hipError_t e = qg::launch_quantize_rows_int8(A, M, K, A_q, a_scale, (hipStream_t)stream);
-    return launch_status(e, "quantize_rows_int8");
+    rc = launch_status(e, "quantize_rows_int8", (hipStream_t)stream);
+    if (rc == QG_OK) log_first("quantize_rows_int8 M=%d K=%d", M, K);
+    return rc;
 }
 
 } // extern "C"

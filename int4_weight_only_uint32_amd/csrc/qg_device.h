@@ -143,6 +143,20 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, size_t bytes
 }
 
 // s_waitcnt immediate: vmcnt n (6 bits, split), expcnt and lgkmcnt not waited
+// QG_DEBUG_SYNC (compile time, 0 unless defined): every pipeline stage of the
+// GEMM kernels starts by waiting for all of the wave's outstanding memory
+// operations, so nothing loaded ahead stays in flight across a stage and the
+// only overlap left is between waves.  Such a build computes the same bits as
+// the normal one, only slower; a difference between the two points to a
+// missing wait in the normal build.
+#ifndef QG_DEBUG_SYNC
+#define QG_DEBUG_SYNC 0
+#endif
+__device__ inline void debug_stage_sync()
+{
+    if (QG_DEBUG_SYNC) __builtin_amdgcn_s_waitcnt(0);
+}
+
 constexpr unsigned waitcnt_vm(int n)
 {
     return (unsigned)((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));

@@ -15,6 +15,11 @@ void padded_shape(int K, int N, int g, int *Kp, int *Np, int *gp);
 // W4A16 on a shape with tails (is_tail_shape): A padded and C cropped through
 // `ws` (tail_workspace_bytes), the GEMM on the padded shape.
 bool is_tail_shape(int N, int K, int g);
+
+// The kernel(s) a W4A16 (or, gated, SwiGLU) call of this padded shape runs, in
+// words (for the first-dispatch log line).
+void describe_w4a16(int M, int N, int K, bool delta, bool gated, char *buf, size_t n);
+bool use_mid2(int M, int N, int K);
 size_t tail_workspace_bytes(int M, int N, int K, int g);
 hipError_t launch_w4a16_tail(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                              const uint16_t *D, uint16_t *C, int M, int N, int K, int g,

@@ -26,6 +26,7 @@
 #include "qg_device.h"
 #include "qg_launch.h"
 
+#include <cstdio>
 #include <type_traits>
 
 namespace qg {
@@ -121,6 +122,7 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
     };
     auto stage = [&](const uint4v (&ar)[MT * 4], const uint4v (&w)[NT], const uint32_t (&sv)[NT],
                      const uint32_t (&dv)[NT], Staged &st) {
+        debug_stage_sync();
 #pragma unroll
         for (int j = 0; j < MT * 4; ++j) *reinterpret_cast<uint4v *>(scratch + adst[j]) = ar[j];
 #pragma unroll
@@ -318,6 +320,35 @@ hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                                    st);
     return launch_w4a16_skinny_cfg(skinny_config(M, N, K), A, W, S, D, C, M, N, K, g,
                                    fuse_delta, ws, st);
+}
+
+// The kernels launch_w4a16 / launch_w4a16_swiglu run for a shape (K and N
+// multiples of 128), in words, for the first-dispatch log line.
+static const char *big_kernel(int M, int N, int K, bool delta)
+{
+    switch (tiled_config(M, N)) {
+    case 0: return use_mid2(M, N, K) ? "mid 64x128 (K split in the workgroup)" : "mid 64x64";
+    case 1: return "tiled 64x128";
+    default: return delta ? "tiled 128x256" : "tiled 128x256 symmetric";
+    }
+}
+
+void describe_w4a16(int M, int N, int K, bool delta, bool gated, char *buf, size_t n)
+{
+    const int N2 = gated ? 2 * N : N;
+    const char *gate = gated ? "gated " : "";
+    if (gated ? swiglu_uses_decode(M, N, K) : (M < TILED_MIN_M && use_decode_kernel(M, N, K))) {
+        snprintf(buf, n, "%sdecode, %d K-split(s)", gate,
+                 decode_workspace_bytes(M, N2, K) ? decode_splits(N2, K) : 1);
+    } else if (M < TILED_MIN_M) {
+        snprintf(buf, n, "%sskinny", gate);
+    } else if (tiled_config(M, N2) == 2 && tiled_row_split(M, N2) < M) {
+        const int m1 = tiled_row_split(M, N2);
+        snprintf(buf, n, "%s%s rows 0-%d, %s rows %d-%d", gate, big_kernel(m1, N2, K, delta), m1 - 1,
+                 big_kernel(M - m1, N2, K, delta), m1, M - 1);
+    } else {
+        snprintf(buf, n, "%s%s", gate, big_kernel(M, N2, K, delta));
+    }
 }
 
 // ---- shapes with tails: K or N not a multiple of 128 (the pages' dispatcher

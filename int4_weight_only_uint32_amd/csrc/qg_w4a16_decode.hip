@@ -171,6 +171,7 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
         // unconditional (clamped) refill: a conditional load would make every
         // later wait assume it might be missing and wait for everything
         load(kt_next, ra[slot], rw[slot]);
+        debug_stage_sync();
         __syncthreads();
         finish(buf, kt, ops);
     };

@@ -202,6 +202,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
     auto step = [&](int kt, int slot) {
         constexpr unsigned WAIT = waitcnt_vm((SG - 2) * L);
         __builtin_amdgcn_s_waitcnt(WAIT);
+        debug_stage_sync();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -449,6 +450,7 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
         }
     };
     auto sync = [&]() {
+        debug_stage_sync();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");

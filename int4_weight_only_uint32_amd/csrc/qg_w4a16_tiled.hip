@@ -476,6 +476,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
         // 2 WN code and scale loads may still be in flight); the barrier then
         // makes every wave's part visible and frees this tile's buffer
         __builtin_amdgcn_s_waitcnt((2 * WN) | (0x7 << 4) | (0xF << 8));
+        debug_stage_sync();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");

@@ -153,6 +153,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
                 if (DELTA) pin(dv[t]);
             }
             load(kt + P, sl);
+            debug_stage_sync();
             __syncthreads();
             int4v alo[MT], ahi[MT];
 #pragma unroll

@@ -171,7 +171,7 @@ extern "C" long long qgprobe_mfma_flops(int shape, int workgroups, int iters)
 extern "C" int qgprobe_hbm_read(const void *buf, size_t bytes, unsigned *out, int workgroups, int unroll,
                                 void *stream)
 {
-    if (!buf || !out || workgroups < 1 || bytes < 1024 || (unroll != 1 && unroll != 2 && unroll != 4)) return 1;
+    if (!buf || !out || workgroups < 1 || bytes < 1024 || (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16)) return 1;
     const long long nblk = (long long)(bytes / 1024);
     const long long waves = (long long)workgroups * 4;
     const long long per_wave = (nblk + waves - 1) / waves;
@@ -181,6 +181,8 @@ extern "C" int qgprobe_hbm_read(const void *buf, size_t bytes, unsigned *out, in
     case 1: hipLaunchKernelGGL(stream_read<1>, dim3(workgroups), dim3(256), 0, st, src, out, nblk, per_wave); break;
     case 2: hipLaunchKernelGGL(stream_read<2>, dim3(workgroups), dim3(256), 0, st, src, out, nblk, per_wave); break;
     case 4: hipLaunchKernelGGL(stream_read<4>, dim3(workgroups), dim3(256), 0, st, src, out, nblk, per_wave); break;
+    case 8: hipLaunchKernelGGL(stream_read<8>, dim3(workgroups), dim3(256), 0, st, src, out, nblk, per_wave); break;
+    case 16: hipLaunchKernelGGL(stream_read<16>, dim3(workgroups), dim3(256), 0, st, src, out, nblk, per_wave); break;
     default: return 1;
     }
     return hipGetLastError() == hipSuccess ? 0 : 5;

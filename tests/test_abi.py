@@ -35,6 +35,17 @@ def test_library_exports_every_declared_symbol():
     assert sorted(qg.EXPORTED) == _declared()
 
 
+def test_debug_sync_library_exports_every_declared_symbol():
+    """The QG_DEBUG_SYNC build (race checks) carries the same entry points
+    and validates arguments the same way."""
+    L = qg.debug_sync_lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+    assert L.qgemm_w4a16(None, FAKE, FAKE, None, FAKE, 16, 128, 128, 128, 0, None, 0, None) \
+        == qg.QG_ERR_INVALID_ARG
+    assert b"qgemm_w4a16" in L.qg_last_error()
+
+
 def test_probe_library_exports_every_declared_symbol():
     from int4_weight_only_uint32_amd import probe
     L = probe.lib()
@@ -46,6 +57,7 @@ def test_probe_library_exports_every_declared_symbol():
     assert L.qgprobe_mfma_f16(8, FAKE, 1, 1, None) == 1
     assert L.qgprobe_mfma_f16(16, FAKE, 0, 1, None) == 1
     assert L.qgprobe_hbm_read(FAKE, 4096, FAKE, 1, 3, None) == 1
+    assert L.qgprobe_hbm_read(FAKE, 4096, FAKE, 1, 32, None) == 1
     assert L.qgprobe_hbm_read(FAKE, 100, FAKE, 1, 2, None) == 1
     assert L.qgprobe_mfma_flops(16, 2, 3) == 16 * 16 * 32 * 2 * 16 * 3 * 2 * 4
     assert L.qgprobe_mfma_flops(32, 2, 3) == 32 * 32 * 16 * 2 * 4 * 3 * 2 * 4
