@@ -51,8 +51,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--only-primary", action="store_true", help="skip the secondary cases")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-full", action="store_true",
-                   help="run the oracle on every row of every workload (prefill: minutes)")
+    p.add_argument("--cpu-sample", action="store_true",
+                   help="run the oracle on the first rows of the large workloads only")
     p.add_argument("--cpu-only", action="store_true",
                    help="only the CPU oracle baseline (no GPU needed)")
     p.add_argument("--cases", default="all", help="comma list of case names, or 'all'")
@@ -362,14 +362,15 @@ def _oracle_case(oracle, nm, rows, full):
             "full_call_s_linear": round(dt * total / M, 2)}
 
 
-def cpu_baseline(case, full=False):
+def cpu_baseline(case, full=True):
     """The oracle (fp64 dequant + naive loop, OpenMP) on this host.  Primary
     workload: whole calls repeated until at least 8 s have passed (at most 40
     calls); returns the mean TFLOP/s and the thread count it used.  Then one
-    oracle call per named workload: whole for the decode shapes, the first 64
-    rows for M >= 256 (all rows with `full`), the first 8 rows of every expert
-    for the W4A8 batch; each with its seconds, GFLOP/s, weight GB/s and the
-    seconds a whole call would take if the time grew linearly in the rows."""
+    whole oracle call per named workload (about 20 s in all on a 16-core
+    host; with full=False only the first 64 rows for M >= 256 and the first 8
+    rows of every expert of the W4A8 batch), each with its seconds, GFLOP/s,
+    weight GB/s and the seconds a whole call takes (measured, or linear in the
+    rows for a sample)."""
     import oracle
     import synth
     oracle.build(force=False)
@@ -498,7 +499,7 @@ def main():
     import synth
     if args.cpu_only:
         print(json.dumps({"cpu_baseline": cpu_baseline(
-            synth.workload("w4a16-decode-M16-K5120-N17408-g128-asym"), full=args.cpu_full)}),
+            synth.workload("w4a16-decode-M16-K5120-N17408-g128-asym"), full=not args.cpu_sample)}),
               flush=True)
         return
     import torch
@@ -618,7 +619,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(pcase, full=args.cpu_full)
+        cpu = cpu_baseline(pcase, full=not args.cpu_sample)
         log(json.dumps(cpu))
 
     launch_us = primary["us_per_call"]

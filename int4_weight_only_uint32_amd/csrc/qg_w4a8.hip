@@ -83,7 +83,11 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
         // last row read that last row (never stored).
         int arow = m0 + (tid >> 2);
         arow = arow < r1 ? arow : r1 - 1;
-        const int8_t *asrc = Aq + (size_t)arow * K + 32 * (tid & 3);
+        // buffer resources with wave-uniform bases: per-lane offsets are 32-bit
+        // and the k-tile advance is a scalar offset, so no 64-bit address
+        // arithmetic runs per load (reads past a resource's range return 0)
+        const __amdgpu_buffer_rsrc_t a_rs = buffer_rsrc(Aq + (size_t)m0 * K, (size_t)(r1 - m0) * K);
+        const int a_off = (arow - m0) * K + 32 * (tid & 3);
         // the 32 bytes k0 .. k0+31 (k0 = 32 (t%4)) split into four 8-byte pieces:
         // piece j holds k = k0 + 8j .. k0 + 8j + 7 -> operand op = k0 / 64, slot
         // kq = j, half = (k0 / 32) % 2
@@ -100,8 +104,13 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
             }
         };
 
-        const uint4v *wp = W + (size_t)nt0 * KT * 64 + lane;
         const int col0 = nt0 * NTILE + c;
+        const __amdgpu_buffer_rsrc_t w_rs =
+            buffer_rsrc(W + (size_t)nt0 * KT * 64, (size_t)(N / NTILE - nt0) * KT * 1024);
+        const __amdgpu_buffer_rsrc_t s_rs = buffer_rsrc(S + nt0 * NTILE, ((size_t)G * N - nt0 * NTILE) * 2);
+        const __amdgpu_buffer_rsrc_t d_rs =
+            buffer_rsrc(DELTA ? D + nt0 * NTILE : S, DELTA ? ((size_t)G * N - nt0 * NTILE) * 2 : 4);
+        const int s_off = (c & ~1) * 2;     // this lane's column pair, bytes
 
         float4v accf[MT][NT];
         int4v acci[MT][NT];
@@ -122,18 +131,18 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
         uint32_t rs[P][NT], rd[P][NT];
         auto load = [&](int kt, int sl) {
             const int k = kt < KT ? kt : KT - 1;
-            ra[sl][0] = *reinterpret_cast<const uint4v *>(asrc + k * KTILE);
-            ra[sl][1] = *reinterpret_cast<const uint4v *>(asrc + k * KTILE + 16);
+            ra[sl][0] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off, k * KTILE, 0));
+            ra[sl][1] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off + 16, k * KTILE, 0));
 #pragma unroll
-            for (int t = 0; t < NT; ++t) rw[sl][t] = wp[((size_t)t * KT + k) * 64];
-            const int gi = (k * KTILE) / g;
-            const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
+            for (int t = 0; t < NT; ++t)
+                rw[sl][t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           w_rs, (t * KT * 64 + lane) * 16, k * 1024, 0));
+            const int so = ((k * KTILE) / g) * N * 2;   // the group's scale row, bytes
 #pragma unroll
-            for (int t = 0; t < NT; ++t) rs[sl][t] = srow[8 * t];
+            for (int t = 0; t < NT; ++t) rs[sl][t] = __builtin_amdgcn_raw_buffer_load_b32(s_rs, s_off + 32 * t, so, 0);
             if (DELTA) {
-                const uint32_t *drow = reinterpret_cast<const uint32_t *>(D + (size_t)gi * N + (col0 & ~1));
 #pragma unroll
-                for (int t = 0; t < NT; ++t) rd[sl][t] = drow[8 * t];
+                for (int t = 0; t < NT; ++t) rd[sl][t] = __builtin_amdgcn_raw_buffer_load_b32(d_rs, s_off + 32 * t, so, 0);
             }
         };
 
