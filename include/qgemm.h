@@ -43,12 +43,15 @@
  *     QG_* status; qg_last_error() gives a per-thread description.  There is no
  *     internal fallback to another path: the caller decides what to do.
  *   - Shapes: K % 128 == 0 and N % 128 == 0 (the tile multiples the pages'
- *     dispatcher requires), M >= 1.  group_size must divide K and be a multiple
- *     of 128, or equal K; -1 is accepted as an alias of K (per-column scales).
+ *     dispatcher requires), M >= 1.  group_size must divide K and be 32, 64,
+ *     a multiple of 128, or K; -1 is accepted as an alias of K (per-column
+ *     scales).  qgemm_w4a8 takes group sizes of 64 and up (a group of 32
+ *     would split its 64-k int8 MFMA step: QG_ERR_UNSUPPORTED).
  *     pack_int4_weights, qgemm_w4a16 and qgemm_w4a8 also take any K, N >= 1
  *     ("tails"):
- *     group_size is then a multiple of 128 (the last group of g consecutive k
- *     may be partial: G = ceil(K / g)), K, or -1; see qg_padded_shape.
+ *     group_size is then 32, 64, a multiple of 128 (the last group of g
+ *     consecutive k may be partial: G = ceil(K / g)), K, or -1; see
+ *     qg_padded_shape.
  *     Limits: K < 2^22 and ceil(K / g) * N * 2 < 2^31 (the kernels' 32-bit
  *     offsets; qgemm_w4a16_swiglu counts the pair's 2N), else
  *     QG_ERR_UNSUPPORTED.
@@ -111,7 +114,7 @@ const char *qg_last_error(void);
 /* Padded shape of a pack of [K,N] codes with this group size (any K, N >= 1):
  * the packed weight holds K_padded * N_padded / 8 uint32, scale_out and
  * delta_out are [groups, N_padded] fp16.  K_padded = K rounded up to a whole
- * group (to 128 when group_size is K or -1), N_padded = N rounded up to 128,
+ * group (to 128 when group_size is K, -1, 32 or 64), N_padded = N rounded up to 128,
  * groups = ceil(K / group_size) (1 per column).  Equal to K, N, K/g for shapes
  * without tails.  Any output pointer may be NULL.  Returns a QG_* status.  */
 int qg_padded_shape(int K, int N, int group_size, int *K_padded, int *N_padded, int *groups);

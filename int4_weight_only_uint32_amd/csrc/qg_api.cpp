@@ -115,17 +115,18 @@ int check_shape(const char *what, int M, int N, int K, int *g)
     if (*g == -1) *g = K;
     if (*g < 1 || K % *g != 0)
         return fail(QG_ERR_INVALID_ARG, "%s: group_size %d does not divide K=%d", what, *g, K);
-    if (*g != K && *g % 128 != 0)
+    if (*g != K && *g % 128 != 0 && *g != 64 && *g != 32)
         return fail(QG_ERR_UNSUPPORTED,
-                    "%s: group_size %d unsupported (must be a multiple of 128, K, or -1)", what, *g);
+                    "%s: group_size %d unsupported (must be 32, 64, a multiple of 128, K, or -1)",
+                    what, *g);
     if ((long long)M * K > (1ll << 40) || (long long)K * N > (1ll << 40))
         return fail(QG_ERR_UNSUPPORTED, "%s: shape too large", what);
     return check_offsets(what, N, K, *g);
 }
 
 // Shape rules of the entry points that take tails (pack_int4_weights,
-// qgemm_w4a16): K and N any positive size; group_size a multiple of 128 (the
-// last group may be partial), K, or -1 (normalised to K).
+// qgemm_w4a16): K and N any positive size; group_size 32, 64, a multiple of
+// 128 (the last group may be partial), K, or -1 (normalised to K).
 int check_shape_tail(const char *what, int M, int N, int K, int *g)
 {
     if (M < 1 || N < 1 || K < 1)
@@ -133,11 +134,12 @@ int check_shape_tail(const char *what, int M, int N, int K, int *g)
     if (*g == -1) *g = K;
     if (*g < 1)
         return fail(QG_ERR_INVALID_ARG, "%s: group_size %d", what, *g);
-    if (*g != K && *g % 128 != 0) {
+    if (*g != K && *g % 128 != 0 && *g != 64 && *g != 32) {
         if (K % *g != 0)
             return fail(QG_ERR_INVALID_ARG, "%s: group_size %d does not divide K=%d", what, *g, K);
         return fail(QG_ERR_UNSUPPORTED,
-                    "%s: group_size %d unsupported (must be a multiple of 128, K, or -1)", what, *g);
+                    "%s: group_size %d unsupported (must be 32, 64, a multiple of 128, K, or -1)",
+                    what, *g);
     }
     if (K > (1 << 28) || N > (1 << 28) || (long long)M * K > (1ll << 40) ||
         (long long)K * N > (1ll << 40))
@@ -153,16 +155,16 @@ size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // separate].  The counter region is always first, whatever the call, so a
 // workspace shared by different shapes never has group sums or partials
 // written over a counter.
-size_t w4a16_gemm_ws_bytes(int M, int N, int K, bool separate)
+size_t w4a16_gemm_ws_bytes(int M, int N, int K, int g, bool separate)
 {
-    const size_t gemm = qg::w4a16_workspace_bytes(M, N, K);
+    const size_t gemm = qg::w4a16_workspace_bytes(M, N, K, g);
     if (gemm) return gemm;
     return separate ? qg::W4A16_WS_COUNTER_BYTES : 0;
 }
 
 size_t w4a16_ws_bytes(int M, int N, int K, int g, bool separate)
 {
-    const size_t gemm = w4a16_gemm_ws_bytes(M, N, K, separate);
+    const size_t gemm = w4a16_gemm_ws_bytes(M, N, K, g, separate);
     if (!separate) return gemm;
     return align256(gemm) + corr_ws_bytes(M, K, g);
 }
@@ -212,9 +214,9 @@ int w4a16_launch(const char *what, const W4A16Call &call, const uint16_t *A,
                                                  workspace, st),
                            what, st);
     } else {
-        const size_t gemm_ws = w4a16_gemm_ws_bytes(M, N, K, call.separate);
+        const size_t gemm_ws = w4a16_gemm_ws_bytes(M, N, K, g, call.separate);
         hipError_t e = qg::launch_w4a16(A, w_packed, scale, delta, C, M, N, K, g, !call.separate,
-                                        qg::w4a16_workspace_bytes(M, N, K) ? workspace : nullptr, st);
+                                        qg::w4a16_workspace_bytes(M, N, K, g) ? workspace : nullptr, st);
         if (e == hipSuccess && call.separate)
             e = qg::launch_group_sum_correction(A, delta, C, M, N, K, g,
                                                 (float *)((char *)workspace + align256(gemm_ws)), st);
@@ -224,7 +226,7 @@ int w4a16_launch(const char *what, const W4A16Call &call, const uint16_t *A,
         int Kp = K, Np = N, gp = g;
         if (call.tail) qg::padded_shape(K, N, g, &Kp, &Np, &gp);
         char kern[160];
-        qg::describe_w4a16(M, Np, Kp, delta && !call.separate, false, kern, sizeof(kern));
+        qg::describe_w4a16(M, Np, Kp, gp, delta && !call.separate, false, kern, sizeof(kern));
         log_first("%s M=%d N=%d K=%d gs=%d %s: %s%s%s", what, M, N, K, g,
                   delta ? (call.separate ? "asymmetric (separate correction)" : "asymmetric")
                         : "symmetric",
@@ -307,12 +309,16 @@ size_t qg_workspace_bytes(int op, int M, int N, int K, int group_size, int num_e
     case QG_OP_W4A16_SWIGLU:
         if (check_shape("qg_workspace_bytes", M, N, K, &g) != QG_OK) return (size_t)-1;
         if (N > 0x3FFFFFFF) return (size_t)-1;
-        return qg::swiglu_workspace_bytes(M, N, K);
+        return qg::swiglu_workspace_bytes(M, N, K, g);
     case QG_OP_GROUP_SUM_CORRECTION:
         if (check_shape("qg_workspace_bytes", M, N, K, &g) != QG_OK) return (size_t)-1;
         return corr_ws_bytes(M, K, g);
     case QG_OP_W4A8:
         if (check_shape_tail("qg_workspace_bytes", M < 1 ? 1 : M, N, K, &g) != QG_OK) return (size_t)-1;
+        if (g < 64) {
+            fail(QG_ERR_UNSUPPORTED, "qg_workspace_bytes: W4A8 group_size %d below 64", g);
+            return (size_t)-1;
+        }
         return qg::is_tail_shape(N, K, g) ? qg::w4a8_tail_workspace_bytes(M < 1 ? 1 : M, N, K, g) : 0;
     case QG_OP_PACK:
         if (check_shape("qg_workspace_bytes", M < 1 ? 1 : M, N, K, &g) != QG_OK) return (size_t)-1;
@@ -415,7 +421,7 @@ int qgemm_w4a16_swiglu(const uint16_t *A, const uint32_t *w_packed, const uint16
         return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16_swiglu: misaligned pointer");
     if (flags != 0)
         return fail(QG_ERR_INVALID_ARG, "qgemm_w4a16_swiglu: unknown flags 0x%x", flags);
-    const size_t need = qg::swiglu_workspace_bytes(M, N, K);
+    const size_t need = qg::swiglu_workspace_bytes(M, N, K, g);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(QG_ERR_WORKSPACE, "qgemm_w4a16_swiglu: workspace of %zu bytes needed, got %zu",
@@ -429,7 +435,7 @@ int qgemm_w4a16_swiglu(const uint16_t *A, const uint32_t *w_packed, const uint16
     rc = launch_status(e, "qgemm_w4a16_swiglu", (hipStream_t)stream);
     if (rc == QG_OK && log_enabled()) {
         char kern[160];
-        qg::describe_w4a16(M, N, K, delta != nullptr, true, kern, sizeof(kern));
+        qg::describe_w4a16(M, N, K, g, delta != nullptr, true, kern, sizeof(kern));
         log_first("qgemm_w4a16_swiglu M=%d N=%d (pair %d) K=%d gs=%d %s: %s", M, N, 2 * N, K, g,
                   delta ? "asymmetric" : "symmetric", kern);
     }
@@ -471,6 +477,9 @@ int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed
     int g = group_size;
     int rc = check_shape_tail("qgemm_w4a8", M_total, N, K, &g);
     if (rc) return rc;
+    if (g < 64)
+        return fail(QG_ERR_UNSUPPORTED,
+                    "qgemm_w4a8: group_size %d splits a 64-k int8 MFMA step (64 or more)", g);
     const bool tail = qg::is_tail_shape(N, K, g);
     if (!A_q || !a_scale || !w_packed || !w_scale || !C)
         return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: NULL A_q/a_scale/w_packed/w_scale/C");

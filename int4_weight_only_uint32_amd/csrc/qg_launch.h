@@ -18,7 +18,7 @@ bool is_tail_shape(int N, int K, int g);
 
 // The kernel(s) a W4A16 (or, gated, SwiGLU) call of this padded shape runs, in
 // words (for the first-dispatch log line).
-void describe_w4a16(int M, int N, int K, bool delta, bool gated, char *buf, size_t n);
+void describe_w4a16(int M, int N, int K, int g, bool delta, bool gated, char *buf, size_t n);
 bool use_mid2(int M, int N, int K);
 size_t tail_workspace_bytes(int M, int N, int K, int g);
 hipError_t launch_w4a16_tail(const uint16_t *A, const uint32_t *W, const uint16_t *S,
@@ -76,9 +76,11 @@ constexpr size_t W4A16_WS_COUNTER_BYTES = 65536;
 
 // Decode kernel (M <= 16): split count the heuristic picks, and a launch with
 // an explicit split count (nsplit > 1 needs `ws` of decode_workspace_bytes).
-int decode_splits(int N, int K);
-bool use_decode_kernel(int M, int N, int K);
-size_t decode_workspace_bytes(int M, int N, int K);
+// g: the weight group size (groups of 64 or 32 take the decode kernel at
+// every M <= 16 and may change the split count; the default is any g >= 128)
+int decode_splits(int N, int K, int g = 128);
+bool use_decode_kernel(int M, int N, int K, int g = 128);
+size_t decode_workspace_bytes(int M, int N, int K, int g = 128);
 hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                                const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                                bool fuse_delta, int nsplit, void *ws, hipStream_t st,
@@ -89,20 +91,20 @@ hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint1
 constexpr int TILED_MIN_M = 81;
 
 // Bytes of workspace the W4A16 GEMM kernels need for this shape (0 = none).
-size_t w4a16_workspace_bytes(int M, int N, int K);
+size_t w4a16_workspace_bytes(int M, int N, int K, int g);
 
 // C = A . W; when D != nullptr and fuse_delta, the delta term is added in the
 // epilogue; when D == nullptr or !fuse_delta, C is the symmetric product.
-// `ws` must hold w4a16_workspace_bytes(M, N, K) bytes (may be null when 0).
+// `ws` must hold w4a16_workspace_bytes(M, N, K, g) bytes (may be null when 0).
 hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                         const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                         bool fuse_delta, void *ws, hipStream_t st);
 
 // H = silu(A . W[:, :N]) * (A . W[:, N:]) for a gate/up pair packed as one
-// [K, 2N] weight; `ws` of swiglu_workspace_bytes(M, N, K) bytes (counters
+// [K, 2N] weight; `ws` of swiglu_workspace_bytes(M, N, K, g) bytes (counters
 // first, zero-filled once, as for the W4A16 workspace).
-bool swiglu_uses_decode(int M, int N, int K);
-size_t swiglu_workspace_bytes(int M, int N, int K);
+bool swiglu_uses_decode(int M, int N, int K, int g);
+size_t swiglu_workspace_bytes(int M, int N, int K, int g);
 hipError_t launch_w4a16_swiglu(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                                const uint16_t *D, uint16_t *H, int M, int N, int K, int g,
                                void *ws, hipStream_t st);

@@ -109,8 +109,9 @@ __global__ void pack_scales_kernel(const uint16_t *__restrict__ s, const uint16_
 void padded_shape(int K, int N, int g, int *Kp, int *Np, int *gp)
 {
     // g == K: one group per column, padded with K to a multiple of 128;
+    // g = 32 or 64: K padded to a multiple of 128 (whole groups, whole tiles);
     // otherwise g is a multiple of 128 and K is padded to a whole group
-    const int kp = g == K ? (K + KTILE - 1) / KTILE * KTILE : (K + g - 1) / g * g;
+    const int kp = (g == K || g < KTILE) ? (K + KTILE - 1) / KTILE * KTILE : (K + g - 1) / g * g;
     *Kp = kp;
     *Np = (N + 127) / 128 * 128;
     *gp = g == K ? kp : g;

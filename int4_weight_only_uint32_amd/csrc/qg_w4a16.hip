@@ -274,11 +274,11 @@ SkinnyCfg skinny_config(int M, int N, int K)
     return c;
 }
 
-size_t w4a16_workspace_bytes(int M, int N, int K)
+size_t w4a16_workspace_bytes(int M, int N, int K, int g)
 {
     // the decode kernel's split-K counters and partial sums (M <= 16); the
     // skinny and tiled kernels need none
-    return decode_workspace_bytes(M, N, K);
+    return decode_workspace_bytes(M, N, K, g);
 }
 
 template <bool DELTA, bool GATED>
@@ -313,10 +313,12 @@ hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                         const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                         bool fuse_delta, void *ws, hipStream_t st)
 {
-    if (M >= TILED_MIN_M) return launch_w4a16_tiled(A, W, S, D, C, M, N, K, g, fuse_delta, st);
-    if (use_decode_kernel(M, N, K))
+    // groups of 64 or 32: the decode kernel (M <= 16) or the generic tiled ones
+    if (M >= TILED_MIN_M || (g < KTILE && !use_decode_kernel(M, N, K, g)))
+        return launch_w4a16_tiled(A, W, S, D, C, M, N, K, g, fuse_delta, st);
+    if (use_decode_kernel(M, N, K, g))
         return launch_w4a16_decode(A, W, S, D, C, M, N, K, g, fuse_delta,
-                                   decode_workspace_bytes(M, N, K) ? decode_splits(N, K) : 1, ws,
+                                   decode_workspace_bytes(M, N, K, g) ? decode_splits(N, K, g) : 1, ws,
                                    st);
     return launch_w4a16_skinny_cfg(skinny_config(M, N, K), A, W, S, D, C, M, N, K, g,
                                    fuse_delta, ws, st);
@@ -324,8 +326,9 @@ hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
 
 // The kernels launch_w4a16 / launch_w4a16_swiglu run for a shape (K and N
 // multiples of 128), in words, for the first-dispatch log line.
-static const char *big_kernel(int M, int N, int K, bool delta)
+static const char *big_kernel(int M, int N, int K, int g, bool delta)
 {
+    if (g < KTILE) return tiled_config(M, N) == 2 ? "tiled 128x256" : "tiled 64x128";
     switch (tiled_config(M, N)) {
     case 0: return use_mid2(M, N, K) ? "mid 64x128 (K split in the workgroup)" : "mid 64x64";
     case 1: return "tiled 64x128";
@@ -333,21 +336,21 @@ static const char *big_kernel(int M, int N, int K, bool delta)
     }
 }
 
-void describe_w4a16(int M, int N, int K, bool delta, bool gated, char *buf, size_t n)
+void describe_w4a16(int M, int N, int K, int g, bool delta, bool gated, char *buf, size_t n)
 {
     const int N2 = gated ? 2 * N : N;
     const char *gate = gated ? "gated " : "";
-    if (gated ? swiglu_uses_decode(M, N, K) : (M < TILED_MIN_M && use_decode_kernel(M, N, K))) {
+    if (gated ? swiglu_uses_decode(M, N, K, g) : (M < TILED_MIN_M && use_decode_kernel(M, N, K, g))) {
         snprintf(buf, n, "%sdecode, %d K-split(s)", gate,
-                 decode_workspace_bytes(M, N2, K) ? decode_splits(N2, K) : 1);
-    } else if (M < TILED_MIN_M) {
+                 decode_workspace_bytes(M, N2, K, g) ? decode_splits(N2, K, g) : 1);
+    } else if (M < TILED_MIN_M && g >= KTILE) {
         snprintf(buf, n, "%sskinny", gate);
     } else if (tiled_config(M, N2) == 2 && tiled_row_split(M, N2) < M) {
         const int m1 = tiled_row_split(M, N2);
-        snprintf(buf, n, "%s%s rows 0-%d, %s rows %d-%d", gate, big_kernel(m1, N2, K, delta), m1 - 1,
-                 big_kernel(M - m1, N2, K, delta), m1, M - 1);
+        snprintf(buf, n, "%s%s rows 0-%d, %s rows %d-%d", gate, big_kernel(m1, N2, K, g, delta), m1 - 1,
+                 big_kernel(M - m1, N2, K, g, delta), m1, M - 1);
     } else {
-        snprintf(buf, n, "%s%s", gate, big_kernel(M, N2, K, delta));
+        snprintf(buf, n, "%s%s", gate, big_kernel(M, N2, K, g, delta));
     }
 }
 
@@ -401,7 +404,7 @@ size_t tail_workspace_bytes(int M, int N, int K, int g)
 {
     int Kp, Np, gp;
     padded_shape(K, N, g, &Kp, &Np, &gp);
-    const size_t gemm = w4a16_workspace_bytes(M, Np, Kp);
+    const size_t gemm = w4a16_workspace_bytes(M, Np, Kp, gp);
     size_t off = al256(gemm > W4A16_WS_COUNTER_BYTES ? gemm : W4A16_WS_COUNTER_BYTES);
     if (Kp != K) off += al256((size_t)M * Kp * sizeof(uint16_t));
     if (Np != N) off += (size_t)M * Np * sizeof(uint16_t);
@@ -415,7 +418,7 @@ hipError_t launch_w4a16_tail(const uint16_t *A, const uint32_t *W, const uint16_
     if (!ws) return hipErrorInvalidValue;
     int Kp, Np, gp;
     padded_shape(K, N, g, &Kp, &Np, &gp);
-    const size_t gemm = w4a16_workspace_bytes(M, Np, Kp);
+    const size_t gemm = w4a16_workspace_bytes(M, Np, Kp, gp);
     char *p = static_cast<char *>(ws) + al256(gemm > W4A16_WS_COUNTER_BYTES ? gemm : W4A16_WS_COUNTER_BYTES);
     const uint16_t *Ause = A;
     if (Kp != K) {
@@ -445,12 +448,12 @@ hipError_t launch_w4a16_tail(const uint16_t *A, const uint32_t *W, const uint16_
 // kernel (M <= 16 where it is chosen), otherwise the skinny, mid or tiled
 // kernel with the gated epilogue (gated_tile pairs their n-tiles).
 
-bool swiglu_uses_decode(int M, int N, int K) { return M <= 16 && use_decode_kernel(M, 2 * N, K); }
+bool swiglu_uses_decode(int M, int N, int K, int g) { return M <= 16 && use_decode_kernel(M, 2 * N, K, g); }
 
-size_t swiglu_workspace_bytes(int M, int N, int K)
+size_t swiglu_workspace_bytes(int M, int N, int K, int g)
 {
     // only the decode kernel's split-K needs a workspace
-    return swiglu_uses_decode(M, N, K) ? decode_workspace_bytes(M, 2 * N, K) : 0;
+    return swiglu_uses_decode(M, N, K, g) ? decode_workspace_bytes(M, 2 * N, K, g) : 0;
 }
 
 hipError_t launch_w4a16_swiglu(const uint16_t *A, const uint32_t *W, const uint16_t *S,
@@ -458,12 +461,12 @@ hipError_t launch_w4a16_swiglu(const uint16_t *A, const uint32_t *W, const uint1
                                void *ws, hipStream_t st)
 {
     const int N2 = 2 * N;
-    if (swiglu_uses_decode(M, N, K)) {
-        const int ns = decode_workspace_bytes(M, N2, K) ? decode_splits(N2, K) : 1;
+    if (swiglu_uses_decode(M, N, K, g)) {
+        const int ns = decode_workspace_bytes(M, N2, K, g) ? decode_splits(N2, K, g) : 1;
         if (ns > 1 && !ws) return hipErrorInvalidValue;
         return launch_w4a16_decode(A, W, S, D, H, M, N2, K, g, true, ns, ws, st, true);
     }
-    if (M >= TILED_MIN_M) return launch_w4a16_tiled(A, W, S, D, H, M, N2, K, g, true, st, true);
+    if (M >= TILED_MIN_M || g < KTILE) return launch_w4a16_tiled(A, W, S, D, H, M, N2, K, g, true, st, true);
     return launch_w4a16_skinny_cfg(skinny_config(M, N2, K), A, W, S, D, H, M, N2, K, g, true,
                                    nullptr, st, true);
 }

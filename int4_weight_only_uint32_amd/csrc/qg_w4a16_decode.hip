@@ -34,7 +34,12 @@ namespace qg {
 // Waves 0, 1 of workgroup cg take gate n-tiles 2cg, 2cg+1, waves 2, 3 the up
 // n-tiles of the same columns; after the (split-K) sums, the up waves hand
 // their values to the gate waves through LDS.
-template <int NT, int P, int WV, bool DELTA, bool GATED = false>
+// GPT: weight groups per 128-k tile (1 for g >= 128; 2 for g = 64, 4 for
+// g = 32).  Each 32-k MFMA step lies inside one group (the packed layout puts
+// k-steps 0, 1 in the low nibbles and 2, 3 in the high ones), so with g = 64
+// the low- and high-nibble products are the two groups' and with g = 32 each
+// step's product is its own group's; the group sums of A split the same way.
+template <int NT, int P, int WV, bool DELTA, bool GATED = false, int GPT = 1>
 __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g,
@@ -70,7 +75,7 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     // preceding them
     constexpr int TB = 4;
     const int gi0 = (kt_beg * KTILE) / g;
-    const int ng = n > 0 ? ((kt_end - 1) * KTILE) / g - gi0 + 1 : 0;
+    const int ng = n > 0 ? (kt_end * KTILE - 1) / g - gi0 + 1 : 0;
     const int total = ng * (COLS / 2);
     const bool tfast = total <= TB * 64 * WV;
     // scale pairs of the table's COLS columns: contiguous, or (GATED) the 32
@@ -136,6 +141,42 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
 #pragma unroll
         for (int o = 0; o < 4; ++o)
             a[o] = *reinterpret_cast<const half8 *>(&As[buf][c * KTILE + 8 * ((4 * o + kq) ^ c)]);
+        if (GPT > 1) {
+            // groups of 64 or 32 k: one scale and delta per group of the tile
+            constexpr int SPG = 4 / GPT;                // MFMA steps per group
+            const uint32_t *sdp = &sdt[((kt * KTILE) / g - gbase) * COLS + 16 * wave + c];
+            float4v as[GPT];
+#pragma unroll
+            for (int q = 0; q < GPT; ++q) {
+                as[q] = mfma_f16(a[SPG * q], ones, fzero);
+                if (SPG == 2) as[q] = mfma_f16(a[SPG * q + 1], ones, as[q]);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const half8 op[4] = {ops[t].lo[0], ops[t].lo[1], ops[t].hi[0], ops[t].hi[1]};
+                float4v x[GPT];
+#pragma unroll
+                for (int q = 0; q < GPT; ++q) {
+                    x[q] = mfma_f16(a[SPG * q], op[SPG * q], fzero);
+                    if (SPG == 2) x[q] = mfma_f16(a[SPG * q + 1], op[SPG * q + 1], x[q]);
+                }
+#pragma unroll
+                for (int q = 0; q < GPT; ++q) {
+                    const uint32_t sd = sdp[q * COLS];
+                    const float s = h2f((uint16_t)(sd & 0xFFFFu));
+                    const float d = DELTA ? h2f((uint16_t)(sd >> 16)) : 0.f;
+                    // steps 0, 1 hold low nibbles (2^-24 v), steps 2, 3 high ones (2^-20 v)
+                    const float cx = s * (SPG * q < 2 ? 0x1p24f : 0x1p20f);
+                    const float c2 = DELTA ? (d - 8.0f * s) : (-8.0f * s);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float v = __builtin_fmaf(cx, x[q][r], acc[t][r]);
+                        acc[t][r] = __builtin_fmaf(c2, as[q][r], v);
+                    }
+                }
+            }
+            return;
+        }
         const uint32_t sd = sdt[((kt * KTILE) / g - gbase) * COLS + 16 * wave + c];
         float4v as = mfma_f16(a[0], ones, fzero);
         as = mfma_f16(a[1], ones, as);
@@ -286,7 +327,8 @@ int decode_max_groups(int K, int g, int nsplit)
 {
     const int KT = K / KTILE;
     const int span = (KT + nsplit - 1) / nsplit;          // k-tiles per split, at most
-    const int per_group = g / KTILE > 0 ? g / KTILE : 1;  // k-tiles per group
+    if (g < KTILE) return span * (KTILE / g);             // whole groups per k-tile
+    const int per_group = g / KTILE;                      // k-tiles per group
     return (span + per_group - 1) / per_group + 1;
 }
 
@@ -306,7 +348,7 @@ static int decode_balanced_splits(int N, int K)
     return (fit >= 2 && fit <= 16 && ncg * fit >= 448 && KT / fit >= 2) ? fit : 0;
 }
 
-int decode_splits(int N, int K)
+int decode_splits(int N, int K, int g)
 {
     const int KT = K / KTILE, ncg = N / decode::COLS;
     int ns = 1;
@@ -315,7 +357,9 @@ int decode_splits(int N, int K)
         ns = fit;
     else
         while (ns < 16 && (long)ncg * ns < 512 && KT / (2 * ns) >= 2) ns *= 2;
-    while (ns < 1024 && (size_t)decode_max_groups(K, KTILE, ns) * decode::COLS * 4 > 32768) ns *= 2;
+    // the table's largest size over group sizes >= 128 is that of g = 128
+    const int gt = g < KTILE ? g : KTILE;
+    while (ns < 1024 && (size_t)decode_max_groups(K, gt, ns) * decode::COLS * 4 > 32768) ns *= 2;
     return ns;
 }
 
@@ -335,26 +379,27 @@ int decode_splits(int N, int K)
 //   shorter splits its fixed costs (scale table, split-K epilogue) lose
 //   (K = 4096, N = 4096-8192: 9.2-10 against 7.2-8.5 us; K = N = 8192: 12.7
 //   against 11.7).
-bool use_decode_kernel(int M, int N, int K)
+bool use_decode_kernel(int M, int N, int K, int g)
 {
     if (M > 16 || N % decode::COLS) return false;
-    const int ns = decode_splits(N, K);
+    if (g < KTILE) return true;     // groups of 64 or 32: the only M <= 16 kernel that has them
+    const int ns = decode_splits(N, K, g);
     if (ns <= 2) return true;
     const long skinny_wgs = N / 32;
     if (skinny_wgs > 256) return (long long)K * N >= (1ll << 25);
     return skinny_wgs < 256 && (K / KTILE) / ns >= 16;
 }
 
-size_t decode_workspace_bytes(int M, int N, int K)
+size_t decode_workspace_bytes(int M, int N, int K, int g)
 {
-    if (!use_decode_kernel(M, N, K)) return 0;
-    const int ns = decode_splits(N, K);
+    if (!use_decode_kernel(M, N, K, g)) return 0;
+    const int ns = decode_splits(N, K, g);
     if (ns == 1) return 0;
     const size_t ncg = (size_t)(N / decode::COLS);
     return W4A16_WS_COUNTER_BYTES + ncg * ns * 16 * decode::COLS * sizeof(float);
 }
 
-template <bool DELTA, bool GATED = false>
+template <bool DELTA, bool GATED = false, int GPT = 1>
 static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                              const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                              int nsplit, void *ws, hipStream_t st)
@@ -367,7 +412,13 @@ static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_
         partials = reinterpret_cast<float *>(static_cast<char *>(ws) + W4A16_WS_COUNTER_BYTES);
     }
     const size_t table = (size_t)decode_max_groups(K, g, nsplit) * decode::COLS * sizeof(uint32_t);
-    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED>),
+    if (table > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)table);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT>),
                        dim3(ncg * nsplit), dim3(64 * decode::WV), table, st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M,
                        N, K, g, nsplit, counters, partials);
     return hipGetLastError();
@@ -381,11 +432,18 @@ hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint1
     if (M > 16 || N % decode::COLS || nsplit < 1 || (nsplit > 1 && !ws))
         return hipErrorInvalidValue;
     const bool dl = D && fuse_delta;
-    if (gated)
-        return dl ? run_decode<true, true>(A, W, S, D, C, M, N, K, g, nsplit, ws, st)
-                  : run_decode<false, true>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st);
-    return dl ? run_decode<true>(A, W, S, D, C, M, N, K, g, nsplit, ws, st)
-              : run_decode<false>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st);
+    const int gpt = g < KTILE ? KTILE / g : 1;
+#define QG_DEC(GPT_)                                                                          \
+    if (gpt == GPT_) {                                                                        \
+        if (gated)                                                                            \
+            return dl ? run_decode<true, true, GPT_>(A, W, S, D, C, M, N, K, g, nsplit, ws, st) \
+                      : run_decode<false, true, GPT_>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st); \
+        return dl ? run_decode<true, false, GPT_>(A, W, S, D, C, M, N, K, g, nsplit, ws, st)   \
+                  : run_decode<false, false, GPT_>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st); \
+    }
+    QG_DEC(1) QG_DEC(2) QG_DEC(4)
+#undef QG_DEC
+    return hipErrorInvalidValue;
 }
 
 } // namespace qg

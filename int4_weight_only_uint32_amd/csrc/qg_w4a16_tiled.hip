@@ -62,7 +62,11 @@ __device__ inline half8 dequant_scaled(uint4v w, half2v s2)
     return __builtin_bit_cast(half8, uint4v{out[0], out[1], out[2], out[3]});
 }
 
-template <int WM, int WN, bool DELTA, bool GATED>
+// GPT: weight groups per 128-k tile (1 for g >= 128, 2 for g = 64, 4 for
+// g = 32): each 32-k MFMA step lies in one group, so step O dequantizes with
+// the scale of group O / (4 / GPT) of the tile, and the group sums of A are
+// taken per group.
+template <int WM, int WN, bool DELTA, bool GATED, int GPT = 1>
 __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g)
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
     };
     // ---- codes and scales of this wave's WN n-tiles
     uint4v wreg[WN];
-    uint16_t sreg[WN];
+    uint16_t sreg[WN][GPT];
     const int ntw = active ? ntile0 : 0;   // (inactive waves load nothing)
     // first physical tile of the (gate, up) runs; resources in plain
     // variables (a target builtin given an argument whose type depends on a
@@ -150,7 +154,9 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
             const __amdgpu_buffer_rsrc_t sr = odd(t) ? s_rs1 : s_rs0;
             const int wo = (rel(t) * KT + kt) * 1024, so = gb + 32 * rel(t);
             wreg[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off, wo, 0));
-            sreg[t] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off, so, 0);
+#pragma unroll
+            for (int q = 0; q < GPT; ++q)
+                sreg[t][q] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off, so + q * N * 2, 0);
         }
     };
 
@@ -159,9 +165,11 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
     for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
         for (int t = 0; t < WN; ++t) acc[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
-    float4v gsum[GM];
+    float4v gsum[GM][GPT];
 #pragma unroll
-    for (int j = 0; j < GM; ++j) gsum[j] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < GM; ++j)
+#pragma unroll
+        for (int q = 0; q < GPT; ++q) gsum[j][q] = float4v{0.f, 0.f, 0.f, 0.f};
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     if (DELTA)
         for (int i = tid; i < BM * WIN; i += 256) asum_win[i] = 0.f;
@@ -202,12 +210,15 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
     for (int kt = 0; kt < KT; ++kt) {
         const int st = kt & 1;
         uint4v wc[WN];
-        half2v s2[WN];
+        half2v s2[WN][GPT];
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
             wc[t] = wreg[t];
-            const _Float16 sh = __builtin_bit_cast(_Float16, sreg[t]);
-            s2[t] = half2v{sh, sh};
+#pragma unroll
+            for (int q = 0; q < GPT; ++q) {
+                const _Float16 sh = __builtin_bit_cast(_Float16, sreg[t][q]);
+                s2[t][q] = half2v{sh, sh};
+            }
         }
         // unconditional, clamped: the last k-tile reloads its own tile into
         // the idle buffer (a conditional load would leave the compiler unsure
@@ -219,7 +230,7 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
 #define QG_TILED_STEP(O)                                                                      \
     {                                                                                         \
         half8 b[WN];                                                                          \
-        _Pragma("unroll") for (int t = 0; t < WN; ++t) b[t] = dequant_scaled<O>(wc[t], s2[t]); \
+        _Pragma("unroll") for (int t = 0; t < WN; ++t) b[t] = dequant_scaled<O>(wc[t], s2[t][(O) / (4 / GPT)]); \
         _Pragma("unroll") for (int mt = 0; mt < WM; ++mt)                                     \
         {                                                                                     \
             const half8 a = a_frag(as, mt, O);                                                \
@@ -233,26 +244,29 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
 #undef QG_TILED_STEP
         }
         if (DELTA) {
-            // group sums of this wave's GM m-tiles
+            // group sums of this wave's GM m-tiles (per group of the tile)
 #pragma unroll
             for (int j = 0; j < GM; ++j) {
                 const int mt = GM * wave + j;
 #pragma unroll
                 for (int o = 0; o < 4; ++o) {
                     const half8 a = a_frag(as, mt, o);
-                    gsum[j] = mfma_f16(a, ones, gsum[j]);
+                    gsum[j][o / (4 / GPT)] = mfma_f16(a, ones, gsum[j][o / (4 / GPT)]);
                 }
             }
             const int gi = (kt * KTILE) / g;
-            const bool gend = ((kt + 1) * KTILE) % g == 0;
+            const bool gend = GPT > 1 || ((kt + 1) * KTILE) % g == 0;
             if (gend) {
 #pragma unroll
-                for (int j = 0; j < GM; ++j) {
+                for (int j = 0; j < GM; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        asum_win[(16 * (GM * wave + j) + 4 * kq + r) * WIN + (gi % WIN)] = gsum[j][r];
-                    gsum[j] = float4v{0.f, 0.f, 0.f, 0.f};
-                }
+                    for (int q = 0; q < GPT; ++q) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            asum_win[(16 * (GM * wave + j) + 4 * kq + r) * WIN + ((gi + q) % WIN)] =
+                                gsum[j][q][r];
+                        gsum[j][q] = float4v{0.f, 0.f, 0.f, 0.f};
+                    }
             }
         }
         // the direct loads of the next A tile (and the next codes) must have
@@ -260,8 +274,9 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (DELTA) {
-            const int gi = (kt * KTILE) / g;
-            const bool gend = ((kt + 1) * KTILE) % g == 0;
+            // the tile's last group (a window of WIN groups never splits a tile)
+            const int gi = (kt * KTILE) / g + GPT - 1;
+            const bool gend = GPT > 1 || ((kt + 1) * KTILE) % g == 0;
             if (gend && (gi % WIN == WIN - 1 || gi == G - 1)) {
                 delta_step(gi - gi % WIN);
                 // later groups of the next window overwrite these slots only
@@ -500,16 +515,32 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
             }
 }
 
-template <int WM, int WN, bool DELTA, bool GATED>
+template <int WM, int WN, bool DELTA, bool GATED, int GPT = 1>
 static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                             hipStream_t st)
 {
     constexpr int BM = 16 * WM, BN = 64 * WN;
     dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-    hipLaunchKernelGGL((w4a16_tiled_kernel<WM, WN, DELTA, GATED>), grid, dim3(256), 0, st, A,
+    hipLaunchKernelGGL((w4a16_tiled_kernel<WM, WN, DELTA, GATED, GPT>), grid, dim3(256), 0, st, A,
                        reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g);
     return hipGetLastError();
+}
+
+// Groups of 64 or 32 (GPT = 2 or 4 groups per k-tile): the generic tiled
+// kernels at every configuration (64 x 128 in place of the mid kernels,
+// the generic 128 x 256 in place of the symmetric one).
+template <bool GATED, int GPT>
+static hipError_t run_tiled_small_groups(int cfg, const uint16_t *A, const uint32_t *W,
+                                         const uint16_t *S, const uint16_t *D, uint16_t *C, int M,
+                                         int N, int K, int g, bool fuse_delta, hipStream_t st)
+{
+    const bool dl = D && fuse_delta;
+    if (cfg != 2)
+        return dl ? run_tiled<4, 2, true, GATED, GPT>(A, W, S, D, C, M, N, K, g, st)
+                  : run_tiled<4, 2, false, GATED, GPT>(A, W, S, nullptr, C, M, N, K, g, st);
+    return dl ? run_tiled<8, 4, true, GATED, GPT>(A, W, S, D, C, M, N, K, g, st)
+              : run_tiled<8, 4, false, GATED, GPT>(A, W, S, nullptr, C, M, N, K, g, st);
 }
 
 // Configuration for M >= MID_MIN_M: 0 = mid kernel (64 x 64 tiles),
@@ -532,6 +563,10 @@ static hipError_t run_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W, c
                                 const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                                 bool fuse_delta, hipStream_t st)
 {
+    if (g < KTILE)
+        return KTILE / g == 2
+                   ? run_tiled_small_groups<GATED, 2>(cfg, A, W, S, D, C, M, N, K, g, fuse_delta, st)
+                   : run_tiled_small_groups<GATED, 4>(cfg, A, W, S, D, C, M, N, K, g, fuse_delta, st);
     const bool dl = D && fuse_delta;
     if (cfg == 0) return launch_w4a16_mid(A, W, S, D, C, M, N, K, g, fuse_delta, st, GATED);
     if (cfg == 1) {

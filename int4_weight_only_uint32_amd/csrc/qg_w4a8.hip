@@ -39,7 +39,10 @@ namespace qg {
 // its use would wait for every load issued before it.  DELTA: the group
 // deltas ride in the ring beside the scales, and two more MFMAs per 16-row
 // tile and k-tile sum the tile's activations per row.
-template <int NT, int P, bool DEBUG, bool G1, bool DELTA>
+// H2 (groups of 64): the two 64-k MFMA steps of a k-tile are the tile's two
+// groups (the low nibbles hold k 0..63 of the tile, the high ones k 64..127),
+// each product scaled on its own; G1 is then true as well.
+template <int NT, int P, bool DEBUG, bool G1, bool DELTA, bool H2 = false>
 __global__ __launch_bounds__(256, 2) void w4a8_kernel(
     const int8_t *__restrict__ Aq, const float *__restrict__ a_scale,
     const uint4v *__restrict__ Wall, const uint16_t *__restrict__ Sall,
@@ -128,7 +131,8 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
         // register ring: activations, codes, group scales (32-bit pair holding
         // this lane's column, half c & 1)
         uint4v ra[P][2], rw[P][NT];
-        uint32_t rs[P][NT], rd[P][NT];
+        constexpr int GQ = H2 ? 2 : 1;               // groups per k-tile
+        uint32_t rs[P][NT][GQ], rd[P][NT][GQ];
         auto load = [&](int kt, int sl) {
             const int k = kt < KT ? kt : KT - 1;
             ra[sl][0] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off, k * KTILE, 0));
@@ -139,10 +143,16 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
                                                            w_rs, (t * KT * 64 + lane) * 16, k * 1024, 0));
             const int so = ((k * KTILE) / g) * N * 2;   // the group's scale row, bytes
 #pragma unroll
-            for (int t = 0; t < NT; ++t) rs[sl][t] = __builtin_amdgcn_raw_buffer_load_b32(s_rs, s_off + 32 * t, so, 0);
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int q = 0; q < GQ; ++q)
+                    rs[sl][t][q] = __builtin_amdgcn_raw_buffer_load_b32(s_rs, s_off + 32 * t, so + q * N * 2, 0);
             if (DELTA) {
 #pragma unroll
-                for (int t = 0; t < NT; ++t) rd[sl][t] = __builtin_amdgcn_raw_buffer_load_b32(d_rs, s_off + 32 * t, so, 0);
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int q = 0; q < GQ; ++q)
+                        rd[sl][t][q] = __builtin_amdgcn_raw_buffer_load_b32(d_rs, s_off + 32 * t, so + q * N * 2, 0);
             }
         };
 
@@ -150,16 +160,20 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
             const int st = kt & 1;
             store_a(st, ra[sl]);
             CodeOpsI8 b[NT];
-            float sv[NT], dv[NT];
+            float sv[NT], dv[NT], sv2[NT], dv2[NT];   // (sv2, dv2: H2's second group)
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 b[t] = split_codes_i8(rw[sl][t]);
-                sv[t] = h2f((uint16_t)(rs[sl][t] >> sh));
-                dv[t] = DELTA ? h2f((uint16_t)(rd[sl][t] >> sh)) : 0.0f;
+                sv[t] = h2f((uint16_t)(rs[sl][t][0] >> sh));
+                dv[t] = DELTA ? h2f((uint16_t)(rd[sl][t][0] >> sh)) : 0.0f;
+                sv2[t] = H2 ? h2f((uint16_t)(rs[sl][t][GQ - 1] >> sh)) : 0.0f;
+                dv2[t] = H2 && DELTA ? h2f((uint16_t)(rd[sl][t][GQ - 1] >> sh)) : 0.0f;
                 pin(b[t].op[0]);
                 pin(b[t].op[1]);
                 pin(sv[t]);
                 if (DELTA) pin(dv[t]);
+                if (H2) pin(sv2[t]);
+                if (H2 && DELTA) pin(dv2[t]);
             }
             load(kt + P, sl);
             debug_stage_sync();
@@ -170,6 +184,46 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
                 const int row = 16 * mt + c;
                 alo[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 0, kq)]);
                 ahi[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 1, kq)]);
+            }
+            if (H2) {
+                // two groups per k-tile: products and activation sums per 64-k step
+                const int4v z4 = {0, 0, 0, 0};
+                const int4v ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+                int4v qs0[MT], qs1[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    qs0[mt] = DELTA ? mfma_i8(alo[mt], ones, z4) : z4;
+                    qs1[mt] = DELTA ? mfma_i8(ahi[mt], ones, z4) : z4;
+                }
+                const int gi = 2 * kt;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const int4v p0 = mfma_i8(alo[mt], b[t].op[0], z4);
+                        const int4v p1 = mfma_i8(ahi[mt], b[t].op[1], z4);
+                        if (DEBUG) {
+                            const int4v q0 = p0 >> 4, q1 = p1 >> 4;   // exact: multiples of 16
+                            accf[mt][t] += sv[t] * __builtin_convertvector(q0, float4v);
+                            accf[mt][t] += sv2[t] * __builtin_convertvector(q1, float4v);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int row = m0 + 16 * mt + 4 * kq + r;
+                                if (row < r1) {
+                                    acc_debug[((size_t)row * G + gi) * N + col0 + 16 * t] = q0[r];
+                                    acc_debug[((size_t)row * G + gi + 1) * N + col0 + 16 * t] = q1[r];
+                                }
+                            }
+                        } else {
+                            accf[mt][t] += (sv[t] * 0.0625f) * __builtin_convertvector(p0, float4v);
+                            accf[mt][t] += (sv2[t] * 0.0625f) * __builtin_convertvector(p1, float4v);
+                        }
+                        if (DELTA) {
+                            accf[mt][t] += dv[t] * __builtin_convertvector(qs0[mt], float4v);
+                            accf[mt][t] += dv2[t] * __builtin_convertvector(qs1[mt], float4v);
+                        }
+                    }
+                return;
             }
             // G1 (one k-tile per group): each tile's group sum starts from a zero
             // MFMA operand, so nothing is reset and nothing stays live across tiles
@@ -260,7 +314,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
     }
 }
 
-template <int NT, int P, bool DEBUG, bool G1, bool DELTA>
+template <int NT, int P, bool DEBUG, bool G1, bool DELTA, bool H2 = false>
 static hipError_t run_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
                            const uint16_t *S, const uint16_t *D, const int32_t *offsets, int E,
                            int M_total, int max_rows, int N, int K, int g, uint16_t *C,
@@ -268,13 +322,13 @@ static hipError_t run_w4a8(const int8_t *Aq, const float *a_scale, const uint32_
 {
     const int NT16 = N / NTILE;
     dim3 grid((unsigned)((NT16 + 4 * NT - 1) / (4 * NT)), (unsigned)((max_rows + 63) / 64), (unsigned)E);
-    hipLaunchKernelGGL((w4a8_kernel<NT, P, DEBUG, G1, DELTA>), grid, dim3(256), 0, st, Aq, a_scale,
+    hipLaunchKernelGGL((w4a8_kernel<NT, P, DEBUG, G1, DELTA, H2>), grid, dim3(256), 0, st, Aq, a_scale,
                        reinterpret_cast<const uint4v *>(W), S, D, offsets, M_total, N, K, g, C,
                        acc_debug);
     return hipGetLastError();
 }
 
-template <bool DEBUG, bool G1>
+template <bool DEBUG, bool G1, bool H2 = false>
 static hipError_t run_w4a8_d(const int8_t *Aq, const float *a_scale, const uint32_t *W,
                              const uint16_t *S, const uint16_t *D, const int32_t *offsets, int E,
                              int M_total, int max_rows, int N, int K, int g, uint16_t *C,
@@ -285,8 +339,8 @@ static hipError_t run_w4a8_d(const int8_t *Aq, const float *a_scale, const uint3
     // With deltas and groups of several k-tiles the group's activation sums
     // stay live across tiles too: a ring of 2 (204 VGPRs) instead of 3, which
     // would spill at two workgroups per CU.
-    return D ? run_w4a8<2, G1 ? 3 : 2, DEBUG, G1, true>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)
-             : run_w4a8<2, 3, DEBUG, G1, false>(Aq, a_scale, W, S, nullptr, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
+    return D ? run_w4a8<2, G1 ? 3 : 2, DEBUG, G1, true, H2>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)
+             : run_w4a8<2, 3, DEBUG, G1, false, H2>(Aq, a_scale, W, S, nullptr, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
 }
 
 // ---- shapes with tails (K or N not a multiple of 128): the packs are padded
@@ -322,6 +376,12 @@ hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W
                        int M_total, int max_rows, int N, int K, int g, uint16_t *C,
                        int32_t *acc_debug, hipStream_t st)
 {
+    if (g == KTILE / 2) {   // groups of 64
+        if (acc_debug)
+            return run_w4a8_d<true, true, true>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
+        return run_w4a8_d<false, true, true>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st);
+    }
+    if (g < KTILE) return hipErrorInvalidValue;   // groups of 32 split a 64-k MFMA step
     const bool g1 = g == KTILE;
     if (acc_debug)
         return g1 ? run_w4a8_d<true, true>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)

@@ -85,7 +85,9 @@ def _w4a16(M=16, N=1024, K=1024, g=128, A=FAKE, W=FAKE, S=FAKE, D=None, C=FAKE, 
     (dict(K=1000, g=384), qg.QG_ERR_WORKSPACE),        # a partial last group
     (dict(M=0), qg.QG_ERR_INVALID_ARG),
     (dict(g=100), qg.QG_ERR_INVALID_ARG),
-    (dict(g=64), qg.QG_ERR_UNSUPPORTED),
+    (dict(g=48, K=1152), qg.QG_ERR_UNSUPPORTED),       # divides K, but not 32, 64 or 128k
+    (dict(g=16), qg.QG_ERR_UNSUPPORTED),
+    (dict(K=1000, g=64), qg.QG_ERR_WORKSPACE),         # groups of 64 with a K tail
     (dict(A=None), qg.QG_ERR_INVALID_ARG),
     (dict(C=None), qg.QG_ERR_INVALID_ARG),
     (dict(A=P(0x10002)), qg.QG_ERR_INVALID_ARG),
@@ -106,6 +108,8 @@ def test_valid_arguments_reach_the_device_check():
     assert b"device" in qg.lib().qg_last_error()
     rc = _w4a16(M=256, g=-1)
     assert rc == qg.QG_ERR_DEVICE
+    for g in (32, 64):                     # groups of 32 and 64 are served
+        assert _w4a16(M=256, g=g) == qg.QG_ERR_DEVICE
 
 
 def test_split_k_workspace_is_required_and_sized():
@@ -145,6 +149,14 @@ def test_w4a8_validation():
     tail_acc[14], tail_acc[15] = P(0x100000), 1 << 30
     assert L.qgemm_w4a8(*tail_acc) == qg.QG_ERR_UNSUPPORTED
     assert L.qgemm_w4a8(*args(D=P(0x10001))) == qg.QG_ERR_INVALID_ARG  # misaligned deltas
+    g32 = args()
+    g32[11] = 32                                                       # splits a 64-k int8 step
+    assert L.qgemm_w4a8(*g32) == qg.QG_ERR_UNSUPPORTED
+    assert b"64" in L.qg_last_error()
+    g64 = args()
+    g64[11] = 64
+    assert L.qgemm_w4a8(*g64) == qg.QG_ERR_DEVICE                      # served
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 64, 1024, 1024, 64, 1) == 0
 
 
 def test_group_sum_correction_validation():
@@ -317,7 +329,7 @@ def test_noalloc_refuses_shapes_beyond_the_scratch():
     # the other host checks come first, as for qgemm_w4a16
     assert L.qgemm_w4a16_noalloc(None, FAKE, FAKE, None, FAKE, 16, 1024, 1024, 128, 0, None) == \
         qg.QG_ERR_INVALID_ARG
-    assert L.qgemm_w4a16_noalloc(FAKE, FAKE, FAKE, None, FAKE, 16, 1024, 1024, 64, 0, None) == \
+    assert L.qgemm_w4a16_noalloc(FAKE, FAKE, FAKE, None, FAKE, 16, 1024, 1024, 16, 0, None) == \
         qg.QG_ERR_UNSUPPORTED
     assert L.qgemm_w4a16_noalloc(FAKE, FAKE, FAKE, None, FAKE, 16, 1024, 1024, 128, 4, None) == \
         qg.QG_ERR_INVALID_ARG

@@ -58,7 +58,8 @@ def _w4a16_both(libs, fn_name, M, K, N, g, asym, signed=False, op=qg.QG_OP_W4A16
 
 # one shape per kernel path: decode (2 and 6 K-splits), skinny, the two mid
 # kernels, 64x128 tiled (fused delta), 128x256 tiled (fused delta and the
-# symmetric hand-ordered kernel), the row split, the separate correction
+# symmetric hand-ordered kernel), the row split, the separate correction,
+# groups of 64 and 32 (decode and generic tiled kernels)
 @pytest.mark.parametrize("M,K,N,g,asym,flags", [
     (16, 5120, 17408, 128, True, 0),
     (4, 17408, 5120, 128, True, 0),
@@ -70,6 +71,9 @@ def _w4a16_both(libs, fn_name, M, K, N, g, asym, signed=False, op=qg.QG_OP_W4A16
     (2048, 1024, 8192, 128, False, 0),
     (4096, 1024, 17408, 128, False, 0),
     (16, 4096, 4096, 128, True, qg.QG_CORR_SEPARATE),
+    (16, 4096, 4096, 64, True, 0),          # groups of 64 and 32
+    (512, 2048, 4096, 32, True, 0),
+    (2048, 1024, 8192, 64, False, 0),
 ])
 def test_w4a16_matches_debug_sync_build(libs, M, K, N, g, asym, flags):
     note(f"debug-sync w4a16 M={M} K={K} N={N} g={g} asym={asym} flags={flags}")
@@ -86,7 +90,7 @@ def test_swiglu_matches_debug_sync_build(libs, M, K, N):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("g,asym", [(128, False), (128, True), (256, False)])
+@pytest.mark.parametrize("g,asym", [(128, False), (128, True), (256, False), (64, True)])
 def test_w4a8_matches_debug_sync_build(libs, g, asym):
     note(f"debug-sync w4a8 8x64 K=2048 N=7168 g={g} asym={asym}")
     c = synth.w4a8_case(8, 64, 2048, 7168, g, stream=96, case_id=g + asym, asym=asym)
