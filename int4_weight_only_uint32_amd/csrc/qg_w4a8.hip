@@ -298,18 +298,47 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
         for (int i = 0; i < P - 1; ++i)
             if (kt + i < KT) step(kt + i, i);
 
+        // C: the 64 x (64 NT) fp16 tile is assembled in LDS (the activation
+        // stages are dead once every wave is past its last step) and written
+        // as whole 16-byte row pieces; a lane's own 16 x 16 results are two
+        // bytes apart in four rows, which as direct stores cost the kernel
+        // ~13 % at the expert batch (all workgroups end together)
+        constexpr int TW = 4 * NT * NTILE;                    // tile width, columns
+        static_assert(64 * TW * 2 <= (int)sizeof(As), "the C tile fits in the A stages");
+        uint16_t *ct = reinterpret_cast<uint16_t *>(&As[0][0]);
+        __syncthreads();
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + 16 * mt + 4 * kq + r;
-                if (row >= r1) continue;
-                const float as = a_scale[row];
+                const int rl = 16 * mt + 4 * kq + r, row = m0 + rl;
+                const float as = row < r1 ? a_scale[row] : 0.0f;
 #pragma unroll
-                for (int t = 0; t < NT; ++t) C[(size_t)row * N + col0 + 16 * t] = f2h(as * accf[mt][t][r]);
+                for (int t = 0; t < NT; ++t)
+                    ct[rl * TW + wave * NT * NTILE + 16 * t + c] = f2h(as * accf[mt][t][r]);
             }
+        __syncthreads();
+        if ((reinterpret_cast<uintptr_t>(C) & 15) == 0) {
+            constexpr int PPR = TW * 2 / 16;                  // 16-byte pieces per row
+            const int c0 = blockIdx.x * TW;
+#pragma unroll
+            for (int j = 0; j < 64 * PPR / 256; ++j) {
+                const int idx = tid + 256 * j, rl = idx / PPR, pc = idx % PPR;
+                const int row = m0 + rl;
+                if (row < r1)
+                    *reinterpret_cast<uint4v *>(C + (size_t)row * N + c0 + 8 * pc) =
+                        *reinterpret_cast<const uint4v *>(ct + rl * TW + 8 * pc);
+            }
+        } else {
+            // C only 2-byte aligned: the same values, two bytes at a time
+            const int c0 = blockIdx.x * TW;
+            for (int idx = tid; idx < 64 * TW; idx += 256) {
+                const int rl = idx / TW, cc = idx % TW, row = m0 + rl;
+                if (row < r1) C[(size_t)row * N + c0 + cc] = ct[idx];
+            }
+        }
         // the next row block restarts the LDS buffers at stage 0: every wave must
-        // be done reading this block's last stage first
+        // be done reading the C tile first
         __syncthreads();
     }
 }
@@ -339,7 +368,7 @@ static hipError_t run_w4a8_d(const int8_t *Aq, const float *a_scale, const uint3
     // With deltas and groups of several k-tiles the group's activation sums
     // stay live across tiles too: a ring of 2 (204 VGPRs) instead of 3, which
     // would spill at two workgroups per CU.
-    return D ? run_w4a8<2, G1 ? 3 : 2, DEBUG, G1, true, H2>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)
+    return D ? run_w4a8<2, G1 && !H2 ? 3 : 2, DEBUG, G1, true, H2>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)
              : run_w4a8<2, 3, DEBUG, G1, false, H2>(Aq, a_scale, W, S, nullptr, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
 }
 

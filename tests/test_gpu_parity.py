@@ -493,6 +493,25 @@ def test_w4a8_understated_row_bound(max_rows):
     assert elementwise_guard(got, ref) <= 0
 
 
+def test_w4a8_output_only_two_byte_aligned():
+    """C may be any 2-byte aligned pointer: a C that is not 16-byte aligned
+    (a view two bytes into a buffer) gets the same bits as an aligned one
+    (the kernel writes whole 16-byte row pieces only when it can)."""
+    c = synth.w4a8_case(3, 0, 1024, 384, 128, stream=85, case_id=8, rows=[70, 5, 64])
+    note("w4a8 output at a 2-byte offset")
+    W, S, _ = _pack_w4a8(c)
+    mr = int(np.max(np.diff(c.offsets)))
+    A_q, a_sc, off = dev(c.Aq), dev(c.a_scale), dev(c.offsets)
+    C = qg.w4a8(A_q, a_sc, W, S, off, c.E, mr, c.N, c.g)
+    buf = torch.full((c.M_total * c.N + 8,), float("nan"), dtype=torch.float16, device="cuda")
+    C2 = buf[1:1 + c.M_total * c.N].view(c.M_total, c.N)
+    assert C2.data_ptr() % 16 == 2
+    qg.w4a8(A_q, a_sc, W, S, off, c.E, mr, c.N, c.g, C=C2)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2)
+    assert torch.isnan(buf[0]) and torch.isnan(buf[1 + c.M_total * c.N:]).all()
+
+
 # The 8-wave mid-batch kernel (K split between two groups of waves inside the
 # workgroup; taken when (N/128) * ceil(M/64) >= 256): every group form, both
 # weight kinds, k-tile counts that split unevenly (9: 5 + 4; 10 with groups
