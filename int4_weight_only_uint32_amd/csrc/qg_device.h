@@ -105,8 +105,14 @@ __device__ inline unsigned swap_mid_bytes(unsigned x)
 }
 
 // The gated activation of a gate/up pair, silu(g) * u with silu(x) = x / (1 +
-// e^-x), in fp32 (the device library's expf).
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __builtin_expf(-g)) * u; }
+// e^-x), in fp32: the hardware exponential (__expf) and reciprocal, each a few
+// ulps of fp32 -- far inside the one fp16 rounding of the result, and 3-6 %
+// of a prefill-size gated GEMM faster than expf and an IEEE division.  For
+// g -> -inf, e^-g overflows to inf and the reciprocal gives 0 (silu -> 0).
+__device__ inline float silu_mul(float g, float u)
+{
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // Gate/up pairs in the GEMM kernels (GATED): the pair is one packed [K, 2Nh]
 // weight, gate columns first.  A kernel runs over the pair's 2Nh columns in a

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
                 for (int r = 0; r < 4; ++r) {
                     const int row = 4 * kq + r;
                     const float gv = v[0][r], u = xch[wave * 256 + r * 64 + lane];
-                    if (row < M) C[(size_t)row * Nh + col0] = f2h(gv / (1.0f + __builtin_expf(-gv)) * u);
+                    if (row < M) C[(size_t)row * Nh + col0] = f2h(silu_mul(gv, u));
                 }
             return;
         }
