@@ -115,7 +115,10 @@ const char *qg_last_error(void);
  * the packed weight holds K_padded * N_padded / 8 uint32, scale_out and
  * delta_out are [groups, N_padded] fp16.  K_padded = K rounded up to a whole
  * group (to 128 when group_size is K, -1, 32 or 64), N_padded = N rounded up to 128,
- * groups = ceil(K / group_size) (1 per column).  Equal to K, N, K/g for shapes
+ * groups = K_padded / group_size (1 per column): ceil(K / group_size), except
+ * that groups of 32 or 64 may add whole groups past K (zero scale and delta in
+ * the pack; the input scale and zero keep ceil(K / group_size) rows).  Equal
+ * to K, N, K/g for shapes
  * without tails.  Any output pointer may be NULL.  Returns a QG_* status.  */
 int qg_padded_shape(int K, int N, int group_size, int *K_padded, int *N_padded, int *groups);
 
@@ -128,18 +131,19 @@ size_t qg_workspace_bytes(int op, int M, int N, int K, int group_size,
  *      [HyperQwen] negative group-scale section) ----
  * q         [K,N] uint8, one code (0..15) per byte; larger values are an
  *           error the kernel cannot report and give unspecified codes.
- * scale     [G,N] fp16, G = ceil(K / group_size) (qg_padded_shape).
- * zero      [G,N] fp16, or NULL for a symmetric weight.
+ * scale     [ceil(K / group_size), N] fp16.
+ * zero      [ceil(K / group_size), N] fp16, or NULL for a symmetric weight.
  * flags     QG_PACK_FOLD_NEG_SCALES: for a symmetric weight, every (g,n) with
  *           scale < 0 (strictly; -0.0 is left alone) gets scale -> -scale and
  *           codes v -> min(16 - v, 15) over that group.
  * w_packed  [K_padded*N_padded/8] uint32 out, in this library's MFMA-operand
  *           tile order (private layout; the only consumers are the GEMMs);
  *           padding codes are 8.
- * scale_out [G,N_padded] fp16 out: the (folded) scale, 0 in padded columns.
- *           May alias `scale` when N % 128 == 0.
- * delta_out [G,N_padded] fp16 out, required iff zero != NULL (0 in padded
- *           columns):
+ * scale_out [groups,N_padded] fp16 out (groups from qg_padded_shape): the
+ *           (folded) scale, 0 in padded columns and padded groups.  May
+ *           alias `scale` when N % 128 == 0 and groups == ceil(K / g).
+ * delta_out [groups,N_padded] fp16 out, required iff zero != NULL (0 in
+ *           padded columns and groups):
  *           delta = round_to_nearest_even_fp16(zero + 8*scale), with the
  *           pre-fold scale and the sum formed exactly.
  * Runs one or two kernels on `stream`. No workspace.                        */

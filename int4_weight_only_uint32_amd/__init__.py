@@ -172,7 +172,7 @@ def pack_int4_weights(q, scale, zero, K, N, group_size, flags, w_packed, scale_o
     Kp, Np, G = padded_shape(K, N, group_size)
     _need(q, K * N, "q")
     for t, nm in ((scale, "scale"), (zero, "zero")):
-        _need(t, G * N, nm)
+        _need(t, _groups(K, group_size) * N, nm)
     _need(w_packed, Kp * Np // 8, "w_packed")
     for t, nm in ((scale_out, "scale_out"), (delta_out, "delta_out")):
         _need(t, G * Np, nm)

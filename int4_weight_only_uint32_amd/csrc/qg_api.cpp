@@ -345,9 +345,14 @@ int pack_int4_weights(const uint8_t *q, const uint16_t *scale, const uint16_t *z
         return fail(QG_ERR_INVALID_ARG, "pack_int4_weights: misaligned pointer");
     if (flags & ~QG_PACK_FOLD_NEG_SCALES)
         return fail(QG_ERR_INVALID_ARG, "pack_int4_weights: unknown flags 0x%x", flags);
-    if (N % 128 != 0 && (const void *)scale_out == (const void *)scale)
-        return fail(QG_ERR_INVALID_ARG,
-                    "pack_int4_weights: scale_out may alias scale only when N %% 128 == 0");
+    if ((const void *)scale_out == (const void *)scale) {
+        int Kp, Np, gp;
+        qg::padded_shape(K, N, g, &Kp, &Np, &gp);
+        if (Np != N || Kp / gp != (K + g - 1) / g)
+            return fail(QG_ERR_INVALID_ARG,
+                        "pack_int4_weights: scale_out may alias scale only when the padded "
+                        "shape adds no columns and no groups");
+    }
     if ((rc = check_device())) return rc;
     hipError_t e = qg::launch_pack(q, scale, zero, K, N, g, (flags & QG_PACK_FOLD_NEG_SCALES) != 0,
                                    w_packed, scale_out, zero ? delta_out : nullptr,

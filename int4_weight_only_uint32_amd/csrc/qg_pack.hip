@@ -86,16 +86,18 @@ __global__ void pack_codes_kernel(const uint8_t *__restrict__ q, const uint16_t 
 }
 
 // One thread per (group, column) of the padded [G, Np] outputs: folded scale
-// and delta; 0 in the columns past N.
+// and delta; 0 in the columns past N and in the groups past the Gin groups of
+// the input (groups of 32 or 64 with K padded to a multiple of 128 can add
+// whole groups that hold no k < K).
 __global__ void pack_scales_kernel(const uint16_t *__restrict__ s, const uint16_t *__restrict__ z,
-                                   int N, int Np, int fold, uint16_t *s_out,
+                                   int N, int Np, int Gin, int fold, uint16_t *s_out,
                                    uint16_t *__restrict__ d_out, size_t total)
 {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total) return;
     const size_t gi = i / Np;
     const int n = (int)(i % Np);
-    if (n >= N) {
+    if (n >= N || gi >= (size_t)Gin) {
         if (z) d_out[i] = 0;
         s_out[i] = 0;
         return;
@@ -133,8 +135,9 @@ hipError_t launch_pack(const uint8_t *q, const uint16_t *s, const uint16_t *z, i
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     size_t gt = (size_t)(Kp / gp) * Np;
+    const int gin = (K + g - 1) / g;          // groups the input scale rows hold
     hipLaunchKernelGGL(pack_scales_kernel, dim3((unsigned)((gt + bs - 1) / bs)), dim3(bs), 0, st,
-                       s, z, N, Np, f, s_out, d_out, gt);
+                       s, z, N, Np, gin, f, s_out, d_out, gt);
     return hipGetLastError();
 }
 

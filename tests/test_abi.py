@@ -128,6 +128,14 @@ def test_pack_validation():
     # N tail: the padded scale_out cannot alias scale
     assert L.pack_int4_weights(FAKE, FAKE, None, 1024, 1000, 128, 1, FAKE, FAKE, None, None) == qg.QG_ERR_INVALID_ARG
     assert b"alias" in L.qg_last_error()
+    # groups of 64 over K = 1025: the pack holds 18 groups (K padded to 1152),
+    # the input scale 17 rows -- scale_out cannot alias it either
+    assert L.pack_int4_weights(FAKE, FAKE, None, 1025, 1024, 64, 1, FAKE, FAKE, None, None) == qg.QG_ERR_INVALID_ARG
+    assert b"alias" in L.qg_last_error()
+    kp, np_, gg = qg.padded_shape(1025, 1024, 64)
+    assert (kp, np_, gg) == (1152, 1024, 18)
+    assert qg.padded_shape(1025, 1024, 32) == (1152, 1024, 36)
+    assert L.pack_int4_weights(FAKE, FAKE, None, 1024, 1024, 64, 1, FAKE, FAKE, None, None) == qg.QG_ERR_DEVICE
     assert L.pack_int4_weights(FAKE, FAKE, None, 1024, 1000, 100, 1, FAKE, P(0x20000), None, None) == qg.QG_ERR_INVALID_ARG
     assert L.pack_int4_weights(FAKE, FAKE, None, 1024, 1024, 128, 4, FAKE, FAKE, None, None) == qg.QG_ERR_INVALID_ARG
     assert L.pack_int4_weights(None, FAKE, None, 1024, 1024, 128, 1, FAKE, FAKE, None, None) == qg.QG_ERR_INVALID_ARG

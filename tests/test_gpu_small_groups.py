@@ -78,11 +78,12 @@ def test_w4a16_small_groups_separate_correction(g):
     _w4a16(16, 4096, 4096, g, True, flags=qg.QG_CORR_SEPARATE, case_id=2000 + g)
 
 
-@pytest.mark.parametrize("g,M", [(64, 16), (32, 300)])
-def test_w4a16_small_groups_k_and_n_tails(g, M):
-    """K = 1000 (padded to 1024: whole groups of 64 or 32 past K hold code 8
-    and zero activations) and N = 1000 (padded to 1024, cropped)."""
-    _w4a16(M, 1000, 1000, g, True, case_id=3000 + g)
+@pytest.mark.parametrize("g,M,K", [(64, 16, 1000), (32, 300, 1000), (64, 16, 1025), (32, 100, 1025)])
+def test_w4a16_small_groups_k_and_n_tails(g, M, K):
+    """K = 1000 (padded to 1024) or 1025 (padded to 1152, which adds whole
+    groups past the input's ceil(K/g): the pack gives them zero scale and
+    delta) and N = 1000 (padded to 1024, cropped)."""
+    _w4a16(M, K, 1000, g, True, case_id=3000 + g + K)
 
 
 @pytest.mark.parametrize("g", [64, 32])
