@@ -31,7 +31,10 @@
 
 namespace qg {
 
-template <int MT, int NT, int P, int NWMAX, bool DELTA, bool GATED>
+// GPT: weight groups per 128-k tile (1 for g >= 128, 2 for g = 64, 4 for
+// g = 32), as in the decode kernel: each 32-k MFMA step's products are scaled
+// with the scale, delta and activation sum of the step's own group.
+template <int MT, int NT, int P, int NWMAX, bool DELTA, bool GATED, int GPT = 1>
 __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g, int nw)
@@ -93,10 +96,10 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
     // Scales and deltas are fetched as the aligned 32-bit pair holding this
     // lane's column (half c&1 of it): 16-bit ring registers get packed in
     // pairs by the compiler, and the packing waits for loads just issued.
-    uint32_t rs[P][NT], rd[P][NT];
+    uint32_t rs[P][NT][GPT], rd[P][NT][GPT];
     const int sh = 16 * (c & 1);
-    auto load = [&](int kt, uint4v (&a)[MT * 4], uint4v (&w)[NT], uint32_t (&sv)[NT],
-                    uint32_t (&dv)[NT]) {
+    auto load = [&](int kt, uint4v (&a)[MT * 4], uint4v (&w)[NT], uint32_t (&sv)[NT][GPT],
+                    uint32_t (&dv)[NT][GPT]) {
 #pragma unroll
         for (int j = 0; j < MT * 4; ++j) a[j] = asrc[j][kt * (KTILE / 8)];
 #pragma unroll
@@ -104,11 +107,15 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
         const int gi = (kt * KTILE) / g;
         const uint32_t *srow = reinterpret_cast<const uint32_t *>(S + (size_t)gi * N + (col0 & ~1));
 #pragma unroll
-        for (int t = 0; t < NT; ++t) sv[t] = srow[8 * trel(t)];
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int q = 0; q < GPT; ++q) sv[t][q] = srow[(size_t)q * (N / 2) + 8 * trel(t)];
         if (DELTA) {
             const uint32_t *drow = reinterpret_cast<const uint32_t *>(D + (size_t)gi * N + (col0 & ~1));
 #pragma unroll
-            for (int t = 0; t < NT; ++t) dv[t] = drow[8 * trel(t)];
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int q = 0; q < GPT; ++q) dv[t][q] = drow[(size_t)q * (N / 2) + 8 * trel(t)];
         }
     };
     // Consuming a slot happens in two halves: `stage` moves the slot's
@@ -118,18 +125,21 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
     // flight.
     struct Staged {
         CodeOps ops[NT];
-        float s[NT], d[NT];
+        float s[NT][GPT], d[NT][GPT];
     };
-    auto stage = [&](const uint4v (&ar)[MT * 4], const uint4v (&w)[NT], const uint32_t (&sv)[NT],
-                     const uint32_t (&dv)[NT], Staged &st) {
+    auto stage = [&](const uint4v (&ar)[MT * 4], const uint4v (&w)[NT], const uint32_t (&sv)[NT][GPT],
+                     const uint32_t (&dv)[NT][GPT], Staged &st) {
         debug_stage_sync();
 #pragma unroll
         for (int j = 0; j < MT * 4; ++j) *reinterpret_cast<uint4v *>(scratch + adst[j]) = ar[j];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             st.ops[t] = split_codes(w[t]);
-            st.s[t] = h2f((uint16_t)(sv[t] >> sh));
-            st.d[t] = DELTA ? h2f((uint16_t)(dv[t] >> sh)) : 0.f;
+#pragma unroll
+            for (int q = 0; q < GPT; ++q) {
+                st.s[t][q] = h2f((uint16_t)(sv[t][q] >> sh));
+                st.d[t][q] = DELTA ? h2f((uint16_t)(dv[t][q] >> sh)) : 0.f;
+            }
         }
     };
     auto finish = [&](const Staged &st) {
@@ -141,6 +151,39 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
             for (int o = 0; o < 4; ++o)
                 a[mt][o] = *reinterpret_cast<const half8 *>(scratch + r * KTILE + 8 * ((4 * o + kq) ^ c));
         }
+        if (GPT > 1) {
+            // groups of 64 or 32: per group, its steps' products and sums
+            constexpr int SPG = 4 / GPT;                  // MFMA steps per group
+            float4v asg[MT][GPT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int q = 0; q < GPT; ++q) {
+                    asg[mt][q] = mfma_f16(a[mt][SPG * q], ones, fzero);
+                    if (SPG == 2) asg[mt][q] = mfma_f16(a[mt][SPG * q + 1], ones, asg[mt][q]);
+                }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const half8 op[4] = {st.ops[t].lo[0], st.ops[t].lo[1], st.ops[t].hi[0], st.ops[t].hi[1]};
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int q = 0; q < GPT; ++q) {
+                        float4v x = mfma_f16(a[mt][SPG * q], op[SPG * q], fzero);
+                        if (SPG == 2) x = mfma_f16(a[mt][SPG * q + 1], op[SPG * q + 1], x);
+                        const float sq = st.s[t][q];
+                        // steps 0, 1: low nibbles (2^-24 v); 2, 3: high ones (2^-20 v)
+                        const float cx = sq * (SPG * q < 2 ? 0x1p24f : 0x1p20f);
+                        const float c2 = DELTA ? (st.d[t][q] - 8.0f * sq) : (-8.0f * sq);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float v = __builtin_fmaf(cx, x[r], acc[mt][t][r]);
+                            acc[mt][t][r] = __builtin_fmaf(c2, asg[mt][q][r], v);
+                        }
+                    }
+            }
+            return;
+        }
         float4v as[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -151,9 +194,9 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float s = st.s[t];
+            const float s = st.s[t][0];
             const float c1 = s * 0x1p20f, c16 = s * 0x1p24f;
-            const float c2 = DELTA ? (st.d[t] - 8.0f * s) : (-8.0f * s);
+            const float c2 = DELTA ? (st.d[t][0] - 8.0f * s) : (-8.0f * s);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 float4v xl = mfma_f16(a[mt][0], st.ops[t].lo[0], fzero);
@@ -235,7 +278,7 @@ __global__ __launch_bounds__(NWMAX * 64) void w4a16_skinny_kernel(
     }
 }
 
-template <int MT, int NT, int P, int NWMAX, bool DELTA, bool GATED>
+template <int MT, int NT, int P, int NWMAX, bool DELTA, bool GATED, int GPT>
 static hipError_t run_skinny(const SkinnyCfg &cf, const uint16_t *A, const uint32_t *W,
                              const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
                              int K, int g, hipStream_t st)
@@ -246,7 +289,7 @@ static hipError_t run_skinny(const SkinnyCfg &cf, const uint16_t *A, const uint3
     const size_t lds = ring > sum ? ring : sum;
     if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
     if (cf.nw < 1 || cf.nw > NWMAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((w4a16_skinny_kernel<MT, NT, P, NWMAX, DELTA, GATED>), grid, dim3(64 * cf.nw), lds,
+    hipLaunchKernelGGL((w4a16_skinny_kernel<MT, NT, P, NWMAX, DELTA, GATED, GPT>), grid, dim3(64 * cf.nw), lds,
                        st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g, cf.nw);
     return hipGetLastError();
 }
@@ -281,18 +324,30 @@ size_t w4a16_workspace_bytes(int M, int N, int K, int g)
     return decode_workspace_bytes(M, N, K, g);
 }
 
+template <bool DELTA, bool GATED, int GPT>
+static hipError_t dispatch_skinny_g(const SkinnyCfg &c, const uint16_t *A, const uint32_t *W,
+                                    const uint16_t *S, const uint16_t *D, uint16_t *C, int M,
+                                    int N, int K, int g, hipStream_t st)
+{
+    if (c.S != 1) return hipErrorInvalidConfiguration;
+#define QG_SK(MT_, NT_, P_, NWMAX_)                                                             \
+    if (c.MT == MT_ && c.NT == NT_ && c.P == P_ && c.nw <= NWMAX_)                              \
+        return run_skinny<MT_, NT_, P_, NWMAX_, DELTA, GATED, GPT>(c, A, W, S, D, C, M, N, K, g, st);
+    QG_SK(1, 2, 2, 8) QG_SK(2, 4, 2, 4) QG_SK(4, 2, 2, 4)
+#undef QG_SK
+    return hipErrorInvalidConfiguration;
+}
+
+// groups per k-tile: 1 (g >= 128), 2 (g = 64), 4 (g = 32)
 template <bool DELTA, bool GATED>
 static hipError_t dispatch_skinny(const SkinnyCfg &c, const uint16_t *A, const uint32_t *W,
                                   const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
                                   int K, int g, hipStream_t st)
 {
-    if (c.S != 1) return hipErrorInvalidConfiguration;
-#define QG_SK(MT_, NT_, P_, NWMAX_)                                                             \
-    if (c.MT == MT_ && c.NT == NT_ && c.P == P_ && c.nw <= NWMAX_)                              \
-        return run_skinny<MT_, NT_, P_, NWMAX_, DELTA, GATED>(c, A, W, S, D, C, M, N, K, g, st);
-    QG_SK(1, 2, 2, 8) QG_SK(2, 4, 2, 4) QG_SK(4, 2, 2, 4)
-#undef QG_SK
-    return hipErrorInvalidConfiguration;
+    if (g >= KTILE) return dispatch_skinny_g<DELTA, GATED, 1>(c, A, W, S, D, C, M, N, K, g, st);
+    if (g == KTILE / 2) return dispatch_skinny_g<DELTA, GATED, 2>(c, A, W, S, D, C, M, N, K, g, st);
+    if (g == KTILE / 4) return dispatch_skinny_g<DELTA, GATED, 4>(c, A, W, S, D, C, M, N, K, g, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_w4a16_skinny_cfg(const SkinnyCfg &c, const uint16_t *A, const uint32_t *W,
@@ -313,9 +368,7 @@ hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                         const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                         bool fuse_delta, void *ws, hipStream_t st)
 {
-    // groups of 64 or 32: the decode kernel (M <= 16) or the generic tiled ones
-    if (M >= TILED_MIN_M || (g < KTILE && !use_decode_kernel(M, N, K, g)))
-        return launch_w4a16_tiled(A, W, S, D, C, M, N, K, g, fuse_delta, st);
+    if (M >= TILED_MIN_M) return launch_w4a16_tiled(A, W, S, D, C, M, N, K, g, fuse_delta, st);
     if (use_decode_kernel(M, N, K, g))
         return launch_w4a16_decode(A, W, S, D, C, M, N, K, g, fuse_delta,
                                    decode_workspace_bytes(M, N, K, g) ? decode_splits(N, K, g) : 1, ws,
@@ -343,7 +396,7 @@ void describe_w4a16(int M, int N, int K, int g, bool delta, bool gated, char *bu
     if (gated ? swiglu_uses_decode(M, N, K, g) : (M < TILED_MIN_M && use_decode_kernel(M, N, K, g))) {
         snprintf(buf, n, "%sdecode, %d K-split(s)", gate,
                  decode_workspace_bytes(M, N2, K, g) ? decode_splits(N2, K, g) : 1);
-    } else if (M < TILED_MIN_M && g >= KTILE) {
+    } else if (M < TILED_MIN_M) {
         snprintf(buf, n, "%sskinny", gate);
     } else if (tiled_config(M, N2) == 2 && tiled_row_split(M, N2) < M) {
         const int m1 = tiled_row_split(M, N2);
@@ -466,7 +519,7 @@ hipError_t launch_w4a16_swiglu(const uint16_t *A, const uint32_t *W, const uint1
         if (ns > 1 && !ws) return hipErrorInvalidValue;
         return launch_w4a16_decode(A, W, S, D, H, M, N2, K, g, true, ns, ws, st, true);
     }
-    if (M >= TILED_MIN_M || g < KTILE) return launch_w4a16_tiled(A, W, S, D, H, M, N2, K, g, true, st, true);
+    if (M >= TILED_MIN_M) return launch_w4a16_tiled(A, W, S, D, H, M, N2, K, g, true, st, true);
     return launch_w4a16_skinny_cfg(skinny_config(M, N2, K), A, W, S, D, H, M, N2, K, g, true,
                                    nullptr, st, true);
 }

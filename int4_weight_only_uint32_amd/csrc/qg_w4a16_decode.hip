@@ -382,7 +382,6 @@ int decode_splits(int N, int K, int g)
 bool use_decode_kernel(int M, int N, int K, int g)
 {
     if (M > 16 || N % decode::COLS) return false;
-    if (g < KTILE) return true;     // groups of 64 or 32: the only M <= 16 kernel that has them
     const int ns = decode_splits(N, K, g);
     if (ns <= 2) return true;
     const long skinny_wgs = N / 32;

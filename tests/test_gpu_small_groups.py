@@ -2,9 +2,9 @@
 
 Every 32-k MFMA step of a packed 128-k tile lies inside one such group (the
 packed layout gives k-steps 0, 1 to the low nibbles and 2, 3 to the high
-ones), so the decode kernel scales each step's products with its own group's
-scale and delta, and the generic tiled kernels dequantize each step with its
-group's scale; the grouped W4A8 kernel takes groups of 64 (one 64-k int8
+ones), so the decode and skinny kernels scale each step's products with its
+own group's scale and delta, and the generic tiled kernels dequantize each
+step with its group's scale; the grouped W4A8 kernel takes groups of 64 (one 64-k int8
 MFMA step each).  Checked against the oracle, which applies W = q s + z per
 group of g consecutive k ("Marlin INT4 on Ada - how it works", "The core
 mismatch: symmetric vs asymmetric"), to the W4A16 bar (relative Frobenius
@@ -56,12 +56,14 @@ def _w4a16(M, K, N, g, asym, flags=0, case_id=0):
     return err
 
 
-# decode kernel (M <= 16, with and without K splits), the generic 64x128
-# tiles (17 <= M and mid-size batches), the generic 128x256 tiles and the
+# decode kernel (M <= 16, with and without K splits), the skinny kernel
+# (narrow decode shapes, 17 <= M <= 80, every configuration), the generic
+# 64x128 tiles (mid-size batches), the generic 128x256 tiles and the
 # prefill-size row split
 @pytest.mark.parametrize("g", [64, 32])
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (16, 5120, 8192), (16, 17408, 5120),
-                                   (33, 2048, 1024), (256, 2048, 4096), (2048, 1024, 8192),
+                                   (8, 1024, 1024), (33, 2048, 1024), (64, 4096, 2048),
+                                   (80, 1024, 4096), (256, 2048, 4096), (2048, 1024, 8192),
                                    (4096, 1024, 17408)])
 def test_w4a16_small_groups_asym(M, K, N, g):
     _w4a16(M, K, N, g, True, case_id=M + g)
@@ -87,7 +89,7 @@ def test_w4a16_small_groups_k_and_n_tails(g, M, K):
 
 
 @pytest.mark.parametrize("g", [64, 32])
-@pytest.mark.parametrize("M,K,N", [(16, 4096, 4096), (512, 1024, 2048)])
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 4096), (40, 2048, 1024), (512, 1024, 2048)])
 def test_swiglu_small_groups(M, K, N, g):
     c = synth.w4a16_case(M, K, 2 * N, g, asym=True, stream=98, case_id=4000 + M + g,
                          zero_points="awq")
