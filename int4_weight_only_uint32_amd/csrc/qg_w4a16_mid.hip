@@ -24,8 +24,10 @@ namespace qg {
 // per-k-tile scaling and one group over all of K (g = K) almost none (the
 // loop is issue-bound: 24 MFMAs against ~110 VALU instructions per k-tile and
 // wave with per-k-tile scaling).  GK selects the form: 1 = every k-tile is
-// scaled on its own (any g), 2 = groups of two k-tiles (g = 256), 0 = one
-// group (g = K).  Pipeline: MID_STAGES k-tiles in flight.
+// scaled on its own (g = 128), 3 = likewise for any other g, 2 = groups of
+// two k-tiles (g = 256), 0 = one group (g = K); the forms also fix how a
+// k-tile finds its group row (none, the k-tile itself, a shift; a division
+// only for form 3).  Pipeline: MID_STAGES k-tiles in flight.
 // A k-tile of A (64 rows, 16 KB) goes straight from global memory to one of
 // MID_STAGES LDS buffers (wave w fills rows 16w .. 16w + 15; 16-byte chunk ch
 // of row r lands at position ch ^ (r % 16)); codes, scales and deltas of the
@@ -33,6 +35,13 @@ namespace qg {
 // with a wait that leaves the later k-tiles' loads in flight and one barrier,
 // after which the slot used by the previous k-tile is refilled.
 constexpr int MID_STAGES = 4;
+
+// The weight group of k-tile k in form GK (see above).
+template <int GK>
+__device__ inline int mid_group(int k, int g)
+{
+    return GK == 0 ? 0 : GK == 1 ? k : GK == 2 ? (k >> 1) : (k * KTILE) / g;
+}
 
 template <int SG, bool DELTA, int GK, bool GATED>
 __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
@@ -112,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
             const int wo = (rel(t) * KT + k) * 1024;
             rw[slot][t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off, wo, 0));
         }
-        const int gb = ((k * KTILE) / g) * N * 2;      // byte offset of this k-tile's group row
+        const int gb = mid_group<GK>(k, g) * N * 2;    // byte offset of this k-tile's group row
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
             const __amdgpu_buffer_rsrc_t sr = odd(t) ? s_rs1 : s_rs0;
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
         // nothing that reads this slot's registers moves above the wait
         __builtin_amdgcn_sched_barrier(0);
         kt_ = kt;
-        if (GK == 1) {
+        if (GK == 1 || GK == 3) {
             compute(slot, true);
             apply(false);
         } else if (GK == 2) {
@@ -355,7 +364,7 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
             const int wo = (rel(t) * KT + k) * 1024;
             rw[slot][t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off, wo, 0));
         }
-        const int gb = ((k * KTILE) / g) * N * 2;
+        const int gb = mid_group<GK>(k, g) * N * 2;
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
             const __amdgpu_buffer_rsrc_t sr = odd(t) ? s_rs1 : s_rs0;
@@ -463,7 +472,7 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
         // nothing that reads this slot's registers moves above the wait
         __builtin_amdgcn_sched_barrier(0);
         st_ = st;
-        if (GK == 1) {
+        if (GK == 1 || GK == 3) {
             // groups of one k-tile: the previous step's group gets its delta
             // term, this step's group is closed
             if (st > 0 && st - 1 < kn) delta_term((slot - 1) & 1);
@@ -505,7 +514,7 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
     // the last group's delta term (one group over all of K: closed here)
     if (GK == 0) close(0);
     const bool last_pending = GK == 0 ? true : (kn == nsteps && kn > 0);
-    const int last_par = GK == 1 ? ((nsteps - 1) % SG) & 1 : (((nsteps - 1) % SG) >> 1) & 1;
+    const int last_par = GK == 1 || GK == 3 ? ((nsteps - 1) % SG) & 1 : (((nsteps - 1) % SG) >> 1) & 1;
     sync();
     if (last_pending) delta_term(GK == 0 ? 0 : last_par);
 
@@ -566,7 +575,8 @@ static hipError_t run_mid_g(const uint16_t *A, const uint32_t *W, const uint16_t
     static_assert(MID_STAGES % 2 == 0, "k-tile parity must follow the ring slot");
     if (g == K) return run_mid<DELTA, 0, GATED>(A, W, S, D, C, M, N, K, g, st);
     if (g == 2 * KTILE) return run_mid<DELTA, 2, GATED>(A, W, S, D, C, M, N, K, g, st);
-    return run_mid<DELTA, 1, GATED>(A, W, S, D, C, M, N, K, g, st);
+    if (g == KTILE) return run_mid<DELTA, 1, GATED>(A, W, S, D, C, M, N, K, g, st);
+    return run_mid<DELTA, 3, GATED>(A, W, S, D, C, M, N, K, g, st);
 }
 
 template <bool DELTA, int GK, bool GATED>
@@ -597,7 +607,8 @@ static hipError_t run_mid2_g(const uint16_t *A, const uint32_t *W, const uint16_
 {
     if (g == K) return run_mid2<DELTA, 0, GATED>(A, W, S, D, C, M, N, K, g, st);
     if (g == 2 * KTILE) return run_mid2<DELTA, 2, GATED>(A, W, S, D, C, M, N, K, g, st);
-    return run_mid2<DELTA, 1, GATED>(A, W, S, D, C, M, N, K, g, st);
+    if (g == KTILE) return run_mid2<DELTA, 1, GATED>(A, W, S, D, C, M, N, K, g, st);
+    return run_mid2<DELTA, 3, GATED>(A, W, S, D, C, M, N, K, g, st);
 }
 
 // The 8-wave 64 x 128 kernel (K split inside the workgroup) when it still

@@ -192,6 +192,19 @@ def test_w4a16_mid_kernel_short_k(K, g, asym):
     _check_w4a16(c)
 
 
+@pytest.mark.parametrize("g,asym", [(128, True), (256, True), (384, True), (512, False), (1536, True)])
+def test_w4a16_mid2_group_forms(g, asym):
+    # M = 256 on N = 8192 takes the 8-wave mid kernel (K split between two
+    # k-groups inside the workgroup), 12 k-tiles; every way a k-tile finds
+    # its weight group: the k-tile itself (g = 128), a shift (g = 256), a
+    # division (g = 384: groups of three k-tiles, scaled per k-tile; g = 512),
+    # one group over all of K (g = K)
+    M, K, N = 256, 1536, 8192
+    c = synth.w4a16_case(M, K, N, g, asym=asym, signed_scales=not asym, stream=90,
+                         case_id=5000 + g + asym, name="mid2-group-forms")
+    _check_w4a16(c)
+
+
 def test_w4a16_small_asym():
     c = synth.workload("w4a16-small-asym-M16-K1024-N1024-g128")
     _check_w4a16(c)
