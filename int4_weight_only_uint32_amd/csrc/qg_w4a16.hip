@@ -381,7 +381,11 @@ hipError_t launch_w4a16(const uint16_t *A, const uint32_t *W, const uint16_t *S,
 // multiples of 128), in words, for the first-dispatch log line.
 static const char *big_kernel(int M, int N, int K, int g, bool delta)
 {
-    if (g < KTILE) return tiled_config(M, N) == 2 ? "tiled 128x256" : "tiled 64x128";
+    if (g < KTILE) {
+        if (g == KTILE / 2 && tiled_config(M, N) == 0 && use_mid2(M, N, K))
+            return "mid 64x128 (K split in the workgroup)";
+        return tiled_config(M, N) == 2 ? "tiled 128x256" : "tiled 64x128";
+    }
     switch (tiled_config(M, N)) {
     case 0: return use_mid2(M, N, K) ? "mid 64x128 (K split in the workgroup)" : "mid 64x64";
     case 1: return "tiled 64x128";

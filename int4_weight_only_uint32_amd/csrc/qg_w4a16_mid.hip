@@ -40,7 +40,7 @@ constexpr int MID_STAGES = 4;
 template <int GK>
 __device__ inline int mid_group(int k, int g)
 {
-    return GK == 0 ? 0 : GK == 1 ? k : GK == 2 ? (k >> 1) : (k * KTILE) / g;
+    return GK == 0 ? 0 : GK == 1 ? k : GK == 2 ? (k >> 1) : GK == 4 ? 2 * k : (k * KTILE) / g;
 }
 
 template <int SG, bool DELTA, int GK, bool GATED>
@@ -290,11 +290,12 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g)
 {
     constexpr int WM = 4, WN = 2, BM = 64;
-    constexpr int L = 4 + WN + WN + (DELTA ? WN : 0);     // loads per thread and step
+    constexpr int NS = GK == 4 ? 2 : 1;                    // weight groups per k-tile
+    constexpr int L = 4 + WN + NS * WN + (DELTA ? NS * WN : 0);   // loads per thread and step
     static_assert((SG - 2) * L < 64, "vmcnt holds 6 bits");
     static_assert(SG % 4 == 0, "group parities follow the ring slot");
     // LDS: the ring [SG][2 k-groups][BM * KTILE] fp16, then the group sums
-    // shared within a k-group [2 k-groups][2 parities][BM] fp32
+    // shared within a k-group [2 k-groups][2 parities][NS][BM] fp32
     extern __shared__ __attribute__((aligned(16))) _Float16 Asm[];
     float *gx = reinterpret_cast<float *>(Asm + (size_t)SG * 2 * BM * KTILE);
 
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
     const __amdgpu_buffer_rsrc_t d_rs0 = buffer_rsrc(DELTA ? D + pt0 * NTILE : S, DELTA ? ((size_t)(K / g) * N - pt0 * NTILE) * 2 : 4);
     const __amdgpu_buffer_rsrc_t d_rs1 = buffer_rsrc(DELTA ? D + pt1 * NTILE : S, DELTA ? ((size_t)(K / g) * N - pt1 * NTILE) * 2 : 4);
     uint4v rw[SG][WN];
-    uint32_t rs[SG][WN], rd[SG][WN];   // aligned scale / delta pairs (half c & 1)
+    uint32_t rs[SG][WN][NS], rd[SG][WN][NS];   // aligned scale / delta pairs (half c & 1)
     const unsigned w_off = (unsigned)lane * 16u;
     const unsigned s_off = ((unsigned)c >> 1) * 4u;
     // every load of step st (clamped: the count per step is fixed, which the
@@ -368,39 +369,55 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
             const __amdgpu_buffer_rsrc_t sr = odd(t) ? s_rs1 : s_rs0;
-            const int so = gb + 32 * rel(t);
-            rs[slot][t] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_off, so, 0);
+#pragma unroll
+            for (int h = 0; h < NS; ++h) {
+                const int so = gb + h * N * 2 + 32 * rel(t);
+                rs[slot][t][h] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_off, so, 0);
+            }
         }
         if (DELTA) {
 #pragma unroll
             for (int t = 0; t < WN; ++t) {
                 const __amdgpu_buffer_rsrc_t dr = odd(t) ? d_rs1 : d_rs0;
-                const int so = gb + 32 * rel(t);
-                rd[slot][t] = __builtin_amdgcn_raw_buffer_load_b32(dr, s_off, so, 0);
+#pragma unroll
+                for (int h = 0; h < NS; ++h) {
+                    const int so = gb + h * N * 2 + 32 * rel(t);
+                    rd[slot][t][h] = __builtin_amdgcn_raw_buffer_load_b32(dr, s_off, so, 0);
+                }
             }
         }
     };
 
-    float4v acc[WM][WN], xl[WM][WN], xh[WM][WN], asum;
+    // GK == 4 (g = 64): the k-tile's two groups are its low-nibble k-steps
+    // 0, 1 (xl, group sums asum[0]) and its high-nibble k-steps 2, 3 (xh,
+    // asum[1]), each with its own scale and delta
+    float4v acc[WM][WN], xl[WM][WN], xh[WM][WN], asum[NS];
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     const float4v fzero = {0.f, 0.f, 0.f, 0.f};
-    asum = fzero;
+#pragma unroll
+    for (int h = 0; h < NS; ++h) asum[h] = fzero;
 #pragma unroll
     for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
         for (int t = 0; t < WN; ++t) acc[mt][t] = xl[mt][t] = xh[mt][t] = fzero;
     int st_ = 0;   // the step being computed
-    float k16[WN], k1[WN], k2[WN], k2s[WN];   // k2s: k2 of the group whose delta term is pending
+    // k2s: k2 of the group(s) whose delta term is pending
+    float k16[WN], k1[WN], k2[WN][NS], k2s[WN][NS];
 
     auto compute = [&](int slot, bool first) {
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
-            const float sv = h2f((uint16_t)(rs[slot][t] >> sh));
-            const float dv = DELTA ? h2f((uint16_t)(rd[slot][t] >> sh)) : 0.f;
-            k16[t] = sv * 0x1p24f;
-            k1[t] = sv * 0x1p20f;
-            k2[t] = DELTA ? (dv - 8.0f * sv) : (-8.0f * sv);
-            pin(k16[t]); pin(k1[t]); pin(k2[t]);
+            float sv[NS];
+#pragma unroll
+            for (int h = 0; h < NS; ++h) {
+                sv[h] = h2f((uint16_t)(rs[slot][t][h] >> sh));
+                const float dv = DELTA ? h2f((uint16_t)(rd[slot][t][h] >> sh)) : 0.f;
+                k2[t][h] = DELTA ? (dv - 8.0f * sv[h]) : (-8.0f * sv[h]);
+                pin(k2[t][h]);
+            }
+            k16[t] = sv[0] * 0x1p24f;
+            k1[t] = sv[NS - 1] * 0x1p20f;
+            pin(k16[t]); pin(k1[t]);
         }
         // (the refill below goes to the previous step's slot: this slot's
         // code registers stay valid until they are split here)
@@ -418,10 +435,10 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
             for (int o = 0; o < 4; ++o)
                 a[o] = *reinterpret_cast<const half8 *>(as + r * KTILE + 8 * ((4 * o + kq) ^ c));
             if (mt == wn) {   // this wave's share of the group sums
-                asum = mfma_f16(a[0], ones, first ? fzero : asum);
-                asum = mfma_f16(a[1], ones, asum);
-                asum = mfma_f16(a[2], ones, asum);
-                asum = mfma_f16(a[3], ones, asum);
+                asum[0] = mfma_f16(a[0], ones, first ? fzero : asum[0]);
+                asum[0] = mfma_f16(a[1], ones, asum[0]);
+                asum[NS - 1] = mfma_f16(a[2], ones, NS == 2 ? fzero : asum[0]);
+                asum[NS - 1] = mfma_f16(a[3], ones, asum[NS - 1]);
             }
 #pragma unroll
             for (int t = 0; t < WN; ++t) {
@@ -443,20 +460,26 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
                 for (int r = 0; r < 4; ++r)
                     acc[mt][t][r] = __builtin_fmaf(k1[t], xh[mt][t][r], __builtin_fmaf(k16[t], xl[mt][t][r], acc[mt][t][r]));
         if (c == 0)
-            *reinterpret_cast<float4v *>(gx + (kg * 2 + par) * BM + 16 * wn + 4 * kq) = asum;
 #pragma unroll
-        for (int t = 0; t < WN; ++t) k2s[t] = k2[t];
+            for (int h = 0; h < NS; ++h)
+                *reinterpret_cast<float4v *>(gx + ((kg * 2 + par) * NS + h) * BM + 16 * wn + 4 * kq) = asum[h];
+#pragma unroll
+        for (int t = 0; t < WN; ++t)
+#pragma unroll
+            for (int h = 0; h < NS; ++h) k2s[t][h] = k2[t][h];
     };
     // the pending delta term of the group published with parity par
     auto delta_term = [&](int par) {
 #pragma unroll
-        for (int mt = 0; mt < WM; ++mt) {
-            const float4v gs = *reinterpret_cast<const float4v *>(gx + (kg * 2 + par) * BM + 16 * mt + 4 * kq);
+        for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-            for (int t = 0; t < WN; ++t)
+            for (int h = 0; h < NS; ++h) {
+                const float4v gs = *reinterpret_cast<const float4v *>(gx + ((kg * 2 + par) * NS + h) * BM + 16 * mt + 4 * kq);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mt][t][r] = __builtin_fmaf(k2s[t], gs[r], acc[mt][t][r]);
-        }
+                for (int t = 0; t < WN; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[mt][t][r] = __builtin_fmaf(k2s[t][h], gs[r], acc[mt][t][r]);
+            }
     };
     auto sync = [&]() {
         debug_stage_sync();
@@ -472,8 +495,8 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
         // nothing that reads this slot's registers moves above the wait
         __builtin_amdgcn_sched_barrier(0);
         st_ = st;
-        if (GK == 1 || GK == 3) {
-            // groups of one k-tile: the previous step's group gets its delta
+        if (GK == 1 || GK == 3 || GK == 4) {
+            // groups of one k-tile (or two per k-tile): the previous step's group gets its delta
             // term, this step's group is closed
             if (st > 0 && st - 1 < kn) delta_term((slot - 1) & 1);
             compute(slot, true);
@@ -514,7 +537,7 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
     // the last group's delta term (one group over all of K: closed here)
     if (GK == 0) close(0);
     const bool last_pending = GK == 0 ? true : (kn == nsteps && kn > 0);
-    const int last_par = GK == 1 || GK == 3 ? ((nsteps - 1) % SG) & 1 : (((nsteps - 1) % SG) >> 1) & 1;
+    const int last_par = GK == 2 ? (((nsteps - 1) % SG) >> 1) & 1 : ((nsteps - 1) % SG) & 1;
     sync();
     if (last_pending) delta_term(GK == 0 ? 0 : last_par);
 
@@ -584,8 +607,8 @@ static hipError_t run_mid2(const uint16_t *A, const uint32_t *W, const uint16_t 
                            const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                            hipStream_t st)
 {
-    constexpr int SG = MID2_STAGES;
-    const size_t lds = (size_t)SG * 2 * 64 * KTILE * sizeof(_Float16) + 2 * 2 * 64 * sizeof(float);
+    constexpr int SG = MID2_STAGES, NS = GK == 4 ? 2 : 1;
+    const size_t lds = (size_t)SG * 2 * 64 * KTILE * sizeof(_Float16) + 2 * 2 * NS * 64 * sizeof(float);
     auto kern = w4a16_mid2_kernel<SG, DELTA, GK, GATED>;
     static bool attr_set = false;   // (per instantiation) LDS beyond 64 KB
     if (!attr_set) {
@@ -608,6 +631,7 @@ static hipError_t run_mid2_g(const uint16_t *A, const uint32_t *W, const uint16_
     if (g == K) return run_mid2<DELTA, 0, GATED>(A, W, S, D, C, M, N, K, g, st);
     if (g == 2 * KTILE) return run_mid2<DELTA, 2, GATED>(A, W, S, D, C, M, N, K, g, st);
     if (g == KTILE) return run_mid2<DELTA, 1, GATED>(A, W, S, D, C, M, N, K, g, st);
+    if (g == KTILE / 2) return run_mid2<DELTA, 4, GATED>(A, W, S, D, C, M, N, K, g, st);
     return run_mid2<DELTA, 3, GATED>(A, W, S, D, C, M, N, K, g, st);
 }
 
@@ -631,6 +655,7 @@ hipError_t launch_w4a16_mid(const uint16_t *A, const uint32_t *W, const uint16_t
         return dl ? run_mid2_g<true, false>(A, W, S, D, C, M, N, K, g, st)
                   : run_mid2_g<false, false>(A, W, S, nullptr, C, M, N, K, g, st);
     }
+    if (g < KTILE) return hipErrorInvalidValue;   // (the 64 x 64 kernel takes g >= 128)
     const bool dl = D && fuse_delta;
     if (gated)
         return dl ? run_mid_g<true, true>(A, W, S, D, C, M, N, K, g, st)

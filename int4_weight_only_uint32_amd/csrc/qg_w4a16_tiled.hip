@@ -528,8 +528,8 @@ static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t
 }
 
 // Groups of 64 or 32 (GPT = 2 or 4 groups per k-tile): the generic tiled
-// kernels at every configuration (64 x 128 in place of the mid kernels,
-// the generic 128 x 256 in place of the symmetric one).
+// kernels (64 x 128 in place of the mid kernels, except the 8-wave one with
+// groups of 64; the generic 128 x 256 in place of the symmetric one).
 template <bool GATED, int GPT>
 static hipError_t run_tiled_small_groups(int cfg, const uint16_t *A, const uint32_t *W,
                                          const uint16_t *S, const uint16_t *D, uint16_t *C, int M,
@@ -563,10 +563,15 @@ static hipError_t run_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W, c
                                 const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                                 bool fuse_delta, hipStream_t st)
 {
-    if (g < KTILE)
+    if (g < KTILE) {
+        // groups of 64 on the 8-wave mid kernel (its low- and high-nibble
+        // sums are the two groups of a k-tile)
+        if (g == KTILE / 2 && cfg == 0 && use_mid2(M, N, K))
+            return launch_w4a16_mid(A, W, S, D, C, M, N, K, g, fuse_delta, st, GATED);
         return KTILE / g == 2
                    ? run_tiled_small_groups<GATED, 2>(cfg, A, W, S, D, C, M, N, K, g, fuse_delta, st)
                    : run_tiled_small_groups<GATED, 4>(cfg, A, W, S, D, C, M, N, K, g, fuse_delta, st);
+    }
     const bool dl = D && fuse_delta;
     if (cfg == 0) return launch_w4a16_mid(A, W, S, D, C, M, N, K, g, fuse_delta, st, GATED);
     if (cfg == 1) {

@@ -59,7 +59,7 @@ def _w4a16_both(libs, fn_name, M, K, N, g, asym, signed=False, op=qg.QG_OP_W4A16
 # one shape per kernel path: decode (2 and 6 K-splits), skinny, the two mid
 # kernels, 64x128 tiled (fused delta), 128x256 tiled (fused delta and the
 # symmetric hand-ordered kernel), the row split, the separate correction,
-# groups of 64 and 32 (decode, skinny and generic tiled kernels)
+# groups of 64 and 32 (decode, skinny, 8-wave mid and generic tiled kernels)
 @pytest.mark.parametrize("M,K,N,g,asym,flags", [
     (16, 5120, 17408, 128, True, 0),
     (4, 17408, 5120, 128, True, 0),
@@ -74,6 +74,7 @@ def _w4a16_both(libs, fn_name, M, K, N, g, asym, signed=False, op=qg.QG_OP_W4A16
     (16, 4096, 4096, 64, True, 0),          # groups of 64 and 32
     (33, 2048, 1024, 64, True, 0),
     (64, 4096, 2048, 32, False, 0),
+    (256, 2048, 8192, 64, True, 0),
     (512, 2048, 4096, 32, True, 0),
     (2048, 1024, 8192, 64, False, 0),
 ])

@@ -3,8 +3,9 @@
 Every 32-k MFMA step of a packed 128-k tile lies inside one such group (the
 packed layout gives k-steps 0, 1 to the low nibbles and 2, 3 to the high
 ones), so the decode and skinny kernels scale each step's products with its
-own group's scale and delta, and the generic tiled kernels dequantize each
-step with its group's scale; the grouped W4A8 kernel takes groups of 64 (one 64-k int8
+own group's scale and delta, the 8-wave mid kernel takes its low- and
+high-nibble sums as the two groups of 64, and the generic tiled kernels
+dequantize each step with its group's scale; the grouped W4A8 kernel takes groups of 64 (one 64-k int8
 MFMA step each).  Checked against the oracle, which applies W = q s + z per
 group of g consecutive k ("Marlin INT4 on Ada - how it works", "The core
 mismatch: symmetric vs asymmetric"), to the W4A16 bar (relative Frobenius
@@ -58,19 +59,21 @@ def _w4a16(M, K, N, g, asym, flags=0, case_id=0):
 
 # decode kernel (M <= 16, with and without K splits), the skinny kernel
 # (narrow decode shapes, 17 <= M <= 80, every configuration), the generic
-# 64x128 tiles (mid-size batches), the generic 128x256 tiles and the
-# prefill-size row split
+# 64x128 tiles (mid-size batches), the 8-wave mid kernel (g = 64 on mid-size
+# batches over wide N; g = 32 takes the 64x128 tiles there), the generic
+# 128x256 tiles and the prefill-size row split
 @pytest.mark.parametrize("g", [64, 32])
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (16, 5120, 8192), (16, 17408, 5120),
                                    (8, 1024, 1024), (33, 2048, 1024), (64, 4096, 2048),
-                                   (80, 1024, 4096), (256, 2048, 4096), (2048, 1024, 8192),
-                                   (4096, 1024, 17408)])
+                                   (80, 1024, 4096), (256, 2048, 4096), (256, 2048, 8192),
+                                   (200, 1536, 8192), (2048, 1024, 8192), (4096, 1024, 17408)])
 def test_w4a16_small_groups_asym(M, K, N, g):
     _w4a16(M, K, N, g, True, case_id=M + g)
 
 
 @pytest.mark.parametrize("g", [64, 32])
-@pytest.mark.parametrize("M,K,N", [(4, 4096, 4096), (100, 1024, 2048), (2048, 1024, 8192)])
+@pytest.mark.parametrize("M,K,N", [(4, 4096, 4096), (100, 1024, 2048), (256, 1024, 8192),
+                                   (2048, 1024, 8192)])
 def test_w4a16_small_groups_symmetric_signed(M, K, N, g):
     _w4a16(M, K, N, g, False, case_id=1000 + M + g)
 
