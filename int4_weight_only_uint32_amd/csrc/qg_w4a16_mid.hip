@@ -5,6 +5,7 @@
 #include "qg_device.h"
 #include "qg_launch.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace qg {
@@ -610,12 +611,16 @@ static hipError_t run_mid2(const uint16_t *A, const uint32_t *W, const uint16_t 
     constexpr int SG = MID2_STAGES, NS = GK == 4 ? 2 : 1;
     const size_t lds = (size_t)SG * 2 * 64 * KTILE * sizeof(_Float16) + 2 * 2 * NS * 64 * sizeof(float);
     auto kern = w4a16_mid2_kernel<SG, DELTA, GK, GATED>;
-    static bool attr_set = false;   // (per instantiation) LDS beyond 64 KB
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // LDS beyond 64 KB: the attribute is set once per device (and instantiation)
+    static std::atomic<unsigned> attr_devs{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned bit = dev >= 0 && dev < 32 ? 1u << dev : 0u;
+    if (!(attr_devs.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_devs.fetch_or(bit, std::memory_order_release);
     }
     dim3 grid((unsigned)(N / 128), (unsigned)((M + 63) / 64));
     hipLaunchKernelGGL(kern, grid, dim3(512), lds, st, A, reinterpret_cast<const uint4v *>(W), S, D,

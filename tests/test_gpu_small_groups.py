@@ -91,6 +91,13 @@ def test_w4a16_small_groups_k_and_n_tails(g, M, K):
     _w4a16(M, K, 1000, g, True, case_id=3000 + g + K)
 
 
+def test_w4a16_groups_of_64_mid_kernel_tails():
+    """K = 1000 and N = 8100 (padded to 1024 and 8192) at M = 256: the 8-wave
+    mid kernel over the padded shape, whose last group of 64 is partly and
+    the padded columns wholly outside the logical weight."""
+    _w4a16(256, 1000, 8100, 64, True, case_id=3500)
+
+
 @pytest.mark.parametrize("g", [64, 32])
 @pytest.mark.parametrize("M,K,N", [(16, 4096, 4096), (40, 2048, 1024), (512, 1024, 2048)])
 def test_swiglu_small_groups(M, K, N, g):
