@@ -116,11 +116,17 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     using AVec = typename std::conditional<WV == 4, uint4v, uint2v>::type;
     constexpr int APR = 256 / sizeof(AVec);      // pieces per row
     const int arow_i = tid / APR, apc = tid % APR;
-    const int arow = arow_i < M ? arow_i : M - 1;
-    const AVec *asrc = reinterpret_cast<const AVec *>(A + (size_t)arow * K) + apc;
+    // loads through buffer resources: a uniform base, a fixed per-lane byte
+    // offset and the k-tile's offset in a scalar register.  Rows past M get
+    // an offset beyond the resource's range, so their loads return zeros
+    // without a memory access (those rows' results are never stored).
+    const __amdgpu_buffer_rsrc_t a_rs = buffer_rsrc(A, (size_t)M * K * 2);
+    const unsigned a_off = arow_i < M ? (unsigned)(arow_i * K) * 2u + (unsigned)(apc * (int)sizeof(AVec))
+                                      : 0x80000000u;
     const int ach = apc * (int)sizeof(AVec) / 16, asub = (apc * (int)sizeof(AVec) % 16) / 2;
     const int adst = arow_i * KTILE + 8 * (ach ^ (arow_i & 15)) + asub;
-    const uint4v *wbase = W + (size_t)nt0 * KT * 64 + lane;
+    const __amdgpu_buffer_rsrc_t w_rs = buffer_rsrc(W + (size_t)nt0 * KT * 64, (size_t)NT * KT * 1024);
+    const unsigned w_off = (unsigned)lane * 16u;
     const int gbase = (kt_beg * KTILE) / g;
 
     float4v acc[NT];
@@ -132,9 +138,13 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     AVec ra[P];
     uint4v rw[P][NT];
     auto load = [&](int kt, AVec &a, uint4v (&w)[NT]) {
-        a = asrc[(size_t)kt * (KTILE * 2 / sizeof(AVec))];
+        if constexpr (WV == 4)
+            a = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off, kt * KTILE * 2, 0));
+        else
+            a = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(a_rs, a_off, kt * KTILE * 2, 0));
 #pragma unroll
-        for (int t = 0; t < NT; ++t) w[t] = wbase[((size_t)t * KT + kt) * 64];
+        for (int t = 0; t < NT; ++t)
+            w[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off, (t * KT + kt) * 1024, 0));
     };
     auto finish = [&](int buf, int kt, const CodeOps (&ops)[NT]) {
         half8 a[4];
