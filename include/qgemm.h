@@ -28,7 +28,8 @@
  *     device state; scratch memory is a caller-provided workspace whose size
  *     qg_workspace_bytes() reports (0 for every path that needs none).
  *   - A W4A16 workspace starts with QG_W4A16_WS_COUNTER_BYTES bytes of
- *     split-K counters, then the fp32 partial sums (M <= 16) and the
+ *     split-K counters, then the fp32 partial sums (decode-size batches,
+ *     M <= 80, where the split-K decode kernel runs) and the
  *     correction's group sums (QG_CORR_SEPARATE).  It must be zero-filled
  *     before its first use; every qgemm_w4a16 call leaves the counters at zero
  *     again, so one zero-filled workspace serves any sequence of qgemm_w4a16
@@ -168,7 +169,8 @@ int pack_int4_weights(const uint8_t *q, const uint16_t *scale, const uint16_t *z
  *          the padded shape and its product is cropped into C; the delta term
  *          is fused; QG_CORR_SEPARATE is QG_ERR_UNSUPPORTED.
  * workspace/workspace_bytes: qg_workspace_bytes(QG_OP_W4A16, ...) bytes,
- *          256-byte aligned (NULL when that is 0).  For M <= 16 the K range
+ *          256-byte aligned (NULL when that is 0).  For decode-size batches
+ *          (M <= 16, and up to M = 80 on all but small weights) the K range
  *          is split over several workgroups whose fp32 partial sums meet in
  *          the workspace; the last to finish adds them in a fixed order, so
  *          results do not depend on timing.                                 */
@@ -193,7 +195,7 @@ int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *sca
  * that GPU's one array, which keeps the last call's contents: calls that may
  * overlap in time on one GPU (different streams, threads or graphs) race and
  * must be ordered by the caller.                                            */
-#define QG_NOALLOC_SCRATCH_BYTES 8388608u
+#define QG_NOALLOC_SCRATCH_BYTES 33554432u
 int qgemm_w4a16_noalloc(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,
                         const uint16_t *delta, uint16_t *C, int M, int N, int K,
                         int group_size, unsigned flags, void *stream);

@@ -35,7 +35,7 @@ QG_PACK_FOLD_NEG_SCALES = 0x1
 QG_CORR_SEPARATE = 0x1
 
 QG_W4A16_WS_COUNTER_BYTES = 65536
-QG_NOALLOC_SCRATCH_BYTES = 8388608
+QG_NOALLOC_SCRATCH_BYTES = 33554432
 
 QG_OP_W4A16 = 1
 QG_OP_W4A8 = 2

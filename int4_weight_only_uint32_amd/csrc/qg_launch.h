@@ -89,6 +89,7 @@ hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint1
 // Rows from which the tiled/mid kernels take over from the skinny one (the mid
 // kernel measured faster from about M = 80 on).
 constexpr int TILED_MIN_M = 81;
+constexpr int DECODE_MAX_M = TILED_MIN_M - 1;   // the decode kernel's m-tiles cover M <= 80
 
 // Bytes of workspace the W4A16 GEMM kernels need for this shape (0 = none).
 size_t w4a16_workspace_bytes(int M, int N, int K, int g);

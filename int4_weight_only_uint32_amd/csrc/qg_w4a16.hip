@@ -9,8 +9,8 @@
 // K/N tail path, the SwiGLU dispatch and the two-stage correction; the decode,
 // mid-batch and tiled kernels have files of their own.
 //
-// Skinny kernel (M < 128; for most M <= 16 shapes the decode kernel, which
-// shares the activation tile between waves, is used instead).  A wave owns MT 16-row m-tiles x NT 16-column
+// Skinny kernel (M <= 80; for most shapes the decode kernel, which shares the
+// activation tile between waves, is used instead: see use_decode_kernel).  A wave owns MT 16-row m-tiles x NT 16-column
 // n-tiles and a contiguous range of 128-k tiles, with P tiles of codes and
 // activations in flight in a register ring; the waves of a workgroup split K
 // and are summed through LDS at the end (one launch, no workspace).
@@ -502,10 +502,10 @@ hipError_t launch_w4a16_tail(const uint16_t *A, const uint32_t *W, const uint16_
 // The pair is one packed [K, 2N] weight, gate columns first.  Every batch
 // runs one launch whose kernel holds the gate and the up product of the same
 // output columns in fp32 and stores silu(gate) * up once: the gated decode
-// kernel (M <= 16 where it is chosen), otherwise the skinny, mid or tiled
+// kernel (M <= 80 where it is chosen), otherwise the skinny, mid or tiled
 // kernel with the gated epilogue (gated_tile pairs their n-tiles).
 
-bool swiglu_uses_decode(int M, int N, int K, int g) { return M <= 16 && use_decode_kernel(M, 2 * N, K, g); }
+bool swiglu_uses_decode(int M, int N, int K, int g) { return use_decode_kernel(M, 2 * N, K, g); }
 
 size_t swiglu_workspace_bytes(int M, int N, int K, int g)
 {

@@ -1,4 +1,5 @@
-// W4A16 decode kernel (M <= 16): activation tile shared through LDS, split-K
+// W4A16 decode kernel (M <= 16, and up to 80 with several m-tiles):
+// activation tile shared through LDS, split-K
 // with a last-arriver reduction.  Arithmetic as in the skinny kernel
 // ("Marlin INT4 on Ada - how it works", "The core mismatch: symmetric vs
 // asymmetric"): codes as exact fp16 subnormals in the MFMAs, group scale and
@@ -10,7 +11,7 @@
 
 namespace qg {
 
-// ---- decode kernel (M <= 16) ----
+// ---- decode kernel (decode-size batches) ----
 // A workgroup of 4 waves owns 4*NT consecutive 16-column strips (wave w the
 // strips 4*NT*cg + NT*w .. +NT-1) and one of `nsplit` contiguous ranges of
 // 128-k tiles.  Each k-tile of A (16 rows x 128 k, 4 KB) is fetched once per
@@ -39,7 +40,10 @@ namespace qg {
 // k-steps 0, 1 in the low nibbles and 2, 3 in the high ones), so with g = 64
 // the low- and high-nibble products are the two groups' and with g = 32 each
 // step's product is its own group's; the group sums of A split the same way.
-template <int NT, int P, int WV, bool DELTA, bool GATED = false, int GPT = 1>
+// MT: 16-row m-tiles (M <= 16 MT).  Each k-tile of A is 16 MT rows (MT
+// 16-byte loads per thread), every wave multiplies each of its code tiles
+// into all MT m-tiles, and the split-K slots hold 16 MT rows.
+template <int NT, int P, int WV, bool DELTA, bool GATED = false, int GPT = 1, int MT = 1>
 __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g,
@@ -48,10 +52,11 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     static_assert(NT == 1, "the scale table holds one column per lane");
     static_assert(WV == 4 || WV == 8, "4 or 8 waves per workgroup");
     static_assert(!GATED || WV == 4, "the gate/up pairing takes 4 waves");
+    static_assert(MT == 1 || WV == 4, "several m-tiles take 4 waves");
     constexpr int COLS = 16 * WV;            // columns per workgroup
-    __shared__ __attribute__((aligned(16))) _Float16 As[2][16 * KTILE];
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][MT * 16 * KTILE];
     __shared__ unsigned arrived;
-    __shared__ float xch[GATED ? 2 * 4 * 64 : 1];   // up values for the gate waves
+    __shared__ float xch[GATED ? MT * 2 * 4 * 64 : 1];   // up values for the gate waves
     // (scale | delta << 16) of this workgroup's 64 columns for every group its
     // k-range touches: filled once, read once per k-tile (an LDS read instead
     // of two global loads per k-tile)
@@ -109,8 +114,9 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
         }
     }
 
-    // activation tile (16 rows x 256 bytes): with 4 waves thread t fetches
-    // row t/16, 16-byte chunk t%16; with 8 waves row t/32, 8-byte piece t%32.
+    // activation tile (16 MT rows x 256 bytes): with 4 waves thread t fetches
+    // rows t/16 + 16 i (i < MT), 16-byte chunk t%16; with 8 waves row t/32,
+    // 8-byte piece t%32.
     // A 16-byte chunk lands at position chunk ^ row within its 256-byte LDS
     // row so the 16 rows an MFMA operand reads fall in distinct banks.
     using AVec = typename std::conditional<WV == 4, uint4v, uint2v>::type;
@@ -121,36 +127,48 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     // an offset beyond the resource's range, so their loads return zeros
     // without a memory access (those rows' results are never stored).
     const __amdgpu_buffer_rsrc_t a_rs = buffer_rsrc(A, (size_t)M * K * 2);
-    const unsigned a_off = arow_i < M ? (unsigned)(arow_i * K) * 2u + (unsigned)(apc * (int)sizeof(AVec))
-                                      : 0x80000000u;
     const int ach = apc * (int)sizeof(AVec) / 16, asub = (apc * (int)sizeof(AVec) % 16) / 2;
-    const int adst = arow_i * KTILE + 8 * (ach ^ (arow_i & 15)) + asub;
+    unsigned a_off[MT];
+    int adst[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int row = arow_i + 16 * i;
+        a_off[i] = row < M ? (unsigned)(row * K) * 2u + (unsigned)(apc * (int)sizeof(AVec)) : 0x80000000u;
+        adst[i] = row * KTILE + 8 * (ach ^ (row & 15)) + asub;
+    }
     const __amdgpu_buffer_rsrc_t w_rs = buffer_rsrc(W + (size_t)nt0 * KT * 64, (size_t)NT * KT * 1024);
     const unsigned w_off = (unsigned)lane * 16u;
     const int gbase = (kt_beg * KTILE) / g;
 
-    float4v acc[NT];
+    float4v acc[MT][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     const float4v fzero = {0.f, 0.f, 0.f, 0.f};
 
-    AVec ra[P];
+    AVec ra[P][MT];
     uint4v rw[P][NT];
-    auto load = [&](int kt, AVec &a, uint4v (&w)[NT]) {
-        if constexpr (WV == 4)
-            a = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off, kt * KTILE * 2, 0));
-        else
-            a = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(a_rs, a_off, kt * KTILE * 2, 0));
+    auto load = [&](int kt, AVec (&a)[MT], uint4v (&w)[NT]) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            if constexpr (WV == 4)
+                a[i] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[i], kt * KTILE * 2, 0));
+            else
+                a[i] = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(a_rs, a_off[i], kt * KTILE * 2, 0));
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             w[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off, (t * KT + kt) * 1024, 0));
     };
     auto finish = [&](int buf, int kt, const CodeOps (&ops)[NT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
         half8 a[4];
 #pragma unroll
         for (int o = 0; o < 4; ++o)
-            a[o] = *reinterpret_cast<const half8 *>(&As[buf][c * KTILE + 8 * ((4 * o + kq) ^ c)]);
+            a[o] = *reinterpret_cast<const half8 *>(&As[buf][(16 * mt + c) * KTILE + 8 * ((4 * o + kq) ^ c)]);
         if (GPT > 1) {
             // groups of 64 or 32 k: one scale and delta per group of the tile
             constexpr int SPG = 4 / GPT;                // MFMA steps per group
@@ -180,12 +198,12 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
                     const float c2 = DELTA ? (d - 8.0f * s) : (-8.0f * s);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float v = __builtin_fmaf(cx, x[q][r], acc[t][r]);
-                        acc[t][r] = __builtin_fmaf(c2, as[q][r], v);
+                        const float v = __builtin_fmaf(cx, x[q][r], acc[mt][t][r]);
+                        acc[mt][t][r] = __builtin_fmaf(c2, as[q][r], v);
                     }
                 }
             }
-            return;
+            continue;
         }
         const uint32_t sd = sdt[((kt * KTILE) / g - gbase) * COLS + 16 * wave + c];
         float4v as = mfma_f16(a[0], ones, fzero);
@@ -204,15 +222,17 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
             xh = mfma_f16(a[3], ops[t].hi[1], xh);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float v = __builtin_fmaf(c16, xl[r], acc[t][r]);
+                float v = __builtin_fmaf(c16, xl[r], acc[mt][t][r]);
                 v = __builtin_fmaf(c1, xh[r], v);
-                acc[t][r] = __builtin_fmaf(c2, as[r], v);
+                acc[mt][t][r] = __builtin_fmaf(c2, as[r], v);
             }
         }
+    }
     };
     auto step = [&](int kt, int slot, int kt_next) {
         const int buf = (kt - kt_beg) & 1;
-        *reinterpret_cast<AVec *>(&As[buf][adst]) = ra[slot];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) *reinterpret_cast<AVec *>(&As[buf][adst[i]]) = ra[slot][i];
         CodeOps ops[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -264,63 +284,75 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
             if (j + i < n) step(kt_beg + j + i, i, last);
     }
 
-    // C rows 4 kq + r, columns (nt0 + t) * 16 + c; GATED: silu(gate) * up
-    // into C [M, Nh] by the gate waves (reached by every thread of the
+    // C rows 16 mt + 4 kq + r, columns (nt0 + t) * 16 + c; GATED: silu(gate)
+    // * up into C [M, Nh] by the gate waves (reached by every thread of the
     // workgroup, or of none: the barrier is uniform)
-    auto store = [&](const float4v (&v)[NT]) {
+    auto store = [&](const float4v (&v)[MT][NT]) {
         if (GATED) {
             if (wave >= 2)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) xch[(wave - 2) * 256 + r * 64 + lane] = v[0][r];
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) xch[((mt * 2 + wave - 2) * 4 + r) * 64 + lane] = v[mt][0][r];
             __syncthreads();
             if (wave < 2)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 4 * kq + r;
-                    const float gv = v[0][r], u = xch[wave * 256 + r * 64 + lane];
-                    if (row < M) C[(size_t)row * Nh + col0] = f2h(silu_mul(gv, u));
-                }
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * mt + 4 * kq + r;
+                        const float gv = v[mt][0][r], u = xch[((mt * 2 + wave) * 4 + r) * 64 + lane];
+                        if (row < M) C[(size_t)row * Nh + col0] = f2h(silu_mul(gv, u));
+                    }
             return;
         }
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 4 * kq + r;
-                if (row < M) C[(size_t)row * N + col0 + 16 * t] = f2h(v[t][r]);
-            }
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * mt + 4 * kq + r;
+                    if (row < M) C[(size_t)row * N + col0 + 16 * t] = f2h(v[mt][t][r]);
+                }
     };
     if (nsplit == 1) {
         store(acc);
         return;
     }
-    // slot layout: [cg][split][wave][t][r][lane] fp32
-    constexpr int PER_WAVE = NT * 4 * 64;
+    // slot layout: [cg][split][wave][mt][t][r][lane] fp32
+    constexpr int PER_WAVE = MT * NT * 4 * 64;
     float *mine = partials + ((size_t)cg * nsplit + sp) * WV * PER_WAVE + wave * PER_WAVE + lane;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            __hip_atomic_store(mine + (t * 4 + r) * 64, acc[t][r], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                __hip_atomic_store(mine + ((mt * NT + t) * 4 + r) * 64, acc[mt][t][r], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);          // this thread's slot stores are complete
     __syncthreads();                        // ... and every thread's
     if (tid == 0)
         arrived = __hip_atomic_fetch_add(&counters[cg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (arrived != (unsigned)(nsplit - 1)) return;
-    float4v tot[NT];
+    float4v tot[MT][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) tot[t] = fzero;
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) tot[mt][t] = fzero;
     const float *base = partials + (size_t)cg * nsplit * WV * PER_WAVE + wave * PER_WAVE + lane;
     for (int s2 = 0; s2 < nsplit; ++s2) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                tot[t][r] += (s2 == sp) ? acc[t][r]
-                                        : __hip_atomic_load(base + (size_t)s2 * WV * PER_WAVE + (t * 4 + r) * 64,
-                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    tot[mt][t][r] += (s2 == sp) ? acc[mt][t][r]
+                                                : __hip_atomic_load(base + (size_t)s2 * WV * PER_WAVE + ((mt * NT + t) * 4 + r) * 64,
+                                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     store(tot);
     if (tid == 0) __hip_atomic_store(&counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -389,9 +421,25 @@ int decode_splits(int N, int K, int g)
 //   shorter splits its fixed costs (scale table, split-K epilogue) lose
 //   (K = 4096, N = 4096-8192: 9.2-10 against 7.2-8.5 us; K = N = 8192: 12.7
 //   against 11.7).
+// 17 <= M <= 80 (several m-tiles, g >= 128): whether the decode kernel beats
+// the skinny kernel, whose waves each stage their own activation rows (16 MT
+// rows per k-tile) where the decode kernel's four waves share one tile.
+// Measured on MI355X (A/B in one process, µs skinny -> decode): two m-tiles
+// always (K4096 N4096 M32 13.0 -> 11.7, K2048 N2048 M32 9.4 -> 9.3, K5120
+// N17408 M32 30.4 -> 23.0); three to five when the weight has more than 2^24
+// elements (K5120 N17408 M80 77.1 -> 40.8, K4096 N8192 M48 16.6 -> 14.1,
+// K5120 N5120 M64 18.1 -> 16.3), not at or below it (K4096 N4096 M64 15.1
+// against 16.6, K2048 N2048 M64 10.7 against 12.9).
+static bool decode_multi_tile_pays(int M, int N, int K)
+{
+    const int mt = (M + 15) / 16;
+    return mt <= 2 || (long long)K * N > (1ll << 24);
+}
+
 bool use_decode_kernel(int M, int N, int K, int g)
 {
-    if (M > 16 || N % decode::COLS) return false;
+    if (M > DECODE_MAX_M || N % decode::COLS) return false;
+    if (M > 16) return g >= KTILE && decode_multi_tile_pays(M, N, K);
     const int ns = decode_splits(N, K, g);
     if (ns <= 2) return true;
     const long skinny_wgs = N / 32;
@@ -405,10 +453,11 @@ size_t decode_workspace_bytes(int M, int N, int K, int g)
     const int ns = decode_splits(N, K, g);
     if (ns == 1) return 0;
     const size_t ncg = (size_t)(N / decode::COLS);
-    return W4A16_WS_COUNTER_BYTES + ncg * ns * 16 * decode::COLS * sizeof(float);
+    const size_t rows = 16 * (size_t)((M + 15) / 16);   // the m-tiles' rows
+    return W4A16_WS_COUNTER_BYTES + ncg * ns * rows * decode::COLS * sizeof(float);
 }
 
-template <bool DELTA, bool GATED = false, int GPT = 1>
+template <bool DELTA, bool GATED = false, int GPT = 1, int MT = 1>
 static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                              const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                              int nsplit, void *ws, hipStream_t st)
@@ -421,13 +470,16 @@ static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_
         partials = reinterpret_cast<float *>(static_cast<char *>(ws) + W4A16_WS_COUNTER_BYTES);
     }
     const size_t table = (size_t)decode_max_groups(K, g, nsplit) * decode::COLS * sizeof(uint32_t);
-    if (table > 64 * 1024) {
+    // the kernel's static LDS: two activation tiles, the counter word, the
+    // gated hand-over
+    constexpr size_t stat = 2 * MT * 16 * KTILE * 2 + 4 + (GATED ? MT * 2 * 4 * 64 * 4 : 4);
+    if (table + stat > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT>),
+            reinterpret_cast<const void *>(&w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT, MT>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)table);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT>),
+    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT, MT>),
                        dim3(ncg * nsplit), dim3(64 * decode::WV), table, st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M,
                        N, K, g, nsplit, counters, partials);
     return hipGetLastError();
@@ -438,19 +490,22 @@ hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint1
                                bool fuse_delta, int nsplit, void *ws, hipStream_t st,
                                bool gated)
 {
-    if (M > 16 || N % decode::COLS || nsplit < 1 || (nsplit > 1 && !ws))
+    if (M > DECODE_MAX_M || N % decode::COLS || nsplit < 1 || (nsplit > 1 && !ws))
         return hipErrorInvalidValue;
     const bool dl = D && fuse_delta;
     const int gpt = g < KTILE ? KTILE / g : 1;
-#define QG_DEC(GPT_)                                                                          \
-    if (gpt == GPT_) {                                                                        \
+    const int mt = (M + 15) / 16;
+    if (gpt > 1 && mt > 1) return hipErrorInvalidValue;   // groups of 64 and 32: M <= 16 only
+#define QG_DEC(GPT_, MT_)                                                                     \
+    if (gpt == GPT_ && mt == MT_) {                                                           \
         if (gated)                                                                            \
-            return dl ? run_decode<true, true, GPT_>(A, W, S, D, C, M, N, K, g, nsplit, ws, st) \
-                      : run_decode<false, true, GPT_>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st); \
-        return dl ? run_decode<true, false, GPT_>(A, W, S, D, C, M, N, K, g, nsplit, ws, st)   \
-                  : run_decode<false, false, GPT_>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st); \
+            return dl ? run_decode<true, true, GPT_, MT_>(A, W, S, D, C, M, N, K, g, nsplit, ws, st) \
+                      : run_decode<false, true, GPT_, MT_>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st); \
+        return dl ? run_decode<true, false, GPT_, MT_>(A, W, S, D, C, M, N, K, g, nsplit, ws, st)   \
+                  : run_decode<false, false, GPT_, MT_>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st); \
     }
-    QG_DEC(1) QG_DEC(2) QG_DEC(4)
+    QG_DEC(1, 1) QG_DEC(2, 1) QG_DEC(4, 1)
+    QG_DEC(1, 2) QG_DEC(1, 3) QG_DEC(1, 4) QG_DEC(1, 5)
 #undef QG_DEC
     return hipErrorInvalidValue;
 }

@@ -178,8 +178,8 @@ CTR = 65536   # QG_W4A16_WS_COUNTER_BYTES
 
 
 def test_decode_workspace_size():
-    # M <= 16: the fixed counter region + fp32 partials (16 rows x 64 columns
-    # per split per 64-column group).  Splits: the most that keep <= 512
+    # the fixed counter region + fp32 partials (16 rows per m-tile x 64
+    # columns per split per 64-column group).  Splits: the most that keep <= 512
     # workgroups (two per CU) when that fills >= 448 of them, else the smallest
     # power of two giving >= 512 workgroups; >= 2 k-tiles per split.
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 17408, 5120, 128) == CTR + 272 * 2 * 4096
@@ -192,7 +192,16 @@ def test_decode_workspace_size():
     # of 22-23 k-tiles); small problems run the skinny kernel
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 8, 5120, 17408, 128) == CTR + 80 * 6 * 4096
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1024, 128) == 0
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 17, 5120, 17408, 128) == 0     # skinny path
+    # 17 <= M <= 80: the decode kernel with 16-row m-tiles (partials of 16 per
+    # m-tile rows) for two m-tiles, and for more on weights of > 2^24
+    # elements; otherwise (and for groups below 128) the skinny kernel
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 17, 5120, 17408, 128) == CTR + 80 * 6 * 8192
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 32, 4096, 4096, 128) == CTR + 64 * 8 * 8192
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 48, 17408, 5120, 128) == CTR + 272 * 2 * 12288
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 80, 17408, 5120, 128) == CTR + 272 * 2 * 20480
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 64, 4096, 4096, 128) == 0
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 32, 4096, 4096, 64) == 0
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 81, 17408, 5120, 128) == 0     # tiled from 81
     # a K range too short to split needs none
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 256, 128) == 0
     # the correction's group sums always come after the counter region
@@ -259,9 +268,11 @@ def test_swiglu_validation():
     assert L.qgemm_w4a16_swiglu(*ok(flags=1)) == qg.QG_ERR_INVALID_ARG
     assert L.qgemm_w4a16_swiglu(*ok(N=1000)) == qg.QG_ERR_UNSUPPORTED
     # every batch is one fused launch: only the decode kernel's split-K (here
-    # M = 16, K 17408 -> N 5120 per half: 3 splits) takes a workspace
-    for M in (17, 64, 256, 4096):
+    # M = 16, K 17408 -> N 5120 per half: 3 splits; M = 17, two m-tiles over
+    # the 2048-column pair, 4 splits) takes a workspace
+    for M in (64, 256, 4096):
         assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, M, 1024, 1024, 128, 1, 0) == 0
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 17, 1024, 1024, 128, 1, 0) == CTR + 32 * 4 * 8192
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 16, 17408, 5120, 128, 1, 0) == 0
     need = qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 16, 5120, 17408, 128, 1, 0)
     assert need == CTR + 160 * 3 * 4096
@@ -328,7 +339,7 @@ def test_noalloc_refuses_shapes_beyond_the_scratch():
     library's static array holds, on the host, before any device call (the
     pointers are never dereferenced), naming the sizes."""
     L = qg.lib()
-    M, K, N = 4096, 1000, 1000        # a tail shape: padded A and C need ~16 MB
+    M, K, N = 8192, 1000, 2000        # a tail shape: padded A and C need ~48 MB
     need = qg.qg_workspace_bytes(qg.QG_OP_W4A16, M, N, K, 128)
     assert need > qg.QG_NOALLOC_SCRATCH_BYTES
     assert L.qgemm_w4a16_noalloc(FAKE, FAKE, FAKE, None, FAKE, M, N, K, 128, 0, None) == \

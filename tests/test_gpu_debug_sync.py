@@ -71,6 +71,8 @@ def _w4a16_both(libs, fn_name, M, K, N, g, asym, signed=False, op=qg.QG_OP_W4A16
     (2048, 1024, 8192, 128, False, 0),
     (4096, 1024, 17408, 128, False, 0),
     (16, 4096, 4096, 128, True, qg.QG_CORR_SEPARATE),
+    (48, 2048, 8704, 128, True, 0),         # decode with three m-tiles
+    (80, 17408, 5120, 128, False, 0),
     (16, 4096, 4096, 64, True, 0),          # groups of 64 and 32
     (33, 2048, 1024, 64, True, 0),
     (64, 4096, 2048, 32, False, 0),

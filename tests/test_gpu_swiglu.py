@@ -32,7 +32,8 @@ def _check(M, K, N, g, asym=True, signed=False, case_id=0, rows=None):
                          case_id=case_id)
     note(f"swiglu M={M} K={K} N={N} g={g} asym={asym} signed={signed}")
     pair = qg.pack(dev(c.q), dev(c.s), dev(c.z) if asym else None, g, fold=True)
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, M, N, K, g, 1, 0) == 0 or M <= 16
+    # only the decode kernel (M <= 80) takes a workspace, for its split-K
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, M, N, K, g, 1, 0) == 0 or M <= 80
     H = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
     qg.w4a16_swiglu(dev(c.A), pair, H=H)
     torch.cuda.synchronize()

@@ -49,6 +49,8 @@ SEQUENCES = [
     [(16, 1000, 3000, 128, True, 0), (3, 1000, 300, -1, True, 0)],
     [(16, 4096, 8192, 128, True, qg.QG_CORR_SEPARATE), (9, 2048, 1024, 256, True, qg.QG_CORR_SEPARATE)],
     [(16, 16384, 4096, 128, False, 0), (1, 5120, 17408, -1, False, 0)],
+    # the decode kernel with five m-tiles (80-row partial sums), then two
+    [(80, 5120, 17408, 128, True, 0), (20, 2048, 8704, 128, True, 0)],
 ]
 
 
