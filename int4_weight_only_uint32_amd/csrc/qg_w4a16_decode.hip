@@ -421,7 +421,7 @@ int decode_splits(int N, int K, int g)
 //   shorter splits its fixed costs (scale table, split-K epilogue) lose
 //   (K = 4096, N = 4096-8192: 9.2-10 against 7.2-8.5 us; K = N = 8192: 12.7
 //   against 11.7).
-// 17 <= M <= 80 (several m-tiles, g >= 128): whether the decode kernel beats
+// 17 <= M <= 80 (several m-tiles): whether the decode kernel beats
 // the skinny kernel, whose waves each stage their own activation rows (16 MT
 // rows per k-tile) where the decode kernel's four waves share one tile.
 // Measured on MI355X (A/B in one process, µs skinny -> decode): two m-tiles
@@ -429,7 +429,10 @@ int decode_splits(int N, int K, int g)
 // N17408 M32 30.4 -> 23.0); three to five when the weight has more than 2^24
 // elements (K5120 N17408 M80 77.1 -> 40.8, K4096 N8192 M48 16.6 -> 14.1,
 // K5120 N5120 M64 18.1 -> 16.3), not at or below it (K4096 N4096 M64 15.1
-// against 16.6, K2048 N2048 M64 10.7 against 12.9).
+// against 16.6, K2048 N2048 M64 10.7 against 12.9).  Groups of 64 and 32
+// alike (g = 64: K5120 N17408 M48 54.3 -> 29.3, K4096 N8192 M64 19.7 ->
+// 16.8; g = 32: K4096 N8192 M80 36.8 -> 20.9; K4096 N4096 M33 g = 64 17.6
+// either way).
 static bool decode_multi_tile_pays(int M, int N, int K)
 {
     const int mt = (M + 15) / 16;
@@ -439,7 +442,7 @@ static bool decode_multi_tile_pays(int M, int N, int K)
 bool use_decode_kernel(int M, int N, int K, int g)
 {
     if (M > DECODE_MAX_M || N % decode::COLS) return false;
-    if (M > 16) return g >= KTILE && decode_multi_tile_pays(M, N, K);
+    if (M > 16) return decode_multi_tile_pays(M, N, K);
     const int ns = decode_splits(N, K, g);
     if (ns <= 2) return true;
     const long skinny_wgs = N / 32;
@@ -495,7 +498,6 @@ hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint1
     const bool dl = D && fuse_delta;
     const int gpt = g < KTILE ? KTILE / g : 1;
     const int mt = (M + 15) / 16;
-    if (gpt > 1 && mt > 1) return hipErrorInvalidValue;   // groups of 64 and 32: M <= 16 only
 #define QG_DEC(GPT_, MT_)                                                                     \
     if (gpt == GPT_ && mt == MT_) {                                                           \
         if (gated)                                                                            \
@@ -506,6 +508,8 @@ hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint1
     }
     QG_DEC(1, 1) QG_DEC(2, 1) QG_DEC(4, 1)
     QG_DEC(1, 2) QG_DEC(1, 3) QG_DEC(1, 4) QG_DEC(1, 5)
+    QG_DEC(2, 2) QG_DEC(2, 3) QG_DEC(2, 4) QG_DEC(2, 5)
+    QG_DEC(4, 2) QG_DEC(4, 3) QG_DEC(4, 4) QG_DEC(4, 5)
 #undef QG_DEC
     return hipErrorInvalidValue;
 }

@@ -194,13 +194,14 @@ def test_decode_workspace_size():
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1024, 128) == 0
     # 17 <= M <= 80: the decode kernel with 16-row m-tiles (partials of 16 per
     # m-tile rows) for two m-tiles, and for more on weights of > 2^24
-    # elements; otherwise (and for groups below 128) the skinny kernel
+    # elements (any group size); otherwise the skinny kernel
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 17, 5120, 17408, 128) == CTR + 80 * 6 * 8192
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 32, 4096, 4096, 128) == CTR + 64 * 8 * 8192
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 48, 17408, 5120, 128) == CTR + 272 * 2 * 12288
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 80, 17408, 5120, 128) == CTR + 272 * 2 * 20480
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 64, 4096, 4096, 128) == 0
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 32, 4096, 4096, 64) == 0
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 32, 4096, 4096, 64) == CTR + 64 * 8 * 8192
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 64, 4096, 4096, 32) == 0
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 81, 17408, 5120, 128) == 0     # tiled from 81
     # a K range too short to split needs none
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 256, 128) == 0

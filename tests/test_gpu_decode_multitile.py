@@ -7,7 +7,7 @@ m-tiles of the shared activation tile, and the split-K partial sums hold 16 MT
 rows.  Checked against the oracle ("Marlin INT4 on Ada - how it works", "The
 core mismatch: symmetric vs asymmetric") to the W4A16 bar (relative Frobenius
 <= 2e-3 and the elementwise guard), with AWQ-style zero-points, random-sign
-symmetric scales, groups of 128 and 256 and one group over K, rows past M in
+symmetric scales, groups of 32, 64, 128 and 256 and one group over K, rows past M in
 the last m-tile, K and N tails, and the gated SwiGLU pair."""
 import numpy as np
 import pytest
@@ -51,7 +51,8 @@ def test_decode_multi_tile_asym(M):
     _w4a16(M, 2048, 8704, 128, True, case_id=M)
 
 
-@pytest.mark.parametrize("M,g", [(48, 256), (40, 2048), (24, 256)])
+@pytest.mark.parametrize("M,g", [(48, 256), (40, 2048), (24, 256), (40, 64), (80, 64), (33, 32),
+                                 (64, 32)])
 def test_decode_multi_tile_group_sizes(M, g):
     _w4a16(M, 2048, 8704, g, True, case_id=100 + M + g)
 
@@ -71,20 +72,20 @@ def test_decode_multi_tile_tails():
     _w4a16(50, 1000, 17000, 128, True, case_id=400)
 
 
-@pytest.mark.parametrize("M", [24, 40, 80])
-def test_swiglu_decode_multi_tile(M):
+@pytest.mark.parametrize("M,g", [(24, 128), (40, 128), (80, 128), (48, 64)])
+def test_swiglu_decode_multi_tile(M, g):
     """The gated decode kernel over MT m-tiles: gate and up waves of the same
     columns, silu(gate) * up formed after the LDS hand-over of every m-tile."""
     K, N = 2048, 4352
-    c = synth.w4a16_case(M, K, 2 * N, 128, asym=True, stream=99, case_id=500 + M,
+    c = synth.w4a16_case(M, K, 2 * N, g, asym=True, stream=99, case_id=500 + M + g,
                          zero_points="awq")
-    note(f"multi-tile gated decode M={M} K={K} N={N}")
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, M, N, K, 128, 1, 0) > 0
-    pw = qg.pack(dev(c.q), dev(c.s), dev(c.z), 128, fold=True)
+    note(f"multi-tile gated decode M={M} K={K} N={N} g={g}")
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, M, N, K, g, 1, 0) > 0
+    pw = qg.pack(dev(c.q), dev(c.s), dev(c.z), g, fold=True)
     H = qg.w4a16_swiglu(dev(c.A), pw)
     torch.cuda.synchronize()
     got = host(H).astype(np.float64)
     assert np.all(np.isfinite(got))
-    ref = oracle.w4a16_swiglu(c.A, c.q, c.s, c.z, 128, fold=True)
+    ref = oracle.w4a16_swiglu(c.A, c.q, c.s, c.z, g, fold=True)
     assert rel_fro(got, ref) <= TOL
     assert elementwise_guard(got, ref) <= 0
