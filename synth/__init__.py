@@ -147,7 +147,8 @@ def w4a8_case(E, rows_per_expert, K, N, g, signed_scales=False, stream=4, case_i
 
 # The named workloads: shapes, value recipe and seed stream of each.
 #   small-asym  16 x 1024 x 1024, group 128, asymmetric (parity and smoke size)
-#   decode      M in {1, 4, 16}; K5120/N17408 and K17408/N5120; group 128 asym
+#   decode      M in {1, 4, 16}; K5120/N17408 and K17408/N5120; group 128 asym;
+#               M=64 on K5120/N17408 (a batched decode step)
 #   midbatch    M=256, K=4096, N=8192; group 256 and per-column; asymmetric
 #   prefill     M=4096, K=5120, N=17408; group 128 symmetric, half the scales
 #               negative (the sign fold matters)
@@ -169,6 +170,9 @@ for _i, (_k, _n, _m) in enumerate([(k, n, m) for (k, n) in ((5120, 17408), (1740
                                    for m in (1, 4, 16)]):
     _add(f"w4a16-decode-M{_m}-K{_k}-N{_n}-g128-asym", "w4a16", 1, _i, M=_m, K=_k, N=_n, g=128,
          asym=True)
+# a batched decode step (64 tokens) on the first weight shape
+_add("w4a16-decode-M64-K5120-N17408-g128-asym", "w4a16", 1, 6, M=64, K=5120, N=17408, g=128,
+     asym=True)
 _add("w4a16-midbatch-M256-K4096-N8192-g256-asym", "w4a16", 2, 0, M=256, K=4096, N=8192, g=256,
      asym=True)
 _add("w4a16-midbatch-M256-K4096-N8192-percol-asym", "w4a16", 2, 1, M=256, K=4096, N=8192,
