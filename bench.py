@@ -235,6 +235,7 @@ def _committed(name):
 # case name -> committed counter record of the kernels it runs
 COUNTER_RECORDS = {
     "w4a16-decode-M16-K5120-N17408-g128-asym": "w4a16_decode_M16_K5120_N17408_counters.json",
+    "w4a16-decode-M64-K5120-N17408-g128-asym": "w4a16_decode_M64_K5120_N17408_counters.json",
     "w4a16-midbatch-M256-K4096-N8192-g256-asym": "w4a16_mid_M256_K4096_N8192_counters.json",
     "w4a16-midbatch-M256-K4096-N8192-percol-asym": "w4a16_mid_M256_K4096_N8192_counters.json",
     "w4a16-prefill-M4096-K5120-N17408-g128-sym-signed": "w4a16_prefill_M4096_K5120_N17408_counters.json",
