@@ -74,10 +74,11 @@ hipError_t launch_w4a16_tiled(const uint16_t *A, const uint32_t *W, const uint16
 // (the partial sums and the correction's group sums come after).
 constexpr size_t W4A16_WS_COUNTER_BYTES = 65536;
 
-// Decode kernel (M <= 16): split count the heuristic picks, and a launch with
-// an explicit split count (nsplit > 1 needs `ws` of decode_workspace_bytes).
-// g: the weight group size (groups of 64 or 32 take the decode kernel at
-// every M <= 16 and may change the split count; the default is any g >= 128)
+// Decode kernel (M <= 80, ceil(M/16) m-tiles): split count the heuristic
+// picks, whether a shape takes it, its workspace, and a launch with an
+// explicit split count (nsplit > 1 needs `ws` of decode_workspace_bytes).
+// g: the weight group size (groups of 64 and 32 can raise the split count,
+// whose scale table grows; the default stands for any g >= 128)
 int decode_splits(int N, int K, int g = 128);
 bool use_decode_kernel(int M, int N, int K, int g = 128);
 size_t decode_workspace_bytes(int M, int N, int K, int g = 128);

@@ -319,8 +319,8 @@ SkinnyCfg skinny_config(int M, int N, int K)
 
 size_t w4a16_workspace_bytes(int M, int N, int K, int g)
 {
-    // the decode kernel's split-K counters and partial sums (M <= 16); the
-    // skinny and tiled kernels need none
+    // the decode kernel's split-K counters and partial sums (decode-size
+    // batches, M <= 80); the skinny and tiled kernels need none
     return decode_workspace_bytes(M, N, K, g);
 }
 

@@ -408,7 +408,8 @@ int decode_splits(int N, int K, int g)
 // Decode workspace: the fixed counter region (W4A16_WS_COUNTER_BYTES, shared
 // by every W4A16 layout and written by nothing but the counters), then the
 // partial-sum slots.  0 when the shape is not split.
-// Whether M <= 16 runs the decode kernel rather than the skinny one (which
+// Whether a shape runs the decode kernel rather than the skinny one.  M <= 16
+// (against the skinny kernel, which
 // splits K between the 8 waves of a workgroup of 32 columns and needs no
 // cross-workgroup step).  Measured on MI355X (M = 4-16, interleaved repeats):
 // * two or fewer decode splits (wide N): the decode kernel;
