@@ -82,10 +82,12 @@ constexpr size_t W4A16_WS_COUNTER_BYTES = 65536;
 int decode_splits(int N, int K, int g = 128);
 bool use_decode_kernel(int M, int N, int K, int g = 128);
 size_t decode_workspace_bytes(int M, int N, int K, int g = 128);
+// ldc, ncols: C's row stride and the columns stored (default N, or N/2 for
+// the gated pair); a padded weight's call stores its logical columns only
 hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                                const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                                bool fuse_delta, int nsplit, void *ws, hipStream_t st,
-                               bool gated = false);
+                               bool gated = false, int ldc = -1, int ncols = -1);
 
 // Rows from which the tiled/mid kernels take over from the skinny one (the mid
 // kernel measured faster from about M = 80 on).

@@ -416,8 +416,9 @@ void describe_w4a16(int M, int N, int K, int g, bool delta, bool gated, char *bu
 //      as the gap) ----
 // The pack pads the weight to [Kp, Np] (codes 8, scales 0); a call copies A
 // into the workspace with zero columns up to Kp, runs the GEMM on the padded
-// shape, and crops the padded product to C.  All in the workspace after the
-// counter region: [counters | GEMM workspace][A padded][C padded].
+// shape, and crops the padded product to C (the decode kernel instead stores
+// C's logical columns directly).  All in the workspace after the counter
+// region: [counters | GEMM workspace][A padded][C padded].
 __global__ __launch_bounds__(256) void pad_cols_kernel(const uint16_t *__restrict__ A,
                                                        uint16_t *__restrict__ Ap, int M, int K,
                                                        int Kp)
@@ -485,6 +486,15 @@ hipError_t launch_w4a16_tail(const uint16_t *A, const uint32_t *W, const uint16_
         hipLaunchKernelGGL(pad_cols_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A,
                            Ap, M, K, Kp);
         Ause = Ap;
+    }
+    if (Np != N && M < TILED_MIN_M && use_decode_kernel(M, Np, Kp, gp)) {
+        // the decode kernel stores the logical columns straight into C (no
+        // padded product, no crop)
+        const int ns = decode_workspace_bytes(M, Np, Kp, gp) ? decode_splits(Np, Kp, gp) : 1;
+        hipError_t e = launch_w4a16_decode(Ause, W, S, D, C, M, Np, Kp, gp, fuse_delta, ns,
+                                           gemm ? ws : nullptr, st, false, N, N);
+        if (e != hipSuccess) return e;
+        return hipGetLastError();
     }
     uint16_t *Cuse = Np != N ? reinterpret_cast<uint16_t *>(p) : C;
     hipError_t e = launch_w4a16(Ause, W, S, D, Cuse, M, Np, Kp, gp, fuse_delta, gemm ? ws : nullptr, st);

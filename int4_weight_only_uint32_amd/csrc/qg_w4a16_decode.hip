@@ -47,7 +47,7 @@ template <int NT, int P, int WV, bool DELTA, bool GATED = false, int GPT = 1, in
 __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g,
-    int nsplit, unsigned *__restrict__ counters, float *__restrict__ partials)
+    int nsplit, unsigned *__restrict__ counters, float *__restrict__ partials, int ldc, int ncols)
 {
     static_assert(NT == 1, "the scale table holds one column per lane");
     static_assert(WV == 4 || WV == 8, "4 or 8 waves per workgroup");
@@ -284,9 +284,11 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
             if (j + i < n) step(kt_beg + j + i, i, last);
     }
 
-    // C rows 16 mt + 4 kq + r, columns (nt0 + t) * 16 + c; GATED: silu(gate)
-    // * up into C [M, Nh] by the gate waves (reached by every thread of the
-    // workgroup, or of none: the barrier is uniform)
+    // C rows 16 mt + 4 kq + r, columns (nt0 + t) * 16 + c below ncols, row
+    // stride ldc (a padded weight writes its logical columns straight into
+    // the caller's C); GATED: silu(gate) * up into C [M, Nh] by the gate
+    // waves (reached by every thread of the workgroup, or of none: the
+    // barrier is uniform)
     auto store = [&](const float4v (&v)[MT][NT]) {
         if (GATED) {
             if (wave >= 2)
@@ -313,7 +315,8 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * mt + 4 * kq + r;
-                    if (row < M) C[(size_t)row * N + col0 + 16 * t] = f2h(v[mt][t][r]);
+                    const int col = col0 + 16 * t;
+                    if (row < M && col < ncols) C[(size_t)row * ldc + col] = f2h(v[mt][t][r]);
                 }
     };
     if (nsplit == 1) {
@@ -464,7 +467,7 @@ size_t decode_workspace_bytes(int M, int N, int K, int g)
 template <bool DELTA, bool GATED = false, int GPT = 1, int MT = 1>
 static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                              const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
-                             int nsplit, void *ws, hipStream_t st)
+                             int nsplit, void *ws, hipStream_t st, int ldc, int ncols)
 {
     const int ncg = N / decode::COLS;
     unsigned *counters = nullptr;
@@ -485,16 +488,19 @@ static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_
     }
     hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT, MT>),
                        dim3(ncg * nsplit), dim3(64 * decode::WV), table, st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M,
-                       N, K, g, nsplit, counters, partials);
+                       N, K, g, nsplit, counters, partials, ldc, ncols);
     return hipGetLastError();
 }
 
 hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                                const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                                bool fuse_delta, int nsplit, void *ws, hipStream_t st,
-                               bool gated)
+                               bool gated, int ldc, int ncols)
 {
-    if (M > DECODE_MAX_M || N % decode::COLS || nsplit < 1 || (nsplit > 1 && !ws))
+    if (ldc < 0) ldc = gated ? N / 2 : N;
+    if (ncols < 0) ncols = gated ? N / 2 : N;
+    if (M > DECODE_MAX_M || N % decode::COLS || nsplit < 1 || (nsplit > 1 && !ws) ||
+        ncols > (gated ? N / 2 : N) || ldc < ncols || (gated && (ldc != N / 2 || ncols != N / 2)))
         return hipErrorInvalidValue;
     const bool dl = D && fuse_delta;
     const int gpt = g < KTILE ? KTILE / g : 1;
@@ -502,10 +508,10 @@ hipError_t launch_w4a16_decode(const uint16_t *A, const uint32_t *W, const uint1
 #define QG_DEC(GPT_, MT_)                                                                     \
     if (gpt == GPT_ && mt == MT_) {                                                           \
         if (gated)                                                                            \
-            return dl ? run_decode<true, true, GPT_, MT_>(A, W, S, D, C, M, N, K, g, nsplit, ws, st) \
-                      : run_decode<false, true, GPT_, MT_>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st); \
-        return dl ? run_decode<true, false, GPT_, MT_>(A, W, S, D, C, M, N, K, g, nsplit, ws, st)   \
-                  : run_decode<false, false, GPT_, MT_>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st); \
+            return dl ? run_decode<true, true, GPT_, MT_>(A, W, S, D, C, M, N, K, g, nsplit, ws, st, ldc, ncols) \
+                      : run_decode<false, true, GPT_, MT_>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st, ldc, ncols); \
+        return dl ? run_decode<true, false, GPT_, MT_>(A, W, S, D, C, M, N, K, g, nsplit, ws, st, ldc, ncols)   \
+                  : run_decode<false, false, GPT_, MT_>(A, W, S, nullptr, C, M, N, K, g, nsplit, ws, st, ldc, ncols); \
     }
     QG_DEC(1, 1) QG_DEC(2, 1) QG_DEC(4, 1)
     QG_DEC(1, 2) QG_DEC(1, 3) QG_DEC(1, 4) QG_DEC(1, 5)
