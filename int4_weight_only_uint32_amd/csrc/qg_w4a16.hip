@@ -555,18 +555,49 @@ __global__ __launch_bounds__(64) void group_sum_kernel(const uint16_t *__restric
     if (threadIdx.x == 0) a_sum[cell] = v;
 }
 
-// Stage 2: one thread per output cell: C += sum_g a_sum[m,g] * delta[g,n].
-__global__ __launch_bounds__(256) void correction_accum_kernel(const float *__restrict__ a_sum,
-                                                               const uint16_t *__restrict__ D,
-                                                               uint16_t *__restrict__ C, int N,
-                                                               int G, size_t total)
+// Stage 2: C += sum_g a_sum[m,g] * delta[g,n].  A wave takes 64 consecutive
+// columns (one per lane) and R rows: each delta value is read once and
+// applied to all R rows, whose a_sum values are the same for every lane
+// (scalar loads).  Per output the sum runs over g in order, one fma each.
+// R = 16 for large M (delta re-read M/16 times), 4 below M = 256 (four times
+// the waves for the same columns).
+template <int R>
+__global__ __launch_bounds__(64) void correction_accum_kernel(const float *__restrict__ a_sum,
+                                                              const uint16_t *__restrict__ D,
+                                                              uint16_t *__restrict__ C, int M,
+                                                              int N, int G)
 {
-    size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= total) return;
-    const size_t m = idx / N, n = idx % N;
-    float corr = 0.f;
-    for (int gi = 0; gi < G; ++gi) corr += a_sum[m * G + gi] * h2f(D[(size_t)gi * N + n]);
-    C[idx] = f2h(h2f(C[idx]) + corr);
+    const int n = blockIdx.x * 64 + threadIdx.x;
+    const int m0 = blockIdx.y * R;
+    const int rows = M - m0 < R ? M - m0 : R;
+    if (n >= N) return;                  // (no barrier in this kernel)
+    float corr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) corr[r] = 0.f;
+    const float *as = a_sum + (size_t)m0 * G;
+    int gi = 0;
+    for (; gi + 4 <= G; gi += 4) {       // four groups' loads in flight at once
+        float d[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) d[u] = h2f(D[(size_t)(gi + u) * N + n]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (r < rows) corr[r] = __builtin_fmaf(as[(size_t)r * G + gi + u], d[u], corr[r]);
+    }
+    for (; gi < G; ++gi) {
+        const float d = h2f(D[(size_t)gi * N + n]);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r < rows) corr[r] = __builtin_fmaf(as[(size_t)r * G + gi], d, corr[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (r < rows) {
+            uint16_t *cp = C + (size_t)(m0 + r) * N + n;
+            *cp = f2h(h2f(*cp) + corr[r]);
+        }
 }
 
 hipError_t launch_group_sum_correction(const uint16_t *A, const uint16_t *D, uint16_t *C,
@@ -578,9 +609,12 @@ hipError_t launch_group_sum_correction(const uint16_t *A, const uint16_t *D, uin
                        g, G, a_sum);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    size_t total = (size_t)M * N;
-    hipLaunchKernelGGL(correction_accum_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
-                       0, st, a_sum, D, C, N, G, total);
+    if (M >= 256)
+        hipLaunchKernelGGL(correction_accum_kernel<16>, dim3((unsigned)((N + 63) / 64), (unsigned)((M + 15) / 16)),
+                           dim3(64), 0, st, a_sum, D, C, M, N, G);
+    else
+        hipLaunchKernelGGL(correction_accum_kernel<4>, dim3((unsigned)((N + 63) / 64), (unsigned)((M + 3) / 4)),
+                           dim3(64), 0, st, a_sum, D, C, M, N, G);
     return hipGetLastError();
 }
 
