@@ -555,43 +555,59 @@ __global__ __launch_bounds__(64) void group_sum_kernel(const uint16_t *__restric
     if (threadIdx.x == 0) a_sum[cell] = v;
 }
 
-// Stage 2: C += sum_g a_sum[m,g] * delta[g,n].  A wave takes 64 consecutive
-// columns (one per lane) and R rows: each delta value is read once and
-// applied to all R rows, whose a_sum values are the same for every lane
-// (scalar loads).  Per output the sum runs over g in order, one fma each.
-// R = 16 for large M (delta re-read M/16 times), 4 below M = 256 (four times
-// the waves for the same columns).
+// Stage 2: C += sum_g a_sum[m,g] * delta[g,n].  A workgroup (one wave)
+// takes 64 consecutive columns (one per lane) and R rows: each delta value is
+// read once and applied to all R rows.  The rows' group sums, the same for
+// every lane, are staged in LDS 64 groups at a time (coalesced loads) and read
+// back four groups per 16-byte broadcast read.  Per output the sum runs over
+// g in order, one fma each.  R = 16 for large M (delta re-read M/16 times),
+// 4 below M = 256 (four times the waves for the same columns).
 template <int R>
 __global__ __launch_bounds__(64) void correction_accum_kernel(const float *__restrict__ a_sum,
                                                               const uint16_t *__restrict__ D,
                                                               uint16_t *__restrict__ C, int M,
                                                               int N, int G)
 {
-    const int n = blockIdx.x * 64 + threadIdx.x;
+    constexpr int GCH = 64;                       // groups per LDS chunk
+    __shared__ __attribute__((aligned(16))) float sa[R][GCH];
+    const int lane = threadIdx.x;
+    const int n = blockIdx.x * 64 + lane;
     const int m0 = blockIdx.y * R;
     const int rows = M - m0 < R ? M - m0 : R;
-    if (n >= N) return;                  // (no barrier in this kernel)
+    const bool col_ok = n < N;                    // (every lane reaches the barriers)
     float corr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) corr[r] = 0.f;
-    const float *as = a_sum + (size_t)m0 * G;
-    int gi = 0;
-    for (; gi + 4 <= G; gi += 4) {       // four groups' loads in flight at once
-        float d[4];
+    for (int g0 = 0; g0 < G; g0 += GCH) {
+        const int gn = G - g0 < GCH ? G - g0 : GCH;
+        __syncthreads();                          // the previous chunk's reads are done
+        for (int i = lane; i < R * GCH; i += 64) {
+            const int r = i / GCH, gg = i % GCH;
+            sa[r][gg] = (r < rows && gg < gn) ? a_sum[(size_t)(m0 + r) * G + g0 + gg] : 0.f;
+        }
+        __syncthreads();
+        if (!col_ok) continue;
+        int gg = 0;
+        for (; gg + 4 <= gn; gg += 4) {
+            float d[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) d[u] = h2f(D[(size_t)(gi + u) * N + n]);
+            for (int u = 0; u < 4; ++u) d[u] = h2f(D[(size_t)(g0 + gg + u) * N + n]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+            for (int r = 0; r < R; ++r) {
+                const float4v a4 = *reinterpret_cast<const float4v *>(&sa[r][gg]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (r < rows) corr[r] = __builtin_fmaf(a4[u], d[u], corr[r]);
+            }
+        }
+        for (; gg < gn; ++gg) {
+            const float d = h2f(D[(size_t)(g0 + gg) * N + n]);
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                if (r < rows) corr[r] = __builtin_fmaf(as[(size_t)r * G + gi + u], d[u], corr[r]);
+                if (r < rows) corr[r] = __builtin_fmaf(sa[r][gg], d, corr[r]);
+        }
     }
-    for (; gi < G; ++gi) {
-        const float d = h2f(D[(size_t)gi * N + n]);
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (r < rows) corr[r] = __builtin_fmaf(as[(size_t)r * G + gi], d, corr[r]);
-    }
+    if (!col_ok) return;
 #pragma unroll
     for (int r = 0; r < R; ++r)
         if (r < rows) {
