@@ -340,7 +340,11 @@ def test_w4a16_deterministic():
 
 
 # ------------------------------------------------------ correction stage --
-@pytest.mark.parametrize("M,K,N,g", [(5, 1024, 256, 128), (64, 4096, 384, 4096), (130, 512, 128, 256)])
+# rows in blocks of 4 (M < 256) or 16 (M >= 256), ragged last blocks; the
+# groups in LDS chunks of 64 (G = 65, 72: a second chunk) and runs of 4 (G = 9,
+# 65: a remainder of one)
+@pytest.mark.parametrize("M,K,N,g", [(5, 1024, 256, 128), (64, 4096, 384, 4096), (130, 512, 128, 256),
+                                     (17, 1152, 128, 128), (300, 8320, 256, 128), (257, 2304, 128, 32)])
 def test_group_sum_correction(M, K, N, g):
     note(f"group_sum_correction M={M} K={K} N={N} g={g}")
     c = synth.w4a16_case(M, K, N, g, asym=True, stream=84, case_id=M)
