@@ -46,8 +46,7 @@
  *   - Shapes: K % 128 == 0 and N % 128 == 0 (the tile multiples the pages'
  *     dispatcher requires), M >= 1.  group_size must divide K and be 32, 64,
  *     a multiple of 128, or K; -1 is accepted as an alias of K (per-column
- *     scales).  qgemm_w4a8 takes group sizes of 64 and up (a group of 32
- *     would split its 64-k int8 MFMA step: QG_ERR_UNSUPPORTED).
+ *     scales), for every operation.
  *     pack_int4_weights, qgemm_w4a16 and qgemm_w4a8 also take any K, N >= 1
  *     ("tails"):
  *     group_size is then 32, 64, a multiple of 128 (the last group of g

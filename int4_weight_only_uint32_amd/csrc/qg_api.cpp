@@ -315,10 +315,6 @@ size_t qg_workspace_bytes(int op, int M, int N, int K, int group_size, int num_e
         return corr_ws_bytes(M, K, g);
     case QG_OP_W4A8:
         if (check_shape_tail("qg_workspace_bytes", M < 1 ? 1 : M, N, K, &g) != QG_OK) return (size_t)-1;
-        if (g < 64) {
-            fail(QG_ERR_UNSUPPORTED, "qg_workspace_bytes: W4A8 group_size %d below 64", g);
-            return (size_t)-1;
-        }
         return qg::is_tail_shape(N, K, g) ? qg::w4a8_tail_workspace_bytes(M < 1 ? 1 : M, N, K, g) : 0;
     case QG_OP_PACK:
         if (check_shape("qg_workspace_bytes", M < 1 ? 1 : M, N, K, &g) != QG_OK) return (size_t)-1;
@@ -482,9 +478,6 @@ int qgemm_w4a8(const int8_t *A_q, const float *a_scale, const uint32_t *w_packed
     int g = group_size;
     int rc = check_shape_tail("qgemm_w4a8", M_total, N, K, &g);
     if (rc) return rc;
-    if (g < 64)
-        return fail(QG_ERR_UNSUPPORTED,
-                    "qgemm_w4a8: group_size %d splits a 64-k int8 MFMA step (64 or more)", g);
     const bool tail = qg::is_tail_shape(N, K, g);
     if (!A_q || !a_scale || !w_packed || !w_scale || !C)
         return fail(QG_ERR_INVALID_ARG, "qgemm_w4a8: NULL A_q/a_scale/w_packed/w_scale/C");

@@ -178,4 +178,13 @@ __device__ inline int4v mfma_i8(int4v a, int4v b, int4v c)
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 int8 MFMA: 8 bytes of A and of B per lane, each passed as its
+// (bytes 0..3, bytes 4..7) words
+__device__ inline int4v mfma_i8_k32(int a0, int a1, int b0, int b1, int4v c)
+{
+    const long a = (long)(((unsigned long)(unsigned)a1 << 32) | (unsigned)a0);
+    const long b = (long)(((unsigned long)(unsigned)b1 << 32) | (unsigned)b0);
+    return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, c, 0, 0, 0);
+}
+
 } // namespace qg

@@ -39,10 +39,15 @@ namespace qg {
 // its use would wait for every load issued before it.  DELTA: the group
 // deltas ride in the ring beside the scales, and two more MFMAs per 16-row
 // tile and k-tile sum the tile's activations per row.
-// H2 (groups of 64): the two 64-k MFMA steps of a k-tile are the tile's two
-// groups (the low nibbles hold k 0..63 of the tile, the high ones k 64..127),
-// each product scaled on its own; G1 is then true as well.
-template <int NT, int P, bool DEBUG, bool G1, bool DELTA, bool H2 = false>
+// GQ: weight groups per k-tile (G1 is then true as well).  GQ = 2 (groups of
+// 64): the two 64-k MFMA steps of a k-tile are the tile's two groups (the low
+// nibbles hold k 0..63 of the tile, the high ones k 64..127).  GQ = 4 (groups
+// of 32): each step's operands split into their two 8-byte halves -- bytes
+// 0..7 of lane kq hold k 8kq .. 8kq + 7 of the step, bytes 8..15 k 32 + 8kq ..
+// 39 + 8kq, on the activation side as on the code side -- so each group of 32
+// is one 16x16x32 int8 MFMA on one half.  Each group's product is scaled on
+// its own.
+template <int NT, int P, bool DEBUG, bool G1, bool DELTA, int GQ = 1>
 __global__ __launch_bounds__(256, 2) void w4a8_kernel(
     const int8_t *__restrict__ Aq, const float *__restrict__ a_scale,
     const uint4v *__restrict__ Wall, const uint16_t *__restrict__ Sall,
@@ -131,7 +136,6 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
         // register ring: activations, codes, group scales (32-bit pair holding
         // this lane's column, half c & 1)
         uint4v ra[P][2], rw[P][NT];
-        constexpr int GQ = H2 ? 2 : 1;               // groups per k-tile
         uint32_t rs[P][NT][GQ], rd[P][NT][GQ];
         auto load = [&](int kt, int sl) {
             const int k = kt < KT ? kt : KT - 1;
@@ -160,20 +164,19 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
             const int st = kt & 1;
             store_a(st, ra[sl]);
             CodeOpsI8 b[NT];
-            float sv[NT], dv[NT], sv2[NT], dv2[NT];   // (sv2, dv2: H2's second group)
+            float sv[NT][GQ], dv[NT][GQ];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 b[t] = split_codes_i8(rw[sl][t]);
-                sv[t] = h2f((uint16_t)(rs[sl][t][0] >> sh));
-                dv[t] = DELTA ? h2f((uint16_t)(rd[sl][t][0] >> sh)) : 0.0f;
-                sv2[t] = H2 ? h2f((uint16_t)(rs[sl][t][GQ - 1] >> sh)) : 0.0f;
-                dv2[t] = H2 && DELTA ? h2f((uint16_t)(rd[sl][t][GQ - 1] >> sh)) : 0.0f;
                 pin(b[t].op[0]);
                 pin(b[t].op[1]);
-                pin(sv[t]);
-                if (DELTA) pin(dv[t]);
-                if (H2) pin(sv2[t]);
-                if (H2 && DELTA) pin(dv2[t]);
+#pragma unroll
+                for (int q = 0; q < GQ; ++q) {
+                    sv[t][q] = h2f((uint16_t)(rs[sl][t][q] >> sh));
+                    dv[t][q] = DELTA ? h2f((uint16_t)(rd[sl][t][q] >> sh)) : 0.0f;
+                    pin(sv[t][q]);
+                    if (DELTA) pin(dv[t][q]);
+                }
             }
             load(kt + P, sl);
             debug_stage_sync();
@@ -185,44 +188,71 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
                 alo[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 0, kq)]);
                 ahi[mt] = __builtin_bit_cast(int4v, As[st][slot(row, 1, kq)]);
             }
-            if (H2) {
-                // two groups per k-tile: products and activation sums per 64-k step
+            if (GQ > 1) {
+                // several groups per k-tile: group q's product (and activation
+                // sums) from its own MFMA: the 64-k step q (GQ = 2) or half q % 2
+                // of step q / 2 (GQ = 4)
                 const int4v z4 = {0, 0, 0, 0};
                 const int4v ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-                int4v qs0[MT], qs1[MT];
+                auto group_mfma = [&](int q, int4v a_lo, int4v a_hi, int4v b_lo, int4v b_hi) {
+                    const int4v av = q * 2 / GQ == 0 ? a_lo : a_hi;
+                    const int4v bv = q * 2 / GQ == 0 ? b_lo : b_hi;
+                    if (GQ == 2) return mfma_i8(av, bv, z4);
+                    return (q & 1) ? mfma_i8_k32(av.z, av.w, bv.z, bv.w, z4)
+                                   : mfma_i8_k32(av.x, av.y, bv.x, bv.y, z4);
+                };
+                const int gi = GQ * kt;
+                // group q's scaled product (its delta term follows separately)
+                auto group_term = [&](int mt, int t, int q) {
+                    const int4v p = group_mfma(q, alo[mt], ahi[mt], b[t].op[0], b[t].op[1]);
+                    if (DEBUG) {
+                        const int4v pq = p >> 4;   // exact: multiples of 16
+                        accf[mt][t] += sv[t][q] * __builtin_convertvector(pq, float4v);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    qs0[mt] = DELTA ? mfma_i8(alo[mt], ones, z4) : z4;
-                    qs1[mt] = DELTA ? mfma_i8(ahi[mt], ones, z4) : z4;
-                }
-                const int gi = 2 * kt;
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = m0 + 16 * mt + 4 * kq + r;
+                            if (row < r1)
+                                acc_debug[((size_t)row * G + gi + q) * N + col0 + 16 * t] = pq[r];
+                        }
+                    } else {
+                        accf[mt][t] += (sv[t][q] * 0.0625f) * __builtin_convertvector(p, float4v);
+                    }
+                };
+                if (GQ == 2) {
+                    // every m-tile's two activation sums first, then n-tile by n-tile
+                    int4v qs[MT][GQ];
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int q = 0; q < GQ; ++q) qs[mt][q] = DELTA ? group_mfma(q, alo[mt], ahi[mt], ones, ones) : z4;
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                            for (int q = 0; q < GQ; ++q) group_term(mt, t, q);
+#pragma unroll
+                            for (int q = 0; q < GQ; ++q)
+                                if (DELTA) accf[mt][t] += dv[t][q] * __builtin_convertvector(qs[mt][q], float4v);
+                        }
+                } else {
+                    // m-tile by m-tile: its four sums live across its n-tiles only
+                    // (all sixteen at once would spill)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
-                        const int4v p0 = mfma_i8(alo[mt], b[t].op[0], z4);
-                        const int4v p1 = mfma_i8(ahi[mt], b[t].op[1], z4);
-                        if (DEBUG) {
-                            const int4v q0 = p0 >> 4, q1 = p1 >> 4;   // exact: multiples of 16
-                            accf[mt][t] += sv[t] * __builtin_convertvector(q0, float4v);
-                            accf[mt][t] += sv2[t] * __builtin_convertvector(q1, float4v);
+                        int4v qs[GQ];
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int row = m0 + 16 * mt + 4 * kq + r;
-                                if (row < r1) {
-                                    acc_debug[((size_t)row * G + gi) * N + col0 + 16 * t] = q0[r];
-                                    acc_debug[((size_t)row * G + gi + 1) * N + col0 + 16 * t] = q1[r];
-                                }
-                            }
-                        } else {
-                            accf[mt][t] += (sv[t] * 0.0625f) * __builtin_convertvector(p0, float4v);
-                            accf[mt][t] += (sv2[t] * 0.0625f) * __builtin_convertvector(p1, float4v);
-                        }
-                        if (DELTA) {
-                            accf[mt][t] += dv[t] * __builtin_convertvector(qs0[mt], float4v);
-                            accf[mt][t] += dv2[t] * __builtin_convertvector(qs1[mt], float4v);
+                        for (int q = 0; q < GQ; ++q) qs[q] = DELTA ? group_mfma(q, alo[mt], ahi[mt], ones, ones) : z4;
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+                            for (int q = 0; q < GQ; ++q) group_term(mt, t, q);
+#pragma unroll
+                            for (int q = 0; q < GQ; ++q)
+                                if (DELTA) accf[mt][t] += dv[t][q] * __builtin_convertvector(qs[q], float4v);
                         }
                     }
+                }
                 return;
             }
             // G1 (one k-tile per group): each tile's group sum starts from a zero
@@ -254,12 +284,12 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
                     // conversion is exact, so scaling it by s/16 (exact) gives the
                     // same fma result as scaling acci >> 4 by s (longer groups, e.g.
                     // one per column, round that conversion once: 2^-24 relative)
-                    const float sv16 = sv[t] * 0.0625f;
+                    const float sv16 = sv[t][0] * 0.0625f;
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         if (DEBUG) {
                             const int4v qv = acci[mt][t] >> 4;   // exact: terms are multiples of 16
-                            accf[mt][t] += sv[t] * __builtin_convertvector(qv, float4v);
+                            accf[mt][t] += sv[t][0] * __builtin_convertvector(qv, float4v);
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 const int row = m0 + 16 * mt + 4 * kq + r;
@@ -270,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
                             accf[mt][t] += sv16 * __builtin_convertvector(acci[mt][t], float4v);
                         }
                         // the delta term: |qsum| <= 127 g < 2^24, exact in fp32
-                        if (DELTA) accf[mt][t] += dv[t] * __builtin_convertvector(qsum[mt], float4v);
+                        if (DELTA) accf[mt][t] += dv[t][0] * __builtin_convertvector(qsum[mt], float4v);
                         if (!G1) acci[mt][t] = int4v{0, 0, 0, 0};
                     }
                 }
@@ -343,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
     }
 }
 
-template <int NT, int P, bool DEBUG, bool G1, bool DELTA, bool H2 = false>
+template <int NT, int P, bool DEBUG, bool G1, bool DELTA, int GQ = 1>
 static hipError_t run_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W,
                            const uint16_t *S, const uint16_t *D, const int32_t *offsets, int E,
                            int M_total, int max_rows, int N, int K, int g, uint16_t *C,
@@ -351,13 +381,13 @@ static hipError_t run_w4a8(const int8_t *Aq, const float *a_scale, const uint32_
 {
     const int NT16 = N / NTILE;
     dim3 grid((unsigned)((NT16 + 4 * NT - 1) / (4 * NT)), (unsigned)((max_rows + 63) / 64), (unsigned)E);
-    hipLaunchKernelGGL((w4a8_kernel<NT, P, DEBUG, G1, DELTA, H2>), grid, dim3(256), 0, st, Aq, a_scale,
+    hipLaunchKernelGGL((w4a8_kernel<NT, P, DEBUG, G1, DELTA, GQ>), grid, dim3(256), 0, st, Aq, a_scale,
                        reinterpret_cast<const uint4v *>(W), S, D, offsets, M_total, N, K, g, C,
                        acc_debug);
     return hipGetLastError();
 }
 
-template <bool DEBUG, bool G1, bool H2 = false>
+template <bool DEBUG, bool G1, int GQ = 1>
 static hipError_t run_w4a8_d(const int8_t *Aq, const float *a_scale, const uint32_t *W,
                              const uint16_t *S, const uint16_t *D, const int32_t *offsets, int E,
                              int M_total, int max_rows, int N, int K, int g, uint16_t *C,
@@ -368,8 +398,8 @@ static hipError_t run_w4a8_d(const int8_t *Aq, const float *a_scale, const uint3
     // With deltas and groups of several k-tiles the group's activation sums
     // stay live across tiles too: a ring of 2 (204 VGPRs) instead of 3, which
     // would spill at two workgroups per CU.
-    return D ? run_w4a8<2, G1 && !H2 ? 3 : 2, DEBUG, G1, true, H2>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)
-             : run_w4a8<2, 3, DEBUG, G1, false, H2>(Aq, a_scale, W, S, nullptr, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
+    return D ? run_w4a8<2, G1 && GQ == 1 ? 3 : 2, DEBUG, G1, true, GQ>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)
+             : run_w4a8<2, GQ == 4 ? 2 : 3, DEBUG, G1, false, GQ>(Aq, a_scale, W, S, nullptr, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
 }
 
 // ---- shapes with tails (K or N not a multiple of 128): the packs are padded
@@ -407,10 +437,15 @@ hipError_t launch_w4a8(const int8_t *Aq, const float *a_scale, const uint32_t *W
 {
     if (g == KTILE / 2) {   // groups of 64
         if (acc_debug)
-            return run_w4a8_d<true, true, true>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
-        return run_w4a8_d<false, true, true>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st);
+            return run_w4a8_d<true, true, 2>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
+        return run_w4a8_d<false, true, 2>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st);
     }
-    if (g < KTILE) return hipErrorInvalidValue;   // groups of 32 split a 64-k MFMA step
+    if (g == KTILE / 4) {   // groups of 32
+        if (acc_debug)
+            return run_w4a8_d<true, true, 4>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st);
+        return run_w4a8_d<false, true, 4>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, nullptr, st);
+    }
+    if (g < KTILE) return hipErrorInvalidValue;   // no other group below a k-tile
     const bool g1 = g == KTILE;
     if (acc_debug)
         return g1 ? run_w4a8_d<true, true>(Aq, a_scale, W, S, D, offsets, E, M_total, max_rows, N, K, g, C, acc_debug, st)

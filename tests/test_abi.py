@@ -157,14 +157,14 @@ def test_w4a8_validation():
     tail_acc[14], tail_acc[15] = P(0x100000), 1 << 30
     assert L.qgemm_w4a8(*tail_acc) == qg.QG_ERR_UNSUPPORTED
     assert L.qgemm_w4a8(*args(D=P(0x10001))) == qg.QG_ERR_INVALID_ARG  # misaligned deltas
-    g32 = args()
-    g32[11] = 32                                                       # splits a 64-k int8 step
-    assert L.qgemm_w4a8(*g32) == qg.QG_ERR_UNSUPPORTED
-    assert b"64" in L.qg_last_error()
-    g64 = args()
-    g64[11] = 64
-    assert L.qgemm_w4a8(*g64) == qg.QG_ERR_DEVICE                      # served
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 64, 1024, 1024, 64, 1) == 0
+    for g in (32, 64):                                                 # served
+        gs = args()
+        gs[11] = g
+        assert L.qgemm_w4a8(*gs) == qg.QG_ERR_DEVICE
+        assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 64, 1024, 1024, g, 1) == 0
+    g48 = args(K=1152)
+    g48[11] = 48                                                       # divides K, not 32, 64 or 128k
+    assert L.qgemm_w4a8(*g48) == qg.QG_ERR_UNSUPPORTED
 
 
 def test_group_sum_correction_validation():

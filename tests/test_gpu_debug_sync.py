@@ -95,7 +95,7 @@ def test_swiglu_matches_debug_sync_build(libs, M, K, N):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("g,asym", [(128, False), (128, True), (256, False), (64, True)])
+@pytest.mark.parametrize("g,asym", [(128, False), (128, True), (256, False), (64, True), (32, False), (32, True)])
 def test_w4a8_matches_debug_sync_build(libs, g, asym):
     note(f"debug-sync w4a8 8x64 K=2048 N=7168 g={g} asym={asym}")
     c = synth.w4a8_case(8, 64, 2048, 7168, g, stream=96, case_id=g + asym, asym=asym)

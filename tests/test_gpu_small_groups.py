@@ -6,7 +6,8 @@ ones), so the decode and skinny kernels scale each step's products with its
 own group's scale and delta, the 8-wave mid kernel takes its low- and
 high-nibble sums as the two groups of 64, and the generic tiled kernels
 dequantize each step with its group's scale; the grouped W4A8 kernel takes groups of 64 (one 64-k int8
-MFMA step each).  Checked against the oracle, which applies W = q s + z per
+MFMA step each) and of 32 (one 16x16x32 int8 MFMA on each 8-byte half of a
+step's operands).  Checked against the oracle, which applies W = q s + z per
 group of g consecutive k ("Marlin INT4 on Ada - how it works", "The core
 mismatch: symmetric vs asymmetric"), to the W4A16 bar (relative Frobenius
 <= 2e-3 and the elementwise guard) with AWQ-style zero-points (delta as large
@@ -114,25 +115,26 @@ def test_swiglu_small_groups(M, K, N, g):
     assert elementwise_guard(got[rows], ref) <= 0
 
 
+@pytest.mark.parametrize("g", [64, 32])
 @pytest.mark.parametrize("asym", [False, True])
-def test_w4a8_groups_of_64(asym):
-    """8 experts x 64 tokens with ragged groups, K 2048, N 1024: the integer
+def test_w4a8_small_groups(asym, g):
+    """4 experts with ragged rows (one empty), K 2048, N 1024: the integer
     group products (acc_debug) bit-exact against the oracle's, C to 1e-2."""
-    c = synth.w4a8_case(4, 0, 2048, 1024, 64, signed_scales=not asym, stream=98,
-                        case_id=5000 + asym, rows=[70, 0, 33, 64], asym=asym)
-    note(f"small groups w4a8 g=64 asym={asym}")
-    packs = [qg.pack(dev(c.q[e]), dev(c.s[e]), dev(c.z[e]) if asym else None, 64)
+    c = synth.w4a8_case(4, 0, 2048, 1024, g, signed_scales=not asym, stream=98,
+                        case_id=5000 + asym + g, rows=[70, 0, 33, 64], asym=asym)
+    note(f"small groups w4a8 g={g} asym={asym}")
+    packs = [qg.pack(dev(c.q[e]), dev(c.s[e]), dev(c.z[e]) if asym else None, g)
              for e in range(c.E)]
     W = torch.stack([p.w for p in packs]).contiguous()
     S = torch.stack([p.scale for p in packs]).contiguous()
     D = torch.stack([p.delta for p in packs]).contiguous() if asym else None
     mr = int(np.max(np.diff(c.offsets)))
-    acc = torch.zeros((c.M_total, c.K // 64, c.N), dtype=torch.int32, device="cuda")
-    C = qg.w4a8(dev(c.Aq), dev(c.a_scale), W, S, dev(c.offsets), c.E, mr, c.N, 64,
+    acc = torch.zeros((c.M_total, c.K // g, c.N), dtype=torch.int32, device="cuda")
+    C = qg.w4a8(dev(c.Aq), dev(c.a_scale), W, S, dev(c.offsets), c.E, mr, c.N, g,
                 acc_debug=acc, w_delta=D)
-    C2 = qg.w4a8(dev(c.Aq), dev(c.a_scale), W, S, dev(c.offsets), c.E, mr, c.N, 64, w_delta=D)
+    C2 = qg.w4a8(dev(c.Aq), dev(c.a_scale), W, S, dev(c.offsets), c.E, mr, c.N, g, w_delta=D)
     torch.cuda.synchronize()
-    ref, ref_acc = oracle.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, 64, fold=True, z=c.z)
+    ref, ref_acc = oracle.w4a8(c.Aq, c.a_scale, c.q, c.s, c.offsets, g, fold=True, z=c.z)
     assert np.array_equal(host(acc).astype(np.int64), ref_acc)
     for out in (C, C2):
         got = host(out).astype(np.float64)

@@ -1,6 +1,6 @@
 """GPU parity of the grouped W4A8 GEMM over a seeded sweep of expert batches:
 1 to 8 experts with ragged row counts (empty experts included), K and N with
-and without tails, groups of 64, 128, 256 and one group over K, symmetric
+and without tails, groups of 32, 64, 128, 256 and one group over K, symmetric
 weights with random-sign scales and AWQ-style zero-points.  The integer group
 products (acc_debug, where the shape has no tail) are compared bit for bit
 and C to the W4A8 bar against the oracle ("HyperQwen ...", "int8 张量核实战数值
@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-2
 
 
-def _cases(n=40, seed=7168):
+def _cases(n=40, seed=7168, groups=(64, 128, 256, -1)):
     r = np.random.RandomState(seed)
     out = []
     while len(out) < n:
@@ -27,7 +27,7 @@ def _cases(n=40, seed=7168):
         rows = [int(x) if r.rand() > 0.15 else 0 for x in r.randint(1, 200, size=E)]
         K = int(r.choice([256, 512, 1000, 2048]))
         N = int(r.choice([128, 300, 1024, 2048]))
-        g = int(r.choice([64, 128, 256, -1]))
+        g = int(r.choice(list(groups)))
         g = K if g == -1 else g
         if g > K or (g >= 128 and g % 128 and g != K) or sum(rows) * K * N > (1 << 29):
             continue
@@ -37,7 +37,8 @@ def _cases(n=40, seed=7168):
     return out
 
 
-@pytest.mark.parametrize("rows,K,N,g,asym", _cases())
+# the 40 mixed-group batches, then 12 with groups of 32
+@pytest.mark.parametrize("rows,K,N,g,asym", _cases() + _cases(12, 3232, (32,)))
 def test_w4a8_sweep(rows, K, N, g, asym):
     E = len(rows)
     c = synth.w4a8_case(E, 0, K, N, g, signed_scales=not asym, stream=87,
