@@ -19,7 +19,8 @@
 namespace qg {
 namespace {
 
-// int8 code of x at scale sc > 0, i.e. clamp(rint(x / sc), -127, 127) with
+// The code pass (`codes` below).  The int8 code of x at scale sc > 0 is
+// clamp(rint(x / sc), -127, 127) with
 // x / sc one correctly rounded binary32 division (sc == 0 only for a row of
 // zeros: code 0).  The division is costly, so the code is first taken from
 // y = x * inv, inv = 1 / sc correctly rounded: |y - x/sc| stays below 2^-15
@@ -27,15 +28,13 @@ namespace {
 // correctly rounded quotient is within 2^-18 of x/sc, so both round to the
 // same integer unless y lies within 2^-15 + 2^-18 of a half-integer.  Only
 // then (|y - rint(y)| within 2^-12 of 1/2, rare) is the division done.
-__device__ inline unsigned q8(float x, float sc, float inv)
-{
-    const float y = x * inv;
-    float r = __builtin_rintf(y);
-    if (__builtin_fabsf(__builtin_fabsf(y - r) - 0.5f) < 0x1p-12f) r = __builtin_rintf(x / sc);
-    r = sc > 0.0f ? r : 0.0f;
-    r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
-    return (unsigned)(int)r & 0xffu;
-}
+// Rounding: y + 1.5 * 2^23 lands in [2^23, 2^24), where the spacing of
+// binary32 is 1, so the sum is y rounded to an integer (nearest, ties to
+// even) and its low significand byte is that integer's two's complement
+// byte -- the code, taken from the bits without a float-to-int conversion.
+// The clamp never acts: |x| <= max_k |A[m,k]| makes |x / sc| at most 127 (1 +
+// 2^-23), so |rint| <= 127 on both routes.  The eight values of a chunk
+// share one branch to the division fallback.
 
 // WPR waves per row, 4 / WPR rows per 256-thread workgroup.  Each lane takes
 // 16-byte chunks of 8 values, the waves of a row interleaved chunk by chunk.
@@ -102,13 +101,30 @@ __global__ __launch_bounds__(256) void quantize_rows_int8_kernel(
     if (part == 0 && lane == 0) a_scale[row] = sc;
     uint2v *q = reinterpret_cast<uint2v *>(Aq + (size_t)row * K);
     auto codes = [&](const uint4v &v) {
+        constexpr float MAGIC = 0x1.8p23f;
+        float x[8], t[8];
+        bool nd[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            x[j] = h2f((uint16_t)(v[j / 2] >> (16 * (j & 1))));
+            const float y = x[j] * inv;
+            t[j] = y + MAGIC;
+            const float r = t[j] - MAGIC;
+            nd[j] = __builtin_fabsf(__builtin_fabsf(y - r) - 0.5f) < 0x1p-12f;
+        }
+        if (nd[0] | nd[1] | nd[2] | nd[3] | nd[4] | nd[5] | nd[6] | nd[7]) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (nd[j]) t[j] = x[j] / sc + MAGIC;
+        }
         unsigned out[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const unsigned w0 = v[2 * h], w1 = v[2 * h + 1];
-            out[h] = q8(h2f((uint16_t)w0), sc, inv) | q8(h2f((uint16_t)(w0 >> 16)), sc, inv) << 8 |
-                     q8(h2f((uint16_t)w1), sc, inv) << 16 |
-                     q8(h2f((uint16_t)(w1 >> 16)), sc, inv) << 24;
+            const unsigned a0 = __builtin_bit_cast(unsigned, t[4 * h]), a1 = __builtin_bit_cast(unsigned, t[4 * h + 1]);
+            const unsigned b0 = __builtin_bit_cast(unsigned, t[4 * h + 2]), b1 = __builtin_bit_cast(unsigned, t[4 * h + 3]);
+            const unsigned pa = __builtin_amdgcn_perm(a1, a0, 0x0c0c0400u);
+            const unsigned pb = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+            out[h] = __builtin_amdgcn_perm(pb, pa, 0x05040100u);
         }
         return uint2v{out[0], out[1]};
     };
