@@ -22,6 +22,7 @@
 namespace qg {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
@@ -82,6 +83,42 @@ __device__ inline CodeOps split_codes(uint4v w)
 // unsigned byte 16 v into the signed byte 16 (v - 8).  Likewise for the odd
 // nibbles with (x & 0xF0F0F0F0).  Returns the two 16x16x64 int8 operands of
 // the tile: [0] covers k-steps 0,1 of the fp16 numbering, [1] k-steps 2,3.
+// (x & m) | c as one v_and_or_b32, the mask in a scalar register and c in a
+// vector register (with two literal constants the compiler emits an AND and
+// an OR)
+__device__ inline unsigned and_or_b32(unsigned x, unsigned m, unsigned c)
+{
+    unsigned r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+    return r;
+}
+
+// The codes of one lane's 128-bit word as exact binary16 values v - 8, in
+// split_codes' operand order (k-steps 0, 1 from the low nibbles, 2, 3 from the
+// high ones).  A low nibble ORed into 0x6400 (1024, spacing 1) reads 1024 + v,
+// a high nibble (bits 4..7 of a half) ORed into 0x5400 (64, spacing 1/16)
+// reads 64 + v, and subtracting 1032 or 72 is exact.  mag_lo, mag_hi: 0x64006400
+// and 0x54005400, held in vector registers by the caller.
+__device__ inline CodeOps center_codes(uint4v w, unsigned mag_lo, unsigned mag_hi)
+{
+    const half2v off_lo = {(_Float16)1032.f, (_Float16)1032.f};
+    const half2v off_hi = {(_Float16)72.f, (_Float16)72.f};
+    auto lo = [&](unsigned x) {
+        return __builtin_bit_cast(unsigned, __builtin_bit_cast(half2v, and_or_b32(x, 0x000F000Fu, mag_lo)) - off_lo);
+    };
+    auto hi = [&](unsigned x) {
+        return __builtin_bit_cast(unsigned, __builtin_bit_cast(half2v, and_or_b32(x, 0x00F000F0u, mag_hi)) - off_hi);
+    };
+    const unsigned x0 = w.x, x1 = w.y, x2 = w.z, x3 = w.w;
+    const unsigned y0 = x0 >> 8, y1 = x1 >> 8, y2 = x2 >> 8, y3 = x3 >> 8;
+    CodeOps r;
+    r.lo[0] = __builtin_bit_cast(half8, uint4v{lo(x0), lo(y0), lo(x1), lo(y1)});
+    r.lo[1] = __builtin_bit_cast(half8, uint4v{lo(x2), lo(y2), lo(x3), lo(y3)});
+    r.hi[0] = __builtin_bit_cast(half8, uint4v{hi(x0), hi(y0), hi(x1), hi(y1)});
+    r.hi[1] = __builtin_bit_cast(half8, uint4v{hi(x2), hi(y2), hi(x3), hi(y3)});
+    return r;
+}
+
 struct CodeOpsI8 {
     int4v op[2];
 };

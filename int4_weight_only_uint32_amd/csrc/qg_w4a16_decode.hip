@@ -1,9 +1,10 @@
 // W4A16 decode kernel (M <= 16, and up to 80 with several m-tiles):
 // activation tile shared through LDS, split-K
-// with a last-arriver reduction.  Arithmetic as in the skinny kernel
-// ("Marlin INT4 on Ada - how it works", "The core mismatch: symmetric vs
-// asymmetric"): codes as exact fp16 subnormals in the MFMAs, group scale and
-// delta applied on the fp32 accumulators.
+// with a last-arriver reduction.  Arithmetic ("Marlin INT4 on Ada - how it
+// works", "The core mismatch: symmetric vs asymmetric"): with one m-tile as in
+// the skinny kernel, codes as exact fp16 subnormals in the MFMAs, group scale
+// and delta applied on the fp32 accumulators; with several, the weights
+// (v - 8) s + delta dequantized to fp16 in registers (DQ below).
 #include "qg_device.h"
 #include "qg_launch.h"
 
@@ -43,7 +44,12 @@ namespace qg {
 // MT: 16-row m-tiles (M <= 16 MT).  Each k-tile of A is 16 MT rows (MT
 // 16-byte loads per thread), every wave multiplies each of its code tiles
 // into all MT m-tiles, and the split-K slots hold 16 MT rows.
-template <int NT, int P, int WV, bool DELTA, bool GATED = false, int GPT = 1, int MT = 1>
+// DQ: the codes are instead dequantized in registers to binary16 weights
+// (v - 8) s + delta (one rounding, v_pk_fma_f16; the group's scale and delta
+// from the table) and the MFMAs accumulate the product itself: no group sums
+// of A and no scaling of the accumulators, for about 16 more VALU
+// instructions per code tile, which the MT m-tiles share.
+template <int NT, int P, int WV, bool DELTA, bool GATED = false, int GPT = 1, int MT = 1, bool DQ = false>
 __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g,
@@ -140,11 +146,21 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const unsigned w_off = (unsigned)lane * 16u;
     const int gbase = (kt_beg * KTILE) / g;
 
-    float4v acc[MT][NT];
+    // DQ: k-steps 0, 1 accumulate into acc, 2, 3 into acc2 (two short MFMA
+    // chains per k-tile instead of one of four), added after the loop
+    float4v acc[MT][NT], acc2[DQ ? MT : 1][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NT; ++t) {
+            acc[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
+            if (DQ) acc2[mt][t] = float4v{0.f, 0.f, 0.f, 0.f};
+        }
+    unsigned mag_lo = 0, mag_hi = 0;   // DQ: center_codes' constants in vector registers
+    if (DQ) {
+        asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(mag_lo));
+        asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(mag_hi));
+    }
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
     const float4v fzero = {0.f, 0.f, 0.f, 0.f};
 
@@ -163,6 +179,51 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
             w[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off, (t * KT + kt) * 1024, 0));
     };
     auto finish = [&](int buf, int kt, const CodeOps (&ops)[NT]) {
+    if constexpr (DQ) {
+        // the binary16 weights of the tile's four k-steps, each step with its
+        // group's scale and delta (both halves of a register alike)
+        const uint32_t *sdp = &sdt[((kt * KTILE) / g - gbase) * COLS + 16 * wave + c];
+        half8 bq[NT][4];
+#pragma unroll
+        for (int q = 0; q < GPT; ++q) {
+            const uint32_t sd = sdp[q * COLS];
+            const half2v s2 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(sd, sd, 0x01000100u));
+            const half2v d2 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(sd, sd, 0x03020302u));
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const half8 cs[4] = {ops[t].lo[0], ops[t].lo[1], ops[t].hi[0], ops[t].hi[1]};
+#pragma unroll
+                for (int k = q * (4 / GPT); k < (q + 1) * (4 / GPT); ++k) {
+                    const uint4v cw = __builtin_bit_cast(uint4v, cs[k]);
+                    unsigned out[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // the element through a scalar: a bit_cast of a vector
+                        // element reads element 0 with this compiler
+                        const unsigned e = cw[i];
+                        const half2v v = __builtin_bit_cast(half2v, e);
+                        out[i] = __builtin_bit_cast(unsigned, DELTA ? __builtin_elementwise_fma(v, s2, d2) : v * s2);
+                    }
+                    bq[t][k] = __builtin_bit_cast(half8, uint4v{out[0], out[1], out[2], out[3]});
+                }
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            half8 a[4];
+#pragma unroll
+            for (int o = 0; o < 4; ++o)
+                a[o] = *reinterpret_cast<const half8 *>(&As[buf][(16 * mt + c) * KTILE + 8 * ((4 * o + kq) ^ c)]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                acc[mt][t] = mfma_f16(a[0], bq[t][0], acc[mt][t]);
+                acc[mt][t] = mfma_f16(a[1], bq[t][1], acc[mt][t]);
+                acc2[mt][t] = mfma_f16(a[2], bq[t][2], acc2[mt][t]);
+                acc2[mt][t] = mfma_f16(a[3], bq[t][3], acc2[mt][t]);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         half8 a[4];
@@ -236,7 +297,7 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
         CodeOps ops[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            ops[t] = split_codes(rw[slot][t]);
+            ops[t] = DQ ? center_codes(rw[slot][t], mag_lo, mag_hi) : split_codes(rw[slot][t]);
             pin(ops[t].lo[0]); pin(ops[t].lo[1]); pin(ops[t].hi[0]); pin(ops[t].hi[1]);
         }
         // unconditional (clamped) refill: a conditional load would make every
@@ -283,6 +344,11 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
         for (int i = 0; i < P - 1; ++i)
             if (j + i < n) step(kt_beg + j + i, i, last);
     }
+    if (DQ)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[mt][t] += acc2[mt][t];
 
     // C rows 16 mt + 4 kq + r, columns (nt0 + t) * 16 + c below ncols, row
     // stride ldc (a padded weight writes its logical columns straight into
@@ -464,6 +530,10 @@ size_t decode_workspace_bytes(int M, int N, int K, int g)
     return W4A16_WS_COUNTER_BYTES + ncg * ns * rows * decode::COLS * sizeof(float);
 }
 
+// Whether MT m-tiles dequantize the codes (DQ above): the dequantization is
+// shared by the m-tiles, the group sums and scaling it saves are per m-tile.
+constexpr bool decode_dq(int MT) { return MT >= 2; }
+
 template <bool DELTA, bool GATED = false, int GPT = 1, int MT = 1>
 static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                              const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
@@ -482,11 +552,11 @@ static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_
     constexpr size_t stat = 2 * MT * 16 * KTILE * 2 + 4 + (GATED ? MT * 2 * 4 * 64 * 4 : 4);
     if (table + stat > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT, MT>),
+            reinterpret_cast<const void *>(&w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT, MT, decode_dq(MT)>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)table);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT, MT>),
+    hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT, MT, decode_dq(MT)>),
                        dim3(ncg * nsplit), dim3(64 * decode::WV), table, st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M,
                        N, K, g, nsplit, counters, partials, ldc, ncols);
     return hipGetLastError();

@@ -32,8 +32,6 @@ namespace tiled {
 constexpr int WIN = 16;                         // groups per correction k-step
 }
 
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-
 // fp16 operand of k-step STEP (0..3) of a 128-k tile, scaled per element.
 template <int STEP>
 __device__ inline half8 dequant_scaled(uint4v w, half2v s2)
@@ -309,16 +307,9 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
 // the MFMAs that use them, and dequantizes the next step's codes between
 // those MFMAs, so that LDS latency and dequantization VALU both hide under
 // matrix work.  sched_barrier fences keep the compiler from regrouping the
-// pairs.  (x & mask) | 0x6400 is one v_and_or_b32 (the compiler emits an AND
-// and an OR when both constants are literals).  Codes and scales of the next
-// tile are issued after its activations, so the end-of-tile wait leaves them
-// in flight.
-__device__ inline unsigned and_or_b32(unsigned x, unsigned m, unsigned c)
-{
-    unsigned r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
-    return r;
-}
+// pairs.  (x & mask) | 0x6400 is one v_and_or_b32 (and_or_b32).  Codes and
+// scales of the next tile are issued after its activations, so the
+// end-of-tile wait leaves them in flight.
 
 template <int STEP>
 __device__ inline half8 dequant_scaled_ao(uint4v w, half2v s2, unsigned magic)
