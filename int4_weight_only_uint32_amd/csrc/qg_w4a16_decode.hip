@@ -502,7 +502,9 @@ int decode_splits(int N, int K, int g)
 // against 16.6, K2048 N2048 M64 10.7 against 12.9).  Groups of 64 and 32
 // alike (g = 64: K5120 N17408 M48 54.3 -> 29.3, K4096 N8192 M64 19.7 ->
 // 16.8; g = 32: K4096 N8192 M80 36.8 -> 20.9; K4096 N4096 M33 g = 64 17.6
-// either way).
+// either way).  Re-measured with the m-tiles' in-register dequantization:
+// the small weights still favour the skinny kernel (K4096 N4096 M64/M80 15.3 /
+// 15.6 against 15.8 / 18.3, K2048 N2048 M64 10.7 against 13.0).
 static bool decode_multi_tile_pays(int M, int N, int K)
 {
     const int mt = (M + 15) / 16;
