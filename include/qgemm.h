@@ -159,11 +159,12 @@ int pack_int4_weights(const uint8_t *q, const uint16_t *scale, const uint16_t *z
  *          for a symmetric one.
  * C        [M,N] fp16 out, OVERWRITTEN with A . W (fp32 accumulation, one
  *          rounding to fp16 at the end).  The weights enter the products
- *          exactly for batches of up to 16 rows and for the mid-batch kernels
- *          (codes as exact fp16 values, scales applied in fp32), and rounded
- *          once per element to fp16 -- (v-8)*scale + delta for decode batches
- *          of 17 to 80 rows, (v-8)*scale for the tiled kernels of larger
- *          batches -- so |W| must stay within the fp16 range.
+ *          exactly in the decode kernel for up to 16 rows and in the skinny
+ *          and mid-batch kernels (codes as exact fp16 values, scales applied
+ *          in fp32), and rounded once per element to fp16 in the decode
+ *          kernel for 17 to 80 rows ((v-8)*scale + delta) and in the tiled
+ *          kernels ((v-8)*scale), so |W| must stay within the fp16 range;
+ *          QGEMM_LOG=1 names the kernel a call runs.
  * flags    0: the delta term sum_g a_sum[m,g]*delta[g,n] is added in fp32 in
  *          the GEMM epilogue (one launch).
  *          QG_CORR_SEPARATE: C is first stored as the symmetric product and
