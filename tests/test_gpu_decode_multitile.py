@@ -2,9 +2,9 @@
 
 Batches of 17 to 80 rows run the decode kernel with MT = ceil(M/16) m-tiles
 when it beats the skinny kernel (two m-tiles always, three to five on weights
-of more than 2^24 elements): every wave multiplies each code tile into all MT
-m-tiles of the shared activation tile, and the split-K partial sums hold 16 MT
-rows.  Checked against the oracle ("Marlin INT4 on Ada - how it works", "The
+of more than 2^24 elements): every wave dequantizes each code tile to fp16
+weights (v - 8) s + delta (one rounding) and multiplies it into all MT m-tiles
+of the shared activation tile, and the split-K partial sums hold 16 MT rows.  Checked against the oracle ("Marlin INT4 on Ada - how it works", "The
 core mismatch: symmetric vs asymmetric") to the W4A16 bar (relative Frobenius
 <= 2e-3 and the elementwise guard), with AWQ-style zero-points, random-sign
 symmetric scales, groups of 32, 64, 128 and 256 and one group over K, rows past M in
