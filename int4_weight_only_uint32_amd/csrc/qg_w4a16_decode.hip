@@ -176,7 +176,7 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            w[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off, (t * KT + kt) * 1024, 0));
+            w[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off, (t * KT + kt) * 1024, QG_NT));
     };
     auto finish = [&](int buf, int kt, const CodeOps (&ops)[NT]) {
     if constexpr (DQ) {

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_kernel(
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 rw[sl][t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(
-                                                           w_rs, (t * KT * 64 + lane) * 16, k * 1024, 0));
+                                                           w_rs, (t * KT * 64 + lane) * 16, k * 1024, QG_NT));
             const int so = ((k * KTILE) / g) * N * 2;   // the group's scale row, bytes
 #pragma unroll
             for (int t = 0; t < NT; ++t)
