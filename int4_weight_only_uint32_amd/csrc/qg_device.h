@@ -176,6 +176,17 @@ __device__ inline void pin(T &x)
     asm volatile("" : "+v"(x));
 }
 
+// A scalar the compiler cannot see through.  Loads whose offset passes
+// through it stay one instruction per pipeline stage even when two stages read
+// the same address (the scale row of a group that spans several k-tiles),
+// which the counted vmcnt waits of the pipelined kernels rely on: merged
+// loads would leave fewer operations per stage than the wait allows in flight.
+__device__ inline int opaque_s(int x)
+{
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 // Cache-policy operand of a buffer load that streams data read once (the
 // weight codes of a kernel whose grid reads each code once): the non-temporal
 // bit, so the stream does not evict the reused activations from the caches

@@ -122,7 +122,8 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
             const int wo = (rel(t) * KT + k) * 1024;
             rw[slot][t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off, wo, 0));
         }
-        const int gb = mid_group<GK>(k, g) * N * 2;    // byte offset of this k-tile's group row
+        // byte offset of this k-tile's group row (opaque: one load per k-tile)
+        const int gb = opaque_s(mid_group<GK>(k, g) * N * 2);
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
             const __amdgpu_buffer_rsrc_t sr = odd(t) ? s_rs1 : s_rs0;
@@ -209,9 +210,16 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
             if (clear) asum[mt] = fzero;
         }
     };
-    auto step = [&](int kt, int slot) {
+    // tail: a step after the main loop.  Its loads (k-tiles past the end) are
+    // never read, so the compiler keeps only the direct-to-LDS ones and fewer
+    // than L follow each k-tile's loads there: those steps wait for every load
+    // in flight instead of counting.
+    auto step = [&](int kt, int slot, bool tail) {
         constexpr unsigned WAIT = waitcnt_vm((SG - 2) * L);
-        __builtin_amdgcn_s_waitcnt(WAIT);
+        if (tail)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        else
+            __builtin_amdgcn_s_waitcnt(WAIT);
         debug_stage_sync();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -242,14 +250,14 @@ __global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(
     for (; kt + SG <= KT; kt += SG) {
 #pragma unroll
         for (int i = 0; i < SG; ++i) {
-            step(kt + i, i);
+            step(kt + i, i, false);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
     for (int i = 0; i < SG - 1; ++i)
-        if (kt + i < KT) step(kt + i, i);
+        if (kt + i < KT) step(kt + i, i, true);
     if (GK == 0) apply(false);   // the single group (g = K) ends with the last k-tile
     __builtin_amdgcn_s_waitcnt(0);   // the last (unused) loads
 
@@ -366,7 +374,7 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
             const int wo = (rel(t) * KT + k) * 1024;
             rw[slot][t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off, wo, 0));
         }
-        const int gb = mid_group<GK>(k, g) * N * 2;
+        const int gb = opaque_s(mid_group<GK>(k, g) * N * 2);   // (one load per step)
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
             const __amdgpu_buffer_rsrc_t sr = odd(t) ? s_rs1 : s_rs0;
@@ -489,9 +497,14 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
         asm volatile("" ::: "memory");
     };
     // st: the step, slot = st % SG (st comes in slot order from a multiple of SG)
-    auto step = [&](int st, int slot) {
+    // tail: a step after the main loop, which waits for every load in flight
+    // (as in the 64 x 64 kernel: the compiler drops the unread loads there)
+    auto step = [&](int st, int slot, bool tail) {
         constexpr unsigned WAIT = waitcnt_vm((SG - 2) * L);
-        __builtin_amdgcn_s_waitcnt(WAIT);
+        if (tail)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        else
+            __builtin_amdgcn_s_waitcnt(WAIT);
         sync();
         // nothing that reads this slot's registers moves above the wait
         __builtin_amdgcn_sched_barrier(0);
@@ -525,14 +538,14 @@ __global__ __launch_bounds__(512) void w4a16_mid2_kernel(
     for (; st + SG <= nsteps; st += SG) {
 #pragma unroll
         for (int i = 0; i < SG; ++i) {
-            step(st + i, i);
+            step(st + i, i, false);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
     for (int i = 0; i < SG - 1; ++i)
-        if (st + i < nsteps) step(st + i, i);
+        if (st + i < nsteps) step(st + i, i, true);
     __builtin_amdgcn_s_waitcnt(0);   // the last (unused) loads
 
     // the last group's delta term (one group over all of K: closed here)
