@@ -178,7 +178,10 @@ int pack_int4_weights(const uint8_t *q, const uint16_t *scale, const uint16_t *z
  *          (M <= 16, and up to M = 80 on all but small weights) the K range
  *          is split over several workgroups whose fp32 partial sums meet in
  *          the workspace; the last to finish adds them in a fixed order, so
- *          results do not depend on timing.                                 */
+ *          results do not depend on timing.  A grid that would leave a few
+ *          CUs one workgroup more than the rest splits its last column groups
+ *          finer (or, when nothing else is split, only those), which also
+ *          takes workspace.                                                 */
 int qgemm_w4a16(const uint16_t *A, const uint32_t *w_packed, const uint16_t *scale,
                 const uint16_t *delta, uint16_t *C, int M, int N, int K,
                 int group_size, unsigned flags, void *workspace,
@@ -221,7 +224,8 @@ int qgemm_w4a16_noalloc(const uint16_t *A, const uint32_t *w_packed, const uint1
  * flags    must be 0.
  * workspace/workspace_bytes: qg_workspace_bytes(QG_OP_W4A16_SWIGLU, M, N, K,
  *          group_size, 1, 0) bytes, 256-byte aligned (NULL when 0: every
- *          shape but the split-K decode batches); it starts with the same
+ *          shape but the decode batches whose grid splits K, for all column
+ *          groups or for the last ones only); it starts with the same
  *          counter region as a W4A16 workspace (zero-filled once, left at
  *          zero by every call), so one workspace of the larger size serves
  *          both kinds of call on one stream.                                */

@@ -80,6 +80,13 @@ constexpr size_t W4A16_WS_COUNTER_BYTES = 65536;
 // g: the weight group size (groups of 64 and 32 can raise the split count,
 // whose scale table grows; the default stands for any g >= 128)
 int decode_splits(int N, int K, int g = 128);
+// The decode grid for split count ns: column groups 0 .. cg_main-1 take ns
+// splits, the others ns2; wgs workgroups, slots partial-sum slots (0: no
+// split-K at all).
+struct DecodeGrid {
+    int cg_main, ns2, wgs, slots;
+};
+DecodeGrid decode_grid(int M, int N, int K, int ns);
 bool use_decode_kernel(int M, int N, int K, int g = 128);
 size_t decode_workspace_bytes(int M, int N, int K, int g = 128);
 // ldc, ncols: C's row stride and the columns stored (default N, or N/2 for

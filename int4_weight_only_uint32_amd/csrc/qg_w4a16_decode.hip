@@ -53,7 +53,8 @@ template <int NT, int P, int WV, bool DELTA, bool GATED = false, int GPT = 1, in
 __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
     const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g,
-    int nsplit, unsigned *__restrict__ counters, float *__restrict__ partials, int ldc, int ncols)
+    int nsplit, int cg_main, int nsplit2, unsigned *__restrict__ counters, float *__restrict__ partials,
+    int ldc, int ncols)
 {
     static_assert(NT == 1, "the scale table holds one column per lane");
     static_assert(WV == 4 || WV == 8, "4 or 8 waves per workgroup");
@@ -71,8 +72,17 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, kq = lane >> 4;
     const int KT = K / KTILE;
-    const int cg = blockIdx.x / nsplit, sp = blockIdx.x - cg * nsplit;
-    const int kt_beg = (sp * KT) / nsplit, kt_end = ((sp + 1) * KT) / nsplit;
+    // column groups below cg_main take nsplit splits, the others nsplit2
+    // (shorter) ones; workgroup b1 + j is split j % nsplit2 of tail column
+    // group j / nsplit2.  slot0: the column group's first partial-sum slot
+    // (the main column groups need none when nsplit == 1).
+    const int b1 = cg_main * nsplit;
+    const bool tail_cg = (int)blockIdx.x >= b1;
+    const int ns = tail_cg ? nsplit2 : nsplit;
+    const int cg = tail_cg ? cg_main + ((int)blockIdx.x - b1) / nsplit2 : (int)blockIdx.x / nsplit;
+    const int sp = tail_cg ? (int)blockIdx.x - b1 - (cg - cg_main) * nsplit2 : (int)blockIdx.x - cg * nsplit;
+    const int slot0 = tail_cg ? (nsplit > 1 ? b1 : 0) + (cg - cg_main) * nsplit2 : cg * nsplit;
+    const int kt_beg = (sp * KT) / ns, kt_end = ((sp + 1) * KT) / ns;
     const int n = kt_end - kt_beg;
     const int last = kt_end - 1;
     const int Nh = N / 2;                    // GATED: output width
@@ -385,13 +395,13 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
                     if (row < M && col < ncols) C[(size_t)row * ldc + col] = f2h(v[mt][t][r]);
                 }
     };
-    if (nsplit == 1) {
+    if (ns == 1) {
         store(acc);
         return;
     }
     // slot layout: [cg][split][wave][mt][t][r][lane] fp32
     constexpr int PER_WAVE = MT * NT * 4 * 64;
-    float *mine = partials + ((size_t)cg * nsplit + sp) * WV * PER_WAVE + wave * PER_WAVE + lane;
+    float *mine = partials + ((size_t)slot0 + sp) * WV * PER_WAVE + wave * PER_WAVE + lane;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -405,14 +415,14 @@ __global__ __launch_bounds__(64 * WV) void w4a16_decode_kernel(
     if (tid == 0)
         arrived = __hip_atomic_fetch_add(&counters[cg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (arrived != (unsigned)(nsplit - 1)) return;
+    if (arrived != (unsigned)(ns - 1)) return;
     float4v tot[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int t = 0; t < NT; ++t) tot[mt][t] = fzero;
-    const float *base = partials + (size_t)cg * nsplit * WV * PER_WAVE + wave * PER_WAVE + lane;
-    for (int s2 = 0; s2 < nsplit; ++s2) {
+    const float *base = partials + (size_t)slot0 * WV * PER_WAVE + wave * PER_WAVE + lane;
+    for (int s2 = 0; s2 < ns; ++s2) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -474,6 +484,40 @@ int decode_splits(int N, int K, int g)
     return ns;
 }
 
+// Grid balance.  All decode workgroups are resident at once, and a CU that
+// holds one workgroup more than most finishes last.  When the plain grid
+// (ncg column groups x ns splits) leaves a small remainder over whole rounds
+// of 256 CUs (at most 64 workgroups), the column groups that fill those rounds
+// keep ns splits and the remaining ones take F x ns shorter splits, so the CUs
+// that get an extra workgroup get a fraction of one.  F is the largest of 8,
+// 4, 2 whose splits still stream >= 10 k-tiles (M <= 8, where a workgroup's
+// fixed costs weigh more) or >= 5 k-tiles (larger M), with <= 256 such
+// workgroups.  Same arithmetic and reduction order per column group.
+// Measured (M = 16 / 1 / 64 on K5120 x N17408: 544 workgroups, 32 CUs holding
+// three): F = 1 15.15 / 13.37 / 30.50 us, F = 2 14.11 / 12.56 / 26.45, F = 4
+// 13.97 / 13.06 / 25.63, F = 8 16.63 / 16.04 / 28.79.
+DecodeGrid decode_grid(int M, int N, int K, int ns)
+{
+    const int ncg = N / decode::COLS, KT = K / KTILE;
+    DecodeGrid d{ncg, ns, ncg * ns, ns > 1 ? ncg * ns : 0};
+    const int full = (d.wgs / 256) * 256;
+    const int rem = d.wgs - full;
+    if (full == 0 || rem == 0 || rem > 64) return d;
+    const int main = full / ns;
+    if (main < 1 || main >= ncg) return d;
+    const int kmin = M <= 8 ? 10 : 5;
+    for (int F = 8; F >= 2; F /= 2) {
+        const int ns2 = ns * F;
+        if (KT / ns2 < kmin || (ncg - main) * ns2 > 256) continue;
+        d.cg_main = main;
+        d.ns2 = ns2;
+        d.wgs = main * ns + (ncg - main) * ns2;
+        d.slots = (ns > 1 ? main * ns : 0) + (ncg - main) * ns2;
+        return d;
+    }
+    return d;
+}
+
 // Decode workspace: the fixed counter region (W4A16_WS_COUNTER_BYTES, shared
 // by every W4A16 layout and written by nothing but the counters), then the
 // partial-sum slots.  0 when the shape is not split.
@@ -525,11 +569,10 @@ bool use_decode_kernel(int M, int N, int K, int g)
 size_t decode_workspace_bytes(int M, int N, int K, int g)
 {
     if (!use_decode_kernel(M, N, K, g)) return 0;
-    const int ns = decode_splits(N, K, g);
-    if (ns == 1) return 0;
-    const size_t ncg = (size_t)(N / decode::COLS);
-    const size_t rows = 16 * (size_t)((M + 15) / 16);   // the m-tiles' rows
-    return W4A16_WS_COUNTER_BYTES + ncg * ns * rows * decode::COLS * sizeof(float);
+    const size_t slots = (size_t)decode_grid(M, N, K, decode_splits(N, K, g)).slots;
+    if (slots == 0) return 0;                                  // nothing split
+    const size_t rows = 16 * (size_t)((M + 15) / 16);          // the m-tiles' rows
+    return W4A16_WS_COUNTER_BYTES + slots * rows * decode::COLS * sizeof(float);
 }
 
 // Whether MT m-tiles dequantize the codes (DQ above): the dequantization is
@@ -541,10 +584,11 @@ static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_
                              const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                              int nsplit, void *ws, hipStream_t st, int ldc, int ncols)
 {
-    const int ncg = N / decode::COLS;
+    const DecodeGrid grid = decode_grid(M, N, K, nsplit);
     unsigned *counters = nullptr;
     float *partials = nullptr;
-    if (nsplit > 1) {
+    if (grid.slots > 0) {
+        if (!ws) return hipErrorInvalidValue;
         counters = static_cast<unsigned *>(ws);
         partials = reinterpret_cast<float *>(static_cast<char *>(ws) + W4A16_WS_COUNTER_BYTES);
     }
@@ -559,8 +603,8 @@ static hipError_t run_decode(const uint16_t *A, const uint32_t *W, const uint16_
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((w4a16_decode_kernel<decode::NT, decode::P, decode::WV, DELTA, GATED, GPT, MT, decode_dq(MT)>),
-                       dim3(ncg * nsplit), dim3(64 * decode::WV), table, st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M,
-                       N, K, g, nsplit, counters, partials, ldc, ncols);
+                       dim3(grid.wgs), dim3(64 * decode::WV), table, st, A, reinterpret_cast<const uint4v *>(W), S, D, C, M,
+                       N, K, g, nsplit, grid.cg_main, grid.ns2, counters, partials, ldc, ncols);
     return hipGetLastError();
 }
 

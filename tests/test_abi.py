@@ -181,8 +181,18 @@ def test_decode_workspace_size():
     # the fixed counter region + fp32 partials (16 rows per m-tile x 64
     # columns per split per 64-column group).  Splits: the most that keep <= 512
     # workgroups (two per CU) when that fills >= 448 of them, else the smallest
-    # power of two giving >= 512 workgroups; >= 2 k-tiles per split.
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 17408, 5120, 128) == CTR + 272 * 2 * 4096
+    # power of two giving >= 512 workgroups; >= 2 k-tiles per split.  A small
+    # remainder over whole rounds of 256 CUs is balanced: at N = 17408 the
+    # first 256 column groups keep 2 splits and the last 16 take 8 (M > 8,
+    # splits of >= 5 k-tiles) or 4 (M <= 8, >= 10 k-tiles), one slot each.
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 17408, 5120, 128) == CTR + (256 * 2 + 16 * 8) * 4096
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 4, 17408, 5120, 128) == CTR + (256 * 2 + 16 * 4) * 4096
+    # unsplit grids with such a remainder split only their last column groups:
+    # the gate/up pair's 34816 columns (512 + 32 groups, K = 5120) and a
+    # 50304-column head (768 + 18)
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 34816, 5120, 128) == CTR + 32 * 8 * 4096
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 1, 34816, 5120, 128) == CTR + 32 * 4 * 4096
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 50304, 5120, 128) == CTR + 18 * 8 * 4096
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 9, 5120, 17408, 128) == CTR + 80 * 6 * 4096
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 4096, 16384, 128) == CTR + 64 * 8 * 4096
     # short decode splits lose to the skinny kernel, which needs none
@@ -197,8 +207,8 @@ def test_decode_workspace_size():
     # elements (any group size); otherwise the skinny kernel
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 17, 5120, 17408, 128) == CTR + 80 * 6 * 8192
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 32, 4096, 4096, 128) == CTR + 64 * 8 * 8192
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 48, 17408, 5120, 128) == CTR + 272 * 2 * 12288
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 80, 17408, 5120, 128) == CTR + 272 * 2 * 20480
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 48, 17408, 5120, 128) == CTR + (256 * 2 + 16 * 8) * 12288
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 80, 17408, 5120, 128) == CTR + (256 * 2 + 16 * 8) * 20480
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 64, 4096, 4096, 128) == 0
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 32, 4096, 4096, 64) == CTR + 64 * 8 * 8192
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 64, 4096, 4096, 32) == 0
@@ -211,7 +221,7 @@ def test_decode_workspace_size():
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 1024, 1024, 128, 1, qg.QG_CORR_SEPARATE) == \
         CTR + 16 * 8 * 4
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 17408, 5120, 128, 1, qg.QG_CORR_SEPARATE) == \
-        CTR + 272 * 2 * 4096 + 16 * 40 * 4
+        CTR + (256 * 2 + 16 * 8) * 4096 + 16 * 40 * 4
 
 
 def test_workspace_bytes():
@@ -270,11 +280,12 @@ def test_swiglu_validation():
     assert L.qgemm_w4a16_swiglu(*ok(N=1000)) == qg.QG_ERR_UNSUPPORTED
     # every batch is one fused launch: only the decode kernel's split-K (here
     # M = 16, K 17408 -> N 5120 per half: 3 splits; M = 17, two m-tiles over
-    # the 2048-column pair, 4 splits) takes a workspace
+    # the 2048-column pair, 4 splits; the 34816-column pair at K 5120, whose
+    # last 32 column groups take 8 splits to balance the grid) takes a workspace
     for M in (64, 256, 4096):
         assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, M, 1024, 1024, 128, 1, 0) == 0
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 17, 1024, 1024, 128, 1, 0) == CTR + 32 * 4 * 8192
-    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 16, 17408, 5120, 128, 1, 0) == 0
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 16, 17408, 5120, 128, 1, 0) == CTR + 32 * 8 * 4096
     need = qg.qg_workspace_bytes(qg.QG_OP_W4A16_SWIGLU, 16, 5120, 17408, 128, 1, 0)
     assert need == CTR + 160 * 3 * 4096
     split = lambda **kw: ok(M=16, N=5120, K=17408, **kw)
