@@ -61,6 +61,7 @@ hipError_t launch_w4a16_mid(const uint16_t *A, const uint32_t *W, const uint16_t
                             bool fuse_delta, hipStream_t st, bool gated = false);
 int tiled_config(int M, int N);
 int tiled_row_split(int M, int N);
+int tiled_col_split(int M, int N, int g, bool gated);
 hipError_t launch_w4a16_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W,
                                   const uint16_t *S, const uint16_t *D, uint16_t *C, int M, int N,
                                   int K, int g, bool fuse_delta, hipStream_t st, bool gated = false);

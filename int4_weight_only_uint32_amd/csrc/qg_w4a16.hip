@@ -402,6 +402,11 @@ void describe_w4a16(int M, int N, int K, int g, bool delta, bool gated, char *bu
                  decode_workspace_bytes(M, N2, K, g) ? decode_splits(N2, K, g) : 1);
     } else if (M < TILED_MIN_M) {
         snprintf(buf, n, "%sskinny", gate);
+    } else if (tiled_config(M, N2) == 2 && tiled_row_split(M, N2) < M &&
+               tiled_col_split(M, N2, g, gated) < N2) {
+        const int n1 = tiled_col_split(M, N2, g, gated);
+        snprintf(buf, n, "%s columns 0-%d, tiled 64x128 columns %d-%d",
+                 big_kernel(M, n1, K, g, delta), n1 - 1, n1, N2 - 1);
     } else if (tiled_config(M, N2) == 2 && tiled_row_split(M, N2) < M) {
         const int m1 = tiled_row_split(M, N2);
         snprintf(buf, n, "%s%s rows 0-%d, %s rows %d-%d", gate, big_kernel(m1, N2, K, g, delta), m1 - 1,

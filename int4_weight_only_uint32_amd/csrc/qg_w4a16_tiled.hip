@@ -67,7 +67,7 @@ __device__ inline half8 dequant_scaled(uint4v w, half2v s2)
 template <int WM, int WN, bool DELTA, bool GATED, int GPT = 1>
 __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
-    const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g)
+    const uint16_t *__restrict__ D, uint16_t *__restrict__ C, int M, int N, int K, int g, int ldn)
 {
     using namespace tiled;
     static_assert(WM % 4 == 0, "each wave sums WM/4 m-tiles of the group sums");
@@ -140,12 +140,12 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
     auto ptile = [&](int t) { return (odd(t) ? pb1 : pb0) + rel(t); };
     const __amdgpu_buffer_rsrc_t w_rs0 = buffer_rsrc(W + (size_t)pb0 * KT * 64, (size_t)(N / NTILE - pb0) * KT * 1024);
     const __amdgpu_buffer_rsrc_t w_rs1 = buffer_rsrc(W + (size_t)pb1 * KT * 64, (size_t)(N / NTILE - pb1) * KT * 1024);
-    const __amdgpu_buffer_rsrc_t s_rs0 = buffer_rsrc(S + pb0 * NTILE, ((size_t)G * N - pb0 * NTILE) * 2);
-    const __amdgpu_buffer_rsrc_t s_rs1 = buffer_rsrc(S + pb1 * NTILE, ((size_t)G * N - pb1 * NTILE) * 2);
+    const __amdgpu_buffer_rsrc_t s_rs0 = buffer_rsrc(S + pb0 * NTILE, ((size_t)(G - 1) * ldn + N - pb0 * NTILE) * 2);
+    const __amdgpu_buffer_rsrc_t s_rs1 = buffer_rsrc(S + pb1 * NTILE, ((size_t)(G - 1) * ldn + N - pb1 * NTILE) * 2);
     const unsigned w_off = (unsigned)lane * 16u, s_off = (unsigned)c * 2u;
     auto load_w = [&](int kt) {
         if (!active) return;
-        const int gb = ((kt * KTILE) / g) * N * 2;
+        const int gb = ((kt * KTILE) / g) * ldn * 2;
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
             const __amdgpu_buffer_rsrc_t wr = odd(t) ? w_rs1 : w_rs0;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
             wreg[t] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off, wo, 0));
 #pragma unroll
             for (int q = 0; q < GPT; ++q)
-                sreg[t][q] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off, so + q * N * 2, 0);
+                sreg[t][q] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off, so + q * ldn * 2, 0);
         }
     };
 
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
 #pragma unroll
             for (int s8 = 0; s8 < 8; ++s8) {
                 const int gg = gw0 + 8 * (kq & 1) + s8;
-                be[t][s8] = gg < G ? __builtin_bit_cast(_Float16, D[(size_t)gg * N + colx])
+                be[t][s8] = gg < G ? __builtin_bit_cast(_Float16, D[(size_t)gg * ldn + colx])
                                    : (_Float16)0.f;
             }
         }
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256, (WM * WN >= 32) ? 2 : 3) void w4a16_tiled_kern
                     C[(size_t)row * (N / 2) + ptile(t) * NTILE + c] =
                         f2h(silu_mul(acc[mt][t][r], acc[mt][t + 1][r]));
                 else
-                    C[(size_t)row * N + n0 + 16 * t + c] = f2h(acc[mt][t][r]);
+                    C[(size_t)row * ldn + n0 + 16 * t + c] = f2h(acc[mt][t][r]);
             }
 }
 
@@ -336,7 +336,7 @@ __device__ inline half8 dequant_scaled_ao(uint4v w, half2v s2, unsigned magic)
 template <bool GATED>
 __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
     const uint16_t *__restrict__ A, const uint4v *__restrict__ W, const uint16_t *__restrict__ S,
-    uint16_t *__restrict__ C, int M, int N, int K, int g)
+    uint16_t *__restrict__ C, int M, int N, int K, int g, int ldn)
 {
     constexpr int WM = 8, WN = 4, BM = 16 * WM, BN = 64 * WN, ABLK = BM / 16;
     __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * 128];
@@ -393,13 +393,13 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
     // type depends on a template parameter loses the kernel's host launch stub)
     const __amdgpu_buffer_rsrc_t w_rs0 = buffer_rsrc(W + (size_t)pb0 * KT * 64, (size_t)(N / NTILE - pb0) * KT * 1024);
     const __amdgpu_buffer_rsrc_t w_rs1 = buffer_rsrc(W + (size_t)pb1 * KT * 64, (size_t)(N / NTILE - pb1) * KT * 1024);
-    const __amdgpu_buffer_rsrc_t s_rs0 = buffer_rsrc(S + pb0 * NTILE, ((size_t)(K / g) * N - pb0 * NTILE) * 2);
-    const __amdgpu_buffer_rsrc_t s_rs1 = buffer_rsrc(S + pb1 * NTILE, ((size_t)(K / g) * N - pb1 * NTILE) * 2);
+    const __amdgpu_buffer_rsrc_t s_rs0 = buffer_rsrc(S + pb0 * NTILE, ((size_t)(K / g - 1) * ldn + N - pb0 * NTILE) * 2);
+    const __amdgpu_buffer_rsrc_t s_rs1 = buffer_rsrc(S + pb1 * NTILE, ((size_t)(K / g - 1) * ldn + N - pb1 * NTILE) * 2);
     const unsigned w_off = (unsigned)lane * 16u;      // this lane's 16 bytes of a code tile
     const unsigned s_off = ((unsigned)c >> 1) * 4u;   // this lane's scale pair within 16 columns
     auto load_w = [&](int kt) {
         const int k = kt < KT ? kt : KT - 1;
-        const int gb = ((k * KTILE) / g) * N * 2;      // byte offset of this k-tile's group row
+        const int gb = ((k * KTILE) / g) * ldn * 2;    // byte offset of this k-tile's group row
 #pragma unroll
         for (int t = 0; t < WN; ++t) {
             const __amdgpu_buffer_rsrc_t wr = odd(t) ? w_rs1 : w_rs0;
@@ -502,19 +502,19 @@ __global__ __launch_bounds__(256, 2) void w4a16_tiled_sym_kernel(
                     C[(size_t)row * (N / 2) + (pb0 + rel(t)) * NTILE + c] =
                         f2h(silu_mul(acc[mt][t][r], acc[mt][t + 1][r]));
                 else
-                    C[(size_t)row * N + n0 + 16 * t + c] = f2h(acc[mt][t][r]);
+                    C[(size_t)row * ldn + n0 + 16 * t + c] = f2h(acc[mt][t][r]);
             }
 }
 
 template <int WM, int WN, bool DELTA, bool GATED, int GPT = 1>
 static hipError_t run_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                             const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
-                            hipStream_t st)
+                            hipStream_t st, int ldn = -1)
 {
     constexpr int BM = 16 * WM, BN = 64 * WN;
     dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
     hipLaunchKernelGGL((w4a16_tiled_kernel<WM, WN, DELTA, GATED, GPT>), grid, dim3(256), 0, st, A,
-                       reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g);
+                       reinterpret_cast<const uint4v *>(W), S, D, C, M, N, K, g, ldn < 0 ? N : ldn);
     return hipGetLastError();
 }
 
@@ -549,11 +549,16 @@ int tiled_config(int M, int N)
     return 0;
 }
 
+// ldn: row stride of S, D and C when the launch covers a column range of a
+// wider weight (W, S, D and C then point at the range's first column); only
+// the tiled kernels with groups of >= 128 take one.
 template <bool GATED>
 static hipError_t run_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W, const uint16_t *S,
                                 const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
-                                bool fuse_delta, hipStream_t st)
+                                bool fuse_delta, hipStream_t st, int ldn = -1)
 {
+    if (ldn < 0) ldn = N;
+    if (ldn != N && (GATED || g < KTILE || cfg == 0)) return hipErrorInvalidValue;
     if (g < KTILE) {
         // groups of 64 on the 8-wave mid kernel (its low- and high-nibble
         // sums are the two groups of a k-tile)
@@ -566,13 +571,13 @@ static hipError_t run_tiled_cfg(int cfg, const uint16_t *A, const uint32_t *W, c
     const bool dl = D && fuse_delta;
     if (cfg == 0) return launch_w4a16_mid(A, W, S, D, C, M, N, K, g, fuse_delta, st, GATED);
     if (cfg == 1) {
-        if (dl) return run_tiled<4, 2, true, GATED>(A, W, S, D, C, M, N, K, g, st);
-        return run_tiled<4, 2, false, GATED>(A, W, S, nullptr, C, M, N, K, g, st);
+        if (dl) return run_tiled<4, 2, true, GATED>(A, W, S, D, C, M, N, K, g, st, ldn);
+        return run_tiled<4, 2, false, GATED>(A, W, S, nullptr, C, M, N, K, g, st, ldn);
     }
-    if (dl) return run_tiled<8, 4, true, GATED>(A, W, S, D, C, M, N, K, g, st);
+    if (dl) return run_tiled<8, 4, true, GATED>(A, W, S, D, C, M, N, K, g, st, ldn);
     dim3 grid((unsigned)((N + 255) / 256), (unsigned)((M + 127) / 128));
     hipLaunchKernelGGL(w4a16_tiled_sym_kernel<GATED>, grid, dim3(256), 0, st, A,
-                       reinterpret_cast<const uint4v *>(W), S, C, M, N, K, g);
+                       reinterpret_cast<const uint4v *>(W), S, C, M, N, K, g, ldn);
     return hipGetLastError();
 }
 
@@ -600,11 +605,43 @@ int tiled_row_split(int M, int N)
     return m1 > 0 && m1 < M ? (int)m1 : M;
 }
 
+// Columns of the first launch when a column split balances the grid better
+// than the row split: the 128 x 256 tiles over the leading columns fill whole
+// rounds of 512 workgroups, and the remaining columns (all rows) are exactly
+// one round of 512 64 x 128 workgroups, two per CU.  (The row split's second
+// launch has 4 x 136 = 544 such workgroups at M = 4096, N = 17408, so 32 CUs
+// take a third; that launch is issue-bound, so those CUs set its length.)
+// N when no such split exists.  Not for gated pairs or groups below 128.
+int tiled_col_split(int M, int N, int g, bool gated)
+{
+    if (gated || g < KTILE || N % 256) return N;
+    const long nbm = (M + 127) / 128, nbn = N / 256;
+    for (long nb1 = nbn - 1; nb1 >= 1; --nb1) {
+        if ((nb1 * nbm) % 512) continue;
+        const int n2 = N - (int)(nb1 * 256);
+        const long tail = (long)((M + 63) / 64) * (n2 / 128);
+        if (tail == 512 && tiled_config(M, n2) == 1) return (int)(nb1 * 256);
+        if (tail > 512) break;
+    }
+    return N;
+}
+
 hipError_t launch_w4a16_tiled(const uint16_t *A, const uint32_t *W, const uint16_t *S,
                               const uint16_t *D, uint16_t *C, int M, int N, int K, int g,
                               bool fuse_delta, hipStream_t st, bool gated)
 {
     const int cfg = tiled_config(M, N);
+    if (cfg == 2 && tiled_row_split(M, N) < M) {
+        const int n1 = tiled_col_split(M, N, g, gated);
+        if (n1 < N) {
+            hipError_t e = run_tiled_cfg<false>(2, A, W, S, D, C, M, n1, K, g, fuse_delta, st, N);
+            if (e != hipSuccess) return e;
+            // the remaining strips of 16 columns: KT KB each
+            const size_t strip_words = (size_t)(K / KTILE) * 256;
+            return run_tiled_cfg<false>(1, A, W + (size_t)(n1 / NTILE) * strip_words, S + n1,
+                                        D ? D + n1 : nullptr, C + n1, M, N - n1, K, g, fuse_delta, st, N);
+        }
+    }
     if (cfg == 2) {
         const int m1 = tiled_row_split(M, N);
         if (m1 < M) {
